@@ -1,0 +1,15 @@
+"""Exact long-accumulator GEMM for AMD MI355X (gfx950).
+
+The det-train operations (page "det-train", sections "Usage" and "Method"):
+det_gemm, det_gemm_partial, det_combine, det_finalize and the DetLinear
+module.  The kernels live in libdetgemm.so (C ABI: include/detgemm.h); this
+package only marshals torch tensors into it.
+"""
+from ._lib import K_MAX, LSB_EXPONENT, NUM_DIGITS, DetGemmError  # noqa: F401
+from .api import (det_combine, det_finalize, det_gemm, det_gemm_partial,  # noqa: F401
+                  has_nonfinite, round_f32_to_bf16)
+from .linear import DetLinear  # noqa: F401
+
+__all__ = ["det_gemm", "det_gemm_partial", "det_combine", "det_finalize", "DetLinear",
+           "round_f32_to_bf16", "has_nonfinite", "NUM_DIGITS", "LSB_EXPONENT", "K_MAX",
+           "DetGemmError"]

@@ -1,0 +1,69 @@
+"""ctypes binding of libdetgemm.so (the C ABI declared in include/detgemm.h).
+
+Loading fails loudly when the library has not been built: there is no
+fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdetgemm.so")
+
+DET_OK, DET_EINVAL, DET_EKLIMIT, DET_EDTYPE, DET_EHIP = 0, 1, 2, 3, 5
+DET_F32, DET_BF16 = 0, 1
+NUM_DIGITS = 18
+LSB_EXPONENT = -298
+K_MAX = 1 << 19
+
+_lib = None
+
+
+class DetGemmError(RuntimeError):
+    """The HIP runtime reported an error inside the library."""
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+            "(hipcc for gfx950).  There is no fallback implementation.")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, i32, vp, c_int = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int
+    sigs = {
+        "det_num_digits": ([], c_int),
+        "det_lsb_exponent": ([], c_int),
+        "det_k_max": ([], i64),
+        "det_last_error": ([], ctypes.c_char_p),
+        "det_gemm": ([c_int, vp, i64, i64, vp, i64, i64, i64, i64, i64, vp, i64, i64, vp], c_int),
+        "det_gemm_partial": ([c_int, vp, i64, i64, vp, i64, i64, i64, i64, i64, vp, vp], c_int),
+        "det_combine": ([ctypes.POINTER(vp), c_int, vp, i64, vp], c_int),
+        "det_finalize": ([vp, vp, i64, vp], c_int),
+        "det_round_f32_to_bf16": ([vp, vp, i64, vp], c_int),
+        "det_check_finite": ([c_int, vp, i64, i64, i64, i64, vp, vp], c_int),
+    }
+    for name, (args, res) in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    if lib.det_num_digits() != NUM_DIGITS or lib.det_lsb_exponent() != LSB_EXPONENT:
+        raise ImportError("libdetgemm.so layout constants do not match the binding")
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().det_last_error().decode(errors="replace")
+
+
+def check(status: int) -> None:
+    """Map a det_status to a Python exception."""
+    if status == DET_OK:
+        return
+    msg = last_error()
+    if status == DET_EHIP:
+        raise DetGemmError(msg)
+    raise ValueError(msg)

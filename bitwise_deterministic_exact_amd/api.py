@@ -1,0 +1,152 @@
+"""The det-train operations on torch tensors ("Usage" section of the det-train
+page): det_gemm, det_gemm_partial, det_combine, det_finalize.
+
+Argument marshalling only: every step runs in libdetgemm.so's HIP kernels on
+the tensors' device, enqueued on the current torch stream.  torch provides the
+device memory and the stream.
+
+Shapes: x is [M, K], w is [N, K] (any strides, e.g. the K-slices x[:, a:b] or
+transposed views), both float32 or both bfloat16, K <= 2^19.  det_gemm
+returns float32 [M, N]; det_gemm_partial returns the raw long-accumulator
+digits int64 [M, N, 18] (digit j weighs 2^(32j-298)).
+
+Non-finite inputs are rejected with ValueError when ``check_finite`` is true;
+its default comes from the environment variable DETGEMM_CHECK_FINITE ("1",
+the default, or "0").  The check costs one small kernel and a device sync.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.DET_F32, torch.bfloat16: _lib.DET_BF16}
+
+
+def _stream(dev: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _want_check(flag: Optional[bool]) -> bool:
+    if flag is not None:
+        return bool(flag)
+    return os.environ.get("DETGEMM_CHECK_FINITE", "1") != "0"
+
+
+def _operands(x: torch.Tensor, w: torch.Tensor):
+    if not isinstance(x, torch.Tensor) or not isinstance(w, torch.Tensor):
+        raise TypeError("x and w must be tensors")
+    if x.dim() != 2 or w.dim() != 2:
+        raise ValueError("x must be [M, K] and w must be [N, K]")
+    if x.shape[1] != w.shape[1]:
+        raise ValueError(f"K mismatch: x has {x.shape[1]}, w has {w.shape[1]}")
+    if x.dtype != w.dtype or x.dtype not in _DT:
+        raise ValueError(f"x and w must both be float32 or both bfloat16 (got {x.dtype}, {w.dtype})")
+    if x.shape[1] > _lib.K_MAX:
+        raise ValueError(f"K = {x.shape[1]} exceeds the limit 2^19 per call")
+    if x.device.type != "cuda" or w.device != x.device:
+        raise ValueError("x and w must be on the same GPU device")
+    return _DT[x.dtype]
+
+
+def has_nonfinite(t: torch.Tensor) -> bool:
+    """True if a float32/bfloat16 tensor (<= 2-D, any strides) holds Inf or NaN."""
+    if t.dtype not in _DT or t.device.type != "cuda":
+        raise ValueError("has_nonfinite needs a float32/bfloat16 GPU tensor")
+    t2 = t.reshape(1, -1) if t.dim() < 2 else t
+    if t2.dim() != 2:
+        t2 = t2.reshape(-1, t2.shape[-1])
+    flag = torch.zeros(1, dtype=torch.int32, device=t.device)
+    _lib.check(_lib.load().det_check_finite(
+        _DT[t.dtype], ctypes.c_void_p(t2.data_ptr()), t2.shape[0], t2.shape[1],
+        t2.stride(0), t2.stride(1), ctypes.c_void_p(flag.data_ptr()), _stream(t.device)))
+    return bool(flag.item())
+
+
+def _reject_nonfinite(x, w, check_finite):
+    if _want_check(check_finite) and x.numel() and w.numel():
+        if has_nonfinite(x) or has_nonfinite(w):
+            raise ValueError("x or w holds Inf or NaN; the exact accumulator takes finite inputs only")
+
+
+def det_gemm(x: torch.Tensor, w: torch.Tensor, *, check_finite: Optional[bool] = None,
+             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = x w^T with every product exact and one rounding to fp32."""
+    dt = _operands(x, w)
+    _reject_nonfinite(x, w, check_finite)
+    M, K = x.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    elif out.shape != (M, N) or out.dtype != torch.float32 or out.device != x.device:
+        raise ValueError("out must be float32 [M, N] on the operands' device")
+    _lib.check(_lib.load().det_gemm(
+        dt, ctypes.c_void_p(x.data_ptr()), x.stride(0), x.stride(1),
+        ctypes.c_void_p(w.data_ptr()), w.stride(0), w.stride(1), M, N, K,
+        ctypes.c_void_p(out.data_ptr()), out.stride(0), out.stride(1), _stream(x.device)))
+    return out
+
+
+def det_gemm_partial(x: torch.Tensor, w: torch.Tensor, *,
+                     check_finite: Optional[bool] = None) -> torch.Tensor:
+    """Raw long-accumulator digits of x w^T: int64 [M, N, 18]."""
+    dt = _operands(x, w)
+    _reject_nonfinite(x, w, check_finite)
+    M, K = x.shape
+    N = w.shape[0]
+    acc = torch.empty((M, N, _lib.NUM_DIGITS), dtype=torch.int64, device=x.device)
+    _lib.check(_lib.load().det_gemm_partial(
+        dt, ctypes.c_void_p(x.data_ptr()), x.stride(0), x.stride(1),
+        ctypes.c_void_p(w.data_ptr()), w.stride(0), w.stride(1), M, N, K,
+        ctypes.c_void_p(acc.data_ptr()), _stream(x.device)))
+    return acc
+
+
+def _check_acc(a: torch.Tensor, what: str) -> None:
+    if a.dtype != torch.int64 or a.dim() < 1 or a.shape[-1] != _lib.NUM_DIGITS:
+        raise ValueError(f"{what} must be int64 digit arrays [..., 18]")
+    if a.device.type != "cuda":
+        raise ValueError(f"{what} must be on a GPU")
+
+
+def det_combine(parts: Sequence[torch.Tensor]) -> torch.Tensor:
+    """Digit-wise int64 sum of accumulator arrays of equal shape."""
+    parts = list(parts)
+    if not parts:
+        raise ValueError("det_combine needs at least one digit array")
+    for p in parts:
+        _check_acc(p, "det_combine inputs")
+        if p.shape != parts[0].shape or p.device != parts[0].device:
+            raise ValueError("det_combine inputs must share shape and device")
+    parts = [p.contiguous() for p in parts]
+    out = torch.empty_like(parts[0])
+    ptrs = (ctypes.c_void_p * len(parts))(*[p.data_ptr() for p in parts])
+    _lib.check(_lib.load().det_combine(ptrs, len(parts), ctypes.c_void_p(out.data_ptr()),
+                                       out.numel() // _lib.NUM_DIGITS, _stream(out.device)))
+    return out
+
+
+def det_finalize(acc: torch.Tensor) -> torch.Tensor:
+    """Round each accumulator once to fp32: [..., 18] int64 -> [...] float32."""
+    _check_acc(acc, "det_finalize input")
+    acc = acc.contiguous()
+    y = torch.empty(acc.shape[:-1], dtype=torch.float32, device=acc.device)
+    _lib.check(_lib.load().det_finalize(ctypes.c_void_p(acc.data_ptr()), ctypes.c_void_p(y.data_ptr()),
+                                        y.numel(), _stream(acc.device)))
+    return y
+
+
+def round_f32_to_bf16(t: torch.Tensor) -> torch.Tensor:
+    """Round float32 to bfloat16, nearest with ties to even (HIP kernel)."""
+    if t.dtype != torch.float32 or t.device.type != "cuda":
+        raise ValueError("round_f32_to_bf16 needs a float32 GPU tensor")
+    t = t.contiguous()
+    out = torch.empty(t.shape, dtype=torch.bfloat16, device=t.device)
+    _lib.check(_lib.load().det_round_f32_to_bf16(ctypes.c_void_p(t.data_ptr()),
+                                                 ctypes.c_void_p(out.data_ptr()), t.numel(),
+                                                 _stream(t.device)))
+    return out

@@ -1,0 +1,78 @@
+"""DetLinear: a bias-free linear layer whose forward and backward GEMMs are
+exact long-accumulator GEMMs (det-train page, "Usage" section:
+DetLinear(4096, 4096) with a deterministic forward and backward).
+
+forward : y  = x W^T                     (K = in_features), fp32 out
+backward: dY rounded to the parameter dtype (nearest-even) when it is bf16,
+          dX = dY W                      (K = out_features)
+          dW = dY^T x                    (K = tokens)
+Each product is exact and each result is rounded once to fp32; dX and dW are
+then rounded (nearest-even) to the dtypes of x and W.  Every step runs in the
+library's kernels; the transposed operands are strided views, not copies.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from .api import det_gemm, round_f32_to_bf16
+
+
+def _to_dtype(t32: torch.Tensor, dtype: torch.dtype) -> torch.Tensor:
+    if dtype == torch.float32:
+        return t32
+    if dtype == torch.bfloat16:
+        return round_f32_to_bf16(t32)
+    raise ValueError(f"unsupported dtype {dtype}")
+
+
+class _DetLinearFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x: torch.Tensor, weight: torch.Tensor) -> torch.Tensor:
+        x2 = x.reshape(-1, x.shape[-1])
+        y = det_gemm(x2, weight, check_finite=False)
+        ctx.save_for_backward(x2, weight)
+        ctx.x_shape = x.shape
+        return y.reshape(*x.shape[:-1], weight.shape[0])
+
+    @staticmethod
+    def backward(ctx, gy: torch.Tensor):
+        x2, weight = ctx.saved_tensors
+        g32 = gy.reshape(-1, weight.shape[0]).to(torch.float32).contiguous()
+        g = _to_dtype(g32, weight.dtype)
+        dx = dw = None
+        if ctx.needs_input_grad[0]:
+            dx32 = det_gemm(g, weight.t(), check_finite=False)        # [T, in], K = out
+            dx = _to_dtype(dx32, x2.dtype).reshape(ctx.x_shape)
+        if ctx.needs_input_grad[1]:
+            dw32 = det_gemm(g.t(), x2.t(), check_finite=False)        # [out, in], K = T
+            dw = _to_dtype(dw32, weight.dtype)
+        return dx, dw
+
+
+class DetLinear(torch.nn.Module):
+    """y = x W^T with exact accumulation; W is [out_features, in_features]."""
+
+    def __init__(self, in_features: int, out_features: int, bias: bool = False,
+                 device=None, dtype=torch.float32):
+        super().__init__()
+        if bias:
+            raise ValueError("DetLinear has no bias")
+        if dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError("DetLinear supports float32 and bfloat16 parameters")
+        self.in_features, self.out_features = in_features, out_features
+        self.weight = torch.nn.Parameter(torch.empty(out_features, in_features, device=device,
+                                                     dtype=dtype))
+        with torch.no_grad():
+            bound = 1.0 / math.sqrt(in_features)
+            w = torch.empty(out_features, in_features, dtype=torch.float32).uniform_(-bound, bound)
+            self.weight.copy_(w.to(dtype))
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        if x.dtype != self.weight.dtype:
+            raise ValueError(f"input dtype {x.dtype} differs from weight dtype {self.weight.dtype}")
+        return _DetLinearFn.apply(x, self.weight)
+
+    def extra_repr(self) -> str:
+        return f"in_features={self.in_features}, out_features={self.out_features}, bias=False"

@@ -1,0 +1,147 @@
+/*
+ * detgemm.h -- C ABI of the exact long-accumulator GEMM for AMD MI355X (gfx950).
+ *
+ * The operation is the one the det-train page defines ("Method" section):
+ *
+ *     y[m, n] = sum_k x[m, k] * w[n, k]
+ *
+ * where every product is exact, each product's base-2^32 limbs are added with
+ * the product's sign into a per-output Kulisch long accumulator of signed
+ * int64 digits, and the exact sum is rounded once to fp32.  Because the digit
+ * sums are plain integer additions, the bits of every result are independent
+ * of tiling, of how K is split, of the order in which partial accumulators
+ * are added, and of repetition.  The interface follows the page's "Usage"
+ * section (det_gemm, det_gemm_partial, det_combine, det_finalize); its limits
+ * follow "Requirements and limits" (K <= 2^19 per call, bf16 and f32 inputs).
+ *
+ * Accumulator layout (the page states none; this is the library's reading):
+ *   - DET_NUM_DIGITS = 18 signed int64 digits per output, digit j weighs
+ *     2^(32*j - 298).  Digit 0 weighs 2^-298, the smallest nonzero product of
+ *     two fp32 numbers; 18*32 = 576 bits hold every product (< 2^256) with
+ *     headroom for 2^19 of them.
+ *   - Digits are RAW sums: digit j is the sum over products of
+ *     sign(p) * (bits [32j, 32j+32) of |p| * 2^298).  No carries are taken
+ *     before rounding, so the digit arrays of K-slices add up, digit for
+ *     digit, to the digit array of the whole K range.
+ *   - An accumulator array is int64 [rows][cols][18], row-major, digit 0
+ *     first, contiguous.
+ *
+ * Rounding (det_gemm, det_finalize): IEEE 754 binary32 round-to-nearest,
+ * ties to even, gradual underflow, overflow to +-inf.  An exact zero gives
+ * +0.0; a nonzero sum that rounds to zero keeps its sign (-0.0).
+ *
+ * Conventions for every entry point:
+ *   - All data pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates no device memory and keeps none between calls.
+ *   - Strides are in elements, must be >= 0, and may describe transposed or
+ *     sliced views (e.g. x[:, a:b] or x^T).  Operand elements must be
+ *     naturally aligned (4 bytes for f32, 2 for bf16).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously and stream-ordered; nothing here synchronises.
+ *   - Argument errors are reported before anything is enqueued; on error
+ *     nothing is written.  det_last_error() returns a message for the calling
+ *     thread's most recent failure.
+ *   - Inputs must be finite.  Inf or NaN operands never cause an
+ *     out-of-bounds access, but their results are unspecified; callers that
+ *     cannot rule them out run det_check_finite first.
+ */
+#ifndef DETGEMM_H
+#define DETGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DET_NUM_DIGITS 18
+#define DET_LSB_EXPONENT (-298)
+#define DET_K_MAX ((int64_t)1 << 19)
+
+typedef enum {
+  DET_OK = 0,
+  DET_EINVAL = 1,      /* bad pointer, size, stride or count */
+  DET_EKLIMIT = 2,     /* K > 2^19 */
+  DET_EDTYPE = 3,      /* unknown dtype */
+  DET_EHIP = 5         /* the HIP runtime reported an error */
+} det_status;
+
+typedef enum { DET_F32 = 0, DET_BF16 = 1 } det_dtype;
+
+/* Layout constants: 18, -298 and 2^19. */
+int det_num_digits(void);
+int det_lsb_exponent(void);
+int64_t det_k_max(void);
+
+/* Message for the calling thread's last failed call ("" if none). */
+const char* det_last_error(void);
+
+/*
+ * det_gemm -- y = x * w^T, exact, rounded once to fp32 ("Usage" and "Method").
+ *   dt           DET_F32 or DET_BF16 (both operands)
+ *   x            element (m, k) at x[m*x_sm + k*x_sk], m < M, k < K
+ *   w            element (n, k) at w[n*w_sn + k*w_sk], n < N, k < K
+ *   y            fp32 output, element (m, n) at y[m*y_sm + n*y_sn]; must not
+ *                overlap x or w
+ *   M, N, K      sizes; M, N, K >= 0 and K <= 2^19.  K = 0 writes +0.0.
+ * Returns DET_OK, DET_EINVAL, DET_EKLIMIT, DET_EDTYPE or DET_EHIP.
+ */
+det_status det_gemm(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk,
+                    const void* w, int64_t w_sn, int64_t w_sk,
+                    int64_t M, int64_t N, int64_t K,
+                    float* y, int64_t y_sm, int64_t y_sn, void* stream);
+
+/*
+ * det_gemm_partial -- the raw digit array of x * w^T ("Usage": the partial of
+ * a K-slice; "Method": digits of the long accumulator).
+ *   Operands as for det_gemm.  acc is int64 [M][N][18], contiguous, written in
+ *   full (K = 0 writes zeros).  Partials of disjoint K-slices combine with
+ *   det_combine into exactly the partial of their union.
+ */
+det_status det_gemm_partial(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk,
+                            const void* w, int64_t w_sn, int64_t w_sk,
+                            int64_t M, int64_t N, int64_t K,
+                            int64_t* acc, void* stream);
+
+/*
+ * det_combine -- digit-wise int64 sum of accumulator arrays ("Usage" and
+ * "Method": sharded partials compose by adding digit arrays).
+ *   parts        HOST array of `nparts` >= 1 device pointers, each to
+ *                n_outputs*18 int64 digits
+ *   out          device pointer to n_outputs*18 int64; may alias a part
+ *   n_outputs    number of accumulators (>= 0)
+ * Precondition (not checked on the device): every digit sum fits int64 with
+ * room for carries, i.e. |sum| <= 2^62; partials of GEMMs whose K values add
+ * up to at most 2^30 always satisfy it.
+ */
+det_status det_combine(const int64_t* const* parts, int nparts, int64_t* out,
+                       int64_t n_outputs, void* stream);
+
+/*
+ * det_finalize -- round each accumulator once to fp32 ("Method": the exact sum
+ * rounded once to fp32).
+ *   acc          n_outputs*18 int64 digits (any raw digits within +-2^62)
+ *   y            n_outputs fp32 results, contiguous
+ */
+det_status det_finalize(const int64_t* acc, float* y, int64_t n_outputs, void* stream);
+
+/*
+ * det_round_f32_to_bf16 -- round fp32 values to bf16 (nearest, ties to even),
+ * used by the DetLinear backward of the "Usage" section to hand dY to a bf16
+ * exact GEMM.  in: n fp32, out: n bf16 bit patterns; contiguous.  NaN stays NaN.
+ */
+det_status det_round_f32_to_bf16(const float* in, uint16_t* out, int64_t n, void* stream);
+
+/*
+ * det_check_finite -- set *flag (a device int32) to 1 if any element of the
+ * [rows][cols] operand at p[r*s_row + c*s_col] is Inf or NaN; leaves it
+ * untouched otherwise.  The caller zeroes the flag first.
+ */
+det_status det_check_finite(det_dtype dt, const void* p, int64_t rows, int64_t cols,
+                            int64_t s_row, int64_t s_col, int32_t* flag, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DETGEMM_H */

@@ -1,0 +1,110 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point that
+include/detgemm.h declares, and rejects bad arguments before touching a GPU.
+No compute call runs here."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from bitwise_deterministic_exact_amd import _lib
+import bitwise_deterministic_exact_amd as det
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "detgemm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(det_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_pages_entry_points():
+    names = declared_functions()
+    for want in ("det_gemm", "det_gemm_partial", "det_combine", "det_finalize"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} missing from libdetgemm.so"
+
+
+def test_layout_constants():
+    lib = _lib.load()
+    assert lib.det_num_digits() == 18
+    assert lib.det_lsb_exponent() == -298
+    assert lib.det_k_max() == 1 << 19
+
+
+def _call_gemm(dt=0, x=1 << 20, w=1 << 20, M=4, N=4, K=4, y=1 << 20, strides=(4, 1, 4, 1, 4, 1)):
+    lib = _lib.load()
+    xs, xk, ws, wk, ys, yn = strides
+    return lib.det_gemm(dt, ctypes.c_void_p(x), xs, xk, ctypes.c_void_p(w), ws, wk, M, N, K,
+                        ctypes.c_void_p(y), ys, yn, None)
+
+
+def test_c_abi_rejects_bad_arguments_without_a_gpu():
+    # every case fails in host-side validation, before any HIP call
+    assert _call_gemm(K=(1 << 19) + 1) == _lib.DET_EKLIMIT
+    assert "2^19" in _lib.last_error()
+    assert _call_gemm(dt=7) == _lib.DET_EDTYPE
+    assert _call_gemm(M=-1) == _lib.DET_EINVAL
+    assert _call_gemm(x=0) == _lib.DET_EINVAL
+    assert _call_gemm(y=0) == _lib.DET_EINVAL
+    assert _call_gemm(strides=(4, -1, 4, 1, 4, 1)) == _lib.DET_EINVAL
+    assert _call_gemm(x=(1 << 20) + 2) == _lib.DET_EINVAL          # misaligned f32
+    lib = _lib.load()
+    assert lib.det_gemm_partial(0, ctypes.c_void_p(1 << 20), 4, 1, ctypes.c_void_p(1 << 20), 4, 1,
+                                4, 4, 4, None, None) == _lib.DET_EINVAL
+    assert lib.det_combine(None, 0, None, 4, None) == _lib.DET_EINVAL
+    ptrs = (ctypes.c_void_p * 1)(None)
+    assert lib.det_combine(ptrs, 1, ctypes.c_void_p(1 << 20), 4, None) == _lib.DET_EINVAL
+    assert lib.det_finalize(None, None, 5, None) == _lib.DET_EINVAL
+    assert lib.det_finalize(None, None, -1, None) == _lib.DET_EINVAL
+    assert lib.det_round_f32_to_bf16(None, None, 3, None) == _lib.DET_EINVAL
+    assert lib.det_check_finite(9, None, 1, 1, 1, 1, None, None) == _lib.DET_EDTYPE
+
+
+def test_c_abi_empty_problems_are_no_ops():
+    # nothing to do: no launch, status OK even with null pointers
+    lib = _lib.load()
+    assert _call_gemm(M=0, x=0, y=0) == _lib.DET_OK
+    assert _call_gemm(N=0, w=0, y=0) == _lib.DET_OK
+    assert lib.det_finalize(None, None, 0, None) == _lib.DET_OK
+    assert lib.det_round_f32_to_bf16(None, None, 0, None) == _lib.DET_OK
+
+
+def test_python_layer_validates_before_launch():
+    meta = dict(device="meta")
+    x = torch.empty(3, (1 << 19) + 1, dtype=torch.float32, **meta)
+    with pytest.raises(ValueError, match="2\\^19"):
+        det.det_gemm(x, x)
+    with pytest.raises(ValueError, match="K mismatch"):
+        det.det_gemm(torch.empty(3, 4, **meta), torch.empty(3, 5, **meta))
+    with pytest.raises(ValueError, match="float32"):
+        det.det_gemm(torch.empty(3, 4, dtype=torch.float16, **meta),
+                     torch.empty(3, 4, dtype=torch.float16, **meta))
+    with pytest.raises(ValueError, match="float32"):
+        det.det_gemm(torch.empty(3, 4, dtype=torch.float32, **meta),
+                     torch.empty(3, 4, dtype=torch.bfloat16, **meta))
+    with pytest.raises(ValueError):
+        det.det_gemm(torch.empty(3, 4), torch.empty(3, 4))          # CPU tensors
+    with pytest.raises(ValueError):
+        det.det_combine([])
+    with pytest.raises(ValueError):
+        det.det_finalize(torch.empty(3, 17, dtype=torch.int64))
+    with pytest.raises(ValueError):
+        det.DetLinear(4, 4, bias=True)
+
+
+def test_no_cpu_fallback_in_the_product():
+    # the product path never imports the oracle and has no CPU compute path
+    pkg = os.path.join(ROOT, "bitwise_deterministic_exact_amd")
+    for fn in os.listdir(pkg):
+        if fn.endswith(".py"):
+            src = open(os.path.join(pkg, fn)).read()
+            assert "oracle" not in src.replace("oracle_", ""), fn
