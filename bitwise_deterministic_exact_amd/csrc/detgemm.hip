@@ -7,17 +7,10 @@
 // bf16 and f32).  The accumulator layout and rounding are documented in
 // include/detgemm.h.
 //
-// The accumulate step is exact integer work, so it runs on the vector ALUs and
-// the LDS, not on the matrix cores:
-//   * a workgroup of 256 lanes owns a 16x16 tile of outputs, one per lane;
-//   * operands are staged per K-chunk into LDS already decoded into an integer
-//     significand and a packed exponent/sign word;
-//   * every lane keeps its output's digits in LDS as two raw sums per digit
-//     (products of either sign), laid out [slot][lane] so that the 64 lanes of
-//     a wave hit distinct banks; each product's limbs go in with ds_add_u64,
-//     whose address is the only per-lane dynamic index the hardware offers;
-//   * the epilogue subtracts the two sums and either writes the raw digits or
-//     rounds them in registers to fp32.
+// The accumulate step is exact integer work, so it runs on the vector and
+// scalar ALUs and the LDS, not on the matrix cores; the GEMM kernel below
+// describes the work split and the accumulator.  The epilogue either writes
+// the raw digits or rounds them in registers to fp32.
 #include <hip/hip_runtime.h>
 
 #include <stdarg.h>
@@ -30,10 +23,6 @@
 namespace {
 
 constexpr int ND = DET_NUM_DIGITS;   // 18 digits per output
-constexpr int TILE = 16;             // outputs per tile edge
-constexpr int NT = TILE * TILE;      // lanes per workgroup, one output each
-constexpr int KC = 16;               // K values staged per chunk
-constexpr int NSLOT = 2 * ND;        // digit sums of positive and of negative products
 constexpr int COMBINE_MAX = 32;      // parts summed per combine launch
 
 thread_local char g_err[512];
@@ -51,40 +40,8 @@ det_status hip_check(hipError_t e, const char* what) {
   return DET_OK;
 }
 
-// ---------------------------------------------------------------- decode
-//
-// An operand element becomes {m, e}: m is the integer significand (hidden bit
-// included for normal numbers, raw fraction for subnormals, never flushed) and
-// e packs an exponent offset in bits 0..9 and the sign in bit 11.  The
-// offsets are chosen so that for a product of two elements, with
-// sum = e_x + e_w,
-//     o = sum & 1023 = ex + ew + 298
-// is the bit position of the product's least significant bit in the digit
-// array (value = m_x*m_w * 2^(o - 298)), and bit 11 of sum is the product's
-// sign (offsets stay below 1024, so nothing carries into bit 11).
-//   f32 : value = m * 2^(max(E,1) - 150)  ->  offset = max(E,1) - 1
-//   bf16: value = m * 2^(max(E,1) - 134)  ->  offset = max(E,1) + 15
-// For every bit pattern (Inf and NaN included) o <= 540, so the limbs of any
-// product land in digits 0..17: no input can index outside the array.
+// Bit 11 of the packed exponent word carries the sign (see decode below).
 constexpr uint32_t SIGN_BIT = 11;
-
-template <int DT>
-__device__ __forceinline__ uint2 decode_elem(const void* __restrict__ base, int64_t idx, bool valid) {
-  if (!valid) return make_uint2(0u, 0u);
-  if (DT == DET_F32) {
-    const uint32_t b = static_cast<const uint32_t*>(base)[idx];
-    const uint32_t E = (b >> 23) & 0xFFu;
-    const uint32_t m = (b & 0x7FFFFFu) | (min(E, 1u) << 23);
-    const uint32_t e = (max(E, 1u) - 1u) | ((b >> 31) << SIGN_BIT);
-    return make_uint2(m, e);
-  } else {
-    const uint32_t b = static_cast<const uint16_t*>(base)[idx];
-    const uint32_t E = (b >> 7) & 0xFFu;
-    const uint32_t m = (b & 0x7Fu) | (min(E, 1u) << 7);
-    const uint32_t e = (max(E, 1u) + 15u) | ((b >> 15) << SIGN_BIT);
-    return make_uint2(m, e);
-  }
-}
 
 // ---------------------------------------------------------------- rounding
 //
@@ -148,99 +105,284 @@ __device__ uint32_t round_digits_to_f32(const int64_t (&dg)[ND]) {
 }
 
 // ---------------------------------------------------------------- GEMM kernel
+//
+// Work split.  Every workgroup is a single wave that owns a 2 x 64 block of
+// outputs: rows m0 and m0+1, lane l owning column n0+l of both.  There is no
+// cross-wave sharing and so no barrier anywhere in the main loop.  Per 16-wide
+// K-chunk:
+//   * each lane loads its column's 16 raw w elements straight into registers
+//     (vector loads issued one chunk ahead, so their latency hides behind the
+//     current chunk; they are tracked by vmcnt, independent of the LDS
+//     atomics);
+//   * lane l loads and decodes x element k0 + (l mod 16) of both rows, so each
+//     16-lane row of the wave holds the chunk's x values; the operand for step
+//     j is broadcast to the whole wave with a DPP row broadcast of lane j;
+//   * each lane decodes its w element once per k and uses it for both rows.
+//
+// Accumulator.  Each output owns 35 signed 32-bit counters in LDS, one per
+// 16-bit field of the digit array (field q weighs 2^(16q - 298); digit
+// j = field 2j + 2^16 * field 2j+1; products never reach bits >= 2^554, so
+// field 35 would always be zero).  A product at bit offset o = ex + ew + 298
+// is shifted by o mod 16 into a 64-bit T (|T| < 2^63) whose four 16-bit
+// fields are added, each with one ds_add_u32, into counters o/16 .. o/16+3
+// (bf16: |T| < 2^31, two fields).  The LDS address is the only per-lane
+// dynamic index the hardware has, and a 32-bit atomic carrying a 16-bit field
+// costs less LDS time per product than 64-bit limb atomics.  A field is below
+// 2^16 in magnitude, so a counter takes 2^15 adds; every 2^15 k the counters
+// are folded into int64 digits held in registers.
+//
+// Field conventions (template parameter TWOS):
+//   false (det_gemm_partial): the fields of |product| each carry the product's
+//     sign, so digit j is exactly the raw digit of the definition, the sum
+//     over products of sign * bits [32j, 32j+32) of |p| * 2^298.
+//   true (det_gemm): the fields of the signed product in two's complement (top
+//     field signed).  Each product's fields still add up to its exact value,
+//     so the digit array holds the same exact sum and rounds to the same fp32,
+//     with fewer instructions per product.
+//
+// Counter layout: byte address field*512 + row*256 + lane*4, so the 64 lanes
+// always hit 64 distinct banks whatever their fields.
+
+constexpr int V_ROWS = 2;                   // rows per wave = outputs per lane
+constexpr int V_BN = 64;                    // columns per wave (one per lane)
+constexpr int V_KC = 16;                    // K per chunk
+constexpr int NF = 35;                      // 16-bit fields per output
+constexpr int ROW_BYTES = 64 * 4;           // 256
+constexpr int FIELD_BYTES = V_ROWS * ROW_BYTES;   // 512
+constexpr int64_t KFLUSH = int64_t(1) << 15;      // adds a counter can take
+
 struct GemmArgs {
   const void* x; int64_t x_sm, x_sk;
   const void* w; int64_t w_sn, w_sk;
   int64_t M, N, K;
   int64_t tiles_n;
+  int w_vec;                          // w rows contiguous and 16-byte aligned per chunk
   int64_t* acc;                       // partial: [M][N][18]
   float* y; int64_t y_sm, y_sn;       // gemm: fp32 out
 };
 
-// Per-lane digit sums in LDS, byte address
-//     lane*8 + sign*2048 + digit*4096
-// i.e. [digit][sign][lane] with 256 lanes of 8 bytes.  Digit and sign move an
-// address by multiples of 2048 bytes, so the bank a lane hits depends only on
-// the lane: a wave's atomics spread over all banks whatever its digits are.
-constexpr int SIGN_STRIDE = NT * 8;          // 2048 bytes
-constexpr int DIGIT_STRIDE = 2 * NT * 8;     // 4096 bytes
-constexpr int KPAD = KC + 2;                 // staging row pitch (uint2), keeps b128 reads conflict-free
-
-// Add one exact product into the lane's digit sums.
-template <int DT>
-__device__ __forceinline__ void accumulate(char* lds_lane, uint2 xv, uint2 wv) {
-  const uint32_t sum = xv.y + wv.y;
-  const uint32_t s = sum & 31u;                                  // shift inside the digit
-  const uint32_t d = (sum >> 5) & 31u;                           // first digit
-  const uint32_t off = (d << 12) | (sum & (1u << SIGN_BIT));     // digit*4096 + sign*2048
-  unsigned long long* p = reinterpret_cast<unsigned long long*>(lds_lane + off);
-  const uint64_t M = static_cast<uint64_t>(xv.x) * wv.x;         // exact significand product
-  const uint64_t lo = M << s;                                    // limbs 0 and 1
-  atomicAdd(p, static_cast<unsigned long long>(static_cast<uint32_t>(lo)));
-  atomicAdd(p + DIGIT_STRIDE / 8, static_cast<unsigned long long>(lo >> 32));
-  if (DT == DET_F32) {                                           // f32 products reach limb 2
-    const uint64_t l2 = (static_cast<uint64_t>(static_cast<uint32_t>(M >> 32)) << s) >> 32;
-    atomicAdd(p + 2 * DIGIT_STRIDE / 8, static_cast<unsigned long long>(l2));
+// Operand decode: value = (signed) m * 2^(e - bias).  SIDE 0 is x, 1 is w; the
+// exponent offsets are split between the sides so that e_x + e_w is the
+// product's bit offset o = ex + ew + 298 (f32: max(Ex,1) + max(Ew,1) - 2,
+// bf16: max(Ex,1) + max(Ew,1) + 30).  With TWOS the sign is applied to m
+// (two's complement); otherwise m is the magnitude and the sign sits in bit
+// 11 of e, so bit 11 of e_x + e_w is the product's sign.  Subnormals keep
+// their raw fraction and exponent 1: nothing is flushed.  For every bit
+// pattern o <= 540, so no field index leaves 0..34.
+template <int DT, bool TWOS, int SIDE>
+__device__ __forceinline__ void decode(uint32_t b, int32_t& m, uint32_t& e) {
+  uint32_t E, mag, neg;
+  if (DT == DET_F32) {
+    E = (b >> 23) & 0xFFu;
+    mag = (b & 0x7FFFFFu) | (min(E, 1u) << 23);
+    neg = b >> 31;
+  } else {
+    E = (b >> 7) & 0xFFu;
+    mag = (b & 0x7Fu) | (min(E, 1u) << 7);
+    neg = (b >> 15) & 1u;
+  }
+  const uint32_t off = SIDE == 1 ? 0u : (DT == DET_F32 ? static_cast<uint32_t>(-2) : 30u);
+  if (TWOS) {
+    const uint32_t sgn = 0u - neg;
+    m = static_cast<int32_t>((mag ^ sgn) + neg);
+    e = max(E, 1u) + off;
+  } else {
+    m = static_cast<int32_t>(mag);
+    e = max(E, 1u) + off + (neg << SIGN_BIT);
   }
 }
 
-// OUT = 0: write raw digits; OUT = 1: round to fp32.
-template <int DT, int OUT>
-__global__ __launch_bounds__(NT) void k_gemm(GemmArgs a) {
-  __shared__ __align__(16) unsigned long long sums[NSLOT * NT];   // see the layout above
-  __shared__ __align__(16) uint2 xs[TILE][KPAD];     // decoded x chunk [row][k]
-  __shared__ __align__(16) uint2 ws[TILE][KPAD];     // decoded w chunk [col][k]
-
-  const int tid = threadIdx.x;
-  const int ty = tid / TILE, tx = tid % TILE;
-  const int64_t tm = blockIdx.x / a.tiles_n, tn = blockIdx.x % a.tiles_n;
-  const int64_t m0 = tm * TILE, n0 = tn * TILE;
-
-#pragma unroll
-  for (int s = 0; s < NSLOT; ++s) sums[s * NT + tid] = 0ull;
-  char* const lds_lane = reinterpret_cast<char*>(sums) + tid * 8;
-
-  // staging role of this lane: element (row sr, k sc) of the chunk
-  const int sr = tid / KC, sc = tid % KC;
-  const bool xrow_ok = m0 + sr < a.M, wrow_ok = n0 + sr < a.N;
-  const int64_t xrow = xrow_ok ? (m0 + sr) * a.x_sm : 0;
-  const int64_t wrow = wrow_ok ? (n0 + sr) * a.w_sn : 0;
-
-  for (int64_t k0 = 0; k0 < a.K; k0 += KC) {
-    const int64_t k = k0 + sc;
-    const bool kok = k < a.K;
-    xs[sr][sc] = decode_elem<DT>(a.x, xrow + k * a.x_sk, xrow_ok && kok);
-    ws[sr][sc] = decode_elem<DT>(a.w, wrow + k * a.w_sk, wrow_ok && kok);
-    __syncthreads();
-    uint4 xq[KC / 2], wq[KC / 2];                    // the whole chunk in registers
-#pragma unroll
-    for (int i = 0; i < KC / 2; ++i) {
-      xq[i] = *reinterpret_cast<const uint4*>(&xs[ty][2 * i]);
-      wq[i] = *reinterpret_cast<const uint4*>(&ws[tx][2 * i]);
+// one exact product into the counters of one output; `sum` = e_x + e_w
+template <int DT, bool TWOS>
+__device__ __forceinline__ void accumulate(char* lane_row, int32_t xm, int32_t wm, uint32_t sum) {
+  const uint32_t s16 = sum & 15u;                       // shift inside the field
+  int* p = reinterpret_cast<int*>(lane_row + ((sum & 0x3F0u) << 5));   // field o/16
+  constexpr int F = FIELD_BYTES / 4;
+  if (DT == DET_F32) {
+    uint64_t T;
+    if (TWOS) T = static_cast<uint64_t>(static_cast<int64_t>(xm) * wm) << s16;
+    else T = (static_cast<uint64_t>(static_cast<uint32_t>(xm)) * static_cast<uint32_t>(wm)) << s16;
+    const uint32_t lo = static_cast<uint32_t>(T), hi = static_cast<uint32_t>(T >> 32);
+    if (TWOS) {
+      atomicAdd(p, static_cast<int>(lo & 0xFFFFu));
+      atomicAdd(p + F, static_cast<int>(lo >> 16));
+      atomicAdd(p + 2 * F, static_cast<int>(hi & 0xFFFFu));
+      atomicAdd(p + 3 * F, static_cast<int>(hi) >> 16);
+    } else {
+      const uint32_t neg = (sum >> SIGN_BIT) & 1u, msk = 0u - neg;   // (f ^ msk) + neg = +-f
+      atomicAdd(p, static_cast<int>(((lo & 0xFFFFu) ^ msk) + neg));
+      atomicAdd(p + F, static_cast<int>(((lo >> 16) ^ msk) + neg));
+      atomicAdd(p + 2 * F, static_cast<int>(((hi & 0xFFFFu) ^ msk) + neg));
+      atomicAdd(p + 3 * F, static_cast<int>(((hi >> 16) ^ msk) + neg));
     }
-    __syncthreads();                                 // staging buffer free again
-#pragma unroll
-    for (int i = 0; i < KC / 2; ++i) {
-      accumulate<DT>(lds_lane, make_uint2(xq[i].x, xq[i].y), make_uint2(wq[i].x, wq[i].y));
-      accumulate<DT>(lds_lane, make_uint2(xq[i].z, xq[i].w), make_uint2(wq[i].z, wq[i].w));
+  } else {
+    if (TWOS) {
+      const int32_t T = (xm * wm) << s16;               // |T| < 2^31
+      atomicAdd(p, T & 0xFFFF);
+      atomicAdd(p + F, T >> 16);
+    } else {
+      const uint32_t T = (static_cast<uint32_t>(xm) * static_cast<uint32_t>(wm)) << s16;
+      const uint32_t neg = (sum >> SIGN_BIT) & 1u, msk = 0u - neg;
+      atomicAdd(p, static_cast<int>(((T & 0xFFFFu) ^ msk) + neg));
+      atomicAdd(p + F, static_cast<int>(((T >> 16) ^ msk) + neg));
     }
   }
-  __syncthreads();
+}
 
-  const int64_t m = m0 + ty, n = n0 + tx;
-  if (m >= a.M || n >= a.N) return;
-  const unsigned long long* mine = reinterpret_cast<const unsigned long long*>(lds_lane);
-  int64_t dg[ND];
+template <int DT>
+__device__ __forceinline__ uint32_t load_elem(const void* base, int64_t idx) {
+  return DT == DET_F32 ? static_cast<const uint32_t*>(base)[idx]
+                       : static_cast<uint32_t>(static_cast<const uint16_t*>(base)[idx]);
+}
+
+// the lane's 16 raw w elements of chunk k0 (zero beyond K or beyond N)
+template <int DT>
+__device__ __forceinline__ void load_w_chunk(const GemmArgs& a, const void* __restrict__ wg, int64_t wrow,
+                                             bool n_ok, int64_t k0, uint32_t (&wr)[V_KC]) {
+  if (a.w_vec && k0 + V_KC <= a.K) {
+    if (DT == DET_F32) {
+      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(wg) + wrow + k0);
 #pragma unroll
-  for (int j = 0; j < ND; ++j)
-    dg[j] = static_cast<int64_t>(mine[j * (DIGIT_STRIDE / 8)] - mine[j * (DIGIT_STRIDE / 8) + SIGN_STRIDE / 8]);
-  if (OUT == 0) {
-    int64_t* out = a.acc + (m * a.N + n) * ND;
+      for (int i = 0; i < V_KC / 4; ++i) {
+        const uint4 v = p[i];
+        wr[4 * i] = v.x; wr[4 * i + 1] = v.y; wr[4 * i + 2] = v.z; wr[4 * i + 3] = v.w;
+      }
+    } else {
+      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(wg) + wrow + k0);
 #pragma unroll
-    for (int j = 0; j < ND; ++j) out[j] = dg[j];
+      for (int i = 0; i < V_KC / 8; ++i) {
+        const uint4 v = p[i];
+        const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) { wr[8 * i + 2 * t] = q[t] & 0xFFFFu; wr[8 * i + 2 * t + 1] = q[t] >> 16; }
+      }
+    }
   } else {
-    const uint32_t bits = round_digits_to_f32(dg);
-    a.y[m * a.y_sm + n * a.y_sn] = __uint_as_float(bits);
+#pragma unroll
+    for (int i = 0; i < V_KC; ++i) {
+      const int64_t k = min<int64_t>(k0 + i, a.K - 1);
+      wr[i] = load_elem<DT>(wg, wrow + k * a.w_sk);
+    }
+  }
+  if (!n_ok) {
+#pragma unroll
+    for (int i = 0; i < V_KC; ++i) wr[i] = 0u;
+  }
+  if (k0 + V_KC > a.K) {
+#pragma unroll
+    for (int i = 0; i < V_KC; ++i) wr[i] = (k0 + i < a.K) ? wr[i] : 0u;
+  }
+}
+
+// fold the counters of one row into int64 digits and clear them
+__device__ __forceinline__ void fold_row(char* lane_row, int64_t (&dg)[ND]) {
+  int* c = reinterpret_cast<int*>(lane_row);
+  constexpr int F = FIELD_BYTES / 4;
+#pragma unroll
+  for (int j = 0; j < ND; ++j) {
+    const int hi = 2 * j + 1 < NF ? c[(2 * j + 1) * F] : 0;
+    dg[j] += static_cast<int64_t>(c[(2 * j) * F]) + (static_cast<int64_t>(hi) << 16);
+    c[(2 * j) * F] = 0;
+    if (2 * j + 1 < NF) c[(2 * j + 1) * F] = 0;
+  }
+}
+
+template <int J>
+__device__ __forceinline__ int bcast(int v) {     // lane J of each 16-lane row, to the whole row
+  return __builtin_amdgcn_update_dpp(0, v, 0x150 + J, 0xF, 0xF, false);
+}
+
+template <int DT, bool TWOS, int J>
+__device__ __forceinline__ void step(char* lane_base, uint32_t wb, int xm0, int xe0, int xm1, int xe1) {
+  int32_t wm;
+  uint32_t we;
+  decode<DT, TWOS, 1>(wb, wm, we);
+  accumulate<DT, TWOS>(lane_base, bcast<J>(xm0), wm, static_cast<uint32_t>(bcast<J>(xe0)) + we);
+  accumulate<DT, TWOS>(lane_base + ROW_BYTES, bcast<J>(xm1), wm, static_cast<uint32_t>(bcast<J>(xe1)) + we);
+}
+
+template <int DT, bool TWOS, int J>
+__device__ __forceinline__ void steps(char* lane_base, const uint32_t (&wr)[V_KC], int xm0, int xe0, int xm1,
+                                      int xe1) {
+  step<DT, TWOS, J>(lane_base, wr[J], xm0, xe0, xm1, xe1);
+  if constexpr (J + 1 < V_KC) steps<DT, TWOS, J + 1>(lane_base, wr, xm0, xe0, xm1, xe1);
+}
+
+// TWOS = false: write raw digits; TWOS = true: round to fp32.
+template <int DT, bool TWOS>
+__global__ __launch_bounds__(64) void k_gemm(GemmArgs a, const void* __restrict__ xg,
+                                             const void* __restrict__ wg) {
+  __shared__ __align__(16) int counters[NF * V_ROWS * 64];   // 17920 bytes
+
+  const int lane = threadIdx.x;
+  const int64_t tm = blockIdx.x / a.tiles_n, tn = blockIdx.x % a.tiles_n;
+  const int64_t m0 = tm * V_ROWS, n0 = tn * V_BN;
+  char* const lane_base = reinterpret_cast<char*>(counters) + lane * 4;
+
+#pragma unroll
+  for (int q = 0; q < NF * V_ROWS; ++q) counters[q * 64 + lane] = 0;
+
+  const int64_t n = n0 + lane;
+  const bool n_ok = n < a.N;
+  const int64_t wrow = (n_ok ? n : a.N - 1) * a.w_sn;
+  const bool row_ok0 = m0 < a.M, row_ok1 = m0 + 1 < a.M;
+  const int64_t xrow0 = min(m0, a.M - 1) * a.x_sm, xrow1 = min(m0 + 1, a.M - 1) * a.x_sm;
+  const int xj = lane & 15;                       // this lane's k within a chunk (x side)
+
+  int64_t dg0[ND], dg1[ND];
+#pragma unroll
+  for (int j = 0; j < ND; ++j) { dg0[j] = 0; dg1[j] = 0; }
+
+  // chunk 0 operands
+  uint32_t wnext[V_KC];
+  uint32_t xn0 = 0u, xn1 = 0u;
+  if (a.K > 0) {
+    load_w_chunk<DT>(a, wg, wrow, n_ok, 0, wnext);
+    const int64_t k = min<int64_t>(xj, a.K - 1);
+    xn0 = load_elem<DT>(xg, xrow0 + k * a.x_sk);
+    xn1 = load_elem<DT>(xg, xrow1 + k * a.x_sk);
+  }
+
+  for (int64_t k0 = 0; k0 < a.K; k0 += V_KC) {
+    uint32_t wr[V_KC];
+#pragma unroll
+    for (int i = 0; i < V_KC; ++i) wr[i] = wnext[i];
+    uint32_t xb0 = xn0, xb1 = xn1;
+    const bool kin = k0 + xj < a.K;
+    xb0 = (row_ok0 && kin) ? xb0 : 0u;
+    xb1 = (row_ok1 && kin) ? xb1 : 0u;
+    if (k0 + V_KC < a.K) {                        // prefetch the next chunk
+      load_w_chunk<DT>(a, wg, wrow, n_ok, k0 + V_KC, wnext);
+      const int64_t k = min<int64_t>(k0 + V_KC + xj, a.K - 1);
+      xn0 = load_elem<DT>(xg, xrow0 + k * a.x_sk);
+      xn1 = load_elem<DT>(xg, xrow1 + k * a.x_sk);
+    }
+    int32_t xm0, xm1;
+    uint32_t xe0, xe1;
+    decode<DT, TWOS, 0>(xb0, xm0, xe0);
+    decode<DT, TWOS, 0>(xb1, xm1, xe1);
+    steps<DT, TWOS, 0>(lane_base, wr, xm0, static_cast<int>(xe0), xm1, static_cast<int>(xe1));
+    if (a.K > KFLUSH && ((k0 + V_KC) % KFLUSH) == 0) {    // counters near their limit
+      fold_row(lane_base, dg0);
+      fold_row(lane_base + ROW_BYTES, dg1);
+    }
+  }
+  fold_row(lane_base, dg0);
+  fold_row(lane_base + ROW_BYTES, dg1);
+
+  if (!n_ok) return;
+#pragma unroll
+  for (int r = 0; r < V_ROWS; ++r) {
+    const int64_t m = m0 + r;
+    if (m >= a.M) continue;
+    int64_t (&dg)[ND] = r == 0 ? dg0 : dg1;
+    if (!TWOS) {
+      int64_t* out = a.acc + (m * a.N + n) * ND;
+#pragma unroll
+      for (int j = 0; j < ND; ++j) out[j] = dg[j];
+    } else {
+      a.y[m * a.y_sm + n * a.y_sn] = __uint_as_float(round_digits_to_f32(dg));
+    }
   }
 }
 
@@ -320,18 +462,21 @@ det_status check_operands(det_dtype dt, const void* x, int64_t x_sm, int64_t x_s
 }
 
 det_status launch_gemm(det_dtype dt, int out_mode, GemmArgs a, hipStream_t s) {
-  const int64_t tiles_m = (a.M + TILE - 1) / TILE;
-  a.tiles_n = (a.N + TILE - 1) / TILE;
+  const int64_t tiles_m = (a.M + V_ROWS - 1) / V_ROWS;
+  a.tiles_n = (a.N + V_BN - 1) / V_BN;
   const int64_t blocks = tiles_m * a.tiles_n;
   if (blocks == 0) return DET_OK;
   if (blocks > 0x7FFFFFFF) return fail(DET_EINVAL, "too many output tiles");
-  const dim3 grid(static_cast<unsigned>(blocks)), block(NT);
+  // 16-byte vector loads of w chunks: unit K-stride and every chunk start aligned
+  const int64_t esz = dt == DET_F32 ? 4 : 2;
+  a.w_vec = a.w_sk == 1 && (reinterpret_cast<uintptr_t>(a.w) % 16) == 0 && (a.w_sn * esz) % 16 == 0;
+  const dim3 grid(static_cast<unsigned>(blocks)), block(64);
   if (dt == DET_F32) {
-    if (out_mode == 0) hipLaunchKernelGGL((k_gemm<DET_F32, 0>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_gemm<DET_F32, 1>), grid, block, 0, s, a);
+    if (out_mode == 0) hipLaunchKernelGGL((k_gemm<DET_F32, false>), grid, block, 0, s, a, a.x, a.w);
+    else hipLaunchKernelGGL((k_gemm<DET_F32, true>), grid, block, 0, s, a, a.x, a.w);
   } else {
-    if (out_mode == 0) hipLaunchKernelGGL((k_gemm<DET_BF16, 0>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_gemm<DET_BF16, 1>), grid, block, 0, s, a);
+    if (out_mode == 0) hipLaunchKernelGGL((k_gemm<DET_BF16, false>), grid, block, 0, s, a, a.x, a.w);
+    else hipLaunchKernelGGL((k_gemm<DET_BF16, true>), grid, block, 0, s, a, a.x, a.w);
   }
   return hip_check(hipGetLastError(), "gemm launch");
 }
