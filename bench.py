@@ -74,6 +74,8 @@ def main() -> int:
     ap.add_argument("--size", type=int, default=4096, help="M = N = K of the workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-aux", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 256 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -184,6 +186,18 @@ def main() -> int:
         result["aux"] = aux
         log(f"aux: {aux}")
         del pa, pb, acc, yf
+
+    if args.copy_probe:
+        # a plain copy of known size: 256 MiB read + 256 MiB written; its
+        # FETCH_SIZE / WRITE_SIZE readings calibrate those counters
+        src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_probe_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
+        del src, dst
 
     if not args.no_cpu_baseline:
         log("timing the C oracle on the host")

@@ -143,19 +143,17 @@ __device__ uint32_t round_digits_to_f32(const int64_t (&dg)[ND]) {
 // Counter layout: byte address field*512 + row*256 + lane*4, so the 64 lanes
 // always hit 64 distinct banks whatever their fields.
 
-constexpr int V_ROWS = 2;                   // rows per wave = outputs per lane
 constexpr int V_BN = 64;                    // columns per wave (one per lane)
 constexpr int V_KC = 16;                    // K per chunk
 constexpr int NF = 35;                      // 16-bit fields per output
-constexpr int ROW_BYTES = 64 * 4;           // 256
-constexpr int FIELD_BYTES = V_ROWS * ROW_BYTES;   // 512
+constexpr int ROW_BYTES = 64 * 4;           // counters of one row: 64 lanes x 4 bytes
 constexpr int64_t KFLUSH = int64_t(1) << 15;      // adds a counter can take
 
 struct GemmArgs {
   const void* x; int64_t x_sm, x_sk;
   const void* w; int64_t w_sn, w_sk;
   int64_t M, N, K;
-  int64_t tiles_n;
+  int64_t tiles_m, tiles_n;
   int w_vec;                          // w rows contiguous and 16-byte aligned per chunk
   int64_t* acc;                       // partial: [M][N][18]
   float* y; int64_t y_sm, y_sn;       // gemm: fp32 out
@@ -192,12 +190,13 @@ __device__ __forceinline__ void decode(uint32_t b, int32_t& m, uint32_t& e) {
   }
 }
 
-// one exact product into the counters of one output; `sum` = e_x + e_w
-template <int DT, bool TWOS>
+// one exact product into the counters of one output; `sum` = e_x + e_w.
+// Counter byte address: field*(R*256) + row*256 + lane*4.
+template <int DT, bool TWOS, int R>
 __device__ __forceinline__ void accumulate(char* lane_row, int32_t xm, int32_t wm, uint32_t sum) {
+  constexpr int F = R * ROW_BYTES / 4;                  // ints between fields
   const uint32_t s16 = sum & 15u;                       // shift inside the field
-  int* p = reinterpret_cast<int*>(lane_row + ((sum & 0x3F0u) << 5));   // field o/16
-  constexpr int F = FIELD_BYTES / 4;
+  int* p = reinterpret_cast<int*>(lane_row + ((sum >> 4) & 63u) * (R * ROW_BYTES));   // field o/16
   if (DT == DET_F32) {
     uint64_t T;
     if (TWOS) T = static_cast<uint64_t>(static_cast<int64_t>(xm) * wm) << s16;
@@ -275,9 +274,10 @@ __device__ __forceinline__ void load_w_chunk(const GemmArgs& a, const void* __re
 }
 
 // fold the counters of one row into int64 digits and clear them
+template <int R>
 __device__ __forceinline__ void fold_row(char* lane_row, int64_t (&dg)[ND]) {
   int* c = reinterpret_cast<int*>(lane_row);
-  constexpr int F = FIELD_BYTES / 4;
+  constexpr int F = R * ROW_BYTES / 4;
 #pragma unroll
   for (int j = 0; j < ND; ++j) {
     const int hi = 2 * j + 1 < NF ? c[(2 * j + 1) * F] : 0;
@@ -289,99 +289,113 @@ __device__ __forceinline__ void fold_row(char* lane_row, int64_t (&dg)[ND]) {
 
 template <int J>
 __device__ __forceinline__ int bcast(int v) {     // lane J of each 16-lane row, to the whole row
-  return __builtin_amdgcn_update_dpp(0, v, 0x150 + J, 0xF, 0xF, false);
+  return __builtin_amdgcn_mov_dpp(v, 0x150 + J, 0xF, 0xF, true);
 }
 
-template <int DT, bool TWOS, int J>
-__device__ __forceinline__ void step(char* lane_base, uint32_t wb, int xm0, int xe0, int xm1, int xe1) {
+template <int DT, bool TWOS, int R, int J>
+__device__ __forceinline__ void steps(char* lane_base, const uint32_t (&wr)[V_KC], const int (&xm)[R],
+                                      const int (&xe)[R]) {
   int32_t wm;
   uint32_t we;
-  decode<DT, TWOS, 1>(wb, wm, we);
-  accumulate<DT, TWOS>(lane_base, bcast<J>(xm0), wm, static_cast<uint32_t>(bcast<J>(xe0)) + we);
-  accumulate<DT, TWOS>(lane_base + ROW_BYTES, bcast<J>(xm1), wm, static_cast<uint32_t>(bcast<J>(xe1)) + we);
+  decode<DT, TWOS, 1>(wr[J], wm, we);
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    accumulate<DT, TWOS, R>(lane_base + r * ROW_BYTES, bcast<J>(xm[r]), wm,
+                            static_cast<uint32_t>(bcast<J>(xe[r])) + we);
+  if constexpr (J + 1 < V_KC) steps<DT, TWOS, R, J + 1>(lane_base, wr, xm, xe);
 }
 
-template <int DT, bool TWOS, int J>
-__device__ __forceinline__ void steps(char* lane_base, const uint32_t (&wr)[V_KC], int xm0, int xe0, int xm1,
-                                      int xe1) {
-  step<DT, TWOS, J>(lane_base, wr[J], xm0, xe0, xm1, xe1);
-  if constexpr (J + 1 < V_KC) steps<DT, TWOS, J + 1>(lane_base, wr, xm0, xe0, xm1, xe1);
-}
-
-// TWOS = false: write raw digits; TWOS = true: round to fp32.
-template <int DT, bool TWOS>
+// R rows per wave.  TWOS = false: write raw digits; TWOS = true: round to fp32.
+template <int DT, bool TWOS, int R>
 __global__ __launch_bounds__(64) void k_gemm(GemmArgs a, const void* __restrict__ xg,
                                              const void* __restrict__ wg) {
-  __shared__ __align__(16) int counters[NF * V_ROWS * 64];   // 17920 bytes
+  __shared__ __align__(16) int counters[NF * R * 64];   // 8960 * R bytes
 
   const int lane = threadIdx.x;
-  const int64_t tm = blockIdx.x / a.tiles_n, tn = blockIdx.x % a.tiles_n;
-  const int64_t m0 = tm * V_ROWS, n0 = tn * V_BN;
+  // Workgroups are dispatched to the 8 XCDs round-robin, each XCD with its
+  // own L2.  Give every XCD a contiguous range of tiles in column-major tile
+  // order, so the waves resident on one XCD share one 64-column slice of w
+  // (kept in that L2) while they walk down the rows.
+  const int64_t nb = gridDim.x, b = blockIdx.x;
+  const int64_t xcd = b % 8, per = nb / 8, extra = nb % 8;
+  const int64_t tile = xcd * per + min(xcd, extra) + b / 8;
+  const int64_t tn = tile / a.tiles_m, tm = tile % a.tiles_m;
+  const int64_t m0 = tm * R, n0 = tn * V_BN;
   char* const lane_base = reinterpret_cast<char*>(counters) + lane * 4;
 
 #pragma unroll
-  for (int q = 0; q < NF * V_ROWS; ++q) counters[q * 64 + lane] = 0;
+  for (int q = 0; q < NF * R; ++q) counters[q * 64 + lane] = 0;
 
   const int64_t n = n0 + lane;
   const bool n_ok = n < a.N;
   const int64_t wrow = (n_ok ? n : a.N - 1) * a.w_sn;
-  const bool row_ok0 = m0 < a.M, row_ok1 = m0 + 1 < a.M;
-  const int64_t xrow0 = min(m0, a.M - 1) * a.x_sm, xrow1 = min(m0 + 1, a.M - 1) * a.x_sm;
+  bool row_ok[R];
+  int64_t xrow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    row_ok[r] = m0 + r < a.M;
+    xrow[r] = min(m0 + r, a.M - 1) * a.x_sm;
+  }
   const int xj = lane & 15;                       // this lane's k within a chunk (x side)
 
-  int64_t dg0[ND], dg1[ND];
+  int64_t dg[R][ND];
 #pragma unroll
-  for (int j = 0; j < ND; ++j) { dg0[j] = 0; dg1[j] = 0; }
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int j = 0; j < ND; ++j) dg[r][j] = 0;
 
   // chunk 0 operands
   uint32_t wnext[V_KC];
-  uint32_t xn0 = 0u, xn1 = 0u;
+  uint32_t xn[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) xn[r] = 0u;
   if (a.K > 0) {
     load_w_chunk<DT>(a, wg, wrow, n_ok, 0, wnext);
     const int64_t k = min<int64_t>(xj, a.K - 1);
-    xn0 = load_elem<DT>(xg, xrow0 + k * a.x_sk);
-    xn1 = load_elem<DT>(xg, xrow1 + k * a.x_sk);
+#pragma unroll
+    for (int r = 0; r < R; ++r) xn[r] = load_elem<DT>(xg, xrow[r] + k * a.x_sk);
   }
 
   for (int64_t k0 = 0; k0 < a.K; k0 += V_KC) {
     uint32_t wr[V_KC];
 #pragma unroll
     for (int i = 0; i < V_KC; ++i) wr[i] = wnext[i];
-    uint32_t xb0 = xn0, xb1 = xn1;
     const bool kin = k0 + xj < a.K;
-    xb0 = (row_ok0 && kin) ? xb0 : 0u;
-    xb1 = (row_ok1 && kin) ? xb1 : 0u;
+    int xm[R], xe[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      int32_t m;
+      uint32_t e;
+      decode<DT, TWOS, 0>((row_ok[r] && kin) ? xn[r] : 0u, m, e);
+      xm[r] = m;
+      xe[r] = static_cast<int>(e);
+    }
     if (k0 + V_KC < a.K) {                        // prefetch the next chunk
       load_w_chunk<DT>(a, wg, wrow, n_ok, k0 + V_KC, wnext);
       const int64_t k = min<int64_t>(k0 + V_KC + xj, a.K - 1);
-      xn0 = load_elem<DT>(xg, xrow0 + k * a.x_sk);
-      xn1 = load_elem<DT>(xg, xrow1 + k * a.x_sk);
+#pragma unroll
+      for (int r = 0; r < R; ++r) xn[r] = load_elem<DT>(xg, xrow[r] + k * a.x_sk);
     }
-    int32_t xm0, xm1;
-    uint32_t xe0, xe1;
-    decode<DT, TWOS, 0>(xb0, xm0, xe0);
-    decode<DT, TWOS, 0>(xb1, xm1, xe1);
-    steps<DT, TWOS, 0>(lane_base, wr, xm0, static_cast<int>(xe0), xm1, static_cast<int>(xe1));
+    steps<DT, TWOS, R, 0>(lane_base, wr, xm, xe);
     if (a.K > KFLUSH && ((k0 + V_KC) % KFLUSH) == 0) {    // counters near their limit
-      fold_row(lane_base, dg0);
-      fold_row(lane_base + ROW_BYTES, dg1);
+#pragma unroll
+      for (int r = 0; r < R; ++r) fold_row<R>(lane_base + r * ROW_BYTES, dg[r]);
     }
   }
-  fold_row(lane_base, dg0);
-  fold_row(lane_base + ROW_BYTES, dg1);
+#pragma unroll
+  for (int r = 0; r < R; ++r) fold_row<R>(lane_base + r * ROW_BYTES, dg[r]);
 
   if (!n_ok) return;
 #pragma unroll
-  for (int r = 0; r < V_ROWS; ++r) {
+  for (int r = 0; r < R; ++r) {
     const int64_t m = m0 + r;
     if (m >= a.M) continue;
-    int64_t (&dg)[ND] = r == 0 ? dg0 : dg1;
     if (!TWOS) {
       int64_t* out = a.acc + (m * a.N + n) * ND;
 #pragma unroll
-      for (int j = 0; j < ND; ++j) out[j] = dg[j];
+      for (int j = 0; j < ND; ++j) out[j] = dg[r][j];
     } else {
-      a.y[m * a.y_sm + n * a.y_sn] = __uint_as_float(round_digits_to_f32(dg));
+      a.y[m * a.y_sm + n * a.y_sn] = __uint_as_float(round_digits_to_f32(dg[r]));
     }
   }
 }
@@ -461,10 +475,11 @@ det_status check_operands(det_dtype dt, const void* x, int64_t x_sm, int64_t x_s
   return DET_OK;
 }
 
-det_status launch_gemm(det_dtype dt, int out_mode, GemmArgs a, hipStream_t s) {
-  const int64_t tiles_m = (a.M + V_ROWS - 1) / V_ROWS;
+template <int R>
+det_status launch_gemm_rows(det_dtype dt, int out_mode, GemmArgs a, hipStream_t s) {
+  a.tiles_m = (a.M + R - 1) / R;
   a.tiles_n = (a.N + V_BN - 1) / V_BN;
-  const int64_t blocks = tiles_m * a.tiles_n;
+  const int64_t blocks = a.tiles_m * a.tiles_n;
   if (blocks == 0) return DET_OK;
   if (blocks > 0x7FFFFFFF) return fail(DET_EINVAL, "too many output tiles");
   // 16-byte vector loads of w chunks: unit K-stride and every chunk start aligned
@@ -472,13 +487,19 @@ det_status launch_gemm(det_dtype dt, int out_mode, GemmArgs a, hipStream_t s) {
   a.w_vec = a.w_sk == 1 && (reinterpret_cast<uintptr_t>(a.w) % 16) == 0 && (a.w_sn * esz) % 16 == 0;
   const dim3 grid(static_cast<unsigned>(blocks)), block(64);
   if (dt == DET_F32) {
-    if (out_mode == 0) hipLaunchKernelGGL((k_gemm<DET_F32, false>), grid, block, 0, s, a, a.x, a.w);
-    else hipLaunchKernelGGL((k_gemm<DET_F32, true>), grid, block, 0, s, a, a.x, a.w);
+    if (out_mode == 0) hipLaunchKernelGGL((k_gemm<DET_F32, false, R>), grid, block, 0, s, a, a.x, a.w);
+    else hipLaunchKernelGGL((k_gemm<DET_F32, true, R>), grid, block, 0, s, a, a.x, a.w);
   } else {
-    if (out_mode == 0) hipLaunchKernelGGL((k_gemm<DET_BF16, false>), grid, block, 0, s, a, a.x, a.w);
-    else hipLaunchKernelGGL((k_gemm<DET_BF16, true>), grid, block, 0, s, a, a.x, a.w);
+    if (out_mode == 0) hipLaunchKernelGGL((k_gemm<DET_BF16, false, R>), grid, block, 0, s, a, a.x, a.w);
+    else hipLaunchKernelGGL((k_gemm<DET_BF16, true, R>), grid, block, 0, s, a, a.x, a.w);
   }
   return hip_check(hipGetLastError(), "gemm launch");
+}
+
+// Two rows per wave: the 17.9 KB of counters per wave let 8-9 waves share a
+// CU; four rows (one wave per SIMD) measured 40% slower on MI355X.
+det_status launch_gemm(det_dtype dt, int out_mode, GemmArgs a, hipStream_t s) {
+  return launch_gemm_rows<2>(dt, out_mode, a, s);
 }
 
 unsigned grid_for(int64_t n, int64_t per_block, unsigned cap) {
