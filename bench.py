@@ -37,6 +37,25 @@ VALU_PEAK_LANE_OPS = 256 * 64 * 2.4e9
 # digit index, shift, limb split, sign, and one add per limb
 OPS_PER_MAC = {"f32": 10, "bf16": 8}
 HBM_PEAK = 8.0e12
+KERNEL_SOURCE = os.path.join(ROOT, "bitwise_deterministic_exact_amd", "csrc", "detgemm.hip")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "k_gemm_f32_4096_wide.md")
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the GEMM kernel from the committed rocprofv3
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by the copy calibration), or
+    None when the kernel source has changed since the counters were taken."""
+    import hashlib
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            line = next(l for l in f if l.startswith("traffic-record:"))
+        rec = json.loads(line.split(":", 1)[1])
+        with open(KERNEL_SOURCE, "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
+                return None
+        return int((rec["fetch_kib"] * rec["fetch_scale"] + rec["write_kib"] * rec["write_scale"]) * 1024)
+    except (OSError, StopIteration, KeyError, ValueError):
+        return None
 
 
 def log(msg: str) -> None:
@@ -146,7 +165,7 @@ def main() -> int:
                    "M": M, "N": N, "K": K, "inputs": "f32", "output": "f32"},
         "roofline": {"bound": "alu", "achieved": round(achieved / 1e12, 3),
                      "peak": round(VALU_PEAK_LANE_OPS / 1e12, 3), "unit": "Tlane-op/s",
-                     "frac": round(achieved / VALU_PEAK_LANE_OPS, 4), "traffic": None,
+                     "frac": round(achieved / VALU_PEAK_LANE_OPS, 4), "traffic": recorded_traffic(),
                      "ops_per_mac": OPS_PER_MAC["f32"], "kernel": "k_gemm<f32, fp32 out>"},
         "parity": {"sampled_outputs": 256, "bit_exact": parity_ok},
     }
