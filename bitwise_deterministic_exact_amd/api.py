@@ -73,9 +73,20 @@ def _reject_nonfinite(x, w, check_finite):
             raise ValueError("x or w holds Inf or NaN; the exact accumulator takes finite inputs only")
 
 
+def _workspace(dt: int, N: int, K: int, device: torch.device, use: bool):
+    """Scratch for the decoded copy of w (torch's caching allocator provides it)."""
+    nbytes = _lib.load().det_gemm_workspace_bytes(dt, N, K) if use else 0
+    if nbytes <= 0:
+        return None, 0
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
 def det_gemm(x: torch.Tensor, w: torch.Tensor, *, check_finite: Optional[bool] = None,
-             out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """y = x w^T with every product exact and one rounding to fp32."""
+             out: Optional[torch.Tensor] = None, workspace: bool = True) -> torch.Tensor:
+    """y = x w^T with every product exact and one rounding to fp32.
+
+    ``workspace=False`` decodes w inside the GEMM kernel instead of once up
+    front; the result is bit-identical either way."""
     dt = _operands(x, w)
     _reject_nonfinite(x, w, check_finite)
     M, K = x.shape
@@ -84,25 +95,35 @@ def det_gemm(x: torch.Tensor, w: torch.Tensor, *, check_finite: Optional[bool] =
         out = torch.empty((M, N), dtype=torch.float32, device=x.device)
     elif out.shape != (M, N) or out.dtype != torch.float32 or out.device != x.device:
         raise ValueError("out must be float32 [M, N] on the operands' device")
-    _lib.check(_lib.load().det_gemm(
-        dt, ctypes.c_void_p(x.data_ptr()), x.stride(0), x.stride(1),
-        ctypes.c_void_p(w.data_ptr()), w.stride(0), w.stride(1), M, N, K,
-        ctypes.c_void_p(out.data_ptr()), out.stride(0), out.stride(1), _stream(x.device)))
+    lib = _lib.load()
+    ops = (dt, ctypes.c_void_p(x.data_ptr()), x.stride(0), x.stride(1),
+           ctypes.c_void_p(w.data_ptr()), w.stride(0), w.stride(1), M, N, K,
+           ctypes.c_void_p(out.data_ptr()), out.stride(0), out.stride(1))
+    ws, nbytes = _workspace(dt, N, K, x.device, workspace and M > 0)
+    if ws is None:
+        _lib.check(lib.det_gemm(*ops, _stream(x.device)))
+    else:
+        _lib.check(lib.det_gemm_ws(*ops, ctypes.c_void_p(ws.data_ptr()), nbytes, _stream(x.device)))
     return out
 
 
-def det_gemm_partial(x: torch.Tensor, w: torch.Tensor, *,
-                     check_finite: Optional[bool] = None) -> torch.Tensor:
+def det_gemm_partial(x: torch.Tensor, w: torch.Tensor, *, check_finite: Optional[bool] = None,
+                     workspace: bool = True) -> torch.Tensor:
     """Raw long-accumulator digits of x w^T: int64 [M, N, 18]."""
     dt = _operands(x, w)
     _reject_nonfinite(x, w, check_finite)
     M, K = x.shape
     N = w.shape[0]
     acc = torch.empty((M, N, _lib.NUM_DIGITS), dtype=torch.int64, device=x.device)
-    _lib.check(_lib.load().det_gemm_partial(
-        dt, ctypes.c_void_p(x.data_ptr()), x.stride(0), x.stride(1),
-        ctypes.c_void_p(w.data_ptr()), w.stride(0), w.stride(1), M, N, K,
-        ctypes.c_void_p(acc.data_ptr()), _stream(x.device)))
+    lib = _lib.load()
+    ops = (dt, ctypes.c_void_p(x.data_ptr()), x.stride(0), x.stride(1),
+           ctypes.c_void_p(w.data_ptr()), w.stride(0), w.stride(1), M, N, K,
+           ctypes.c_void_p(acc.data_ptr()))
+    ws, nbytes = _workspace(dt, N, K, x.device, workspace and M > 0)
+    if ws is None:
+        _lib.check(lib.det_gemm_partial(*ops, _stream(x.device)))
+    else:
+        _lib.check(lib.det_gemm_partial_ws(*ops, ctypes.c_void_p(ws.data_ptr()), nbytes, _stream(x.device)))
     return acc
 
 

@@ -40,8 +40,10 @@ det_status hip_check(hipError_t e, const char* what) {
   return DET_OK;
 }
 
-// Bit 11 of the packed exponent word carries the sign (see decode below).
-constexpr uint32_t SIGN_BIT = 11;
+// Packed exponent word (see decode below): the exponent offset sits at bits
+// 5..14 and, for raw digits, the sign at bit 15.
+constexpr uint32_t EXP_SHIFT = 5;
+constexpr uint32_t SIGN_BIT = 15;
 
 // ---------------------------------------------------------------- rounding
 //
@@ -155,18 +157,24 @@ struct GemmArgs {
   int64_t M, N, K;
   int64_t tiles_m, tiles_n;
   int w_vec;                          // w rows contiguous and 16-byte aligned per chunk
+  const int32_t* wsig;                // pre-decoded w (workspace): significands [Np][Kp]
+  const uint16_t* wexp;               // pre-decoded w: exponent words [Np][Kp]
+  int64_t wld;                        // Kp, the row pitch of both
   int64_t* acc;                       // partial: [M][N][18]
   float* y; int64_t y_sm, y_sn;       // gemm: fp32 out
 };
 
-// Operand decode: value = (signed) m * 2^(e - bias).  SIDE 0 is x, 1 is w; the
-// exponent offsets are split between the sides so that e_x + e_w is the
-// product's bit offset o = ex + ew + 298 (f32: max(Ex,1) + max(Ew,1) - 2,
-// bf16: max(Ex,1) + max(Ew,1) + 30).  With TWOS the sign is applied to m
-// (two's complement); otherwise m is the magnitude and the sign sits in bit
-// 11 of e, so bit 11 of e_x + e_w is the product's sign.  Subnormals keep
-// their raw fraction and exponent 1: nothing is flushed.  For every bit
-// pattern o <= 540, so no field index leaves 0..34.
+// Operand decode: value = (signed) m * 2^(exponent - bias).  SIDE 0 is x, 1
+// is w; the exponent offsets are split between the sides so that, with
+// sum = e_x + e_w, bits 5..14 of sum hold the product's bit offset
+// o = ex + ew + 298 (f32: max(Ex,1) + max(Ew,1) - 2, bf16: max(Ex,1) +
+// max(Ew,1) + 30).  The shift by 5 lets one bit-field extract give the shift
+// inside a 16-bit field (bits 5..8) and one mask give the field's counter
+// offset (bits 9..14).  With TWOS the sign is applied to m (two's
+// complement); otherwise m is the magnitude and the sign sits in bit 15, so
+// bit 15 of sum is the product's sign.  Subnormals keep their raw fraction
+// and exponent 1: nothing is flushed.  For every bit pattern o <= 540, so no
+// field index leaves 0..34.
 template <int DT, bool TWOS, int SIDE>
 __device__ __forceinline__ void decode(uint32_t b, int32_t& m, uint32_t& e) {
   uint32_t E, mag, neg;
@@ -183,10 +191,10 @@ __device__ __forceinline__ void decode(uint32_t b, int32_t& m, uint32_t& e) {
   if (TWOS) {
     const uint32_t sgn = 0u - neg;
     m = static_cast<int32_t>((mag ^ sgn) + neg);
-    e = max(E, 1u) + off;
+    e = (max(E, 1u) + off) << EXP_SHIFT;
   } else {
     m = static_cast<int32_t>(mag);
-    e = max(E, 1u) + off + (neg << SIGN_BIT);
+    e = ((max(E, 1u) + off) << EXP_SHIFT) + (neg << SIGN_BIT);
   }
 }
 
@@ -195,8 +203,8 @@ __device__ __forceinline__ void decode(uint32_t b, int32_t& m, uint32_t& e) {
 template <int DT, bool TWOS, int R>
 __device__ __forceinline__ void accumulate(char* lane_row, int32_t xm, int32_t wm, uint32_t sum) {
   constexpr int F = R * ROW_BYTES / 4;                  // ints between fields
-  const uint32_t s16 = sum & 15u;                       // shift inside the field
-  int* p = reinterpret_cast<int*>(lane_row + ((sum >> 4) & 63u) * (R * ROW_BYTES));   // field o/16
+  const uint32_t s16 = (sum >> EXP_SHIFT) & 15u;        // shift inside the field
+  int* p = reinterpret_cast<int*>(lane_row + ((sum >> (EXP_SHIFT + 4)) & 63u) * (R * ROW_BYTES));   // field o/16
   if (DT == DET_F32) {
     uint64_t T;
     if (TWOS) T = static_cast<uint64_t>(static_cast<int64_t>(xm) * wm) << s16;
@@ -292,21 +300,47 @@ __device__ __forceinline__ int bcast(int v) {     // lane J of each 16-lane row,
   return __builtin_amdgcn_mov_dpp(v, 0x150 + J, 0xF, 0xF, true);
 }
 
-template <int DT, bool TWOS, int R, int J>
-__device__ __forceinline__ void steps(char* lane_base, const uint32_t (&wr)[V_KC], const int (&xm)[R],
-                                      const int (&xe)[R]) {
+// One K-chunk: step J uses w element J of the lane (raw bits to decode, or,
+// with PRE, a pre-decoded significand and the packed exponent words) and
+// broadcasts x element J of each row from lane J of every 16-lane row.
+template <int DT, bool TWOS, int R, bool PRE, int J>
+__device__ __forceinline__ void steps(char* lane_base, const uint32_t (&wa)[V_KC], const uint32_t (&wb)[V_KC / 2],
+                                      const int (&xm)[R], const int (&xe)[R]) {
   int32_t wm;
   uint32_t we;
-  decode<DT, TWOS, 1>(wr[J], wm, we);
+  if (PRE) {
+    wm = static_cast<int32_t>(wa[J]);
+    we = (J & 1) ? (wb[J / 2] >> 16) : (wb[J / 2] & 0xFFFFu);
+  } else {
+    decode<DT, TWOS, 1>(wa[J], wm, we);
+  }
 #pragma unroll
   for (int r = 0; r < R; ++r)
     accumulate<DT, TWOS, R>(lane_base + r * ROW_BYTES, bcast<J>(xm[r]), wm,
                             static_cast<uint32_t>(bcast<J>(xe[r])) + we);
-  if constexpr (J + 1 < V_KC) steps<DT, TWOS, R, J + 1>(lane_base, wr, xm, xe);
+  if constexpr (J + 1 < V_KC) steps<DT, TWOS, R, PRE, J + 1>(lane_base, wa, wb, xm, xe);
+}
+
+// the lane's pre-decoded w chunk: 16 significands and 16 exponent words
+// (rows padded to the tile and K to the chunk, so no bounds logic)
+__device__ __forceinline__ void load_w_pre(const GemmArgs& a, int64_t n, int64_t k0, uint32_t (&wa)[V_KC],
+                                           uint32_t (&wb)[V_KC / 2]) {
+  const uint4* ps = reinterpret_cast<const uint4*>(a.wsig + n * a.wld + k0);
+  const uint4* pe = reinterpret_cast<const uint4*>(a.wexp + n * a.wld + k0);
+#pragma unroll
+  for (int i = 0; i < V_KC / 4; ++i) {
+    const uint4 v = ps[i];
+    wa[4 * i] = v.x; wa[4 * i + 1] = v.y; wa[4 * i + 2] = v.z; wa[4 * i + 3] = v.w;
+  }
+#pragma unroll
+  for (int i = 0; i < V_KC / 8; ++i) {
+    const uint4 v = pe[i];
+    wb[4 * i] = v.x; wb[4 * i + 1] = v.y; wb[4 * i + 2] = v.z; wb[4 * i + 3] = v.w;
+  }
 }
 
 // R rows per wave.  TWOS = false: write raw digits; TWOS = true: round to fp32.
-template <int DT, bool TWOS, int R>
+template <int DT, bool TWOS, int R, bool PRE>
 __global__ __launch_bounds__(64) void k_gemm(GemmArgs a, const void* __restrict__ xg,
                                              const void* __restrict__ wg) {
   __shared__ __align__(16) int counters[NF * R * 64];   // 8960 * R bytes
@@ -345,21 +379,26 @@ __global__ __launch_bounds__(64) void k_gemm(GemmArgs a, const void* __restrict_
     for (int j = 0; j < ND; ++j) dg[r][j] = 0;
 
   // chunk 0 operands
-  uint32_t wnext[V_KC];
+  uint32_t wnext[V_KC], wbnext[V_KC / 2];
+#pragma unroll
+  for (int i = 0; i < V_KC / 2; ++i) wbnext[i] = 0u;
   uint32_t xn[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) xn[r] = 0u;
   if (a.K > 0) {
-    load_w_chunk<DT>(a, wg, wrow, n_ok, 0, wnext);
+    if (PRE) load_w_pre(a, n, 0, wnext, wbnext);
+    else load_w_chunk<DT>(a, wg, wrow, n_ok, 0, wnext);
     const int64_t k = min<int64_t>(xj, a.K - 1);
 #pragma unroll
     for (int r = 0; r < R; ++r) xn[r] = load_elem<DT>(xg, xrow[r] + k * a.x_sk);
   }
 
   for (int64_t k0 = 0; k0 < a.K; k0 += V_KC) {
-    uint32_t wr[V_KC];
+    uint32_t wr[V_KC], wb[V_KC / 2];
 #pragma unroll
     for (int i = 0; i < V_KC; ++i) wr[i] = wnext[i];
+#pragma unroll
+    for (int i = 0; i < V_KC / 2; ++i) wb[i] = wbnext[i];
     const bool kin = k0 + xj < a.K;
     int xm[R], xe[R];
 #pragma unroll
@@ -371,12 +410,13 @@ __global__ __launch_bounds__(64) void k_gemm(GemmArgs a, const void* __restrict_
       xe[r] = static_cast<int>(e);
     }
     if (k0 + V_KC < a.K) {                        // prefetch the next chunk
-      load_w_chunk<DT>(a, wg, wrow, n_ok, k0 + V_KC, wnext);
+      if (PRE) load_w_pre(a, n, k0 + V_KC, wnext, wbnext);
+      else load_w_chunk<DT>(a, wg, wrow, n_ok, k0 + V_KC, wnext);
       const int64_t k = min<int64_t>(k0 + V_KC + xj, a.K - 1);
 #pragma unroll
       for (int r = 0; r < R; ++r) xn[r] = load_elem<DT>(xg, xrow[r] + k * a.x_sk);
     }
-    steps<DT, TWOS, R, 0>(lane_base, wr, xm, xe);
+    steps<DT, TWOS, R, PRE, 0>(lane_base, wr, wb, xm, xe);
     if (a.K > KFLUSH && ((k0 + V_KC) % KFLUSH) == 0) {    // counters near their limit
 #pragma unroll
       for (int r = 0; r < R; ++r) fold_row<R>(lane_base + r * ROW_BYTES, dg[r]);
@@ -397,6 +437,30 @@ __global__ __launch_bounds__(64) void k_gemm(GemmArgs a, const void* __restrict_
     } else {
       a.y[m * a.y_sm + n * a.y_sn] = __uint_as_float(round_digits_to_f32(dg[r]));
     }
+  }
+}
+
+// ---------------------------------------------------------------- w pre-decode
+// w [N][K] (any strides) -> significands int32 [Np][Kp] and exponent words
+// uint16 [Np][Kp], zero outside N x K: the GEMM kernel then loads w with
+// aligned 16-byte loads and spends no instructions on decoding it.
+struct PredecodeArgs {
+  const void* w; int64_t w_sn, w_sk;
+  int64_t N, K, Np, Kp;
+  int32_t* wsig; uint16_t* wexp;
+};
+
+template <int DT, bool TWOS>
+__global__ __launch_bounds__(256) void k_predecode_w(PredecodeArgs a) {
+  const int64_t total = a.Np * a.Kp;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int64_t n = i / a.Kp, k = i % a.Kp;
+    int32_t m = 0;
+    uint32_t e = 0u;
+    if (n < a.N && k < a.K) decode<DT, TWOS, 1>(load_elem<DT>(a.w, n * a.w_sn + k * a.w_sk), m, e);
+    a.wsig[i] = m;
+    a.wexp[i] = static_cast<uint16_t>(e);
   }
 }
 
@@ -475,8 +539,21 @@ det_status check_operands(det_dtype dt, const void* x, int64_t x_sm, int64_t x_s
   return DET_OK;
 }
 
+unsigned grid_for(int64_t n, int64_t per_block, unsigned cap) {
+  int64_t g = (n + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  return static_cast<unsigned>(g > cap ? cap : g);
+}
+
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+// bytes of the pre-decode workspace for w [N, K]
+int64_t workspace_bytes(int64_t N, int64_t K) {
+  return round_up(N, V_BN) * round_up(K, V_KC) * (4 + 2);
+}
+
 template <int R>
-det_status launch_gemm_rows(det_dtype dt, int out_mode, GemmArgs a, hipStream_t s) {
+det_status launch_gemm_rows(det_dtype dt, int out_mode, GemmArgs a, void* ws, hipStream_t s) {
   a.tiles_m = (a.M + R - 1) / R;
   a.tiles_n = (a.N + V_BN - 1) / V_BN;
   const int64_t blocks = a.tiles_m * a.tiles_n;
@@ -485,27 +562,42 @@ det_status launch_gemm_rows(det_dtype dt, int out_mode, GemmArgs a, hipStream_t 
   // 16-byte vector loads of w chunks: unit K-stride and every chunk start aligned
   const int64_t esz = dt == DET_F32 ? 4 : 2;
   a.w_vec = a.w_sk == 1 && (reinterpret_cast<uintptr_t>(a.w) % 16) == 0 && (a.w_sn * esz) % 16 == 0;
-  const dim3 grid(static_cast<unsigned>(blocks)), block(64);
-  if (dt == DET_F32) {
-    if (out_mode == 0) hipLaunchKernelGGL((k_gemm<DET_F32, false, R>), grid, block, 0, s, a, a.x, a.w);
-    else hipLaunchKernelGGL((k_gemm<DET_F32, true, R>), grid, block, 0, s, a, a.x, a.w);
-  } else {
-    if (out_mode == 0) hipLaunchKernelGGL((k_gemm<DET_BF16, false, R>), grid, block, 0, s, a, a.x, a.w);
-    else hipLaunchKernelGGL((k_gemm<DET_BF16, true, R>), grid, block, 0, s, a, a.x, a.w);
+  const bool pre = ws != nullptr && a.K > 0;
+  if (pre) {
+    PredecodeArgs p{};
+    p.w = a.w; p.w_sn = a.w_sn; p.w_sk = a.w_sk;
+    p.N = a.N; p.K = a.K; p.Np = round_up(a.N, V_BN); p.Kp = round_up(a.K, V_KC);
+    p.wsig = static_cast<int32_t*>(ws);
+    p.wexp = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + p.Np * p.Kp * 4);
+    a.wsig = p.wsig; a.wexp = p.wexp; a.wld = p.Kp;
+    const dim3 pg(grid_for(p.Np * p.Kp, 256, 8192));
+    if (dt == DET_F32) {
+      if (out_mode == 0) hipLaunchKernelGGL((k_predecode_w<DET_F32, false>), pg, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((k_predecode_w<DET_F32, true>), pg, dim3(256), 0, s, p);
+    } else {
+      if (out_mode == 0) hipLaunchKernelGGL((k_predecode_w<DET_BF16, false>), pg, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((k_predecode_w<DET_BF16, true>), pg, dim3(256), 0, s, p);
+    }
+    det_status st = hip_check(hipGetLastError(), "predecode launch");
+    if (st != DET_OK) return st;
   }
+  const dim3 grid(static_cast<unsigned>(blocks)), block(64);
+#define DET_LAUNCH(DTV, TW, PR) hipLaunchKernelGGL((k_gemm<DTV, TW, R, PR>), grid, block, 0, s, a, a.x, a.w)
+  if (dt == DET_F32) {
+    if (out_mode == 0) { if (pre) DET_LAUNCH(DET_F32, false, true); else DET_LAUNCH(DET_F32, false, false); }
+    else { if (pre) DET_LAUNCH(DET_F32, true, true); else DET_LAUNCH(DET_F32, true, false); }
+  } else {
+    if (out_mode == 0) { if (pre) DET_LAUNCH(DET_BF16, false, true); else DET_LAUNCH(DET_BF16, false, false); }
+    else { if (pre) DET_LAUNCH(DET_BF16, true, true); else DET_LAUNCH(DET_BF16, true, false); }
+  }
+#undef DET_LAUNCH
   return hip_check(hipGetLastError(), "gemm launch");
 }
 
 // Two rows per wave: the 17.9 KB of counters per wave let 8-9 waves share a
 // CU; four rows (one wave per SIMD) measured 40% slower on MI355X.
-det_status launch_gemm(det_dtype dt, int out_mode, GemmArgs a, hipStream_t s) {
-  return launch_gemm_rows<2>(dt, out_mode, a, s);
-}
-
-unsigned grid_for(int64_t n, int64_t per_block, unsigned cap) {
-  int64_t g = (n + per_block - 1) / per_block;
-  if (g < 1) g = 1;
-  return static_cast<unsigned>(g > cap ? cap : g);
+det_status launch_gemm(det_dtype dt, int out_mode, GemmArgs a, void* ws, hipStream_t s) {
+  return launch_gemm_rows<2>(dt, out_mode, a, ws, s);
 }
 
 }  // namespace
@@ -518,35 +610,70 @@ int det_lsb_exponent(void) { return DET_LSB_EXPONENT; }
 int64_t det_k_max(void) { return DET_K_MAX; }
 const char* det_last_error(void) { return g_err; }
 
-det_status det_gemm(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk, const void* w, int64_t w_sn,
-                    int64_t w_sk, int64_t M, int64_t N, int64_t K, float* y, int64_t y_sm, int64_t y_sn,
-                    void* stream) {
+namespace {
+
+det_status gemm_common(int out_mode, det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk, const void* w,
+                       int64_t w_sn, int64_t w_sk, int64_t M, int64_t N, int64_t K, float* y, int64_t y_sm,
+                       int64_t y_sn, int64_t* acc, void* ws, size_t ws_bytes, void* stream) {
   det_status st = check_operands(dt, x, x_sm, x_sk, w, w_sn, w_sk, M, N, K);
   if (st != DET_OK) return st;
-  if (M > 0 && N > 0 && y == nullptr) return fail(DET_EINVAL, "null output");
-  if (y_sm < 0 || y_sn < 0) return fail(DET_EINVAL, "negative output stride");
-  if (reinterpret_cast<uintptr_t>(y) & 3u) return fail(DET_EINVAL, "output must be 4-byte aligned");
+  if (out_mode == 1) {
+    if (M > 0 && N > 0 && y == nullptr) return fail(DET_EINVAL, "null output");
+    if (y_sm < 0 || y_sn < 0) return fail(DET_EINVAL, "negative output stride");
+    if (reinterpret_cast<uintptr_t>(y) & 3u) return fail(DET_EINVAL, "output must be 4-byte aligned");
+  } else {
+    if (M > 0 && N > 0 && acc == nullptr) return fail(DET_EINVAL, "null accumulator");
+    if (reinterpret_cast<uintptr_t>(acc) & 7u) return fail(DET_EINVAL, "accumulator must be 8-byte aligned");
+  }
+  if (ws != nullptr) {
+    if (reinterpret_cast<uintptr_t>(ws) & 15u) return fail(DET_EINVAL, "workspace must be 16-byte aligned");
+    if (ws_bytes < static_cast<size_t>(workspace_bytes(N, K)))
+      return fail(DET_EINVAL, "workspace of %zu bytes is smaller than the %lld needed", ws_bytes,
+                  (long long)workspace_bytes(N, K));
+  }
   GemmArgs a{};
   a.x = x; a.x_sm = x_sm; a.x_sk = x_sk;
   a.w = w; a.w_sn = w_sn; a.w_sk = w_sk;
   a.M = M; a.N = N; a.K = K;
   a.y = y; a.y_sm = y_sm; a.y_sn = y_sn;
-  return launch_gemm(dt, 1, a, static_cast<hipStream_t>(stream));
+  a.acc = acc;
+  return launch_gemm(dt, out_mode, a, ws, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+int64_t det_gemm_workspace_bytes(det_dtype dt, int64_t N, int64_t K) {
+  (void)dt;
+  if (N <= 0 || K <= 0) return 0;
+  return workspace_bytes(N, K);
+}
+
+det_status det_gemm(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk, const void* w, int64_t w_sn,
+                    int64_t w_sk, int64_t M, int64_t N, int64_t K, float* y, int64_t y_sm, int64_t y_sn,
+                    void* stream) {
+  return gemm_common(1, dt, x, x_sm, x_sk, w, w_sn, w_sk, M, N, K, y, y_sm, y_sn, nullptr, nullptr, 0, stream);
+}
+
+det_status det_gemm_ws(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk, const void* w, int64_t w_sn,
+                       int64_t w_sk, int64_t M, int64_t N, int64_t K, float* y, int64_t y_sm, int64_t y_sn,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace == nullptr && M > 0 && N > 0 && K > 0) return fail(DET_EINVAL, "null workspace");
+  return gemm_common(1, dt, x, x_sm, x_sk, w, w_sn, w_sk, M, N, K, y, y_sm, y_sn, nullptr, workspace,
+                     workspace_bytes, stream);
 }
 
 det_status det_gemm_partial(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk, const void* w,
                             int64_t w_sn, int64_t w_sk, int64_t M, int64_t N, int64_t K, int64_t* acc,
                             void* stream) {
-  det_status st = check_operands(dt, x, x_sm, x_sk, w, w_sn, w_sk, M, N, K);
-  if (st != DET_OK) return st;
-  if (M > 0 && N > 0 && acc == nullptr) return fail(DET_EINVAL, "null accumulator");
-  if (reinterpret_cast<uintptr_t>(acc) & 7u) return fail(DET_EINVAL, "accumulator must be 8-byte aligned");
-  GemmArgs a{};
-  a.x = x; a.x_sm = x_sm; a.x_sk = x_sk;
-  a.w = w; a.w_sn = w_sn; a.w_sk = w_sk;
-  a.M = M; a.N = N; a.K = K;
-  a.acc = acc;
-  return launch_gemm(dt, 0, a, static_cast<hipStream_t>(stream));
+  return gemm_common(0, dt, x, x_sm, x_sk, w, w_sn, w_sk, M, N, K, nullptr, 0, 0, acc, nullptr, 0, stream);
+}
+
+det_status det_gemm_partial_ws(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk, const void* w,
+                               int64_t w_sn, int64_t w_sk, int64_t M, int64_t N, int64_t K, int64_t* acc,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace == nullptr && M > 0 && N > 0 && K > 0) return fail(DET_EINVAL, "null workspace");
+  return gemm_common(0, dt, x, x_sm, x_sk, w, w_sn, w_sk, M, N, K, nullptr, 0, 0, acc, workspace,
+                     workspace_bytes, stream);
 }
 
 det_status det_combine(const int64_t* const* parts, int nparts, int64_t* out, int64_t n_outputs,

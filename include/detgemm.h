@@ -32,7 +32,8 @@
  *
  * Conventions for every entry point:
  *   - All data pointers are DEVICE pointers owned by the caller.  The library
- *     allocates no device memory and keeps none between calls.
+ *     allocates no device memory and keeps none between calls (the _ws
+ *     variants use memory the caller passes in).
  *   - Strides are in elements, must be >= 0, and may describe transposed or
  *     sliced views (e.g. x[:, a:b] or x^T).  Operand elements must be
  *     naturally aligned (4 bytes for f32, 2 for bf16).
@@ -48,6 +49,7 @@
 #ifndef DETGEMM_H
 #define DETGEMM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -102,6 +104,35 @@ det_status det_gemm_partial(det_dtype dt, const void* x, int64_t x_sm, int64_t x
                             const void* w, int64_t w_sn, int64_t w_sk,
                             int64_t M, int64_t N, int64_t K,
                             int64_t* acc, void* stream);
+
+/*
+ * Workspace variants.  det_gemm_ws and det_gemm_partial_ws compute exactly
+ * what det_gemm and det_gemm_partial compute (bit-identical results) but
+ * first decode w once into a caller-provided device workspace (significands
+ * and exponents of w, rows padded), which saves the GEMM kernel the decode
+ * of every w element in every output tile.
+ *   workspace        device memory, 16-byte aligned, at least
+ *                    det_gemm_workspace_bytes(dt, N, K) bytes; owned by the
+ *                    caller, overwritten by the call, and in use until the
+ *                    call's work on `stream` has finished
+ *   workspace_bytes  its size in bytes
+ * det_gemm_workspace_bytes returns the size needed for w [N, K] (0 when N or
+ * K is 0): 6 * roundup(N, 64) * roundup(K, 16).
+ * Errors as for det_gemm, plus DET_EINVAL for a null, misaligned or too small
+ * workspace.
+ */
+int64_t det_gemm_workspace_bytes(det_dtype dt, int64_t N, int64_t K);
+
+det_status det_gemm_ws(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk,
+                       const void* w, int64_t w_sn, int64_t w_sk,
+                       int64_t M, int64_t N, int64_t K,
+                       float* y, int64_t y_sm, int64_t y_sn,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+det_status det_gemm_partial_ws(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk,
+                               const void* w, int64_t w_sn, int64_t w_sk,
+                               int64_t M, int64_t N, int64_t K, int64_t* acc,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * det_combine -- digit-wise int64 sum of accumulator arrays ("Usage" and

@@ -69,6 +69,22 @@ def test_c_abi_rejects_bad_arguments_without_a_gpu():
     assert lib.det_check_finite(9, None, 1, 1, 1, 1, None, None) == _lib.DET_EDTYPE
 
 
+def test_workspace_size_and_checks():
+    lib = _lib.load()
+    assert lib.det_gemm_workspace_bytes(0, 0, 5) == 0
+    assert lib.det_gemm_workspace_bytes(0, 5, 0) == 0
+    assert lib.det_gemm_workspace_bytes(0, 1, 1) == 6 * 64 * 16
+    assert lib.det_gemm_workspace_bytes(1, 4096, 4096) == 6 * 4096 * 4096
+    assert lib.det_gemm_workspace_bytes(0, 65, 17) == 6 * 128 * 32
+    vp = ctypes.c_void_p
+    args = (0, vp(1 << 20), 4, 1, vp(1 << 20), 4, 1, 4, 4, 4, vp(1 << 20), 4, 1)
+    need = lib.det_gemm_workspace_bytes(0, 4, 4)
+    assert lib.det_gemm_ws(*args, None, need, None) == _lib.DET_EINVAL
+    assert lib.det_gemm_ws(*args, vp((1 << 20) + 8), need, None) == _lib.DET_EINVAL   # misaligned
+    assert lib.det_gemm_ws(*args, vp(1 << 20), need - 1, None) == _lib.DET_EINVAL    # too small
+    assert "workspace" in _lib.last_error()
+
+
 def test_c_abi_empty_problems_are_no_ops():
     # nothing to do: no launch, status OK even with null pointers
     lib = _lib.load()

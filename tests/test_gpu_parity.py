@@ -54,6 +54,25 @@ def test_random_shapes_bit_exact(kind, dt):
         assert np.array_equal(fin, want_y), mismatch_report(fin, want_y)
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_workspace_and_inkernel_decode_agree(dt):
+    # the two ways of decoding w (once into a workspace, or in the GEMM
+    # kernel) against the oracle, on strided and transposed w
+    rng = np.random.default_rng(29 if dt == "f32" else 30)
+    for kind in ("wide", "special", "normal"):
+        announce(f"workspace vs in-kernel decode {kind} {dt}")
+        xb, wb = random_operands(rng, 37, 70, 130, dt, kind)
+        x, w = to_device(xb, dt), to_device(wb, dt)
+        want_d = c_oracle.partial(xb, wb)
+        want_y = c_oracle.finalize(want_d)
+        wt = w.t().contiguous().t()
+        for ww in (w, wt, to_device(np.ascontiguousarray(np.pad(wb, ((0, 0), (3, 0)))), dt)[:, 3:]):
+            for use in (True, False):
+                assert np.array_equal(f32_bits(det.det_gemm(x, ww, workspace=use)), want_y), (use,)
+                got = det.det_gemm_partial(x, ww, workspace=use).cpu().numpy()
+                assert np.array_equal(got, want_d), (use,)
+
+
 def test_small_against_python_oracle():
     rng = np.random.default_rng(21)
     for dt in ("f32", "bf16"):
