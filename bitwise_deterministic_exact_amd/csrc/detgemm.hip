@@ -175,7 +175,7 @@ struct GemmArgs {
 // bit 15 of sum is the product's sign.  Subnormals keep their raw fraction
 // and exponent 1: nothing is flushed.  For every bit pattern o <= 540, so no
 // field index leaves 0..34.
-template <int DT, bool TWOS, int SIDE>
+template <int DT, bool TWOS, int SIDE, uint32_t ESH = EXP_SHIFT>
 __device__ __forceinline__ void decode(uint32_t b, int32_t& m, uint32_t& e) {
   uint32_t E, mag, neg;
   if (DT == DET_F32) {
@@ -191,10 +191,10 @@ __device__ __forceinline__ void decode(uint32_t b, int32_t& m, uint32_t& e) {
   if (TWOS) {
     const uint32_t sgn = 0u - neg;
     m = static_cast<int32_t>((mag ^ sgn) + neg);
-    e = (max(E, 1u) + off) << EXP_SHIFT;
+    e = (max(E, 1u) + off) << ESH;
   } else {
     m = static_cast<int32_t>(mag);
-    e = ((max(E, 1u) + off) << EXP_SHIFT) + (neg << SIGN_BIT);
+    e = ((max(E, 1u) + off) << ESH) + (neg << SIGN_BIT);
   }
 }
 
@@ -232,6 +232,53 @@ __device__ __forceinline__ void accumulate(char* lane_row, int32_t xm, int32_t w
       const uint32_t neg = (sum >> SIGN_BIT) & 1u, msk = 0u - neg;
       atomicAdd(p, static_cast<int>(((T & 0xFFFFu) ^ msk) + neg));
       atomicAdd(p + F, static_cast<int>(((T >> 16) ^ msk) + neg));
+    }
+  }
+}
+
+// 24-bit field grid, used by det_gemm on f32 (two's-complement fields):
+// counter p weighs 2^(24p - 298).  A product at offset o (plain, not shifted)
+// goes to p = o div 24 with shift s = o mod 24; its value T = P * 2^s (P the
+// signed significand product, |P| < 2^48, so |T| < 2^71) splits into fields
+// g0 = bits 0..23 and g1 = bits 24..47 (both >= 0) and the signed
+// g2 = T >> 48.  Three atomics per product instead of four; a counter takes
+// 128 adds (|field| < 2^24) before it must be folded.
+constexpr int NF24 = 24;                    // 24 x 24 = 576 bits
+constexpr int64_t KFLUSH24 = 128;
+
+template <int R>
+__device__ __forceinline__ void accumulate24(char* lane_row, int32_t xm, int32_t wm, uint32_t o) {
+  constexpr int F = R * ROW_BYTES / 4;
+  const uint32_t p = __umulhi(o, 178956971u);           // o div 24 (exact for o < 2^30)
+  const uint32_t s = o - 24u * p;
+  int* ptr = reinterpret_cast<int*>(lane_row + p * (R * ROW_BYTES));
+  const int64_t P = static_cast<int64_t>(xm) * wm;
+  const uint64_t T = static_cast<uint64_t>(P) << s;     // bits 0..63 of P * 2^s
+  const uint32_t lo = static_cast<uint32_t>(T), hi = static_cast<uint32_t>(T >> 32);
+  atomicAdd(ptr, static_cast<int>(lo & 0xFFFFFFu));
+  atomicAdd(ptr + F, static_cast<int>(__builtin_amdgcn_perm(hi, lo, 0x0C050403u)));   // bits 24..47
+  atomicAdd(ptr + 2 * F, static_cast<int>(static_cast<uint64_t>(P >> (48u - s))));    // bits 48..71
+}
+
+// fold the 24 counters of one row into int64 digits (counter p lands at bit
+// 24p = 32*(p*3/4) + 8*(3p mod 4)) and clear them; every `norm` folds, carry
+// the digits so that all but the top one lie in [0, 2^32)
+template <int R>
+__device__ __forceinline__ void fold_row24(char* lane_row, int64_t (&dg)[ND], bool norm) {
+  int* c = reinterpret_cast<int*>(lane_row);
+  constexpr int F = R * ROW_BYTES / 4;
+#pragma unroll
+  for (int p = 0; p < NF24; ++p) {
+    const int bit = 24 * p;
+    dg[bit >> 5] += static_cast<int64_t>(c[p * F]) * (int64_t(1) << (bit & 31));
+    c[p * F] = 0;
+  }
+  if (norm) {
+#pragma unroll
+    for (int j = 0; j + 1 < ND; ++j) {
+      const int64_t carry = dg[j] >> 32;
+      dg[j] -= carry * (int64_t(1) << 32);
+      dg[j + 1] += carry;
     }
   }
 }
@@ -303,7 +350,7 @@ __device__ __forceinline__ int bcast(int v) {     // lane J of each 16-lane row,
 // One K-chunk: step J uses w element J of the lane (raw bits to decode, or,
 // with PRE, a pre-decoded significand and the packed exponent words) and
 // broadcasts x element J of each row from lane J of every 16-lane row.
-template <int DT, bool TWOS, int R, bool PRE, int J>
+template <int DT, bool TWOS, int R, bool PRE, bool G24, int J>
 __device__ __forceinline__ void steps(char* lane_base, const uint32_t (&wa)[V_KC], const uint32_t (&wb)[V_KC / 2],
                                       const int (&xm)[R], const int (&xe)[R]) {
   int32_t wm;
@@ -312,13 +359,15 @@ __device__ __forceinline__ void steps(char* lane_base, const uint32_t (&wa)[V_KC
     wm = static_cast<int32_t>(wa[J]);
     we = (J & 1) ? (wb[J / 2] >> 16) : (wb[J / 2] & 0xFFFFu);
   } else {
-    decode<DT, TWOS, 1>(wa[J], wm, we);
+    decode<DT, TWOS, 1, G24 ? 0u : EXP_SHIFT>(wa[J], wm, we);
   }
 #pragma unroll
-  for (int r = 0; r < R; ++r)
-    accumulate<DT, TWOS, R>(lane_base + r * ROW_BYTES, bcast<J>(xm[r]), wm,
-                            static_cast<uint32_t>(bcast<J>(xe[r])) + we);
-  if constexpr (J + 1 < V_KC) steps<DT, TWOS, R, PRE, J + 1>(lane_base, wa, wb, xm, xe);
+  for (int r = 0; r < R; ++r) {
+    const uint32_t sum = static_cast<uint32_t>(bcast<J>(xe[r])) + we;
+    if (G24) accumulate24<R>(lane_base + r * ROW_BYTES, bcast<J>(xm[r]), wm, sum);
+    else accumulate<DT, TWOS, R>(lane_base + r * ROW_BYTES, bcast<J>(xm[r]), wm, sum);
+  }
+  if constexpr (J + 1 < V_KC) steps<DT, TWOS, R, PRE, G24, J + 1>(lane_base, wa, wb, xm, xe);
 }
 
 // the lane's pre-decoded w chunk: 16 significands and 16 exponent words
@@ -340,10 +389,15 @@ __device__ __forceinline__ void load_w_pre(const GemmArgs& a, int64_t n, int64_t
 }
 
 // R rows per wave.  TWOS = false: write raw digits; TWOS = true: round to fp32.
-template <int DT, bool TWOS, int R, bool PRE>
+// R rows per wave; PRE: w comes pre-decoded from the workspace; G24: the
+// 24-bit field grid (f32 with TWOS only), else 16-bit fields.
+template <int DT, bool TWOS, int R, bool PRE, bool G24>
 __global__ __launch_bounds__(64) void k_gemm(GemmArgs a, const void* __restrict__ xg,
                                              const void* __restrict__ wg) {
-  __shared__ __align__(16) int counters[NF * R * 64];   // 8960 * R bytes
+  static_assert(!G24 || (DT == DET_F32 && TWOS), "the 24-bit grid serves f32 det_gemm only");
+  constexpr int NFG = G24 ? NF24 : NF;
+  constexpr int64_t KF = G24 ? KFLUSH24 : KFLUSH;
+  __shared__ __align__(16) int counters[NFG * R * 64];
 
   const int lane = threadIdx.x;
   // Workgroups are dispatched to the 8 XCDs round-robin, each XCD with its
@@ -358,7 +412,7 @@ __global__ __launch_bounds__(64) void k_gemm(GemmArgs a, const void* __restrict_
   char* const lane_base = reinterpret_cast<char*>(counters) + lane * 4;
 
 #pragma unroll
-  for (int q = 0; q < NF * R; ++q) counters[q * 64 + lane] = 0;
+  for (int q = 0; q < NFG * R; ++q) counters[q * 64 + lane] = 0;
 
   const int64_t n = n0 + lane;
   const bool n_ok = n < a.N;
@@ -405,7 +459,7 @@ __global__ __launch_bounds__(64) void k_gemm(GemmArgs a, const void* __restrict_
     for (int r = 0; r < R; ++r) {
       int32_t m;
       uint32_t e;
-      decode<DT, TWOS, 0>((row_ok[r] && kin) ? xn[r] : 0u, m, e);
+      decode<DT, TWOS, 0, G24 ? 0u : EXP_SHIFT>((row_ok[r] && kin) ? xn[r] : 0u, m, e);
       xm[r] = m;
       xe[r] = static_cast<int>(e);
     }
@@ -416,14 +470,22 @@ __global__ __launch_bounds__(64) void k_gemm(GemmArgs a, const void* __restrict_
 #pragma unroll
       for (int r = 0; r < R; ++r) xn[r] = load_elem<DT>(xg, xrow[r] + k * a.x_sk);
     }
-    steps<DT, TWOS, R, PRE, 0>(lane_base, wr, wb, xm, xe);
-    if (a.K > KFLUSH && ((k0 + V_KC) % KFLUSH) == 0) {    // counters near their limit
+    steps<DT, TWOS, R, PRE, G24, 0>(lane_base, wr, wb, xm, xe);
+    if (a.K > KF && ((k0 + V_KC) % KF) == 0) {    // counters near their limit
+      // (24-bit grid: carry the digits every 16 folds, 2^56 growth per fold)
+      const bool norm = ((k0 + V_KC) % (16 * KF)) == 0;
 #pragma unroll
-      for (int r = 0; r < R; ++r) fold_row<R>(lane_base + r * ROW_BYTES, dg[r]);
+      for (int r = 0; r < R; ++r) {
+        if (G24) fold_row24<R>(lane_base + r * ROW_BYTES, dg[r], norm);
+        else fold_row<R>(lane_base + r * ROW_BYTES, dg[r]);
+      }
     }
   }
 #pragma unroll
-  for (int r = 0; r < R; ++r) fold_row<R>(lane_base + r * ROW_BYTES, dg[r]);
+  for (int r = 0; r < R; ++r) {
+    if (G24) fold_row24<R>(lane_base + r * ROW_BYTES, dg[r], true);
+    else fold_row<R>(lane_base + r * ROW_BYTES, dg[r]);
+  }
 
   if (!n_ok) return;
 #pragma unroll
@@ -450,7 +512,7 @@ struct PredecodeArgs {
   int32_t* wsig; uint16_t* wexp;
 };
 
-template <int DT, bool TWOS>
+template <int DT, bool TWOS, uint32_t ESH>
 __global__ __launch_bounds__(256) void k_predecode_w(PredecodeArgs a) {
   const int64_t total = a.Np * a.Kp;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
@@ -458,7 +520,7 @@ __global__ __launch_bounds__(256) void k_predecode_w(PredecodeArgs a) {
     const int64_t n = i / a.Kp, k = i % a.Kp;
     int32_t m = 0;
     uint32_t e = 0u;
-    if (n < a.N && k < a.K) decode<DT, TWOS, 1>(load_elem<DT>(a.w, n * a.w_sn + k * a.w_sk), m, e);
+    if (n < a.N && k < a.K) decode<DT, TWOS, 1, ESH>(load_elem<DT>(a.w, n * a.w_sn + k * a.w_sk), m, e);
     a.wsig[i] = m;
     a.wexp[i] = static_cast<uint16_t>(e);
   }
@@ -572,23 +634,23 @@ det_status launch_gemm_rows(det_dtype dt, int out_mode, GemmArgs a, void* ws, hi
     a.wsig = p.wsig; a.wexp = p.wexp; a.wld = p.Kp;
     const dim3 pg(grid_for(p.Np * p.Kp, 256, 8192));
     if (dt == DET_F32) {
-      if (out_mode == 0) hipLaunchKernelGGL((k_predecode_w<DET_F32, false>), pg, dim3(256), 0, s, p);
-      else hipLaunchKernelGGL((k_predecode_w<DET_F32, true>), pg, dim3(256), 0, s, p);
+      if (out_mode == 0) hipLaunchKernelGGL((k_predecode_w<DET_F32, false, EXP_SHIFT>), pg, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((k_predecode_w<DET_F32, true, 0>), pg, dim3(256), 0, s, p);
     } else {
-      if (out_mode == 0) hipLaunchKernelGGL((k_predecode_w<DET_BF16, false>), pg, dim3(256), 0, s, p);
-      else hipLaunchKernelGGL((k_predecode_w<DET_BF16, true>), pg, dim3(256), 0, s, p);
+      if (out_mode == 0) hipLaunchKernelGGL((k_predecode_w<DET_BF16, false, EXP_SHIFT>), pg, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((k_predecode_w<DET_BF16, true, EXP_SHIFT>), pg, dim3(256), 0, s, p);
     }
     det_status st = hip_check(hipGetLastError(), "predecode launch");
     if (st != DET_OK) return st;
   }
   const dim3 grid(static_cast<unsigned>(blocks)), block(64);
-#define DET_LAUNCH(DTV, TW, PR) hipLaunchKernelGGL((k_gemm<DTV, TW, R, PR>), grid, block, 0, s, a, a.x, a.w)
+#define DET_LAUNCH(DTV, TW, PR, G) hipLaunchKernelGGL((k_gemm<DTV, TW, R, PR, G>), grid, block, 0, s, a, a.x, a.w)
   if (dt == DET_F32) {
-    if (out_mode == 0) { if (pre) DET_LAUNCH(DET_F32, false, true); else DET_LAUNCH(DET_F32, false, false); }
-    else { if (pre) DET_LAUNCH(DET_F32, true, true); else DET_LAUNCH(DET_F32, true, false); }
+    if (out_mode == 0) { if (pre) DET_LAUNCH(DET_F32, false, true, false); else DET_LAUNCH(DET_F32, false, false, false); }
+    else { if (pre) DET_LAUNCH(DET_F32, true, true, true); else DET_LAUNCH(DET_F32, true, false, true); }
   } else {
-    if (out_mode == 0) { if (pre) DET_LAUNCH(DET_BF16, false, true); else DET_LAUNCH(DET_BF16, false, false); }
-    else { if (pre) DET_LAUNCH(DET_BF16, true, true); else DET_LAUNCH(DET_BF16, true, false); }
+    if (out_mode == 0) { if (pre) DET_LAUNCH(DET_BF16, false, true, false); else DET_LAUNCH(DET_BF16, false, false, false); }
+    else { if (pre) DET_LAUNCH(DET_BF16, true, true, false); else DET_LAUNCH(DET_BF16, true, false, false); }
   }
 #undef DET_LAUNCH
   return hip_check(hipGetLastError(), "gemm launch");

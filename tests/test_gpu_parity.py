@@ -73,6 +73,25 @@ def test_workspace_and_inkernel_decode_agree(dt):
                 assert np.array_equal(got, want_d), (use,)
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_long_k_counter_folds(dt):
+    # K long enough for many counter folds and digit carries inside the
+    # kernels (every 128 k on the 24-bit grid with a carry every 2048 k,
+    # every 2^15 k on the 16-bit grid), all signs and magnitudes
+    rng = np.random.default_rng(33 if dt == "f32" else 34)
+    for kind, K in (("wide", 5000), ("normal", 70001), ("special", 3000)):
+        announce(f"long K {kind} {dt} K={K}")
+        xb, wb = random_operands(rng, 5, 66, K, dt, kind)
+        x, w = to_device(xb, dt), to_device(wb, dt)
+        want_d = c_oracle.partial(xb, wb)
+        want_y = c_oracle.finalize(want_d)
+        for use in (True, False):
+            got_y = f32_bits(det.det_gemm(x, w, workspace=use))
+            assert np.array_equal(got_y, want_y), mismatch_report(got_y, want_y)
+            got_d = det.det_gemm_partial(x, w, workspace=use).cpu().numpy()
+            assert np.array_equal(got_d, want_d), mismatch_report(got_d, want_d)
+
+
 def test_small_against_python_oracle():
     rng = np.random.default_rng(21)
     for dt in ("f32", "bf16"):
