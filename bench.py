@@ -95,6 +95,10 @@ def main() -> int:
     ap.add_argument("--no-aux", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (calibrates HBM byte counters)")
+    ap.add_argument("--workload", default="wide4096",
+                    choices=["wide4096", "bf16cancel", "ksharded", "detlinear"],
+                    help="wide4096 (default, the headline): f32 4096^3 wide range; the others time "
+                         "the bf16 1024^3, the 16-shard K=2^19 and the DetLinear configurations")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -106,6 +110,9 @@ def main() -> int:
     import bitwise_deterministic_exact_amd as det
     from oracle import c_oracle
     from workloads import c3_wide_f32, f32_bits
+
+    if args.workload != "wide4096":
+        return other_workload(args)
 
     n = args.size
     log(f"generating the wide-range f32 workload {n}^3 (seed 2)")
@@ -225,6 +232,108 @@ def main() -> int:
 
     print(json.dumps(result), flush=True)
     return 0 if parity_ok else 1
+
+
+def _timed(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
+
+
+def other_workload(args) -> int:
+    """The other configurations: one JSON line each with their throughput and
+    a parity check (full or sampled) against the C oracle."""
+    import torch
+    import bitwise_deterministic_exact_amd as det
+    from oracle import c_oracle
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    threads = min(os.cpu_count() or 1, 16)
+    rng = np.random.default_rng(99)
+    out = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "data": "synthetic"}
+
+    def to_dev(bits, dt):
+        if dt == "f32":
+            return torch.from_numpy(bits.view(np.float32)).to(dev)
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def bits32(t):
+        return t.cpu().contiguous().view(torch.int32).numpy().view(np.uint32)
+
+    if args.workload == "bf16cancel":
+        wl = W.c2_bf16_cancel()
+        xb, wb = wl.bits()
+        x, w = to_dev(xb, "bf16"), to_dev(wb, "bf16")
+        y = torch.empty(1024, 1024, dtype=torch.float32, device=dev)
+        ms = _timed(lambda: det.det_gemm(x, w, check_finite=False, out=y), args.steps, args.warmup)
+        ok = bool(np.array_equal(bits32(y), c_oracle.gemm(xb, wb, nthreads=threads)))
+        macs = 1024 ** 3
+        out.update(metric="exact-GEMM GMAC/s (bf16 1024^3, 10% negated w columns)",
+                   value=round(macs / (ms * 1e-3) / 1e9, 2), unit="GMAC/s", ms_per_step=round(ms, 4),
+                   dtype="int64", parity={"outputs": "all 1024^2", "bit_exact": ok},
+                   config={"workload": wl.name + ", seed 1", "M": 1024, "N": 1024, "K": 1024})
+    elif args.workload == "ksharded":
+        wl = W.c4_ksharded_f32()
+        xb, wb = wl.bits()
+        x, w = to_dev(xb, "f32"), to_dev(wb, "f32")
+        K = x.shape[1]
+        bounds = W.shard_bounds(K, wl.cuts)
+
+        def sharded():
+            parts = [det.det_gemm_partial(x[:, a:b], w[:, a:b], check_finite=False) for a, b in bounds]
+            return det.det_finalize(W.apply_fold(parts, wl.fold, det.det_combine))
+
+        y_s = sharded()
+        y_u = det.det_gemm(x, w, check_finite=False)
+        same = bool(torch.equal(y_s.view(torch.int32), y_u.view(torch.int32)))
+        rows, cols = rng.integers(0, 2048, 16), rng.integers(0, 2048, 16)
+        ok = same and bool(np.array_equal(bits32(y_u)[rows, cols],
+                                          c_oracle.gemm_pairs(xb, wb, rows, cols, nthreads=threads)))
+        steps = max(1, min(args.steps, 3))
+        ms_s = _timed(sharded, steps, 0)
+        ms_u = _timed(lambda: det.det_gemm(x, w, check_finite=False), steps, 0)
+        macs = 2048 * 2048 * K
+        out.update(metric="exact-GEMM GMAC/s (f32 2048^2 x K=2^19, 16 K-shards composed by a fold tree)",
+                   value=round(macs / (ms_s * 1e-3) / 1e9, 2), unit="GMAC/s", ms_per_step=round(ms_s, 3),
+                   steps=steps, warmup=0, dtype="int64",
+                   unsharded={"ms": round(ms_u, 3), "GMAC/s": round(macs / (ms_u * 1e-3) / 1e9, 2)},
+                   parity={"sharded_equals_unsharded": same, "sampled_outputs": 16, "bit_exact": ok},
+                   config={"workload": wl.name + ", seed 3", "M": 2048, "N": 2048, "K": K})
+    else:
+        wl = W.c5_detlinear_bf16()
+        layer = det.DetLinear(4096, 4096, device=dev, dtype=torch.bfloat16)
+        with torch.no_grad():
+            layer.weight.copy_(to_dev(wl.w, "bf16"))
+        x = to_dev(wl.x, "bf16").requires_grad_(True)
+
+        def step():
+            x.grad = None
+            layer.weight.grad = None
+            layer(x).square().mean().backward()
+
+        ms = _timed(step, args.steps, args.warmup)
+        y = layer(x).detach()
+        rows, cols = rng.integers(0, 8192, 64), rng.integers(0, 4096, 64)
+        ok = bool(np.array_equal(bits32(y)[rows, cols],
+                                 c_oracle.gemm_pairs(wl.x, wl.w, rows, cols, nthreads=threads)))
+        macs = 3 * 8192 * 4096 * 4096
+        out.update(metric="DetLinear 4096->4096 bf16 fwd+bwd, 8192 tokens: exact-GEMM GMAC/s",
+                   value=round(macs / (ms * 1e-3) / 1e9, 2), unit="GMAC/s", ms_per_step=round(ms, 3),
+                   tokens_per_s=round(8192 / (ms * 1e-3), 1), dtype="int64",
+                   parity={"sampled_forward_outputs": 64, "bit_exact": ok},
+                   config={"workload": wl.name + ", seed 4", "tokens": 8192, "in": 4096, "out": 4096})
+    print(json.dumps(out), flush=True)
+    return 0 if out["parity"].get("bit_exact", False) else 1
 
 
 if __name__ == "__main__":

@@ -40,7 +40,7 @@ def load() -> ctypes.CDLL:
         "det_last_error": ([], ctypes.c_char_p),
         "det_gemm": ([c_int, vp, i64, i64, vp, i64, i64, i64, i64, i64, vp, i64, i64, vp], c_int),
         "det_gemm_partial": ([c_int, vp, i64, i64, vp, i64, i64, i64, i64, i64, vp, vp], c_int),
-        "det_gemm_workspace_bytes": ([c_int, i64, i64], i64),
+        "det_gemm_workspace_bytes": ([c_int, c_int, i64, i64, i64], i64),
         "det_gemm_ws": ([c_int, vp, i64, i64, vp, i64, i64, i64, i64, i64, vp, i64, i64, vp, ctypes.c_size_t,
                          vp], c_int),
         "det_gemm_partial_ws": ([c_int, vp, i64, i64, vp, i64, i64, i64, i64, i64, vp, vp, ctypes.c_size_t, vp],

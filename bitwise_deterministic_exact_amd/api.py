@@ -73,9 +73,10 @@ def _reject_nonfinite(x, w, check_finite):
             raise ValueError("x or w holds Inf or NaN; the exact accumulator takes finite inputs only")
 
 
-def _workspace(dt: int, N: int, K: int, device: torch.device, use: bool):
-    """Scratch for the decoded copy of w (torch's caching allocator provides it)."""
-    nbytes = _lib.load().det_gemm_workspace_bytes(dt, N, K) if use else 0
+def _workspace(dt: int, partial: bool, M: int, N: int, K: int, device: torch.device, use: bool):
+    """Scratch for the decoded copy of w and, for long K, the carried digits
+    (torch's caching allocator provides it)."""
+    nbytes = _lib.load().det_gemm_workspace_bytes(dt, int(partial), M, N, K) if use else 0
     if nbytes <= 0:
         return None, 0
     return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
@@ -99,7 +100,7 @@ def det_gemm(x: torch.Tensor, w: torch.Tensor, *, check_finite: Optional[bool] =
     ops = (dt, ctypes.c_void_p(x.data_ptr()), x.stride(0), x.stride(1),
            ctypes.c_void_p(w.data_ptr()), w.stride(0), w.stride(1), M, N, K,
            ctypes.c_void_p(out.data_ptr()), out.stride(0), out.stride(1))
-    ws, nbytes = _workspace(dt, N, K, x.device, workspace and M > 0)
+    ws, nbytes = _workspace(dt, False, M, N, K, x.device, workspace)
     if ws is None:
         _lib.check(lib.det_gemm(*ops, _stream(x.device)))
     else:
@@ -119,7 +120,7 @@ def det_gemm_partial(x: torch.Tensor, w: torch.Tensor, *, check_finite: Optional
     ops = (dt, ctypes.c_void_p(x.data_ptr()), x.stride(0), x.stride(1),
            ctypes.c_void_p(w.data_ptr()), w.stride(0), w.stride(1), M, N, K,
            ctypes.c_void_p(acc.data_ptr()))
-    ws, nbytes = _workspace(dt, N, K, x.device, workspace and M > 0)
+    ws, nbytes = _workspace(dt, True, M, N, K, x.device, workspace)
     if ws is None:
         _lib.check(lib.det_gemm_partial(*ops, _stream(x.device)))
     else:

@@ -157,11 +157,12 @@ struct GemmArgs {
   int64_t M, N, K;
   int64_t tiles_m, tiles_n;
   int w_vec;                          // w rows contiguous and 16-byte aligned per chunk
-  const int32_t* wsig;                // pre-decoded w (workspace): significands [Np][Kp]
-  const uint16_t* wexp;               // pre-decoded w: exponent words [Np][Kp]
-  int64_t wld;                        // Kp, the row pitch of both
-  int64_t* acc;                       // partial: [M][N][18]
+  const int32_t* wsig;                // pre-decoded w (workspace): significands [Kp/16][Np][16]
+  const uint16_t* wexp;               // pre-decoded w: exponent words [Kp/16][Np][16]
+  int64_t wld;                        // Np * 16, the chunk pitch of both
+  int64_t* acc;                       // digits [M][N][18]: the partial's output, or scratch
   float* y; int64_t y_sm, y_sn;       // gemm: fp32 out
+  int epi;                            // epilogue, see EPI_* below
 };
 
 // Operand decode: value = (signed) m * 2^(exponent - bias).  SIDE 0 is x, 1
@@ -371,11 +372,14 @@ __device__ __forceinline__ void steps(char* lane_base, const uint32_t (&wa)[V_KC
 }
 
 // the lane's pre-decoded w chunk: 16 significands and 16 exponent words
-// (rows padded to the tile and K to the chunk, so no bounds logic)
+// (rows padded to the tile and K to the chunk, so no bounds logic).  The
+// workspace is chunk-major, so a wave's 64 lanes read one contiguous 4 KiB
+// of significands and 2 KiB of exponents, whatever the length of K.
 __device__ __forceinline__ void load_w_pre(const GemmArgs& a, int64_t n, int64_t k0, uint32_t (&wa)[V_KC],
                                            uint32_t (&wb)[V_KC / 2]) {
-  const uint4* ps = reinterpret_cast<const uint4*>(a.wsig + n * a.wld + k0);
-  const uint4* pe = reinterpret_cast<const uint4*>(a.wexp + n * a.wld + k0);
+  const int64_t off = (k0 / V_KC) * a.wld + n * V_KC;
+  const uint4* ps = reinterpret_cast<const uint4*>(a.wsig + off);
+  const uint4* pe = reinterpret_cast<const uint4*>(a.wexp + off);
 #pragma unroll
   for (int i = 0; i < V_KC / 4; ++i) {
     const uint4 v = ps[i];
@@ -389,6 +393,13 @@ __device__ __forceinline__ void load_w_pre(const GemmArgs& a, int64_t n, int64_t
 }
 
 // R rows per wave.  TWOS = false: write raw digits; TWOS = true: round to fp32.
+// Epilogues.  A K range longer than one block is run as several launches
+// that carry the exact digits from one to the next (see launch_gemm_rows).
+constexpr int EPI_ROUND = 0;        // round the digits to fp32 into y
+constexpr int EPI_STORE = 1;        // write the digits to acc
+constexpr int EPI_ADD = 2;          // add acc's digits, write them back
+constexpr int EPI_ADD_ROUND = 3;    // add acc's digits, round to fp32 into y
+
 // R rows per wave; PRE: w comes pre-decoded from the workspace; G24: the
 // 24-bit field grid (f32 with TWOS only), else 16-bit fields.
 template <int DT, bool TWOS, int R, bool PRE, bool G24>
@@ -492,10 +503,14 @@ __global__ __launch_bounds__(64) void k_gemm(GemmArgs a, const void* __restrict_
   for (int r = 0; r < R; ++r) {
     const int64_t m = m0 + r;
     if (m >= a.M) continue;
-    if (!TWOS) {
-      int64_t* out = a.acc + (m * a.N + n) * ND;
+    int64_t* d = a.acc + (m * a.N + n) * ND;
+    if (a.epi == EPI_ADD || a.epi == EPI_ADD_ROUND) {
 #pragma unroll
-      for (int j = 0; j < ND; ++j) out[j] = dg[r][j];
+      for (int j = 0; j < ND; ++j) dg[r][j] += d[j];
+    }
+    if (a.epi == EPI_STORE || a.epi == EPI_ADD) {
+#pragma unroll
+      for (int j = 0; j < ND; ++j) d[j] = dg[r][j];
     } else {
       a.y[m * a.y_sm + n * a.y_sn] = __uint_as_float(round_digits_to_f32(dg[r]));
     }
@@ -503,9 +518,13 @@ __global__ __launch_bounds__(64) void k_gemm(GemmArgs a, const void* __restrict_
 }
 
 // ---------------------------------------------------------------- w pre-decode
-// w [N][K] (any strides) -> significands int32 [Np][Kp] and exponent words
-// uint16 [Np][Kp], zero outside N x K: the GEMM kernel then loads w with
-// aligned 16-byte loads and spends no instructions on decoding it.
+// w [N][K] (any strides) -> significands int32 and exponent words uint16,
+// both [Kp/16][Np][16] (chunk-major: the 16 k of one chunk of row n are
+// contiguous, rows follow each other), zero outside N x K.  The GEMM kernel
+// then loads w with aligned 16-byte loads, coalesced across the wave, and
+// spends no instructions on decoding it.  (Row-major [Np][Kp] put each lane
+// of a wave in its own 2 MiB page once K reached 2^19, and the GEMM ran at
+// half speed.)
 struct PredecodeArgs {
   const void* w; int64_t w_sn, w_sk;
   int64_t N, K, Np, Kp;
@@ -517,7 +536,8 @@ __global__ __launch_bounds__(256) void k_predecode_w(PredecodeArgs a) {
   const int64_t total = a.Np * a.Kp;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
-    const int64_t n = i / a.Kp, k = i % a.Kp;
+    const int64_t c = i / (a.Np * V_KC), r = i % (a.Np * V_KC);
+    const int64_t n = r / V_KC, k = c * V_KC + r % V_KC;
     int32_t m = 0;
     uint32_t e = 0u;
     if (n < a.N && k < a.K) decode<DT, TWOS, 1, ESH>(load_elem<DT>(a.w, n * a.w_sn + k * a.w_sk), m, e);
@@ -609,9 +629,19 @@ unsigned grid_for(int64_t n, int64_t per_block, unsigned cap) {
 
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
-// bytes of the pre-decode workspace for w [N, K]
-int64_t workspace_bytes(int64_t N, int64_t K) {
-  return round_up(N, V_BN) * round_up(K, V_KC) * (4 + 2);
+// K per launch.  With a longer K range the waves resident on one XCD drift
+// apart in k and stop sharing their slice of w in L2 (measured: 2400 GMAC/s at
+// K = 2^15, 824 at K = 2^19 in one launch), so longer ranges run as several
+// launches of this length that carry the exact digits between them.
+constexpr int64_t K_BLOCK = int64_t(1) << 15;
+
+// workspace: the pre-decoded w, then (det_gemm with K > K_BLOCK) int64
+// digit scratch for the output
+int64_t predecode_bytes(int64_t N, int64_t K) { return round_up(N, V_BN) * round_up(K, V_KC) * (4 + 2); }
+int64_t workspace_bytes(int out_mode, int64_t M, int64_t N, int64_t K) {
+  int64_t b = predecode_bytes(N, K);
+  if (out_mode == 1 && K > K_BLOCK) b += M * N * ND * 8;
+  return b;
 }
 
 template <int R>
@@ -631,7 +661,7 @@ det_status launch_gemm_rows(det_dtype dt, int out_mode, GemmArgs a, void* ws, hi
     p.N = a.N; p.K = a.K; p.Np = round_up(a.N, V_BN); p.Kp = round_up(a.K, V_KC);
     p.wsig = static_cast<int32_t*>(ws);
     p.wexp = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + p.Np * p.Kp * 4);
-    a.wsig = p.wsig; a.wexp = p.wexp; a.wld = p.Kp;
+    a.wsig = p.wsig; a.wexp = p.wexp; a.wld = p.Np * V_KC;
     const dim3 pg(grid_for(p.Np * p.Kp, 256, 8192));
     if (dt == DET_F32) {
       if (out_mode == 0) hipLaunchKernelGGL((k_predecode_w<DET_F32, false, EXP_SHIFT>), pg, dim3(256), 0, s, p);
@@ -644,16 +674,34 @@ det_status launch_gemm_rows(det_dtype dt, int out_mode, GemmArgs a, void* ws, hi
     if (st != DET_OK) return st;
   }
   const dim3 grid(static_cast<unsigned>(blocks)), block(64);
-#define DET_LAUNCH(DTV, TW, PR, G) hipLaunchKernelGGL((k_gemm<DTV, TW, R, PR, G>), grid, block, 0, s, a, a.x, a.w)
-  if (dt == DET_F32) {
-    if (out_mode == 0) { if (pre) DET_LAUNCH(DET_F32, false, true, false); else DET_LAUNCH(DET_F32, false, false, false); }
-    else { if (pre) DET_LAUNCH(DET_F32, true, true, true); else DET_LAUNCH(DET_F32, true, false, true); }
-  } else {
-    if (out_mode == 0) { if (pre) DET_LAUNCH(DET_BF16, false, true, false); else DET_LAUNCH(DET_BF16, false, false, false); }
-    else { if (pre) DET_LAUNCH(DET_BF16, true, true, false); else DET_LAUNCH(DET_BF16, true, false, false); }
+#define DET_LAUNCH(DTV, TW, PR, G) hipLaunchKernelGGL((k_gemm<DTV, TW, R, PR, G>), grid, block, 0, s, b, xb, a.w)
+  // K blocks (one block without a workspace, or when K is short)
+  const int64_t kblk = pre ? K_BLOCK : a.K;
+  const int64_t nblk = a.K > 0 ? (a.K + kblk - 1) / kblk : 1;
+  const int64_t esx = dt == DET_F32 ? 4 : 2;
+  if (out_mode == 1 && nblk > 1)                  // digit scratch behind the decoded w
+    a.acc = reinterpret_cast<int64_t*>(static_cast<char*>(ws) + predecode_bytes(a.N, a.K));
+  for (int64_t ib = 0; ib < nblk; ++ib) {
+    GemmArgs b = a;
+    const int64_t k0 = ib * kblk;
+    b.K = min(kblk, a.K - k0);
+    const void* xb = static_cast<const char*>(a.x) + k0 * a.x_sk * esx;
+    if (pre) { b.wsig = a.wsig + k0 / V_KC * a.wld; b.wexp = a.wexp + k0 / V_KC * a.wld; }
+    const bool first = ib == 0, last = ib + 1 == nblk;
+    if (out_mode == 0) b.epi = first ? EPI_STORE : EPI_ADD;
+    else b.epi = nblk == 1 ? EPI_ROUND : first ? EPI_STORE : last ? EPI_ADD_ROUND : EPI_ADD;
+    if (dt == DET_F32) {
+      if (out_mode == 0) { if (pre) DET_LAUNCH(DET_F32, false, true, false); else DET_LAUNCH(DET_F32, false, false, false); }
+      else { if (pre) DET_LAUNCH(DET_F32, true, true, true); else DET_LAUNCH(DET_F32, true, false, true); }
+    } else {
+      if (out_mode == 0) { if (pre) DET_LAUNCH(DET_BF16, false, true, false); else DET_LAUNCH(DET_BF16, false, false, false); }
+      else { if (pre) DET_LAUNCH(DET_BF16, true, true, false); else DET_LAUNCH(DET_BF16, true, false, false); }
+    }
+    det_status st = hip_check(hipGetLastError(), "gemm launch");
+    if (st != DET_OK) return st;
   }
 #undef DET_LAUNCH
-  return hip_check(hipGetLastError(), "gemm launch");
+  return DET_OK;
 }
 
 // Two rows per wave: the 17.9 KB of counters per wave let 8-9 waves share a
@@ -689,9 +737,9 @@ det_status gemm_common(int out_mode, det_dtype dt, const void* x, int64_t x_sm, 
   }
   if (ws != nullptr) {
     if (reinterpret_cast<uintptr_t>(ws) & 15u) return fail(DET_EINVAL, "workspace must be 16-byte aligned");
-    if (ws_bytes < static_cast<size_t>(workspace_bytes(N, K)))
+    if (ws_bytes < static_cast<size_t>(workspace_bytes(out_mode, M, N, K)))
       return fail(DET_EINVAL, "workspace of %zu bytes is smaller than the %lld needed", ws_bytes,
-                  (long long)workspace_bytes(N, K));
+                  (long long)workspace_bytes(out_mode, M, N, K));
   }
   GemmArgs a{};
   a.x = x; a.x_sm = x_sm; a.x_sk = x_sk;
@@ -704,10 +752,10 @@ det_status gemm_common(int out_mode, det_dtype dt, const void* x, int64_t x_sm, 
 
 }  // namespace
 
-int64_t det_gemm_workspace_bytes(det_dtype dt, int64_t N, int64_t K) {
+int64_t det_gemm_workspace_bytes(det_dtype dt, int partial, int64_t M, int64_t N, int64_t K) {
   (void)dt;
-  if (N <= 0 || K <= 0) return 0;
-  return workspace_bytes(N, K);
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return workspace_bytes(partial ? 0 : 1, M, N, K);
 }
 
 det_status det_gemm(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk, const void* w, int64_t w_sn,

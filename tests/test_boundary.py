@@ -71,14 +71,18 @@ def test_c_abi_rejects_bad_arguments_without_a_gpu():
 
 def test_workspace_size_and_checks():
     lib = _lib.load()
-    assert lib.det_gemm_workspace_bytes(0, 0, 5) == 0
-    assert lib.det_gemm_workspace_bytes(0, 5, 0) == 0
-    assert lib.det_gemm_workspace_bytes(0, 1, 1) == 6 * 64 * 16
-    assert lib.det_gemm_workspace_bytes(1, 4096, 4096) == 6 * 4096 * 4096
-    assert lib.det_gemm_workspace_bytes(0, 65, 17) == 6 * 128 * 32
+    assert lib.det_gemm_workspace_bytes(0, 0, 3, 0, 5) == 0
+    assert lib.det_gemm_workspace_bytes(0, 0, 3, 5, 0) == 0
+    assert lib.det_gemm_workspace_bytes(0, 0, 0, 5, 5) == 0
+    assert lib.det_gemm_workspace_bytes(0, 0, 1, 1, 1) == 6 * 64 * 16
+    assert lib.det_gemm_workspace_bytes(1, 1, 9, 4096, 4096) == 6 * 4096 * 4096
+    assert lib.det_gemm_workspace_bytes(0, 0, 9, 65, 17) == 6 * 128 * 32
+    # det_gemm with K beyond one block also carries 144 bytes of digits per output
+    assert lib.det_gemm_workspace_bytes(0, 0, 7, 64, 40000) == 6 * 64 * 40000 + 144 * 7 * 64
+    assert lib.det_gemm_workspace_bytes(0, 1, 7, 64, 40000) == 6 * 64 * 40000
     vp = ctypes.c_void_p
     args = (0, vp(1 << 20), 4, 1, vp(1 << 20), 4, 1, 4, 4, 4, vp(1 << 20), 4, 1)
-    need = lib.det_gemm_workspace_bytes(0, 4, 4)
+    need = lib.det_gemm_workspace_bytes(0, 0, 4, 4, 4)
     assert lib.det_gemm_ws(*args, None, need, None) == _lib.DET_EINVAL
     assert lib.det_gemm_ws(*args, vp((1 << 20) + 8), need, None) == _lib.DET_EINVAL   # misaligned
     assert lib.det_gemm_ws(*args, vp(1 << 20), need - 1, None) == _lib.DET_EINVAL    # too small
