@@ -106,50 +106,26 @@ __device__ uint32_t round_digits_to_f32(const int64_t (&dg)[ND]) {
   return (neg ? 0x80000000u : 0u) | mag;
 }
 
-// ---------------------------------------------------------------- GEMM kernel
+// ---------------------------------------------------------------- GEMM kernels: shared parts
 //
-// Work split.  Every workgroup is a single wave that owns a 2 x 64 block of
-// outputs: rows m0 and m0+1, lane l owning column n0+l of both.  There is no
-// cross-wave sharing and so no barrier anywhere in the main loop.  Per 16-wide
-// K-chunk:
-//   * each lane loads its column's 16 raw w elements straight into registers
+// Both GEMM kernels give lane l of a wave column n0 + l of a 64-column output
+// tile and walk K in 16-wide chunks.  Per chunk:
+//   * each lane loads its column's 16 w elements straight into registers
 //     (vector loads issued one chunk ahead, so their latency hides behind the
 //     current chunk; they are tracked by vmcnt, independent of the LDS
-//     atomics);
-//   * lane l loads and decodes x element k0 + (l mod 16) of both rows, so each
-//     16-lane row of the wave holds the chunk's x values; the operand for step
-//     j is broadcast to the whole wave with a DPP row broadcast of lane j;
-//   * each lane decodes its w element once per k and uses it for both rows.
-//
-// Accumulator.  Each output owns 35 signed 32-bit counters in LDS, one per
-// 16-bit field of the digit array (field q weighs 2^(16q - 298); digit
-// j = field 2j + 2^16 * field 2j+1; products never reach bits >= 2^554, so
-// field 35 would always be zero).  A product at bit offset o = ex + ew + 298
-// is shifted by o mod 16 into a 64-bit T (|T| < 2^63) whose four 16-bit
-// fields are added, each with one ds_add_u32, into counters o/16 .. o/16+3
-// (bf16: |T| < 2^31, two fields).  The LDS address is the only per-lane
-// dynamic index the hardware has, and a 32-bit atomic carrying a 16-bit field
-// costs less LDS time per product than 64-bit limb atomics.  A field is below
-// 2^16 in magnitude, so a counter takes 2^15 adds; every 2^15 k the counters
-// are folded into int64 digits held in registers.
-//
-// Field conventions (template parameter TWOS):
-//   false (det_gemm_partial): the fields of |product| each carry the product's
-//     sign, so digit j is exactly the raw digit of the definition, the sum
-//     over products of sign * bits [32j, 32j+32) of |p| * 2^298.
-//   true (det_gemm): the fields of the signed product in two's complement (top
-//     field signed).  Each product's fields still add up to its exact value,
-//     so the digit array holds the same exact sum and rounds to the same fp32,
-//     with fewer instructions per product.
-//
-// Counter layout: byte address field*512 + row*256 + lane*4, so the 64 lanes
-// always hit 64 distinct banks whatever their fields.
+//     atomics), either raw or pre-decoded from a workspace;
+//   * lane l loads and decodes x element k0 + (l mod 16) of each of its rows,
+//     so each 16-lane row of the wave holds the chunk's x values; the operand
+//     for step j is broadcast to the whole wave with a DPP row broadcast of
+//     lane j;
+//   * each lane uses its w element once per row.
+// The exact products are accumulated in LDS with integer atomics whose
+// address depends on the product's exponent: the LDS address is the only
+// per-lane dynamic index the hardware has.  k_gemm (the raw digits of
+// det_gemm_partial) and k_gemm8 (det_gemm) differ in what they add where.
 
 constexpr int V_BN = 64;                    // columns per wave (one per lane)
 constexpr int V_KC = 16;                    // K per chunk
-constexpr int NF = 35;                      // 16-bit fields per output
-constexpr int ROW_BYTES = 64 * 4;           // counters of one row: 64 lanes x 4 bytes
-constexpr int64_t KFLUSH = int64_t(1) << 15;      // adds a counter can take
 
 struct GemmArgs {
   const void* x; int64_t x_sm, x_sk;
@@ -158,25 +134,32 @@ struct GemmArgs {
   int64_t tiles_m, tiles_n;
   int w_vec;                          // w rows contiguous and 16-byte aligned per chunk
   const int32_t* wsig;                // pre-decoded w (workspace): significands [Kp/16][Np][16]
-  const uint16_t* wexp;               // pre-decoded w: exponent words [Kp/16][Np][16]
+  const uint16_t* wexp;               // k_gemm: 16-bit exponent words [Kp/16][Np][16]
+  const uint32_t* wexp32;             // k_gemm8: 32-bit exponent words, same layout
   int64_t wld;                        // Np * 16, the chunk pitch of both
   int64_t* acc;                       // digits [M][N][18]: the partial's output, or scratch
   float* y; int64_t y_sm, y_sn;       // gemm: fp32 out
   int epi;                            // epilogue, see EPI_* below
 };
 
+// Epilogues.  A K range longer than one block is run as several launches
+// that carry the exact digits from one to the next (see the launchers).
+constexpr int EPI_ROUND = 0;        // round the digits to fp32 into y
+constexpr int EPI_STORE = 1;        // write the digits to acc
+constexpr int EPI_ADD = 2;          // add acc's digits, write them back
+constexpr int EPI_ADD_ROUND = 3;    // add acc's digits, round to fp32 into y
+
 // Operand decode: value = (signed) m * 2^(exponent - bias).  SIDE 0 is x, 1
-// is w; the exponent offsets are split between the sides so that, with
-// sum = e_x + e_w, bits 5..14 of sum hold the product's bit offset
-// o = ex + ew + 298 (f32: max(Ex,1) + max(Ew,1) - 2, bf16: max(Ex,1) +
-// max(Ew,1) + 30).  The shift by 5 lets one bit-field extract give the shift
-// inside a 16-bit field (bits 5..8) and one mask give the field's counter
-// offset (bits 9..14).  With TWOS the sign is applied to m (two's
-// complement); otherwise m is the magnitude and the sign sits in bit 15, so
-// bit 15 of sum is the product's sign.  Subnormals keep their raw fraction
-// and exponent 1: nothing is flushed.  For every bit pattern o <= 540, so no
-// field index leaves 0..34.
-template <int DT, bool TWOS, int SIDE, uint32_t ESH = EXP_SHIFT>
+// is w; the exponent offsets are split between the sides so that the sum of
+// the two exponent words is the product's bit offset o = ex + ew + 298
+// (f32: max(Ex,1) + max(Ew,1) - 2, bf16: max(Ex,1) + max(Ew,1) + 30)
+// shifted left by ESH, which each kernel picks so that its counter address
+// and shift fall out of the sum with one or two bit operations.  With TWOS
+// the sign is applied to m (two's complement); otherwise m is the magnitude
+// and the sign sits in bit 15 (SIGN_BIT), so bit 15 of the sum is the
+// product's sign.  Subnormals keep their raw fraction and exponent 1: nothing
+// is flushed.  For every bit pattern o <= 540.
+template <int DT, bool TWOS, int SIDE, uint32_t ESH>
 __device__ __forceinline__ void decode(uint32_t b, int32_t& m, uint32_t& e) {
   uint32_t E, mag, neg;
   if (DT == DET_F32) {
@@ -196,91 +179,6 @@ __device__ __forceinline__ void decode(uint32_t b, int32_t& m, uint32_t& e) {
   } else {
     m = static_cast<int32_t>(mag);
     e = ((max(E, 1u) + off) << ESH) + (neg << SIGN_BIT);
-  }
-}
-
-// one exact product into the counters of one output; `sum` = e_x + e_w.
-// Counter byte address: field*(R*256) + row*256 + lane*4.
-template <int DT, bool TWOS, int R>
-__device__ __forceinline__ void accumulate(char* lane_row, int32_t xm, int32_t wm, uint32_t sum) {
-  constexpr int F = R * ROW_BYTES / 4;                  // ints between fields
-  const uint32_t s16 = (sum >> EXP_SHIFT) & 15u;        // shift inside the field
-  int* p = reinterpret_cast<int*>(lane_row + ((sum >> (EXP_SHIFT + 4)) & 63u) * (R * ROW_BYTES));   // field o/16
-  if (DT == DET_F32) {
-    uint64_t T;
-    if (TWOS) T = static_cast<uint64_t>(static_cast<int64_t>(xm) * wm) << s16;
-    else T = (static_cast<uint64_t>(static_cast<uint32_t>(xm)) * static_cast<uint32_t>(wm)) << s16;
-    const uint32_t lo = static_cast<uint32_t>(T), hi = static_cast<uint32_t>(T >> 32);
-    if (TWOS) {
-      atomicAdd(p, static_cast<int>(lo & 0xFFFFu));
-      atomicAdd(p + F, static_cast<int>(lo >> 16));
-      atomicAdd(p + 2 * F, static_cast<int>(hi & 0xFFFFu));
-      atomicAdd(p + 3 * F, static_cast<int>(hi) >> 16);
-    } else {
-      const uint32_t neg = (sum >> SIGN_BIT) & 1u, msk = 0u - neg;   // (f ^ msk) + neg = +-f
-      atomicAdd(p, static_cast<int>(((lo & 0xFFFFu) ^ msk) + neg));
-      atomicAdd(p + F, static_cast<int>(((lo >> 16) ^ msk) + neg));
-      atomicAdd(p + 2 * F, static_cast<int>(((hi & 0xFFFFu) ^ msk) + neg));
-      atomicAdd(p + 3 * F, static_cast<int>(((hi >> 16) ^ msk) + neg));
-    }
-  } else {
-    if (TWOS) {
-      const int32_t T = (xm * wm) << s16;               // |T| < 2^31
-      atomicAdd(p, T & 0xFFFF);
-      atomicAdd(p + F, T >> 16);
-    } else {
-      const uint32_t T = (static_cast<uint32_t>(xm) * static_cast<uint32_t>(wm)) << s16;
-      const uint32_t neg = (sum >> SIGN_BIT) & 1u, msk = 0u - neg;
-      atomicAdd(p, static_cast<int>(((T & 0xFFFFu) ^ msk) + neg));
-      atomicAdd(p + F, static_cast<int>(((T >> 16) ^ msk) + neg));
-    }
-  }
-}
-
-// 24-bit field grid, used by det_gemm on f32 (two's-complement fields):
-// counter p weighs 2^(24p - 298).  A product at offset o (plain, not shifted)
-// goes to p = o div 24 with shift s = o mod 24; its value T = P * 2^s (P the
-// signed significand product, |P| < 2^48, so |T| < 2^71) splits into fields
-// g0 = bits 0..23 and g1 = bits 24..47 (both >= 0) and the signed
-// g2 = T >> 48.  Three atomics per product instead of four; a counter takes
-// 128 adds (|field| < 2^24) before it must be folded.
-constexpr int NF24 = 24;                    // 24 x 24 = 576 bits
-constexpr int64_t KFLUSH24 = 128;
-
-template <int R>
-__device__ __forceinline__ void accumulate24(char* lane_row, int32_t xm, int32_t wm, uint32_t o) {
-  constexpr int F = R * ROW_BYTES / 4;
-  const uint32_t p = __umulhi(o, 178956971u);           // o div 24 (exact for o < 2^30)
-  const uint32_t s = o - 24u * p;
-  int* ptr = reinterpret_cast<int*>(lane_row + p * (R * ROW_BYTES));
-  const int64_t P = static_cast<int64_t>(xm) * wm;
-  const uint64_t T = static_cast<uint64_t>(P) << s;     // bits 0..63 of P * 2^s
-  const uint32_t lo = static_cast<uint32_t>(T), hi = static_cast<uint32_t>(T >> 32);
-  atomicAdd(ptr, static_cast<int>(lo & 0xFFFFFFu));
-  atomicAdd(ptr + F, static_cast<int>(__builtin_amdgcn_perm(hi, lo, 0x0C050403u)));   // bits 24..47
-  atomicAdd(ptr + 2 * F, static_cast<int>(static_cast<uint64_t>(P >> (48u - s))));    // bits 48..71
-}
-
-// fold the 24 counters of one row into int64 digits (counter p lands at bit
-// 24p = 32*(p*3/4) + 8*(3p mod 4)) and clear them; every `norm` folds, carry
-// the digits so that all but the top one lie in [0, 2^32)
-template <int R>
-__device__ __forceinline__ void fold_row24(char* lane_row, int64_t (&dg)[ND], bool norm) {
-  int* c = reinterpret_cast<int*>(lane_row);
-  constexpr int F = R * ROW_BYTES / 4;
-#pragma unroll
-  for (int p = 0; p < NF24; ++p) {
-    const int bit = 24 * p;
-    dg[bit >> 5] += static_cast<int64_t>(c[p * F]) * (int64_t(1) << (bit & 31));
-    c[p * F] = 0;
-  }
-  if (norm) {
-#pragma unroll
-    for (int j = 0; j + 1 < ND; ++j) {
-      const int64_t carry = dg[j] >> 32;
-      dg[j] -= carry * (int64_t(1) << 32);
-      dg[j + 1] += carry;
-    }
   }
 }
 
@@ -329,6 +227,70 @@ __device__ __forceinline__ void load_w_chunk(const GemmArgs& a, const void* __re
   }
 }
 
+template <int J>
+__device__ __forceinline__ int bcast(int v) {     // lane J of each 16-lane row, to the whole row
+  return __builtin_amdgcn_mov_dpp(v, 0x150 + J, 0xF, 0xF, true);
+}
+
+// Workgroups are dispatched to the 8 XCDs round-robin, each XCD with its own
+// L2.  Give every XCD a contiguous range of tiles in column-major tile order,
+// so the workgroups resident on one XCD share one 64-column slice of w (kept
+// in that L2) while they walk down the rows.
+__device__ __forceinline__ int64_t xcd_tile() {
+  const int64_t nb = gridDim.x, b = blockIdx.x;
+  const int64_t xcd = b % 8, per = nb / 8, extra = nb % 8;
+  return xcd * per + min(xcd, extra) + b / 8;
+}
+
+// ---------------------------------------------------------------- raw-digit kernel (det_gemm_partial)
+//
+// Every workgroup is a single wave that owns a 2 x 64 block of outputs: rows
+// m0 and m0+1, lane l owning column n0+l of both.  There is no cross-wave
+// sharing and so no barrier anywhere in the main loop.
+//
+// Accumulator.  Each output owns 35 signed 32-bit counters in LDS, one per
+// 16-bit field of the digit array (field q weighs 2^(16q - 298); digit
+// j = field 2j + 2^16 * field 2j+1; products never reach bits >= 2^554, so
+// field 35 would always be zero).  A product at bit offset o is shifted by
+// o mod 16 into a 64-bit T = |P| * 2^(o mod 16) < 2^63 whose four 16-bit
+// fields are added, each with one ds_add_u32 and each carrying the product's
+// sign, into counters o/16 .. o/16+3 (bf16: T < 2^31, two fields).  So digit
+// j is exactly the raw digit of the definition, the sum over products of
+// sign * bits [32j, 32j+32) of |p| * 2^298.  A field is below 2^16 in
+// magnitude, so a counter takes 2^15 adds; every 2^15 k the counters are
+// folded into int64 digits held in registers.
+//
+// Counter layout: byte address field*512 + row*256 + lane*4, so the 64 lanes
+// always hit 64 distinct banks whatever their fields.  Exponent words carry
+// o << 5 (EXP_SHIFT): bits 5..8 of the sum are the shift inside a field and
+// bits 9..14 the field.
+
+constexpr int NF = 35;                      // 16-bit fields per output
+constexpr int ROW_BYTES = 64 * 4;           // counters of one row: 64 lanes x 4 bytes
+constexpr int64_t KFLUSH = int64_t(1) << 15;      // adds a counter can take
+
+// one exact product into the counters of one output; `sum` = e_x + e_w.
+// Counter byte address: field*(R*256) + row*256 + lane*4.
+template <int DT, int R>
+__device__ __forceinline__ void accumulate(char* lane_row, int32_t xm, int32_t wm, uint32_t sum) {
+  constexpr int F = R * ROW_BYTES / 4;                  // ints between fields
+  const uint32_t s16 = (sum >> EXP_SHIFT) & 15u;        // shift inside the field
+  int* p = reinterpret_cast<int*>(lane_row + ((sum >> (EXP_SHIFT + 4)) & 63u) * (R * ROW_BYTES));   // field o/16
+  const uint32_t neg = (sum >> SIGN_BIT) & 1u, msk = 0u - neg;         // (f ^ msk) + neg = +-f
+  if (DT == DET_F32) {
+    const uint64_t T = (static_cast<uint64_t>(static_cast<uint32_t>(xm)) * static_cast<uint32_t>(wm)) << s16;
+    const uint32_t lo = static_cast<uint32_t>(T), hi = static_cast<uint32_t>(T >> 32);
+    atomicAdd(p, static_cast<int>(((lo & 0xFFFFu) ^ msk) + neg));
+    atomicAdd(p + F, static_cast<int>(((lo >> 16) ^ msk) + neg));
+    atomicAdd(p + 2 * F, static_cast<int>(((hi & 0xFFFFu) ^ msk) + neg));
+    atomicAdd(p + 3 * F, static_cast<int>(((hi >> 16) ^ msk) + neg));
+  } else {
+    const uint32_t T = (static_cast<uint32_t>(xm) * static_cast<uint32_t>(wm)) << s16;
+    atomicAdd(p, static_cast<int>(((T & 0xFFFFu) ^ msk) + neg));
+    atomicAdd(p + F, static_cast<int>(((T >> 16) ^ msk) + neg));
+  }
+}
+
 // fold the counters of one row into int64 digits and clear them
 template <int R>
 __device__ __forceinline__ void fold_row(char* lane_row, int64_t (&dg)[ND]) {
@@ -343,15 +305,10 @@ __device__ __forceinline__ void fold_row(char* lane_row, int64_t (&dg)[ND]) {
   }
 }
 
-template <int J>
-__device__ __forceinline__ int bcast(int v) {     // lane J of each 16-lane row, to the whole row
-  return __builtin_amdgcn_mov_dpp(v, 0x150 + J, 0xF, 0xF, true);
-}
-
 // One K-chunk: step J uses w element J of the lane (raw bits to decode, or,
 // with PRE, a pre-decoded significand and the packed exponent words) and
 // broadcasts x element J of each row from lane J of every 16-lane row.
-template <int DT, bool TWOS, int R, bool PRE, bool G24, int J>
+template <int DT, int R, bool PRE, int J>
 __device__ __forceinline__ void steps(char* lane_base, const uint32_t (&wa)[V_KC], const uint32_t (&wb)[V_KC / 2],
                                       const int (&xm)[R], const int (&xe)[R]) {
   int32_t wm;
@@ -360,15 +317,14 @@ __device__ __forceinline__ void steps(char* lane_base, const uint32_t (&wa)[V_KC
     wm = static_cast<int32_t>(wa[J]);
     we = (J & 1) ? (wb[J / 2] >> 16) : (wb[J / 2] & 0xFFFFu);
   } else {
-    decode<DT, TWOS, 1, G24 ? 0u : EXP_SHIFT>(wa[J], wm, we);
+    decode<DT, false, 1, EXP_SHIFT>(wa[J], wm, we);
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const uint32_t sum = static_cast<uint32_t>(bcast<J>(xe[r])) + we;
-    if (G24) accumulate24<R>(lane_base + r * ROW_BYTES, bcast<J>(xm[r]), wm, sum);
-    else accumulate<DT, TWOS, R>(lane_base + r * ROW_BYTES, bcast<J>(xm[r]), wm, sum);
+    accumulate<DT, R>(lane_base + r * ROW_BYTES, bcast<J>(xm[r]), wm, sum);
   }
-  if constexpr (J + 1 < V_KC) steps<DT, TWOS, R, PRE, G24, J + 1>(lane_base, wa, wb, xm, xe);
+  if constexpr (J + 1 < V_KC) steps<DT, R, PRE, J + 1>(lane_base, wa, wb, xm, xe);
 }
 
 // the lane's pre-decoded w chunk: 16 significands and 16 exponent words
@@ -392,38 +348,37 @@ __device__ __forceinline__ void load_w_pre(const GemmArgs& a, int64_t n, int64_t
   }
 }
 
-// R rows per wave.  TWOS = false: write raw digits; TWOS = true: round to fp32.
-// Epilogues.  A K range longer than one block is run as several launches
-// that carry the exact digits from one to the next (see launch_gemm_rows).
-constexpr int EPI_ROUND = 0;        // round the digits to fp32 into y
-constexpr int EPI_STORE = 1;        // write the digits to acc
-constexpr int EPI_ADD = 2;          // add acc's digits, write them back
-constexpr int EPI_ADD_ROUND = 3;    // add acc's digits, round to fp32 into y
+// one chunk's operands: the lane's w elements (pre-decoded or raw) and, for
+// each row, x element k0 + xj (clamped into the row; beyond K it is masked
+// when decoded)
+template <int DT, bool PRE, int R>
+__device__ __forceinline__ void load_chunk(const GemmArgs& a, const void* __restrict__ xg,
+                                           const void* __restrict__ wg, int64_t n, int64_t wrow, bool n_ok,
+                                           const int64_t (&xrow)[R], int xj, int64_t k0, uint32_t (&w)[V_KC],
+                                           uint32_t (&we)[V_KC / 2], uint32_t (&x)[R]) {
+  if (PRE) load_w_pre(a, n, k0, w, we);
+  else load_w_chunk<DT>(a, wg, wrow, n_ok, k0, w);
+  const int64_t k = min<int64_t>(k0 + xj, a.K - 1);
+#pragma unroll
+  for (int r = 0; r < R; ++r) x[r] = load_elem<DT>(xg, xrow[r] + k * a.x_sk);
+}
 
-// R rows per wave; PRE: w comes pre-decoded from the workspace; G24: the
-// 24-bit field grid (f32 with TWOS only), else 16-bit fields.
-template <int DT, bool TWOS, int R, bool PRE, bool G24>
+// R rows per wave; PRE: w comes pre-decoded from the workspace.  Epilogue
+// EPI_STORE or EPI_ADD.
+template <int DT, int R, bool PRE>
 __global__ __launch_bounds__(64) void k_gemm(GemmArgs a, const void* __restrict__ xg,
                                              const void* __restrict__ wg) {
-  static_assert(!G24 || (DT == DET_F32 && TWOS), "the 24-bit grid serves f32 det_gemm only");
-  constexpr int NFG = G24 ? NF24 : NF;
-  constexpr int64_t KF = G24 ? KFLUSH24 : KFLUSH;
-  __shared__ __align__(16) int counters[NFG * R * 64];
+  constexpr int NB = 2;                           // operand ring slots
+  __shared__ __align__(16) int counters[NF * R * 64];
 
   const int lane = threadIdx.x;
-  // Workgroups are dispatched to the 8 XCDs round-robin, each XCD with its
-  // own L2.  Give every XCD a contiguous range of tiles in column-major tile
-  // order, so the waves resident on one XCD share one 64-column slice of w
-  // (kept in that L2) while they walk down the rows.
-  const int64_t nb = gridDim.x, b = blockIdx.x;
-  const int64_t xcd = b % 8, per = nb / 8, extra = nb % 8;
-  const int64_t tile = xcd * per + min(xcd, extra) + b / 8;
+  const int64_t tile = xcd_tile();
   const int64_t tn = tile / a.tiles_m, tm = tile % a.tiles_m;
   const int64_t m0 = tm * R, n0 = tn * V_BN;
   char* const lane_base = reinterpret_cast<char*>(counters) + lane * 4;
 
 #pragma unroll
-  for (int q = 0; q < NFG * R; ++q) counters[q * 64 + lane] = 0;
+  for (int q = 0; q < NF * R; ++q) counters[q * 64 + lane] = 0;
 
   const int64_t n = n0 + lane;
   const bool n_ok = n < a.N;
@@ -443,60 +398,50 @@ __global__ __launch_bounds__(64) void k_gemm(GemmArgs a, const void* __restrict_
 #pragma unroll
     for (int j = 0; j < ND; ++j) dg[r][j] = 0;
 
-  // chunk 0 operands
-  uint32_t wnext[V_KC], wbnext[V_KC / 2];
+  // Operand ring: chunk c lives in slot c mod NB, and the loads of chunk
+  // c + NB - 1 are issued before chunk c is processed.  The loop over slots
+  // is unrolled, so every slot index is static and nothing is copied between
+  // registers.
+  uint32_t wq[NB][V_KC], wbq[NB][V_KC / 2], xq[NB][R];
 #pragma unroll
-  for (int i = 0; i < V_KC / 2; ++i) wbnext[i] = 0u;
-  uint32_t xn[R];
+  for (int p = 0; p < NB; ++p) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) xn[r] = 0u;
-  if (a.K > 0) {
-    if (PRE) load_w_pre(a, n, 0, wnext, wbnext);
-    else load_w_chunk<DT>(a, wg, wrow, n_ok, 0, wnext);
-    const int64_t k = min<int64_t>(xj, a.K - 1);
+    for (int i = 0; i < V_KC / 2; ++i) wbq[p][i] = 0u;
 #pragma unroll
-    for (int r = 0; r < R; ++r) xn[r] = load_elem<DT>(xg, xrow[r] + k * a.x_sk);
+    for (int r = 0; r < R; ++r) xq[p][r] = 0u;
   }
+#pragma unroll
+  for (int p = 0; p + 1 < NB; ++p)
+    if (p * V_KC < a.K) load_chunk<DT, PRE, R>(a, xg, wg, n, wrow, n_ok, xrow, xj, p * V_KC, wq[p], wbq[p], xq[p]);
 
-  for (int64_t k0 = 0; k0 < a.K; k0 += V_KC) {
-    uint32_t wr[V_KC], wb[V_KC / 2];
+  for (int64_t c0 = 0; c0 * V_KC < a.K; c0 += NB) {
 #pragma unroll
-    for (int i = 0; i < V_KC; ++i) wr[i] = wnext[i];
-#pragma unroll
-    for (int i = 0; i < V_KC / 2; ++i) wb[i] = wbnext[i];
-    const bool kin = k0 + xj < a.K;
-    int xm[R], xe[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      int32_t m;
-      uint32_t e;
-      decode<DT, TWOS, 0, G24 ? 0u : EXP_SHIFT>((row_ok[r] && kin) ? xn[r] : 0u, m, e);
-      xm[r] = m;
-      xe[r] = static_cast<int>(e);
-    }
-    if (k0 + V_KC < a.K) {                        // prefetch the next chunk
-      if (PRE) load_w_pre(a, n, k0 + V_KC, wnext, wbnext);
-      else load_w_chunk<DT>(a, wg, wrow, n_ok, k0 + V_KC, wnext);
-      const int64_t k = min<int64_t>(k0 + V_KC + xj, a.K - 1);
-#pragma unroll
-      for (int r = 0; r < R; ++r) xn[r] = load_elem<DT>(xg, xrow[r] + k * a.x_sk);
-    }
-    steps<DT, TWOS, R, PRE, G24, 0>(lane_base, wr, wb, xm, xe);
-    if (a.K > KF && ((k0 + V_KC) % KF) == 0) {    // counters near their limit
-      // (24-bit grid: carry the digits every 16 folds, 2^56 growth per fold)
-      const bool norm = ((k0 + V_KC) % (16 * KF)) == 0;
+    for (int sl = 0; sl < NB; ++sl) {
+      const int64_t k0 = (c0 + sl) * V_KC;
+      if (k0 >= a.K) break;
+      const int64_t kp = k0 + (NB - 1) * V_KC;    // prefetch into the slot freed by the last chunk
+      if (kp < a.K)
+        load_chunk<DT, PRE, R>(a, xg, wg, n, wrow, n_ok, xrow, xj, kp, wq[(sl + NB - 1) % NB],
+                               wbq[(sl + NB - 1) % NB], xq[(sl + NB - 1) % NB]);
+      const bool kin = k0 + xj < a.K;
+      int xm[R], xe[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        if (G24) fold_row24<R>(lane_base + r * ROW_BYTES, dg[r], norm);
-        else fold_row<R>(lane_base + r * ROW_BYTES, dg[r]);
+        int32_t m;
+        uint32_t e;
+        decode<DT, false, 0, EXP_SHIFT>((row_ok[r] && kin) ? xq[sl][r] : 0u, m, e);
+        xm[r] = m;
+        xe[r] = static_cast<int>(e);
+      }
+      steps<DT, R, PRE, 0>(lane_base, wq[sl], wbq[sl], xm, xe);
+      if (a.K > KFLUSH && ((k0 + V_KC) % KFLUSH) == 0) {   // counters near their limit
+#pragma unroll
+        for (int r = 0; r < R; ++r) fold_row<R>(lane_base + r * ROW_BYTES, dg[r]);
       }
     }
   }
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    if (G24) fold_row24<R>(lane_base + r * ROW_BYTES, dg[r], true);
-    else fold_row<R>(lane_base + r * ROW_BYTES, dg[r]);
-  }
+  for (int r = 0; r < R; ++r) fold_row<R>(lane_base + r * ROW_BYTES, dg[r]);
 
   if (!n_ok) return;
 #pragma unroll
@@ -504,23 +449,277 @@ __global__ __launch_bounds__(64) void k_gemm(GemmArgs a, const void* __restrict_
     const int64_t m = m0 + r;
     if (m >= a.M) continue;
     int64_t* d = a.acc + (m * a.N + n) * ND;
-    if (a.epi == EPI_ADD || a.epi == EPI_ADD_ROUND) {
+    if (a.epi == EPI_ADD) {
 #pragma unroll
       for (int j = 0; j < ND; ++j) dg[r][j] += d[j];
     }
-    if (a.epi == EPI_STORE || a.epi == EPI_ADD) {
 #pragma unroll
-      for (int j = 0; j < ND; ++j) d[j] = dg[r][j];
+    for (int j = 0; j < ND; ++j) d[j] = dg[r][j];
+  }
+}
+
+// ---------------------------------------------------------------- det_gemm kernel
+//
+// det_gemm needs only the exact sum, not the raw digits, so a product may go
+// into the accumulator in any pieces whose values add up to it.  Here it goes
+// whole, with ONE LDS atomic, into one cell of an 8-bit grid: cell c of an
+// output weighs 2^(8c - 298) and a product at bit offset o goes into cell
+// o div 8 as T = P * 2^(o mod 8), P the signed significand product.  f32:
+// |P| < 2^48, so |T| < 2^55 and cells are int64 (ds_add_u64); bf16: |P| <
+// 2^16, |T| < 2^23, int32 cells (ds_add_u32).  Either way a cell takes 256
+// adds before it must be folded into the digits.  f32 offsets reach 506 and
+// bf16 offsets run from 32 to 538, so 64 cells cover every product (bf16:
+// cells 4..67).
+//
+// The cells of R x 64 outputs fill R x 32 KB (f32) or R x 17 KB (bf16): too
+// much for one wave if the CU is to hold enough waves to keep its VALUs
+// busy, so W waves share them.  A workgroup owns rows m0..m0+R-1 and 64
+// columns; its waves take the K-chunks in turn (wave v: chunks v, v + W,
+// ...) and all add into the same cells, which the LDS atomics keep exact.
+// Every 256 k of K (an epoch) the workgroup meets at a barrier, each wave
+// folds its 1/W of the cells into a window of int64 digits in its registers
+// and clears them, and a second barrier opens the next epoch.  At the end the
+// windows are added into one digit array per row in LDS and waves 0..R-1
+// finish the rows (round to fp32, or carry the digits to the next K block).
+//
+// Per product the VALU runs the x broadcast (DPP), the exponent sum (DPP add),
+// the cell address (and-or), the shift (bit-field extract), the product and
+// the shift of T: six instructions, about half of what the same product
+// costs split into 16-bit fields with four atomics.
+constexpr int NC8 = 64;                         // cells per output
+constexpr int64_t KFLUSH8 = 256;                // adds a cell takes between folds
+constexpr int64_t EPOCH8 = KFLUSH8 / V_KC;      // chunks per epoch, all waves together
+template <int DT>
+constexpr int cell_bytes() { return DT == DET_F32 ? 8 : 4; }
+template <int DT>
+constexpr int cell_base() { return DT == DET_F32 ? 0 : 4; }     // first cell a product can reach
+template <int W>
+constexpr int cells_per_wave() { return NC8 / W; }
+template <int W>
+constexpr int window_digits() { return NC8 / W / 4 + 2; }
+
+// Exponent words of k_gemm8 carry the offset times the cell stride / 8
+// (the stride: R rows x 64 lanes x 8 B for f32, x 4 B for bf16), so that
+// o & ~(stride - 1) is the cell's byte offset and bits ESH..ESH+2 are the
+// shift inside the cell.
+template <int DT, int R>
+constexpr uint32_t exp_shift8() { return (DT == DET_F32 ? 6u : 5u) + (R == 2 ? 1u : 0u); }
+
+// the lane's pre-decoded w chunk for k_gemm8: 16 significands and 16 32-bit
+// exponent words, chunk-major like load_w_pre
+__device__ __forceinline__ void load_w_pre8(const GemmArgs& a, int64_t n, int64_t k0, uint32_t (&wa)[V_KC],
+                                            uint32_t (&wb)[V_KC]) {
+  const int64_t off = (k0 / V_KC) * a.wld + n * V_KC;
+  const uint4* ps = reinterpret_cast<const uint4*>(a.wsig + off);
+  const uint4* pe = reinterpret_cast<const uint4*>(a.wexp32 + off);
+#pragma unroll
+  for (int i = 0; i < V_KC / 4; ++i) {
+    const uint4 v = ps[i], e = pe[i];
+    wa[4 * i] = v.x; wa[4 * i + 1] = v.y; wa[4 * i + 2] = v.z; wa[4 * i + 3] = v.w;
+    wb[4 * i] = e.x; wb[4 * i + 1] = e.y; wb[4 * i + 2] = e.z; wb[4 * i + 3] = e.w;
+  }
+}
+
+// One chunk: step J multiplies x element J of the row (broadcast from lane J
+// of every 16-lane row) by the lane's w element J and adds the shifted
+// product into its cell with one atomic.
+template <int DT, bool PRE, int R, int J>
+__device__ __forceinline__ void steps8(char* cbase, uint32_t lane_off, const uint32_t (&wa)[V_KC],
+                                       const uint32_t (&wb)[V_KC], const int (&xm)[R], const int (&xe)[R]) {
+  constexpr uint32_t CS = R * 64u * cell_bytes<DT>();
+  constexpr uint32_t ESH = exp_shift8<DT, R>();
+  int32_t wm;
+  uint32_t we;
+  if (PRE) {
+    wm = static_cast<int32_t>(wa[J]);
+    we = wb[J];
+  } else {
+    decode<DT, true, 1, ESH>(wa[J], wm, we);
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t o = static_cast<uint32_t>(bcast<J>(xe[r])) + we;
+    char* const p = cbase + ((o & ~(CS - 1u)) | (lane_off + r * 64u * cell_bytes<DT>()));
+    const uint32_t sh = (o >> ESH) & 7u;
+    if (DT == DET_F32) {
+      const uint64_t T = static_cast<uint64_t>(static_cast<int64_t>(bcast<J>(xm[r])) * wm) << sh;
+      atomicAdd(reinterpret_cast<unsigned long long*>(p), static_cast<unsigned long long>(T));
     } else {
-      a.y[m * a.y_sm + n * a.y_sn] = __uint_as_float(round_digits_to_f32(dg[r]));
+      atomicAdd(reinterpret_cast<int*>(p),
+                static_cast<int>(static_cast<uint32_t>(__mul24(bcast<J>(xm[r]), wm)) << sh));
     }
+  }
+  if constexpr (J + 1 < V_KC) steps8<DT, PRE, R, J + 1>(cbase, lane_off, wa, wb, xm, xe);
+}
+
+// dg += v * scale for a 32-bit v (unsigned or signed) and a power-of-two
+// scale, as one v_mad_u64_u32 / v_mad_i64_i32 (the compiler would otherwise
+// widen, shift and add in four instructions)
+__device__ __forceinline__ void mad_u32(int64_t& dg, uint32_t v, uint32_t scale) {
+  uint64_t carry;
+  asm("v_mad_u64_u32 %0, %1, %2, %3, %0" : "+v"(dg), "=s"(carry) : "v"(v), "s"(scale));
+}
+__device__ __forceinline__ void mad_i32(int64_t& dg, int32_t v, uint32_t scale) {
+  uint64_t carry;
+  asm("v_mad_i64_i32 %0, %1, %2, %3, %0" : "+v"(dg), "=s"(carry) : "v"(v), "s"(scale));
+}
+
+// Fold the CW8 cells this wave owns (cells c0 .. c0 + CW8 - 1 of this lane)
+// into its window (window digit 0 weighs the cell c0's bit position; cell
+// c0 + i lands at bit 8i of the window) and clear them; with `norm`, carry
+// the window so that all but its top digit lie in [0, 2^32).
+template <int DT, int R, int W>
+__device__ __forceinline__ void fold8(char* cells_c0, int64_t (&dg)[window_digits<W>()], bool norm) {
+  constexpr int CS = R * 64 * cell_bytes<DT>();
+  constexpr int WD8 = window_digits<W>();
+#pragma unroll
+  for (int i = 0; i < cells_per_wave<W>(); ++i) {
+    const uint32_t scale = 1u << (8 * (i & 3));
+    if (DT == DET_F32) {
+      int64_t* q = reinterpret_cast<int64_t*>(cells_c0 + i * CS);
+      const int64_t v = *q;
+      *q = 0;
+      mad_u32(dg[i >> 2], static_cast<uint32_t>(v), scale);
+      mad_i32(dg[(i >> 2) + 1], static_cast<int32_t>(v >> 32), scale);
+    } else {
+      int* q = reinterpret_cast<int*>(cells_c0 + i * CS);
+      mad_i32(dg[i >> 2], *q, scale);
+      *q = 0;
+    }
+  }
+  if (norm) {
+#pragma unroll
+    for (int j = 0; j + 1 < WD8; ++j) {
+      const int64_t carry = dg[j] >> 32;
+      dg[j] -= carry * (int64_t(1) << 32);
+      dg[j + 1] += carry;
+    }
+  }
+}
+
+template <int DT, bool PRE, int R, int W, int MINB>
+__global__ __launch_bounds__(64 * W, MINB) void k_gemm8(GemmArgs a, const void* __restrict__ xg,
+                                                        const void* __restrict__ wg) {
+  constexpr int W8 = W, CW8 = cells_per_wave<W>(), WD8 = window_digits<W>();
+  static_assert(CW8 * W8 == NC8 && EPOCH8 % (2 * W8) == 0 && CW8 % 4 == 0, "epoch layout");
+  constexpr int RB = 64 * cell_bytes<DT>();                     // bytes between rows
+  constexpr int CS = R * RB;                                    // bytes between cells
+  constexpr int CB = cell_base<DT>();                           // first cell a product reaches
+  constexpr uint32_t ESH = exp_shift8<DT, R>();
+  constexpr int NB = 2;                                         // operand ring slots
+  __shared__ __align__(16) char cells[(CB + NC8) * CS];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t tile = xcd_tile();
+  const int64_t m0 = (tile % a.tiles_m) * R, n0 = (tile / a.tiles_m) * V_BN;
+
+  for (int q = threadIdx.x; q < (CB + NC8) * CS / 16; q += 64 * W8)
+    reinterpret_cast<uint4*>(cells)[q] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+
+  const int64_t n = n0 + lane;
+  const bool n_ok = n < a.N;
+  const int64_t wrow = (n_ok ? n : a.N - 1) * a.w_sn;
+  bool row_ok[R];
+  int64_t xrow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    row_ok[r] = m0 + r < a.M;
+    xrow[r] = min(m0 + r, a.M - 1) * a.x_sm;
+  }
+  const int xj = lane & 15;
+  const uint32_t lane_off = static_cast<uint32_t>(lane * cell_bytes<DT>());
+
+  int64_t dg[R][WD8];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int j = 0; j < WD8; ++j) dg[r][j] = 0;
+
+  const int64_t nchunks = (a.K + V_KC - 1) / V_KC;
+  uint32_t wq[NB][V_KC], weq[NB][V_KC], xq[NB][R];
+#pragma unroll
+  for (int i = 0; i < V_KC; ++i) { weq[0][i] = 0u; weq[1][i] = 0u; }
+#pragma unroll
+  for (int r = 0; r < R; ++r) xq[0][r] = xq[1][r] = 0u;
+  auto load = [&](int64_t c, uint32_t (&w)[V_KC], uint32_t (&we)[V_KC], uint32_t (&x)[R]) {
+    const int64_t k0 = c * V_KC;
+    if (PRE) load_w_pre8(a, n, k0, w, we);
+    else load_w_chunk<DT>(a, wg, wrow, n_ok, k0, w);
+    const int64_t k = min<int64_t>(k0 + xj, a.K - 1);
+#pragma unroll
+    for (int r = 0; r < R; ++r) x[r] = load_elem<DT>(xg, xrow[r] + k * a.x_sk);
+  };
+  if (wave < nchunks) load(wave, wq[0], weq[0], xq[0]);
+
+  char* const my_cells = cells + (CB + wave * CW8) * CS + lane * cell_bytes<DT>();
+  int64_t epoch = 0;
+  for (int64_t e0 = 0; e0 < nchunks; e0 += EPOCH8, ++epoch) {
+#pragma unroll
+    for (int i = 0; i < EPOCH8 / W8; ++i) {       // this wave's chunks of the epoch
+      const int64_t c = e0 + wave + i * W8;
+      const int sl = i & 1;
+      if (c < nchunks) {
+        if (c + W8 < nchunks) load(c + W8, wq[sl ^ 1], weq[sl ^ 1], xq[sl ^ 1]);
+        const bool kin = c * V_KC + xj < a.K;
+        int xm[R], xe[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          int32_t m;
+          uint32_t e;
+          decode<DT, true, 0, ESH>(kin && row_ok[r] ? xq[sl][r] : 0u, m, e);
+          xm[r] = m;
+          xe[r] = static_cast<int>(e);
+        }
+        steps8<DT, PRE, R, 0>(cells, lane_off, wq[sl], weq[sl], xm, xe);
+      }
+    }
+    __syncthreads();                              // the epoch's adds are in
+    const bool norm = (epoch & 7) == 7 || e0 + EPOCH8 >= nchunks;
+#pragma unroll
+    for (int r = 0; r < R; ++r) fold8<DT, R, W>(my_cells + r * RB, dg[r], norm);
+    __syncthreads();                              // cells clear before the next epoch
+  }
+
+  // windows -> one digit array per row in LDS (over the cells, all zero now)
+  int64_t* const D = reinterpret_cast<int64_t*>(cells);        // D[(r * ND + j) * 64 + lane]
+  static_assert(R * ND * 64 * 8 <= (CB + NC8) * CS, "digit array fits over the cells");
+  const int jb = (8 * (CB + wave * CW8)) >> 5;                  // window digit 0 in the accumulator
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int d = WD8 - 1; d > 0; --d)             // anything beyond digit ND-1 joins digit ND-1
+      if (jb + d >= ND) { dg[r][d - 1] += dg[r][d] * (int64_t(1) << 32); dg[r][d] = 0; }
+#pragma unroll
+    for (int d = 0; d < WD8; ++d)
+      if (jb + d < ND) atomicAdd(reinterpret_cast<unsigned long long*>(D + (r * ND + jb + d) * 64 + lane),
+                                 static_cast<unsigned long long>(dg[r][d]));
+  }
+  __syncthreads();
+  // wave r finishes row r
+  const int r = wave;
+  if (r >= R || !n_ok || !(m0 + r < a.M)) return;
+  const int64_t m = m0 + r;
+  int64_t acc[ND];
+#pragma unroll
+  for (int j = 0; j < ND; ++j) acc[j] = D[(r * ND + j) * 64 + lane];
+  int64_t* dd = a.acc + (m * a.N + n) * ND;
+  if (a.epi == EPI_ADD || a.epi == EPI_ADD_ROUND) {
+#pragma unroll
+    for (int j = 0; j < ND; ++j) acc[j] += dd[j];
+  }
+  if (a.epi == EPI_STORE || a.epi == EPI_ADD) {
+#pragma unroll
+    for (int j = 0; j < ND; ++j) dd[j] = acc[j];
+  } else {
+    a.y[m * a.y_sm + n * a.y_sn] = __uint_as_float(round_digits_to_f32(acc));
   }
 }
 
 // ---------------------------------------------------------------- w pre-decode
 // w [N][K] (any strides) -> significands int32 and exponent words uint16,
 // both [Kp/16][Np][16] (chunk-major: the 16 k of one chunk of row n are
-// contiguous, rows follow each other), zero outside N x K.  The GEMM kernel
+// contiguous, rows follow each other), +0 outside N x K.  The GEMM kernel
 // then loads w with aligned 16-byte loads, coalesced across the wave, and
 // spends no instructions on decoding it.  (Row-major [Np][Kp] put each lane
 // of a wave in its own 2 MiB page once K reached 2^19, and the GEMM ran at
@@ -528,21 +727,23 @@ __global__ __launch_bounds__(64) void k_gemm(GemmArgs a, const void* __restrict_
 struct PredecodeArgs {
   const void* w; int64_t w_sn, w_sk;
   int64_t N, K, Np, Kp;
-  int32_t* wsig; uint16_t* wexp;
+  int32_t* wsig; void* wexp;          // exponent words: uint16 (k_gemm) or uint32 (k_gemm8)
 };
 
-template <int DT, bool TWOS, uint32_t ESH>
+template <int DT, bool TWOS, uint32_t ESH, typename EW>
 __global__ __launch_bounds__(256) void k_predecode_w(PredecodeArgs a) {
   const int64_t total = a.Np * a.Kp;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
     const int64_t c = i / (a.Np * V_KC), r = i % (a.Np * V_KC);
     const int64_t n = r / V_KC, k = c * V_KC + r % V_KC;
-    int32_t m = 0;
-    uint32_t e = 0u;
-    if (n < a.N && k < a.K) decode<DT, TWOS, 1, ESH>(load_elem<DT>(a.w, n * a.w_sn + k * a.w_sk), m, e);
+    int32_t m;
+    uint32_t e;
+    // padding holds the decode of +0 (significand 0, exponent field 1), so
+    // the exponent sums of padded products stay inside the counter range
+    decode<DT, TWOS, 1, ESH>(n < a.N && k < a.K ? load_elem<DT>(a.w, n * a.w_sn + k * a.w_sk) : 0u, m, e);
     a.wsig[i] = m;
-    a.wexp[i] = static_cast<uint16_t>(e);
+    static_cast<EW*>(a.wexp)[i] = static_cast<EW>(e);
   }
 }
 
@@ -637,22 +838,28 @@ constexpr int64_t K_BLOCK = int64_t(1) << 15;
 
 // workspace: the pre-decoded w, then (det_gemm with K > K_BLOCK) int64
 // digit scratch for the output
-int64_t predecode_bytes(int64_t N, int64_t K) { return round_up(N, V_BN) * round_up(K, V_KC) * (4 + 2); }
+// (det_gemm's kernel takes 32-bit exponent words, the partial's 16-bit ones)
+int64_t predecode_bytes(int out_mode, int64_t N, int64_t K) {
+  return round_up(N, V_BN) * round_up(K, V_KC) * (out_mode == 1 ? 4 + 4 : 4 + 2);
+}
 int64_t workspace_bytes(int out_mode, int64_t M, int64_t N, int64_t K) {
-  int64_t b = predecode_bytes(N, K);
+  int64_t b = predecode_bytes(out_mode, N, K);
   if (out_mode == 1 && K > K_BLOCK) b += M * N * ND * 8;
   return b;
 }
 
-template <int R>
-det_status launch_gemm_rows(det_dtype dt, int out_mode, GemmArgs a, void* ws, hipStream_t s) {
+// Raw digits (det_gemm_partial): k_gemm, two rows per wave (the 17.9 KB of
+// counters per wave let 8-9 waves share a CU; four rows measured 40% slower).
+template <int DT>
+det_status launch_partial(GemmArgs a, void* ws, hipStream_t s) {
+  constexpr int R = 2;
   a.tiles_m = (a.M + R - 1) / R;
   a.tiles_n = (a.N + V_BN - 1) / V_BN;
   const int64_t blocks = a.tiles_m * a.tiles_n;
   if (blocks == 0) return DET_OK;
   if (blocks > 0x7FFFFFFF) return fail(DET_EINVAL, "too many output tiles");
   // 16-byte vector loads of w chunks: unit K-stride and every chunk start aligned
-  const int64_t esz = dt == DET_F32 ? 4 : 2;
+  const int64_t esz = DT == DET_F32 ? 4 : 2;
   a.w_vec = a.w_sk == 1 && (reinterpret_cast<uintptr_t>(a.w) % 16) == 0 && (a.w_sn * esz) % 16 == 0;
   const bool pre = ws != nullptr && a.K > 0;
   if (pre) {
@@ -660,54 +867,86 @@ det_status launch_gemm_rows(det_dtype dt, int out_mode, GemmArgs a, void* ws, hi
     p.w = a.w; p.w_sn = a.w_sn; p.w_sk = a.w_sk;
     p.N = a.N; p.K = a.K; p.Np = round_up(a.N, V_BN); p.Kp = round_up(a.K, V_KC);
     p.wsig = static_cast<int32_t*>(ws);
-    p.wexp = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + p.Np * p.Kp * 4);
-    a.wsig = p.wsig; a.wexp = p.wexp; a.wld = p.Np * V_KC;
+    p.wexp = static_cast<char*>(ws) + p.Np * p.Kp * 4;
+    a.wsig = p.wsig; a.wexp = static_cast<const uint16_t*>(p.wexp); a.wld = p.Np * V_KC;
     const dim3 pg(grid_for(p.Np * p.Kp, 256, 8192));
-    if (dt == DET_F32) {
-      if (out_mode == 0) hipLaunchKernelGGL((k_predecode_w<DET_F32, false, EXP_SHIFT>), pg, dim3(256), 0, s, p);
-      else hipLaunchKernelGGL((k_predecode_w<DET_F32, true, 0>), pg, dim3(256), 0, s, p);
-    } else {
-      if (out_mode == 0) hipLaunchKernelGGL((k_predecode_w<DET_BF16, false, EXP_SHIFT>), pg, dim3(256), 0, s, p);
-      else hipLaunchKernelGGL((k_predecode_w<DET_BF16, true, EXP_SHIFT>), pg, dim3(256), 0, s, p);
-    }
+    hipLaunchKernelGGL((k_predecode_w<DT, false, EXP_SHIFT, uint16_t>), pg, dim3(256), 0, s, p);
     det_status st = hip_check(hipGetLastError(), "predecode launch");
     if (st != DET_OK) return st;
   }
   const dim3 grid(static_cast<unsigned>(blocks)), block(64);
-#define DET_LAUNCH(DTV, TW, PR, G) hipLaunchKernelGGL((k_gemm<DTV, TW, R, PR, G>), grid, block, 0, s, b, xb, a.w)
-  // K blocks (one block without a workspace, or when K is short)
+  // K blocks (one block without a workspace, or when K is short); the digits
+  // are carried in acc itself
   const int64_t kblk = pre ? K_BLOCK : a.K;
   const int64_t nblk = a.K > 0 ? (a.K + kblk - 1) / kblk : 1;
-  const int64_t esx = dt == DET_F32 ? 4 : 2;
-  if (out_mode == 1 && nblk > 1)                  // digit scratch behind the decoded w
-    a.acc = reinterpret_cast<int64_t*>(static_cast<char*>(ws) + predecode_bytes(a.N, a.K));
   for (int64_t ib = 0; ib < nblk; ++ib) {
     GemmArgs b = a;
     const int64_t k0 = ib * kblk;
     b.K = min(kblk, a.K - k0);
-    const void* xb = static_cast<const char*>(a.x) + k0 * a.x_sk * esx;
+    const void* xb = static_cast<const char*>(a.x) + k0 * a.x_sk * esz;
     if (pre) { b.wsig = a.wsig + k0 / V_KC * a.wld; b.wexp = a.wexp + k0 / V_KC * a.wld; }
-    const bool first = ib == 0, last = ib + 1 == nblk;
-    if (out_mode == 0) b.epi = first ? EPI_STORE : EPI_ADD;
-    else b.epi = nblk == 1 ? EPI_ROUND : first ? EPI_STORE : last ? EPI_ADD_ROUND : EPI_ADD;
-    if (dt == DET_F32) {
-      if (out_mode == 0) { if (pre) DET_LAUNCH(DET_F32, false, true, false); else DET_LAUNCH(DET_F32, false, false, false); }
-      else { if (pre) DET_LAUNCH(DET_F32, true, true, true); else DET_LAUNCH(DET_F32, true, false, true); }
-    } else {
-      if (out_mode == 0) { if (pre) DET_LAUNCH(DET_BF16, false, true, false); else DET_LAUNCH(DET_BF16, false, false, false); }
-      else { if (pre) DET_LAUNCH(DET_BF16, true, true, false); else DET_LAUNCH(DET_BF16, true, false, false); }
-    }
+    b.epi = ib == 0 ? EPI_STORE : EPI_ADD;
+    if (pre) hipLaunchKernelGGL((k_gemm<DT, R, true>), grid, block, 0, s, b, xb, a.w);
+    else hipLaunchKernelGGL((k_gemm<DT, R, false>), grid, block, 0, s, b, xb, a.w);
     det_status st = hip_check(hipGetLastError(), "gemm launch");
     if (st != DET_OK) return st;
   }
-#undef DET_LAUNCH
   return DET_OK;
 }
 
-// Two rows per wave: the 17.9 KB of counters per wave let 8-9 waves share a
-// CU; four rows (one wave per SIMD) measured 40% slower on MI355X.
+// det_gemm: k_gemm8 with two rows and 64 columns per workgroup.  f32 (64 KB
+// of cells, two workgroups per CU): 8 waves per workgroup, held to 128 VGPRs
+// so that all 16 waves fit; bf16 (35 KB): 4 waves per workgroup.
+template <int DT>
+det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s) {
+  constexpr int R = 2;
+  constexpr int W = DT == DET_F32 ? 8 : 4;
+  constexpr int MINB = DT == DET_F32 ? 2 : 1;
+  a.tiles_m = (a.M + R - 1) / R;
+  a.tiles_n = (a.N + V_BN - 1) / V_BN;
+  const int64_t blocks = a.tiles_m * a.tiles_n;
+  if (blocks == 0) return DET_OK;
+  if (blocks > 0x7FFFFFFF) return fail(DET_EINVAL, "too many output tiles");
+  const int64_t esz = DT == DET_F32 ? 4 : 2;
+  a.w_vec = a.w_sk == 1 && (reinterpret_cast<uintptr_t>(a.w) % 16) == 0 && (a.w_sn * esz) % 16 == 0;
+  const bool pre = ws != nullptr && a.K > 0;
+  if (pre) {
+    PredecodeArgs p{};
+    p.w = a.w; p.w_sn = a.w_sn; p.w_sk = a.w_sk;
+    p.N = a.N; p.K = a.K; p.Np = round_up(a.N, V_BN); p.Kp = round_up(a.K, V_KC);
+    p.wsig = static_cast<int32_t*>(ws);
+    p.wexp = static_cast<char*>(ws) + p.Np * p.Kp * 4;
+    a.wsig = p.wsig; a.wexp32 = static_cast<const uint32_t*>(p.wexp); a.wld = p.Np * V_KC;
+    const dim3 pg(grid_for(p.Np * p.Kp, 256, 8192));
+    hipLaunchKernelGGL((k_predecode_w<DT, true, exp_shift8<DT, R>(), uint32_t>), pg, dim3(256), 0, s, p);
+    det_status st = hip_check(hipGetLastError(), "predecode launch");
+    if (st != DET_OK) return st;
+  }
+  const dim3 grid(static_cast<unsigned>(blocks)), block(64 * W);
+  // K blocks; beyond one block the exact digits are carried in the
+  // workspace, behind the decoded w
+  const int64_t kblk = pre ? K_BLOCK : a.K;
+  const int64_t nblk = a.K > 0 ? (a.K + kblk - 1) / kblk : 1;
+  if (nblk > 1) a.acc = reinterpret_cast<int64_t*>(static_cast<char*>(ws) + predecode_bytes(1, a.N, a.K));
+  for (int64_t ib = 0; ib < nblk; ++ib) {
+    GemmArgs b = a;
+    const int64_t k0 = ib * kblk;
+    b.K = min(kblk, a.K - k0);
+    const void* xb = static_cast<const char*>(a.x) + k0 * a.x_sk * esz;
+    if (pre) { b.wsig = a.wsig + k0 / V_KC * a.wld; b.wexp32 = a.wexp32 + k0 / V_KC * a.wld; }
+    const bool first = ib == 0, last = ib + 1 == nblk;
+    b.epi = nblk == 1 ? EPI_ROUND : first ? EPI_STORE : last ? EPI_ADD_ROUND : EPI_ADD;
+    if (pre) hipLaunchKernelGGL((k_gemm8<DT, true, R, W, MINB>), grid, block, 0, s, b, xb, a.w);
+    else hipLaunchKernelGGL((k_gemm8<DT, false, R, W, MINB>), grid, block, 0, s, b, xb, a.w);
+    det_status st = hip_check(hipGetLastError(), "gemm launch");
+    if (st != DET_OK) return st;
+  }
+  return DET_OK;
+}
+
 det_status launch_gemm(det_dtype dt, int out_mode, GemmArgs a, void* ws, hipStream_t s) {
-  return launch_gemm_rows<2>(dt, out_mode, a, ws, s);
+  if (out_mode == 0) return dt == DET_F32 ? launch_partial<DET_F32>(a, ws, s) : launch_partial<DET_BF16>(a, ws, s);
+  return dt == DET_F32 ? launch_gemm8<DET_F32>(a, ws, s) : launch_gemm8<DET_BF16>(a, ws, s);
 }
 
 }  // namespace
