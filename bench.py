@@ -10,7 +10,9 @@ current stream), bracketed by device synchronisation.
 
 Besides the headline line this prints nothing on stdout.  The JSON line also
 carries:
-  roofline      the GEMM kernel against the VALU lane-op peak (bound "alu")
+  roofline      the GEMM kernel against the VALU lane-op peak (bound "alu"):
+                the VALU lane-ops it issues per launch (rocprofv3 SQ_INSTS_VALU x 64,
+                from the committed profile) over its time measured here
   cpu_baseline  the plain C oracle timed on the host cores over a bounded
                 block of output rows of the same workload
   parity        sampled outputs compared bit for bit with the oracle
@@ -30,30 +32,27 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-# VALU lane-op peak: 256 CUs x 64 lanes x 2.4 GHz (one full-rate wave64
-# instruction per CU per clock)
+# VALU lane-op peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (one full-rate
+# wave64 instruction per SIMD every 4 clocks)
 VALU_PEAK_LANE_OPS = 256 * 64 * 2.4e9
-# algorithmic VALU lane-ops per MAC: product, exponent sum,
-# digit index, shift, limb split, sign, and one add per limb
-OPS_PER_MAC = {"f32": 10, "bf16": 8}
 HBM_PEAK = 8.0e12
 KERNEL_SOURCE = os.path.join(ROOT, "bitwise_deterministic_exact_amd", "csrc", "detgemm.hip")
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "k_gemm_f32_4096_wide.md")
+PROFILE_RECORD = os.path.join(ROOT, "profiles", "k_gemm8_f32_4096_wide.md")
 
 
-def recorded_traffic():
-    """HBM bytes per launch of the GEMM kernel from the committed rocprofv3
-    summary (FETCH_SIZE and WRITE_SIZE, scaled by the copy calibration), or
-    None when the kernel source has changed since the counters were taken."""
+def profile_record():
+    """The GEMM kernel's per-launch counters from the committed rocprofv3
+    summary (its `profile-record:` line): VALU instructions, FETCH_SIZE and
+    WRITE_SIZE with the copy calibration, and whether the kernel source is
+    still the one they were taken on.  None if there is no record."""
     import hashlib
     try:
-        with open(TRAFFIC_RECORD) as f:
-            line = next(l for l in f if l.startswith("traffic-record:"))
+        with open(PROFILE_RECORD) as f:
+            line = next(l for l in f if l.startswith("profile-record:"))
         rec = json.loads(line.split(":", 1)[1])
         with open(KERNEL_SOURCE, "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
-                return None
-        return int((rec["fetch_kib"] * rec["fetch_scale"] + rec["write_kib"] * rec["write_scale"]) * 1024)
+            rec["current"] = hashlib.sha256(f.read()).hexdigest() == rec["source_sha256"]
+        return rec
     except (OSError, StopIteration, KeyError, ValueError):
         return None
 
@@ -153,7 +152,15 @@ def main() -> int:
     parity_ok = bool(np.array_equal(got, want))
     log(f"parity on 256 sampled outputs: {'bit-exact' if parity_ok else 'MISMATCH'}")
 
-    achieved = OPS_PER_MAC["f32"] * macs / (ms * 1e-3)
+    # roofline: VALU lane-ops the GEMM kernel issues per MAC (rocprofv3,
+    # committed profile) times the MACs of one launch, over the launch time
+    # measured above (the step is one w pre-decode, 0.2% of it, and one GEMM
+    # launch); traffic only while the profile matches the kernel source
+    rec = profile_record()
+    ops_per_mac = rec["valu_insts"] * 64 / rec["macs"] if rec else None
+    achieved = ops_per_mac * macs / (ms * 1e-3) if rec else None
+    traffic = (int((rec["fetch_kib"] * rec["fetch_scale"] + rec["write_kib"] * rec["write_scale"]) * 1024)
+               if rec and rec["current"] and rec["macs"] == macs else None)
     result = {
         "metric": "exact-GEMM GMAC/s (f32 4096^3) + % VALU peak; bit-exact vs oracle",
         "value": round(gmacs, 2),
@@ -170,10 +177,15 @@ def main() -> int:
         "config": {"workload": f"det_gemm f32 M=N=K={n}, entries sign*m*2^e, m~U[1,2), "
                                f"e~U{{-70..70}}, 1% subnormal (e in [-149,-127]), seed 2",
                    "M": M, "N": N, "K": K, "inputs": "f32", "output": "f32"},
-        "roofline": {"bound": "alu", "achieved": round(achieved / 1e12, 3),
+        "roofline": {"bound": "alu",
+                     "achieved": round(achieved / 1e12, 3) if achieved else None,
                      "peak": round(VALU_PEAK_LANE_OPS / 1e12, 3), "unit": "Tlane-op/s",
-                     "frac": round(achieved / VALU_PEAK_LANE_OPS, 4), "traffic": recorded_traffic(),
-                     "ops_per_mac": OPS_PER_MAC["f32"], "kernel": "k_gemm<f32, fp32 out>"},
+                     "frac": round(achieved / VALU_PEAK_LANE_OPS, 4) if achieved else None,
+                     "traffic": traffic,
+                     "ops_per_mac": round(ops_per_mac, 3) if ops_per_mac else None,
+                     "ops_source": "rocprofv3 SQ_INSTS_VALU x 64 per launch / MACs per launch",
+                     "profile_current": bool(rec and rec["current"]),
+                     "kernel": "k_gemm8<f32, 2 rows, 8 waves>"},
         "parity": {"sampled_outputs": 256, "bit_exact": parity_ok},
     }
 
