@@ -597,8 +597,8 @@ __device__ __forceinline__ void fold8(char* cells_c0, int64_t (&dg)[window_digit
   }
 }
 
-template <int DT, bool PRE, int R, int W, int MINB>
-__global__ __launch_bounds__(64 * W, MINB) void k_gemm8(GemmArgs a, const void* __restrict__ xg,
+template <int DT, bool PRE, int R, int W, int WPE>
+__global__ __launch_bounds__(64 * W, WPE) void k_gemm8(GemmArgs a, const void* __restrict__ xg,
                                                         const void* __restrict__ wg) {
   constexpr int W8 = W, CW8 = cells_per_wave<W>(), WD8 = window_digits<W>();
   static_assert(CW8 * W8 == NC8 && EPOCH8 % (2 * W8) == 0 && CW8 % 4 == 0, "epoch layout");
@@ -642,13 +642,25 @@ __global__ __launch_bounds__(64 * W, MINB) void k_gemm8(GemmArgs a, const void* 
   for (int i = 0; i < V_KC; ++i) { weq[0][i] = 0u; weq[1][i] = 0u; }
 #pragma unroll
   for (int r = 0; r < R; ++r) xq[0][r] = xq[1][r] = 0u;
+  // x element k0 + xj of each row: a per-row pointer plus a wave-uniform
+  // chunk offset, clamped into the row only in the last, partial chunk
+  constexpr int64_t ESZ = DT == DET_F32 ? 4 : 2;
+  const char* const xp = static_cast<const char*>(xg) + (xrow[0] + xj * a.x_sk) * ESZ;
+  const int64_t xstep = V_KC * a.x_sk * ESZ, xrstep = (xrow[R - 1] - xrow[0]) * ESZ;
   auto load = [&](int64_t c, uint32_t (&w)[V_KC], uint32_t (&we)[V_KC], uint32_t (&x)[R]) {
     const int64_t k0 = c * V_KC;
     if (PRE) load_w_pre8(a, n, k0, w, we);
     else load_w_chunk<DT>(a, wg, wrow, n_ok, k0, w);
-    const int64_t k = min<int64_t>(k0 + xj, a.K - 1);
+    if (k0 + V_KC <= a.K) {
+      static_assert(R <= 2, "rows beyond the second would need their own offsets");
+      const char* const p = xp + c * xstep;
+      x[0] = load_elem<DT>(p, 0);
+      if (R == 2) x[R - 1] = load_elem<DT>(p + xrstep, 0);
+    } else {
+      const int64_t k = min<int64_t>(k0 + xj, a.K - 1);
 #pragma unroll
-    for (int r = 0; r < R; ++r) x[r] = load_elem<DT>(xg, xrow[r] + k * a.x_sk);
+      for (int r = 0; r < R; ++r) x[r] = load_elem<DT>(xg, xrow[r] + k * a.x_sk);
+    }
   };
   if (wave < nchunks) load(wave, wq[0], weq[0], xq[0]);
 
@@ -896,12 +908,14 @@ det_status launch_partial(GemmArgs a, void* ws, hipStream_t s) {
 
 // det_gemm: k_gemm8 with two rows and 64 columns per workgroup.  f32 (64 KB
 // of cells, two workgroups per CU): 8 waves per workgroup, held to 128 VGPRs
-// so that all 16 waves fit; bf16 (35 KB): 4 waves per workgroup.
+// (4 waves per SIMD) so that both workgroups fit; bf16 (35 KB): 4 waves per
+// workgroup, 3 workgroups per CU.  WPE is the minimum of waves per SIMD the
+// register allocation must allow.
 template <int DT>
 det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s) {
   constexpr int R = 2;
   constexpr int W = DT == DET_F32 ? 8 : 4;
-  constexpr int MINB = DT == DET_F32 ? 2 : 1;
+  constexpr int WPE = DT == DET_F32 ? 4 : 3;
   a.tiles_m = (a.M + R - 1) / R;
   a.tiles_n = (a.N + V_BN - 1) / V_BN;
   const int64_t blocks = a.tiles_m * a.tiles_n;
@@ -936,8 +950,8 @@ det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s) {
     if (pre) { b.wsig = a.wsig + k0 / V_KC * a.wld; b.wexp32 = a.wexp32 + k0 / V_KC * a.wld; }
     const bool first = ib == 0, last = ib + 1 == nblk;
     b.epi = nblk == 1 ? EPI_ROUND : first ? EPI_STORE : last ? EPI_ADD_ROUND : EPI_ADD;
-    if (pre) hipLaunchKernelGGL((k_gemm8<DT, true, R, W, MINB>), grid, block, 0, s, b, xb, a.w);
-    else hipLaunchKernelGGL((k_gemm8<DT, false, R, W, MINB>), grid, block, 0, s, b, xb, a.w);
+    if (pre) hipLaunchKernelGGL((k_gemm8<DT, true, R, W, WPE>), grid, block, 0, s, b, xb, a.w);
+    else hipLaunchKernelGGL((k_gemm8<DT, false, R, W, WPE>), grid, block, 0, s, b, xb, a.w);
     det_status st = hip_check(hipGetLastError(), "gemm launch");
     if (st != DET_OK) return st;
   }
