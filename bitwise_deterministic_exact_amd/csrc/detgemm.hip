@@ -18,6 +18,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "detgemm.h"
 
 namespace {
@@ -133,10 +135,10 @@ struct GemmArgs {
   int64_t M, N, K;
   int64_t tiles_m, tiles_n;
   int w_vec;                          // w rows contiguous and 16-byte aligned per chunk
-  const int32_t* wsig;                // pre-decoded w (workspace): significands [Kp/16][Np][16]
-  const uint16_t* wexp;               // k_gemm: 16-bit exponent words [Kp/16][Np][16]
-  const uint32_t* wexp32;             // k_gemm8: 32-bit exponent words, same layout
-  int64_t wld;                        // Np * 16, the chunk pitch of both
+  const int32_t* wsig;                // pre-decoded w (workspace): significands [Kp/16][Np/64][4][64][4]
+  const uint16_t* wexp;               // k_gemm: 16-bit exponent words [Kp/16][Np/64][2][64][8]
+  const uint32_t* wexp32;             // k_gemm8: 32-bit words [Kp/16][Np/64][4][64][4]
+  int64_t wld;                        // Np * 16, the chunk pitch of all three
   int64_t* acc;                       // digits [M][N][18]: the partial's output, or scratch
   float* y; int64_t y_sm, y_sn;       // gemm: fp32 out
   int epi;                            // epilogue, see EPI_* below
@@ -328,22 +330,25 @@ __device__ __forceinline__ void steps(char* lane_base, const uint32_t (&wa)[V_KC
 }
 
 // the lane's pre-decoded w chunk: 16 significands and 16 exponent words
-// (rows padded to the tile and K to the chunk, so no bounds logic).  The
-// workspace is chunk-major, so a wave's 64 lanes read one contiguous 4 KiB
-// of significands and 2 KiB of exponents, whatever the length of K.
-__device__ __forceinline__ void load_w_pre(const GemmArgs& a, int64_t n, int64_t k0, uint32_t (&wa)[V_KC],
-                                           uint32_t (&wb)[V_KC / 2]) {
-  const int64_t off = (k0 / V_KC) * a.wld + n * V_KC;
-  const uint4* ps = reinterpret_cast<const uint4*>(a.wsig + off);
-  const uint4* pe = reinterpret_cast<const uint4*>(a.wexp + off);
+// (rows padded to the tile and K to the chunk, so no bounds logic).  Each
+// chunk of the workspace holds, per 64-column tile, 16-byte sub-blocks laid
+// out [4][64][4] for 32-bit words and [2][64][8] for 16-bit ones: every
+// 16-byte load of the wave reads one contiguous 1 KiB, and the sub-blocks
+// sit at fixed 1 KiB steps from the lane's pointer (immediate offsets).
+// `ws`, `we` point at the lane's sub-block 0 of chunk 0.
+__device__ __forceinline__ void load_w_pre(const GemmArgs& a, const int32_t* ws, const uint16_t* we, int64_t k0,
+                                           uint32_t (&wa)[V_KC], uint32_t (&wb)[V_KC / 2]) {
+  const int64_t c = (k0 / V_KC) * a.wld;
+  const uint4* ps = reinterpret_cast<const uint4*>(ws + c);
+  const uint4* pe = reinterpret_cast<const uint4*>(we + c);
 #pragma unroll
   for (int i = 0; i < V_KC / 4; ++i) {
-    const uint4 v = ps[i];
+    const uint4 v = ps[i * 64];
     wa[4 * i] = v.x; wa[4 * i + 1] = v.y; wa[4 * i + 2] = v.z; wa[4 * i + 3] = v.w;
   }
 #pragma unroll
   for (int i = 0; i < V_KC / 8; ++i) {
-    const uint4 v = pe[i];
+    const uint4 v = pe[i * 64];
     wb[4 * i] = v.x; wb[4 * i + 1] = v.y; wb[4 * i + 2] = v.z; wb[4 * i + 3] = v.w;
   }
 }
@@ -353,10 +358,10 @@ __device__ __forceinline__ void load_w_pre(const GemmArgs& a, int64_t n, int64_t
 // when decoded)
 template <int DT, bool PRE, int R>
 __device__ __forceinline__ void load_chunk(const GemmArgs& a, const void* __restrict__ xg,
-                                           const void* __restrict__ wg, int64_t n, int64_t wrow, bool n_ok,
-                                           const int64_t (&xrow)[R], int xj, int64_t k0, uint32_t (&w)[V_KC],
-                                           uint32_t (&we)[V_KC / 2], uint32_t (&x)[R]) {
-  if (PRE) load_w_pre(a, n, k0, w, we);
+                                           const void* __restrict__ wg, const int32_t* wsl, const uint16_t* wel,
+                                           int64_t wrow, bool n_ok, const int64_t (&xrow)[R], int xj, int64_t k0,
+                                           uint32_t (&w)[V_KC], uint32_t (&we)[V_KC / 2], uint32_t (&x)[R]) {
+  if (PRE) load_w_pre(a, wsl, wel, k0, w, we);
   else load_w_chunk<DT>(a, wg, wrow, n_ok, k0, w);
   const int64_t k = min<int64_t>(k0 + xj, a.K - 1);
 #pragma unroll
@@ -391,6 +396,9 @@ __global__ __launch_bounds__(64) void k_gemm(GemmArgs a, const void* __restrict_
     xrow[r] = min(m0 + r, a.M - 1) * a.x_sm;
   }
   const int xj = lane & 15;                       // this lane's k within a chunk (x side)
+  // the lane's sub-block 0 in chunk 0 of the decoded w
+  const int32_t* const wsl = a.wsig + n0 * V_KC + lane * 4;
+  const uint16_t* const wel = a.wexp + n0 * V_KC + lane * 8;
 
   int64_t dg[R][ND];
 #pragma unroll
@@ -412,7 +420,7 @@ __global__ __launch_bounds__(64) void k_gemm(GemmArgs a, const void* __restrict_
   }
 #pragma unroll
   for (int p = 0; p + 1 < NB; ++p)
-    if (p * V_KC < a.K) load_chunk<DT, PRE, R>(a, xg, wg, n, wrow, n_ok, xrow, xj, p * V_KC, wq[p], wbq[p], xq[p]);
+    if (p * V_KC < a.K) load_chunk<DT, PRE, R>(a, xg, wg, wsl, wel, wrow, n_ok, xrow, xj, p * V_KC, wq[p], wbq[p], xq[p]);
 
   for (int64_t c0 = 0; c0 * V_KC < a.K; c0 += NB) {
 #pragma unroll
@@ -421,7 +429,7 @@ __global__ __launch_bounds__(64) void k_gemm(GemmArgs a, const void* __restrict_
       if (k0 >= a.K) break;
       const int64_t kp = k0 + (NB - 1) * V_KC;    // prefetch into the slot freed by the last chunk
       if (kp < a.K)
-        load_chunk<DT, PRE, R>(a, xg, wg, n, wrow, n_ok, xrow, xj, kp, wq[(sl + NB - 1) % NB],
+        load_chunk<DT, PRE, R>(a, xg, wg, wsl, wel, wrow, n_ok, xrow, xj, kp, wq[(sl + NB - 1) % NB],
                                wbq[(sl + NB - 1) % NB], xq[(sl + NB - 1) % NB]);
       const bool kin = k0 + xj < a.K;
       int xm[R], xe[R];
@@ -462,94 +470,144 @@ __global__ __launch_bounds__(64) void k_gemm(GemmArgs a, const void* __restrict_
 //
 // det_gemm needs only the exact sum, not the raw digits, so a product may go
 // into the accumulator in any pieces whose values add up to it.  Here it goes
-// whole, with ONE LDS atomic, into one cell of an 8-bit grid: cell c of an
-// output weighs 2^(8c - 298) and a product at bit offset o goes into cell
-// o div 8 as T = P * 2^(o mod 8), P the signed significand product.  f32:
-// |P| < 2^48, so |T| < 2^55 and cells are int64 (ds_add_u64); bf16: |P| <
-// 2^16, |T| < 2^23, int32 cells (ds_add_u32).  Either way a cell takes 256
-// adds before it must be folded into the digits.  f32 offsets reach 506 and
-// bf16 offsets run from 32 to 538, so 64 cells cover every product (bf16:
-// cells 4..67).
+// whole, with ONE LDS atomic, into one cell of a fixed grid: cell c of an
+// output weighs 2^(B*c - 298) and takes T = P * 2^s, P the product of the
+// (sign-applied) significands and s the product's bit offset o modulo B.
+// Two grids (the traits below):
+//   Cells8 (f32): B = 8, cell o div 8, s = o mod 8 applied per product;
+//     |P| < 2^48, so |T| < 2^55 and the cells are int64 (ds_add_u64), 256
+//     adds between folds, 64 cells (o <= 506).  Exponent words carry
+//     o * stride / 8, so the cell's byte offset is o & ~(stride - 1) (one
+//     and-or with the lane's offset) and s one bit-field extract.
+//   Cells4 (bf16): B = 4, and each side's exponent is split into a cell part
+//     and a 2-bit shift that is applied to that side's significand when it is
+//     decoded: ex = 4cx + sx, ew = 4cw + sw, x' = x_sig << sx, w' = w_sig <<
+//     sw, |x'|, |w'| < 2^11, so T = x' * w' has |T| < 2^22 and goes into cell
+//     cx + cw.  Both sides also carry their part of the byte address (x: the
+//     cell part and the row, w: the cell part and the lane), so one DPP add
+//     gives the address and one 24-bit multiply the value: two VALU
+//     instructions per product.  int32 cells, 512 adds between folds, 128
+//     cells (offsets 32..538 are cells 7..134).
 //
-// The cells of R x 64 outputs fill R x 32 KB (f32) or R x 17 KB (bf16): too
-// much for one wave if the CU is to hold enough waves to keep its VALUs
-// busy, so W waves share them.  A workgroup owns rows m0..m0+R-1 and 64
-// columns; its waves take the K-chunks in turn (wave v: chunks v, v + W,
-// ...) and all add into the same cells, which the LDS atomics keep exact.
-// Every 256 k of K (an epoch) the workgroup meets at a barrier, each wave
-// folds its 1/W of the cells into a window of int64 digits in its registers
-// and clears them, and a second barrier opens the next epoch.  At the end the
-// windows are added into one digit array per row in LDS and waves 0..R-1
-// finish the rows (round to fp32, or carry the digits to the next K block).
-//
-// Per product the VALU runs the x broadcast (DPP), the exponent sum (DPP add),
-// the cell address (and-or), the shift (bit-field extract), the product and
-// the shift of T: six instructions, about half of what the same product
-// costs split into 16-bit fields with four atomics.
-constexpr int NC8 = 64;                         // cells per output
-constexpr int64_t KFLUSH8 = 256;                // adds a cell takes between folds
-constexpr int64_t EPOCH8 = KFLUSH8 / V_KC;      // chunks per epoch, all waves together
-template <int DT>
-constexpr int cell_bytes() { return DT == DET_F32 ? 8 : 4; }
-template <int DT>
-constexpr int cell_base() { return DT == DET_F32 ? 0 : 4; }     // first cell a product can reach
-template <int W>
-constexpr int cells_per_wave() { return NC8 / W; }
-template <int W>
-constexpr int window_digits() { return NC8 / W / 4 + 2; }
+// The cells of R x 64 outputs fill R x 32 KB: too much for one wave if the
+// CU is to hold enough waves to keep its VALUs busy, so W waves share them.
+// A workgroup owns rows m0..m0+R-1 and 64 columns; its waves take the
+// K-chunks in turn (wave v: chunks v, v + W, ...) and all add into the same
+// cells, which the LDS atomics keep exact.  At the end of every epoch (the
+// adds a cell can take) the workgroup meets at a barrier, each wave folds its
+// 1/W of the cells into a window of int64 digits in its registers and clears
+// them, and a second barrier opens the next epoch.  At the end the windows
+// are added into one digit array per row in LDS and waves 0..R-1 finish the
+// rows (round to fp32, or carry the digits to the next K block).
 
-// Exponent words of k_gemm8 carry the offset times the cell stride / 8
-// (the stride: R rows x 64 lanes x 8 B for f32, x 4 B for bf16), so that
-// o & ~(stride - 1) is the cell's byte offset and bits ESH..ESH+2 are the
-// shift inside the cell.
 template <int DT, int R>
-constexpr uint32_t exp_shift8() { return (DT == DET_F32 ? 6u : 5u) + (R == 2 ? 1u : 0u); }
+struct Cells8 {
+  static constexpr int NCELL = 64;              // cells that products reach
+  static constexpr int FIRST = DT == DET_F32 ? 0 : 4;     // first reachable cell (bf16: offset >= 32)
+  static constexpr int BITS = 8;
+  static constexpr int ES = DT == DET_F32 ? 8 : 4;        // bytes per cell
+  static constexpr int RB = 64 * ES;                      // bytes between rows
+  static constexpr uint32_t CS = R * RB;                  // bytes between cells
+  static constexpr int ALLOC = FIRST + NCELL;             // cells allocated (the first FIRST unused)
+  static constexpr int64_t KFLUSH = 256;
+  static constexpr int NORM_EVERY = 8;                    // folds between carry passes
+  static constexpr uint32_t ESH = (DT == DET_F32 ? 6u : 5u) + (R == 4 ? 2u : R == 2 ? 1u : 0u);   // log2(CS / 8)
+  static_assert(R == 1 || R == 2 || R == 4, "the cell stride must be a power of two");
+  using cell_t = typename std::conditional<DT == DET_F32, int64_t, int32_t>::type;
+
+  __device__ static void decode_x(uint32_t b, int /*r*/, int32_t& m, uint32_t& e) {
+    decode<DT, true, 0, ESH>(b, m, e);
+  }
+  __device__ static void decode_w(uint32_t b, uint32_t /*lane*/, int32_t& m, uint32_t& e) {
+    decode<DT, true, 1, ESH>(b, m, e);
+  }
+  // one product; xm, xe are x's (already broadcast) significand and word
+  __device__ static void step(char* cbase, uint32_t lane_off, int r, int xm, uint32_t xe, int32_t wm,
+                              uint32_t we) {
+    const uint32_t o = xe + we;
+    char* const p = cbase + ((o & ~(CS - 1u)) | (lane_off + r * RB));
+    const uint32_t sh = (o >> ESH) & 7u;
+    if (DT == DET_F32) {
+      const uint64_t T = static_cast<uint64_t>(static_cast<int64_t>(xm) * wm) << sh;
+      atomicAdd(reinterpret_cast<unsigned long long*>(p), static_cast<unsigned long long>(T));
+    } else {
+      atomicAdd(reinterpret_cast<int*>(p), static_cast<int>(static_cast<uint32_t>(__mul24(xm, wm)) << sh));
+    }
+  }
+};
+
+template <int R>
+struct Cells4 {
+  static constexpr int NCELL = 128;
+  static constexpr int FIRST = 7;                         // offsets >= 32 -> cells >= 7
+  static constexpr int BITS = 4;
+  static constexpr int ES = 4;
+  static constexpr int RB = 64 * ES;
+  static constexpr uint32_t CS = R * RB;
+  static constexpr int ALLOC = NCELL;                     // addresses are rebased to cell 7
+  static constexpr int64_t KFLUSH = 512;
+  static constexpr int NORM_EVERY = 1;
+  using cell_t = int32_t;
+
+  // bf16 bits -> shifted significand and address word.  x: exponent offset
+  // ex = max(E,1) + 30 (31..284), word (ex div 4 - 7) * CS + row offset;
+  // w: ew = max(E,1) (1..254), word ew div 4 * CS + lane offset.  The two
+  // words add up to (o div 4 - 7) * CS + row + lane, o = ex + ew, within the
+  // 128 cells.
+  __device__ static void decode_x(uint32_t b, int r, int32_t& m, uint32_t& e) {
+    const uint32_t E = (b >> 7) & 0xFFu;
+    const uint32_t mag = (b & 0x7Fu) | (min(E, 1u) << 7);
+    const uint32_t ex = max(E, 1u) + 30u;
+    const uint32_t neg = (b >> 15) & 1u, sgn = 0u - neg;
+    m = static_cast<int32_t>(((mag << (ex & 3u)) ^ sgn) + neg);
+    e = ((ex >> 2) - FIRST) * CS + static_cast<uint32_t>(r) * RB;
+  }
+  __device__ static void decode_w(uint32_t b, uint32_t lane, int32_t& m, uint32_t& e) {
+    const uint32_t E = (b >> 7) & 0xFFu;
+    const uint32_t mag = (b & 0x7Fu) | (min(E, 1u) << 7);
+    const uint32_t ew = max(E, 1u);
+    const uint32_t neg = (b >> 15) & 1u, sgn = 0u - neg;
+    m = static_cast<int32_t>(((mag << (ew & 3u)) ^ sgn) + neg);
+    e = (ew >> 2) * CS + lane * 4u;
+  }
+  __device__ static void step(char* cbase, uint32_t /*lane_off*/, int /*r*/, int xm, uint32_t xe, int32_t wm,
+                              uint32_t we) {
+    atomicAdd(reinterpret_cast<int*>(cbase + (xe + we)), __mul24(xm, wm));
+  }
+};
 
 // the lane's pre-decoded w chunk for k_gemm8: 16 significands and 16 32-bit
-// exponent words, chunk-major like load_w_pre
-__device__ __forceinline__ void load_w_pre8(const GemmArgs& a, int64_t n, int64_t k0, uint32_t (&wa)[V_KC],
-                                            uint32_t (&wb)[V_KC]) {
-  const int64_t off = (k0 / V_KC) * a.wld + n * V_KC;
-  const uint4* ps = reinterpret_cast<const uint4*>(a.wsig + off);
-  const uint4* pe = reinterpret_cast<const uint4*>(a.wexp32 + off);
+// words, both laid out like load_w_pre's 32-bit words
+__device__ __forceinline__ void load_w_pre8(const GemmArgs& a, const int32_t* ws, const uint32_t* we, int64_t k0,
+                                            uint32_t (&wa)[V_KC], uint32_t (&wb)[V_KC]) {
+  const int64_t c = (k0 / V_KC) * a.wld;
+  const uint4* ps = reinterpret_cast<const uint4*>(ws + c);
+  const uint4* pe = reinterpret_cast<const uint4*>(we + c);
 #pragma unroll
   for (int i = 0; i < V_KC / 4; ++i) {
-    const uint4 v = ps[i], e = pe[i];
+    const uint4 v = ps[i * 64], e = pe[i * 64];
     wa[4 * i] = v.x; wa[4 * i + 1] = v.y; wa[4 * i + 2] = v.z; wa[4 * i + 3] = v.w;
     wb[4 * i] = e.x; wb[4 * i + 1] = e.y; wb[4 * i + 2] = e.z; wb[4 * i + 3] = e.w;
   }
 }
 
-// One chunk: step J multiplies x element J of the row (broadcast from lane J
-// of every 16-lane row) by the lane's w element J and adds the shifted
-// product into its cell with one atomic.
-template <int DT, bool PRE, int R, int J>
-__device__ __forceinline__ void steps8(char* cbase, uint32_t lane_off, const uint32_t (&wa)[V_KC],
+// One chunk: step J takes x element J of each row (DPP broadcast from lane J
+// of every 16-lane row) and the lane's w element J.
+template <class G, int DT, bool PRE, int R, int J>
+__device__ __forceinline__ void steps8(char* cbase, uint32_t lane, uint32_t lane_off, const uint32_t (&wa)[V_KC],
                                        const uint32_t (&wb)[V_KC], const int (&xm)[R], const int (&xe)[R]) {
-  constexpr uint32_t CS = R * 64u * cell_bytes<DT>();
-  constexpr uint32_t ESH = exp_shift8<DT, R>();
   int32_t wm;
   uint32_t we;
   if (PRE) {
     wm = static_cast<int32_t>(wa[J]);
     we = wb[J];
   } else {
-    decode<DT, true, 1, ESH>(wa[J], wm, we);
+    G::decode_w(wa[J], lane, wm, we);
   }
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const uint32_t o = static_cast<uint32_t>(bcast<J>(xe[r])) + we;
-    char* const p = cbase + ((o & ~(CS - 1u)) | (lane_off + r * 64u * cell_bytes<DT>()));
-    const uint32_t sh = (o >> ESH) & 7u;
-    if (DT == DET_F32) {
-      const uint64_t T = static_cast<uint64_t>(static_cast<int64_t>(bcast<J>(xm[r])) * wm) << sh;
-      atomicAdd(reinterpret_cast<unsigned long long*>(p), static_cast<unsigned long long>(T));
-    } else {
-      atomicAdd(reinterpret_cast<int*>(p),
-                static_cast<int>(static_cast<uint32_t>(__mul24(bcast<J>(xm[r]), wm)) << sh));
-    }
-  }
-  if constexpr (J + 1 < V_KC) steps8<DT, PRE, R, J + 1>(cbase, lane_off, wa, wb, xm, xe);
+  for (int r = 0; r < R; ++r)
+    G::step(cbase, lane_off, r, bcast<J>(xm[r]), static_cast<uint32_t>(bcast<J>(xe[r])), wm, we);
+  if constexpr (J + 1 < V_KC) steps8<G, DT, PRE, R, J + 1>(cbase, lane, lane_off, wa, wb, xm, xe);
 }
 
 // dg += v * scale for a 32-bit v (unsigned or signed) and a power-of-two
@@ -564,32 +622,34 @@ __device__ __forceinline__ void mad_i32(int64_t& dg, int32_t v, uint32_t scale) 
   asm("v_mad_i64_i32 %0, %1, %2, %3, %0" : "+v"(dg), "=s"(carry) : "v"(v), "s"(scale));
 }
 
-// Fold the CW8 cells this wave owns (cells c0 .. c0 + CW8 - 1 of this lane)
-// into its window (window digit 0 weighs the cell c0's bit position; cell
-// c0 + i lands at bit 8i of the window) and clear them; with `norm`, carry
-// the window so that all but its top digit lie in [0, 2^32).
-template <int DT, int R, int W>
-__device__ __forceinline__ void fold8(char* cells_c0, int64_t (&dg)[window_digits<W>()], bool norm) {
-  constexpr int CS = R * 64 * cell_bytes<DT>();
-  constexpr int WD8 = window_digits<W>();
+// Fold the CW cells this wave owns (CW consecutive cells of this lane and
+// row, starting at `c0`) into its window and clear them.  Window digit 0
+// weighs 2^(32 jb) with jb = (first cell's bit position) div 32; cell i of
+// the wave sits OFF + B*i bits above it, OFF the same for every wave.  With
+// `norm`, carry the window so that all but its top digit lie in [0, 2^32).
+template <class G, int CW, int OFF, int WD>
+__device__ __forceinline__ void fold8(char* c0, int64_t (&dg)[WD], bool norm) {
 #pragma unroll
-  for (int i = 0; i < cells_per_wave<W>(); ++i) {
-    const uint32_t scale = 1u << (8 * (i & 3));
-    if (DT == DET_F32) {
-      int64_t* q = reinterpret_cast<int64_t*>(cells_c0 + i * CS);
+  for (int i = 0; i < CW; ++i) {
+    const int bit = OFF + G::BITS * i;
+    const uint32_t scale = 1u << (bit & 31);
+    if (sizeof(typename G::cell_t) == 8) {
+      int64_t* q = reinterpret_cast<int64_t*>(c0 + i * G::CS);
       const int64_t v = *q;
       *q = 0;
-      mad_u32(dg[i >> 2], static_cast<uint32_t>(v), scale);
-      mad_i32(dg[(i >> 2) + 1], static_cast<int32_t>(v >> 32), scale);
+      mad_u32(dg[bit >> 5], static_cast<uint32_t>(v), scale);
+      mad_i32(dg[(bit >> 5) + 1], static_cast<int32_t>(v >> 32), scale);
     } else {
-      int* q = reinterpret_cast<int*>(cells_c0 + i * CS);
-      mad_i32(dg[i >> 2], *q, scale);
+      int* q = reinterpret_cast<int*>(c0 + i * G::CS);
+      mad_i32(dg[bit >> 5], *q, scale);
       *q = 0;
     }
+    // keep the scheduler from reading many cells ahead (register pressure)
+    if ((i & 3) == 3) asm volatile("" ::: "memory");
   }
   if (norm) {
 #pragma unroll
-    for (int j = 0; j + 1 < WD8; ++j) {
+    for (int j = 0; j + 1 < WD; ++j) {
       const int64_t carry = dg[j] >> 32;
       dg[j] -= carry * (int64_t(1) << 32);
       dg[j + 1] += carry;
@@ -597,23 +657,25 @@ __device__ __forceinline__ void fold8(char* cells_c0, int64_t (&dg)[window_digit
   }
 }
 
-template <int DT, bool PRE, int R, int W, int WPE>
+template <class G, int DT, bool PRE, int R, int W, int WPE>
 __global__ __launch_bounds__(64 * W, WPE) void k_gemm8(GemmArgs a, const void* __restrict__ xg,
-                                                        const void* __restrict__ wg) {
-  constexpr int W8 = W, CW8 = cells_per_wave<W>(), WD8 = window_digits<W>();
-  static_assert(CW8 * W8 == NC8 && EPOCH8 % (2 * W8) == 0 && CW8 % 4 == 0, "epoch layout");
-  constexpr int RB = 64 * cell_bytes<DT>();                     // bytes between rows
-  constexpr int CS = R * RB;                                    // bytes between cells
-  constexpr int CB = cell_base<DT>();                           // first cell a product reaches
-  constexpr uint32_t ESH = exp_shift8<DT, R>();
-  constexpr int NB = 2;                                         // operand ring slots
-  __shared__ __align__(16) char cells[(CB + NC8) * CS];
+                                                       const void* __restrict__ wg) {
+  constexpr int CW = G::NCELL / W;                          // cells each wave folds
+  constexpr int OFF = (G::BITS * G::FIRST) & 31;            // bit of a wave's first cell within its digit
+  // window digits: the window's value stays below 2^(OFF + B(CW-1) + cell
+  // bits + log2 CW + 1), so this many digits hold it with the top one signed
+  constexpr int VB = sizeof(typename G::cell_t) == 8 ? 63 : 31;
+  constexpr int LOG2CW = CW <= 1 ? 0 : CW <= 2 ? 1 : CW <= 4 ? 2 : CW <= 8 ? 3 : CW <= 16 ? 4 : 5;
+  constexpr int WD = (OFF + G::BITS * (CW - 1) + VB + LOG2CW + 1 + 31) / 32;
+  constexpr int64_t EPOCH = G::KFLUSH / V_KC;               // chunks per epoch, all waves together
+  static_assert(CW * W == G::NCELL && EPOCH % (2 * W) == 0 && (G::BITS * CW) % 32 == 0, "epoch layout");
+  __shared__ __align__(16) char cells[G::ALLOC * G::CS];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t tile = xcd_tile();
   const int64_t m0 = (tile % a.tiles_m) * R, n0 = (tile / a.tiles_m) * V_BN;
 
-  for (int q = threadIdx.x; q < (CB + NC8) * CS / 16; q += 64 * W8)
+  for (int q = threadIdx.x; q < G::ALLOC * static_cast<int>(G::CS) / 16; q += 64 * W)
     reinterpret_cast<uint4*>(cells)[q] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
 
@@ -628,34 +690,36 @@ __global__ __launch_bounds__(64 * W, WPE) void k_gemm8(GemmArgs a, const void* _
     xrow[r] = min(m0 + r, a.M - 1) * a.x_sm;
   }
   const int xj = lane & 15;
-  const uint32_t lane_off = static_cast<uint32_t>(lane * cell_bytes<DT>());
+  const uint32_t lane_off = static_cast<uint32_t>(lane * G::ES);
 
-  int64_t dg[R][WD8];
+  int64_t dg[R][WD];
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int j = 0; j < WD8; ++j) dg[r][j] = 0;
+    for (int j = 0; j < WD; ++j) dg[r][j] = 0;
 
   const int64_t nchunks = (a.K + V_KC - 1) / V_KC;
-  uint32_t wq[NB][V_KC], weq[NB][V_KC], xq[NB][R];
+  uint32_t wq[2][V_KC], weq[2][V_KC], xq[2][R];
 #pragma unroll
   for (int i = 0; i < V_KC; ++i) { weq[0][i] = 0u; weq[1][i] = 0u; }
 #pragma unroll
   for (int r = 0; r < R; ++r) xq[0][r] = xq[1][r] = 0u;
-  // x element k0 + xj of each row: a per-row pointer plus a wave-uniform
+  // x element k0 + xj of each row: a per-lane pointer plus a wave-uniform
   // chunk offset, clamped into the row only in the last, partial chunk
   constexpr int64_t ESZ = DT == DET_F32 ? 4 : 2;
   const char* const xp = static_cast<const char*>(xg) + (xrow[0] + xj * a.x_sk) * ESZ;
-  const int64_t xstep = V_KC * a.x_sk * ESZ, xrstep = (xrow[R - 1] - xrow[0]) * ESZ;
+  const int64_t xstep = V_KC * a.x_sk * ESZ, xrstep = a.x_sm * ESZ;
+  const bool rows_in = m0 + R <= a.M;             // all R rows exist: rows are x_sm apart
+  const int32_t* const wsl = a.wsig + n0 * V_KC + lane * 4;       // the lane's sub-block 0 of chunk 0
+  const uint32_t* const wel = a.wexp32 + n0 * V_KC + lane * 4;
   auto load = [&](int64_t c, uint32_t (&w)[V_KC], uint32_t (&we)[V_KC], uint32_t (&x)[R]) {
     const int64_t k0 = c * V_KC;
-    if (PRE) load_w_pre8(a, n, k0, w, we);
+    if (PRE) load_w_pre8(a, wsl, wel, k0, w, we);
     else load_w_chunk<DT>(a, wg, wrow, n_ok, k0, w);
-    if (k0 + V_KC <= a.K) {
-      static_assert(R <= 2, "rows beyond the second would need their own offsets");
+    if (k0 + V_KC <= a.K && rows_in) {
       const char* const p = xp + c * xstep;
-      x[0] = load_elem<DT>(p, 0);
-      if (R == 2) x[R - 1] = load_elem<DT>(p + xrstep, 0);
+#pragma unroll
+      for (int r = 0; r < R; ++r) x[r] = load_elem<DT>(p + r * xrstep, 0);
     } else {
       const int64_t k = min<int64_t>(k0 + xj, a.K - 1);
 #pragma unroll
@@ -664,46 +728,52 @@ __global__ __launch_bounds__(64 * W, WPE) void k_gemm8(GemmArgs a, const void* _
   };
   if (wave < nchunks) load(wave, wq[0], weq[0], xq[0]);
 
-  char* const my_cells = cells + (CB + wave * CW8) * CS + lane * cell_bytes<DT>();
+  // this wave's cells: CW consecutive cells from cell FIRST + wave * CW
+  char* const my_cells = cells + (G::ALLOC - G::NCELL + wave * CW) * G::CS + lane * G::ES;
+  // Epochs of EPOCH chunks; within one, the wave takes chunks e0 + wave +
+  // i*W, i < EPOCH/W, in pairs so that the ring slot of each is static.  The
+  // barriers stay outside the unrolled pairs, so every wave meets each of
+  // them once per epoch.
   int64_t epoch = 0;
-  for (int64_t e0 = 0; e0 < nchunks; e0 += EPOCH8, ++epoch) {
+  for (int64_t e0 = 0; e0 < nchunks; e0 += EPOCH, ++epoch) {
+#pragma unroll 1
+    for (int i2 = 0; i2 < EPOCH / W; i2 += 2)
 #pragma unroll
-    for (int i = 0; i < EPOCH8 / W8; ++i) {       // this wave's chunks of the epoch
-      const int64_t c = e0 + wave + i * W8;
-      const int sl = i & 1;
+    for (int sl = 0; sl < 2; ++sl) {
+      const int64_t c = e0 + wave + (i2 + sl) * W;
       if (c < nchunks) {
-        if (c + W8 < nchunks) load(c + W8, wq[sl ^ 1], weq[sl ^ 1], xq[sl ^ 1]);
+        if (c + W < nchunks) load(c + W, wq[sl ^ 1], weq[sl ^ 1], xq[sl ^ 1]);
         const bool kin = c * V_KC + xj < a.K;
         int xm[R], xe[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           int32_t m;
           uint32_t e;
-          decode<DT, true, 0, ESH>(kin && row_ok[r] ? xq[sl][r] : 0u, m, e);
+          G::decode_x(kin && row_ok[r] ? xq[sl][r] : 0u, r, m, e);
           xm[r] = m;
           xe[r] = static_cast<int>(e);
         }
-        steps8<DT, PRE, R, 0>(cells, lane_off, wq[sl], weq[sl], xm, xe);
+        steps8<G, DT, PRE, R, 0>(cells, static_cast<uint32_t>(lane), lane_off, wq[sl], weq[sl], xm, xe);
       }
     }
     __syncthreads();                              // the epoch's adds are in
-    const bool norm = (epoch & 7) == 7 || e0 + EPOCH8 >= nchunks;
+    const bool norm = (epoch % G::NORM_EVERY) == G::NORM_EVERY - 1 || e0 + EPOCH >= nchunks;
 #pragma unroll
-    for (int r = 0; r < R; ++r) fold8<DT, R, W>(my_cells + r * RB, dg[r], norm);
+    for (int r = 0; r < R; ++r) fold8<G, CW, OFF, WD>(my_cells + r * G::RB, dg[r], norm);
     __syncthreads();                              // cells clear before the next epoch
   }
 
   // windows -> one digit array per row in LDS (over the cells, all zero now)
   int64_t* const D = reinterpret_cast<int64_t*>(cells);        // D[(r * ND + j) * 64 + lane]
-  static_assert(R * ND * 64 * 8 <= (CB + NC8) * CS, "digit array fits over the cells");
-  const int jb = (8 * (CB + wave * CW8)) >> 5;                  // window digit 0 in the accumulator
+  static_assert(R * ND * 64 * 8 <= G::ALLOC * G::CS, "digit array fits over the cells");
+  const int jb = (G::BITS * (G::FIRST + wave * CW)) >> 5;      // window digit 0 in the accumulator
 #pragma unroll
   for (int r = 0; r < R; ++r) {
 #pragma unroll
-    for (int d = WD8 - 1; d > 0; --d)             // anything beyond digit ND-1 joins digit ND-1
+    for (int d = WD - 1; d > 0; --d)              // anything beyond digit ND-1 joins digit ND-1
       if (jb + d >= ND) { dg[r][d - 1] += dg[r][d] * (int64_t(1) << 32); dg[r][d] = 0; }
 #pragma unroll
-    for (int d = 0; d < WD8; ++d)
+    for (int d = 0; d < WD; ++d)
       if (jb + d < ND) atomicAdd(reinterpret_cast<unsigned long long*>(D + (r * ND + jb + d) * 64 + lane),
                                  static_cast<unsigned long long>(dg[r][d]));
   }
@@ -729,33 +799,66 @@ __global__ __launch_bounds__(64 * W, WPE) void k_gemm8(GemmArgs a, const void* _
 }
 
 // ---------------------------------------------------------------- w pre-decode
-// w [N][K] (any strides) -> significands int32 and exponent words uint16,
-// both [Kp/16][Np][16] (chunk-major: the 16 k of one chunk of row n are
-// contiguous, rows follow each other), +0 outside N x K.  The GEMM kernel
-// then loads w with aligned 16-byte loads, coalesced across the wave, and
-// spends no instructions on decoding it.  (Row-major [Np][Kp] put each lane
-// of a wave in its own 2 MiB page once K reached 2^19, and the GEMM ran at
-// half speed.)
+// w [N][K] (any strides) -> significands int32 and exponent words (uint16
+// for k_gemm, uint32 for k_gemm8), +0 outside N x K.  Layout: chunk-major
+// (the 16 k of one chunk for all rows, then the next chunk), each chunk by
+// 64-column tile, each tile in 16-byte sub-blocks: [Kp/16][Np/64][4][64][4]
+// for 32-bit words, [Kp/16][Np/64][2][64][8] for 16-bit ones.  A GEMM wave
+// then reads w with 16-byte loads that each cover one contiguous 1 KiB, and
+// spends no instructions on decoding it.
+// (Row-major [Np][Kp] put each lane of a wave in its own 2 MiB page once K
+// reached 2^19, and the GEMM ran at half speed.)
 struct PredecodeArgs {
   const void* w; int64_t w_sn, w_sk;
   int64_t N, K, Np, Kp;
   int32_t* wsig; void* wexp;          // exponent words: uint16 (k_gemm) or uint32 (k_gemm8)
 };
 
+// Element i of a 32-bit array (layout [Kp/16][Np/64][4][64][4]) is (n, k);
+// the 16-bit exponent array of k_gemm is [Kp/16][Np/64][2][64][8].
+__device__ __forceinline__ void subblock_nk(int64_t i, int64_t np, int64_t& n, int64_t& k) {
+  const int64_t c = i / (np * V_KC), r = i % (np * V_KC);
+  const int64_t t = r / (V_BN * V_KC), r2 = r % (V_BN * V_KC);
+  const int64_t q = r2 / (V_BN * 4), r3 = r2 % (V_BN * 4);
+  n = t * V_BN + r3 / 4;
+  k = c * V_KC + q * 4 + r3 % 4;
+}
+__device__ __forceinline__ int64_t exp16_index(int64_t n, int64_t k, int64_t np) {
+  return (k / V_KC) * np * V_KC + (n / V_BN) * V_BN * V_KC + ((k % V_KC) / 8) * V_BN * 8 + (n % V_BN) * 8 + k % 8;
+}
+
 template <int DT, bool TWOS, uint32_t ESH, typename EW>
 __global__ __launch_bounds__(256) void k_predecode_w(PredecodeArgs a) {
+  static_assert(sizeof(EW) == 2, "k_gemm's exponent words are 16-bit");
   const int64_t total = a.Np * a.Kp;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
-    const int64_t c = i / (a.Np * V_KC), r = i % (a.Np * V_KC);
-    const int64_t n = r / V_KC, k = c * V_KC + r % V_KC;
+    int64_t n, k;
+    subblock_nk(i, a.Np, n, k);
     int32_t m;
     uint32_t e;
     // padding holds the decode of +0 (significand 0, exponent field 1), so
     // the exponent sums of padded products stay inside the counter range
     decode<DT, TWOS, 1, ESH>(n < a.N && k < a.K ? load_elem<DT>(a.w, n * a.w_sn + k * a.w_sk) : 0u, m, e);
     a.wsig[i] = m;
-    static_cast<EW*>(a.wexp)[i] = static_cast<EW>(e);
+    static_cast<EW*>(a.wexp)[exp16_index(n, k, a.Np)] = static_cast<EW>(e);
+  }
+}
+
+// the same for k_gemm8: the grid's w-side words (32-bit), lane = n mod 64
+template <class G, int DT>
+__global__ __launch_bounds__(256) void k_predecode_w8(PredecodeArgs a) {
+  const int64_t total = a.Np * a.Kp;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
+    int64_t n, k;
+    subblock_nk(i, a.Np, n, k);
+    int32_t m;
+    uint32_t e;
+    G::decode_w(n < a.N && k < a.K ? load_elem<DT>(a.w, n * a.w_sn + k * a.w_sk) : 0u,
+                static_cast<uint32_t>(n & (V_BN - 1)), m, e);
+    a.wsig[i] = m;
+    static_cast<uint32_t*>(a.wexp)[i] = e;
   }
 }
 
@@ -906,16 +1009,13 @@ det_status launch_partial(GemmArgs a, void* ws, hipStream_t s) {
   return DET_OK;
 }
 
-// det_gemm: k_gemm8 with two rows and 64 columns per workgroup.  f32 (64 KB
-// of cells, two workgroups per CU): 8 waves per workgroup, held to 128 VGPRs
-// (4 waves per SIMD) so that both workgroups fit; bf16 (35 KB): 4 waves per
-// workgroup, 3 workgroups per CU.  WPE is the minimum of waves per SIMD the
-// register allocation must allow.
+// det_gemm: k_gemm8 with two rows and 64 columns per workgroup, 64 KB of
+// cells (f32: Cells8, bf16: Cells4), so two workgroups share a CU: 8 waves
+// each, held to 128 VGPRs (WPE = 4 waves per SIMD) so that all 16 fit.
 template <int DT>
 det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s) {
-  constexpr int R = 2;
-  constexpr int W = DT == DET_F32 ? 8 : 4;
-  constexpr int WPE = DT == DET_F32 ? 4 : 3;
+  constexpr int R = 2, W = 8, WPE = 4;
+  using G = typename std::conditional<DT == DET_F32, Cells8<DET_F32, R>, Cells4<R>>::type;
   a.tiles_m = (a.M + R - 1) / R;
   a.tiles_n = (a.N + V_BN - 1) / V_BN;
   const int64_t blocks = a.tiles_m * a.tiles_n;
@@ -932,7 +1032,7 @@ det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s) {
     p.wexp = static_cast<char*>(ws) + p.Np * p.Kp * 4;
     a.wsig = p.wsig; a.wexp32 = static_cast<const uint32_t*>(p.wexp); a.wld = p.Np * V_KC;
     const dim3 pg(grid_for(p.Np * p.Kp, 256, 8192));
-    hipLaunchKernelGGL((k_predecode_w<DT, true, exp_shift8<DT, R>(), uint32_t>), pg, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((k_predecode_w8<G, DT>), pg, dim3(256), 0, s, p);
     det_status st = hip_check(hipGetLastError(), "predecode launch");
     if (st != DET_OK) return st;
   }
@@ -950,8 +1050,8 @@ det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s) {
     if (pre) { b.wsig = a.wsig + k0 / V_KC * a.wld; b.wexp32 = a.wexp32 + k0 / V_KC * a.wld; }
     const bool first = ib == 0, last = ib + 1 == nblk;
     b.epi = nblk == 1 ? EPI_ROUND : first ? EPI_STORE : last ? EPI_ADD_ROUND : EPI_ADD;
-    if (pre) hipLaunchKernelGGL((k_gemm8<DT, true, R, W, WPE>), grid, block, 0, s, b, xb, a.w);
-    else hipLaunchKernelGGL((k_gemm8<DT, false, R, W, WPE>), grid, block, 0, s, b, xb, a.w);
+    if (pre) hipLaunchKernelGGL((k_gemm8<G, DT, true, R, W, WPE>), grid, block, 0, s, b, xb, a.w);
+    else hipLaunchKernelGGL((k_gemm8<G, DT, false, R, W, WPE>), grid, block, 0, s, b, xb, a.w);
     det_status st = hip_check(hipGetLastError(), "gemm launch");
     if (st != DET_OK) return st;
   }
