@@ -246,73 +246,37 @@ __device__ __forceinline__ int64_t xcd_tile() {
 
 // ---------------------------------------------------------------- raw-digit kernel (det_gemm_partial)
 //
-// Every workgroup is a single wave that owns a 2 x 64 block of outputs: rows
-// m0 and m0+1, lane l owning column n0+l of both.  There is no cross-wave
-// sharing and so no barrier anywhere in the main loop.
+// The raw digits are per product and per 32-bit limb by definition (digit j
+// = sum over products of sign * bits [32j, 32j+32) of |p| * 2^298), so the
+// product is split at fixed 16-bit field boundaries: a product at bit offset
+// o is shifted by o mod 16 into the 64-bit T = |P| * 2^(o mod 16) < 2^63,
+// whose four 16-bit fields (bf16: T < 2^31, two fields) are added into
+// counters o/16 .. o/16+3 with ds_add_u32.  Digit j is then field 2j +
+// 2^16 * field 2j+1.  Products with a negative sign go into a second set of
+// counters (slots 64..98), so every add is an unsigned 16-bit field and
+// the sign costs no instruction: digit j = (P[2j] - N[2j]) + 2^16 (P[2j+1] -
+// N[2j+1]).
 //
-// Accumulator.  Each output owns 35 signed 32-bit counters in LDS, one per
-// 16-bit field of the digit array (field q weighs 2^(16q - 298); digit
-// j = field 2j + 2^16 * field 2j+1; products never reach bits >= 2^554, so
-// field 35 would always be zero).  A product at bit offset o is shifted by
-// o mod 16 into a 64-bit T = |P| * 2^(o mod 16) < 2^63 whose four 16-bit
-// fields are added, each with one ds_add_u32 and each carrying the product's
-// sign, into counters o/16 .. o/16+3 (bf16: T < 2^31, two fields).  So digit
-// j is exactly the raw digit of the definition, the sum over products of
-// sign * bits [32j, 32j+32) of |p| * 2^298.  A field is below 2^16 in
-// magnitude, so a counter takes 2^15 adds; every 2^15 k the counters are
-// folded into int64 digits held in registers.
+// Exponent words carry o << 5 and the sign at bit 15, so the sum of x's and
+// w's words holds the shift inside a field at bits 5..8 and the slot (field
+// + 64 * sign) at bits 9..15: the slot's byte offset is sum & 0xFE00 for a
+// slot stride of 512 bytes (2 rows x 64 lanes x 4 bytes), one and-or with
+// the lane's offset.  A counter takes 2^16 adds of a 16-bit field, and a
+// launch covers at most 2^15 k, so there is nothing to fold before the end.
 //
-// Counter layout: byte address field*512 + row*256 + lane*4, so the 64 lanes
-// always hit 64 distinct banks whatever their fields.  Exponent words carry
-// o << 5 (EXP_SHIFT): bits 5..8 of the sum are the shift inside a field and
-// bits 9..14 the field.
-
+// The counters of a 2 x 64 tile fill 50 KB, shared, as in k_gemm8, by the W
+// waves of a workgroup that take the K-chunks in turn; with no folds there
+// is no barrier in the main loop.  At the end waves 0 and 1 turn their row's
+// counters into digits.
 constexpr int NF = 35;                      // 16-bit fields per output
-constexpr int ROW_BYTES = 64 * 4;           // counters of one row: 64 lanes x 4 bytes
-constexpr int64_t KFLUSH = int64_t(1) << 15;      // adds a counter can take
+constexpr int NEG_SLOT = 64;                // negative products' fields start here
+constexpr int NSLOT = NEG_SLOT + NF;        // slots per output
 
-// one exact product into the counters of one output; `sum` = e_x + e_w.
-// Counter byte address: field*(R*256) + row*256 + lane*4.
-template <int DT, int R>
-__device__ __forceinline__ void accumulate(char* lane_row, int32_t xm, int32_t wm, uint32_t sum) {
-  constexpr int F = R * ROW_BYTES / 4;                  // ints between fields
-  const uint32_t s16 = (sum >> EXP_SHIFT) & 15u;        // shift inside the field
-  int* p = reinterpret_cast<int*>(lane_row + ((sum >> (EXP_SHIFT + 4)) & 63u) * (R * ROW_BYTES));   // field o/16
-  const uint32_t neg = (sum >> SIGN_BIT) & 1u, msk = 0u - neg;         // (f ^ msk) + neg = +-f
-  if (DT == DET_F32) {
-    const uint64_t T = (static_cast<uint64_t>(static_cast<uint32_t>(xm)) * static_cast<uint32_t>(wm)) << s16;
-    const uint32_t lo = static_cast<uint32_t>(T), hi = static_cast<uint32_t>(T >> 32);
-    atomicAdd(p, static_cast<int>(((lo & 0xFFFFu) ^ msk) + neg));
-    atomicAdd(p + F, static_cast<int>(((lo >> 16) ^ msk) + neg));
-    atomicAdd(p + 2 * F, static_cast<int>(((hi & 0xFFFFu) ^ msk) + neg));
-    atomicAdd(p + 3 * F, static_cast<int>(((hi >> 16) ^ msk) + neg));
-  } else {
-    const uint32_t T = (static_cast<uint32_t>(xm) * static_cast<uint32_t>(wm)) << s16;
-    atomicAdd(p, static_cast<int>(((T & 0xFFFFu) ^ msk) + neg));
-    atomicAdd(p + F, static_cast<int>(((T >> 16) ^ msk) + neg));
-  }
-}
-
-// fold the counters of one row into int64 digits and clear them
-template <int R>
-__device__ __forceinline__ void fold_row(char* lane_row, int64_t (&dg)[ND]) {
-  int* c = reinterpret_cast<int*>(lane_row);
-  constexpr int F = R * ROW_BYTES / 4;
-#pragma unroll
-  for (int j = 0; j < ND; ++j) {
-    const int hi = 2 * j + 1 < NF ? c[(2 * j + 1) * F] : 0;
-    dg[j] += static_cast<int64_t>(c[(2 * j) * F]) + (static_cast<int64_t>(hi) << 16);
-    c[(2 * j) * F] = 0;
-    if (2 * j + 1 < NF) c[(2 * j + 1) * F] = 0;
-  }
-}
-
-// One K-chunk: step J uses w element J of the lane (raw bits to decode, or,
-// with PRE, a pre-decoded significand and the packed exponent words) and
-// broadcasts x element J of each row from lane J of every 16-lane row.
+// One chunk of the raw-digit kernel: step J, all rows.
 template <int DT, int R, bool PRE, int J>
-__device__ __forceinline__ void steps(char* lane_base, const uint32_t (&wa)[V_KC], const uint32_t (&wb)[V_KC / 2],
-                                      const int (&xm)[R], const int (&xe)[R]) {
+__device__ __forceinline__ void steps_raw(char* cbase, uint32_t lane_off, const uint32_t (&wa)[V_KC],
+                                          const uint32_t (&wb)[V_KC / 2], const int (&xm)[R], const int (&xe)[R]) {
+  static_assert(R * 64 * 4 == 512, "slot offsets come from bits 9..15 of the exponent sum");
   int32_t wm;
   uint32_t we;
   if (PRE) {
@@ -324,9 +288,25 @@ __device__ __forceinline__ void steps(char* lane_base, const uint32_t (&wa)[V_KC
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const uint32_t sum = static_cast<uint32_t>(bcast<J>(xe[r])) + we;
-    accumulate<DT, R>(lane_base + r * ROW_BYTES, bcast<J>(xm[r]), wm, sum);
+    int* const p = reinterpret_cast<int*>(cbase + ((sum & 0xFE00u) | (lane_off + r * 256u)));
+    const uint32_t s16 = (sum >> EXP_SHIFT) & 15u;
+    constexpr int F = 512 / 4;                  // ints between consecutive fields
+    if (DT == DET_F32) {
+      const uint64_t T = (static_cast<uint64_t>(static_cast<uint32_t>(bcast<J>(xm[r]))) *
+                          static_cast<uint32_t>(wm)) << s16;
+      const uint32_t lo = static_cast<uint32_t>(T), hi = static_cast<uint32_t>(T >> 32);
+      atomicAdd(p, static_cast<int>(lo & 0xFFFFu));
+      atomicAdd(p + F, static_cast<int>(lo >> 16));
+      atomicAdd(p + 2 * F, static_cast<int>(hi & 0xFFFFu));
+      atomicAdd(p + 3 * F, static_cast<int>(hi >> 16));
+    } else {
+      const uint32_t T = static_cast<uint32_t>(__umul24(static_cast<uint32_t>(bcast<J>(xm[r])),
+                                                         static_cast<uint32_t>(wm))) << s16;
+      atomicAdd(p, static_cast<int>(T & 0xFFFFu));
+      atomicAdd(p + F, static_cast<int>(T >> 16));
+    }
   }
-  if constexpr (J + 1 < V_KC) steps<DT, R, PRE, J + 1>(lane_base, wa, wb, xm, xe);
+  if constexpr (J + 1 < V_KC) steps_raw<DT, R, PRE, J + 1>(cbase, lane_off, wa, wb, xm, xe);
 }
 
 // the lane's pre-decoded w chunk: 16 significands and 16 exponent words
@@ -353,37 +333,21 @@ __device__ __forceinline__ void load_w_pre(const GemmArgs& a, const int32_t* ws,
   }
 }
 
-// one chunk's operands: the lane's w elements (pre-decoded or raw) and, for
-// each row, x element k0 + xj (clamped into the row; beyond K it is masked
-// when decoded)
-template <int DT, bool PRE, int R>
-__device__ __forceinline__ void load_chunk(const GemmArgs& a, const void* __restrict__ xg,
-                                           const void* __restrict__ wg, const int32_t* wsl, const uint16_t* wel,
-                                           int64_t wrow, bool n_ok, const int64_t (&xrow)[R], int xj, int64_t k0,
-                                           uint32_t (&w)[V_KC], uint32_t (&we)[V_KC / 2], uint32_t (&x)[R]) {
-  if (PRE) load_w_pre(a, wsl, wel, k0, w, we);
-  else load_w_chunk<DT>(a, wg, wrow, n_ok, k0, w);
-  const int64_t k = min<int64_t>(k0 + xj, a.K - 1);
-#pragma unroll
-  for (int r = 0; r < R; ++r) x[r] = load_elem<DT>(xg, xrow[r] + k * a.x_sk);
-}
+// R rows (2) and 64 columns per workgroup of W waves; PRE: w comes
+// pre-decoded from the workspace.  Epilogue EPI_STORE or EPI_ADD.
+template <int DT, bool PRE, int R, int W, int WPE>
+__global__ __launch_bounds__(64 * W, WPE) void k_partial(GemmArgs a, const void* __restrict__ xg,
+                                                         const void* __restrict__ wg) {
+  constexpr int SLOT = R * 64 * 4;                // bytes between slots
+  __shared__ __align__(16) char cnt[NSLOT * SLOT];
 
-// R rows per wave; PRE: w comes pre-decoded from the workspace.  Epilogue
-// EPI_STORE or EPI_ADD.
-template <int DT, int R, bool PRE>
-__global__ __launch_bounds__(64) void k_gemm(GemmArgs a, const void* __restrict__ xg,
-                                             const void* __restrict__ wg) {
-  constexpr int NB = 2;                           // operand ring slots
-  __shared__ __align__(16) int counters[NF * R * 64];
-
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t tile = xcd_tile();
-  const int64_t tn = tile / a.tiles_m, tm = tile % a.tiles_m;
-  const int64_t m0 = tm * R, n0 = tn * V_BN;
-  char* const lane_base = reinterpret_cast<char*>(counters) + lane * 4;
+  const int64_t m0 = (tile % a.tiles_m) * R, n0 = (tile / a.tiles_m) * V_BN;
 
-#pragma unroll
-  for (int q = 0; q < NF * R; ++q) counters[q * 64 + lane] = 0;
+  for (int q = threadIdx.x; q < NSLOT * SLOT / 16; q += 64 * W)
+    reinterpret_cast<uint4*>(cnt)[q] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
 
   const int64_t n = n0 + lane;
   const bool n_ok = n < a.N;
@@ -395,74 +359,73 @@ __global__ __launch_bounds__(64) void k_gemm(GemmArgs a, const void* __restrict_
     row_ok[r] = m0 + r < a.M;
     xrow[r] = min(m0 + r, a.M - 1) * a.x_sm;
   }
-  const int xj = lane & 15;                       // this lane's k within a chunk (x side)
-  // the lane's sub-block 0 in chunk 0 of the decoded w
-  const int32_t* const wsl = a.wsig + n0 * V_KC + lane * 4;
+  const int xj = lane & 15;
+  const uint32_t lane_off = static_cast<uint32_t>(lane * 4);
+  const int32_t* const wsl = a.wsig + n0 * V_KC + lane * 4;     // the lane's sub-block 0 of chunk 0
   const uint16_t* const wel = a.wexp + n0 * V_KC + lane * 8;
 
-  int64_t dg[R][ND];
+  const int64_t nchunks = (a.K + V_KC - 1) / V_KC;
+  uint32_t wq[2][V_KC], wbq[2][V_KC / 2], xq[2][R];
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+  for (int i = 0; i < V_KC / 2; ++i) { wbq[0][i] = 0u; wbq[1][i] = 0u; }
 #pragma unroll
-    for (int j = 0; j < ND; ++j) dg[r][j] = 0;
+  for (int r = 0; r < R; ++r) xq[0][r] = xq[1][r] = 0u;
+  constexpr int64_t ESZ = DT == DET_F32 ? 4 : 2;
+  const char* const xp = static_cast<const char*>(xg) + (xrow[0] + xj * a.x_sk) * ESZ;
+  const int64_t xstep = V_KC * a.x_sk * ESZ, xrstep = a.x_sm * ESZ;
+  const bool rows_in = m0 + R <= a.M;
+  auto load = [&](int64_t c, uint32_t (&w)[V_KC], uint32_t (&we)[V_KC / 2], uint32_t (&x)[R]) {
+    const int64_t k0 = c * V_KC;
+    if (PRE) load_w_pre(a, wsl, wel, k0, w, we);
+    else load_w_chunk<DT>(a, wg, wrow, n_ok, k0, w);
+    if (k0 + V_KC <= a.K && rows_in) {
+      const char* const p = xp + c * xstep;
+#pragma unroll
+      for (int r = 0; r < R; ++r) x[r] = load_elem<DT>(p + r * xrstep, 0);
+    } else {
+      const int64_t k = min<int64_t>(k0 + xj, a.K - 1);
+#pragma unroll
+      for (int r = 0; r < R; ++r) x[r] = load_elem<DT>(xg, xrow[r] + k * a.x_sk);
+    }
+  };
+  if (wave < nchunks) load(wave, wq[0], wbq[0], xq[0]);
 
-  // Operand ring: chunk c lives in slot c mod NB, and the loads of chunk
-  // c + NB - 1 are issued before chunk c is processed.  The loop over slots
-  // is unrolled, so every slot index is static and nothing is copied between
-  // registers.
-  uint32_t wq[NB][V_KC], wbq[NB][V_KC / 2], xq[NB][R];
+  // this wave's chunks: wave, wave + W, ...; in pairs so that the ring slot of
+  // each is static
+  for (int64_t c0 = wave; c0 < nchunks; c0 += 2 * W) {
 #pragma unroll
-  for (int p = 0; p < NB; ++p) {
-#pragma unroll
-    for (int i = 0; i < V_KC / 2; ++i) wbq[p][i] = 0u;
-#pragma unroll
-    for (int r = 0; r < R; ++r) xq[p][r] = 0u;
-  }
-#pragma unroll
-  for (int p = 0; p + 1 < NB; ++p)
-    if (p * V_KC < a.K) load_chunk<DT, PRE, R>(a, xg, wg, wsl, wel, wrow, n_ok, xrow, xj, p * V_KC, wq[p], wbq[p], xq[p]);
-
-  for (int64_t c0 = 0; c0 * V_KC < a.K; c0 += NB) {
-#pragma unroll
-    for (int sl = 0; sl < NB; ++sl) {
-      const int64_t k0 = (c0 + sl) * V_KC;
-      if (k0 >= a.K) break;
-      const int64_t kp = k0 + (NB - 1) * V_KC;    // prefetch into the slot freed by the last chunk
-      if (kp < a.K)
-        load_chunk<DT, PRE, R>(a, xg, wg, wsl, wel, wrow, n_ok, xrow, xj, kp, wq[(sl + NB - 1) % NB],
-                               wbq[(sl + NB - 1) % NB], xq[(sl + NB - 1) % NB]);
-      const bool kin = k0 + xj < a.K;
+    for (int sl = 0; sl < 2; ++sl) {
+      const int64_t c = c0 + sl * W;
+      if (c >= nchunks) break;
+      if (c + W < nchunks) load(c + W, wq[sl ^ 1], wbq[sl ^ 1], xq[sl ^ 1]);
+      const bool kin = c * V_KC + xj < a.K;
       int xm[R], xe[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         int32_t m;
         uint32_t e;
-        decode<DT, false, 0, EXP_SHIFT>((row_ok[r] && kin) ? xq[sl][r] : 0u, m, e);
+        decode<DT, false, 0, EXP_SHIFT>(kin && row_ok[r] ? xq[sl][r] : 0u, m, e);
         xm[r] = m;
         xe[r] = static_cast<int>(e);
       }
-      steps<DT, R, PRE, 0>(lane_base, wq[sl], wbq[sl], xm, xe);
-      if (a.K > KFLUSH && ((k0 + V_KC) % KFLUSH) == 0) {   // counters near their limit
-#pragma unroll
-        for (int r = 0; r < R; ++r) fold_row<R>(lane_base + r * ROW_BYTES, dg[r]);
-      }
+      steps_raw<DT, R, PRE, 0>(cnt, lane_off, wq[sl], wbq[sl], xm, xe);
     }
   }
-#pragma unroll
-  for (int r = 0; r < R; ++r) fold_row<R>(lane_base + r * ROW_BYTES, dg[r]);
+  __syncthreads();
 
-  if (!n_ok) return;
+  // wave r turns row r's counters into digits
+  const int r = wave;
+  if (r >= R || !n_ok || !(m0 + r < a.M)) return;
+  const int64_t m = m0 + r;
+  const int* const c = reinterpret_cast<const int*>(cnt + r * 256 + lane * 4);
+  constexpr int F = SLOT / 4;
+  int64_t* const d = a.acc + (m * a.N + n) * ND;
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int64_t m = m0 + r;
-    if (m >= a.M) continue;
-    int64_t* d = a.acc + (m * a.N + n) * ND;
-    if (a.epi == EPI_ADD) {
-#pragma unroll
-      for (int j = 0; j < ND; ++j) dg[r][j] += d[j];
-    }
-#pragma unroll
-    for (int j = 0; j < ND; ++j) d[j] = dg[r][j];
+  for (int j = 0; j < ND; ++j) {
+    const int64_t lo = static_cast<int64_t>(c[(2 * j) * F]) - c[(NEG_SLOT + 2 * j) * F];
+    const int64_t hi = 2 * j + 1 < NF ? static_cast<int64_t>(c[(2 * j + 1) * F]) - c[(NEG_SLOT + 2 * j + 1) * F] : 0;
+    const int64_t v = lo + hi * 65536;
+    d[j] = a.epi == EPI_ADD ? d[j] + v : v;
   }
 }
 
@@ -963,11 +926,13 @@ int64_t workspace_bytes(int out_mode, int64_t M, int64_t N, int64_t K) {
   return b;
 }
 
-// Raw digits (det_gemm_partial): k_gemm, two rows per wave (the 17.9 KB of
-// counters per wave let 8-9 waves share a CU; four rows measured 40% slower).
+// Raw digits (det_gemm_partial): k_partial with two rows and 64 columns per
+// workgroup of 4 waves (50 KB of counters, three workgroups per CU, at most
+// 168 VGPRs: 3 waves per SIMD).  K runs in blocks of 2^15, with or without
+// a workspace, so no counter can overflow; the digits are carried in acc.
 template <int DT>
 det_status launch_partial(GemmArgs a, void* ws, hipStream_t s) {
-  constexpr int R = 2;
+  constexpr int R = 2, W = 4, WPE = 3;
   a.tiles_m = (a.M + R - 1) / R;
   a.tiles_n = (a.N + V_BN - 1) / V_BN;
   const int64_t blocks = a.tiles_m * a.tiles_n;
@@ -989,20 +954,21 @@ det_status launch_partial(GemmArgs a, void* ws, hipStream_t s) {
     det_status st = hip_check(hipGetLastError(), "predecode launch");
     if (st != DET_OK) return st;
   }
-  const dim3 grid(static_cast<unsigned>(blocks)), block(64);
-  // K blocks (one block without a workspace, or when K is short); the digits
-  // are carried in acc itself
-  const int64_t kblk = pre ? K_BLOCK : a.K;
-  const int64_t nblk = a.K > 0 ? (a.K + kblk - 1) / kblk : 1;
+  const dim3 grid(static_cast<unsigned>(blocks)), block(64 * W);
+  const int64_t nblk = a.K > 0 ? (a.K + K_BLOCK - 1) / K_BLOCK : 1;
   for (int64_t ib = 0; ib < nblk; ++ib) {
     GemmArgs b = a;
-    const int64_t k0 = ib * kblk;
-    b.K = min(kblk, a.K - k0);
+    const int64_t k0 = ib * K_BLOCK;
+    b.K = min(K_BLOCK, a.K - k0);
     const void* xb = static_cast<const char*>(a.x) + k0 * a.x_sk * esz;
+    const void* wb = static_cast<const char*>(a.w) + k0 * a.w_sk * esz;
+    // raw w of this block: alignment of its chunk starts as for the whole w
+    b.w = wb;
+    b.w_vec = a.w_vec && (reinterpret_cast<uintptr_t>(wb) % 16) == 0;
     if (pre) { b.wsig = a.wsig + k0 / V_KC * a.wld; b.wexp = a.wexp + k0 / V_KC * a.wld; }
     b.epi = ib == 0 ? EPI_STORE : EPI_ADD;
-    if (pre) hipLaunchKernelGGL((k_gemm<DT, R, true>), grid, block, 0, s, b, xb, a.w);
-    else hipLaunchKernelGGL((k_gemm<DT, R, false>), grid, block, 0, s, b, xb, a.w);
+    if (pre) hipLaunchKernelGGL((k_partial<DT, true, R, W, WPE>), grid, block, 0, s, b, xb, wb);
+    else hipLaunchKernelGGL((k_partial<DT, false, R, W, WPE>), grid, block, 0, s, b, xb, wb);
     det_status st = hip_check(hipGetLastError(), "gemm launch");
     if (st != DET_OK) return st;
   }
