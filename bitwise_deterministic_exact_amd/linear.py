@@ -9,6 +9,13 @@ backward: dY rounded to the parameter dtype (nearest-even) when it is bf16,
 Each product is exact and each result is rounded once to fp32; dX and dW are
 then rounded (nearest-even) to the dtypes of x and W.  Every step runs in the
 library's kernels; the transposed operands are strided views, not copies.
+
+With k_shards > 1 the forward is computed the way a row-parallel
+(K-sharded) layer computes it: in_features is cut into k_shards contiguous
+slices, each slice's raw digits come from det_gemm_partial, the digit arrays
+are added with det_combine (where a multi-GPU layer would all-reduce them) and
+det_finalize rounds once.  The page's "Method" section makes this bit-for-bit
+the unsharded result, so a model trains to the same bytes either way.
 """
 from __future__ import annotations
 
@@ -16,7 +23,7 @@ import math
 
 import torch
 
-from .api import det_gemm, round_f32_to_bf16
+from .api import det_combine, det_finalize, det_gemm, det_gemm_partial, round_f32_to_bf16
 
 
 def _to_dtype(t32: torch.Tensor, dtype: torch.dtype) -> torch.Tensor:
@@ -27,11 +34,25 @@ def _to_dtype(t32: torch.Tensor, dtype: torch.dtype) -> torch.Tensor:
     raise ValueError(f"unsupported dtype {dtype}")
 
 
+def shard_bounds(k: int, shards: int):
+    """Contiguous [a, b) slices of range(k), as equal as possible."""
+    cuts = [k * i // shards for i in range(shards + 1)]
+    return [(cuts[i], cuts[i + 1]) for i in range(shards) if cuts[i] < cuts[i + 1]]
+
+
+def _forward_gemm(x2: torch.Tensor, weight: torch.Tensor, k_shards: int) -> torch.Tensor:
+    if k_shards <= 1:
+        return det_gemm(x2, weight, check_finite=False)
+    parts = [det_gemm_partial(x2[:, a:b], weight[:, a:b], check_finite=False)
+             for a, b in shard_bounds(x2.shape[1], k_shards)]
+    return det_finalize(det_combine(parts))
+
+
 class _DetLinearFn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, x: torch.Tensor, weight: torch.Tensor) -> torch.Tensor:
+    def forward(ctx, x: torch.Tensor, weight: torch.Tensor, k_shards: int) -> torch.Tensor:
         x2 = x.reshape(-1, x.shape[-1])
-        y = det_gemm(x2, weight, check_finite=False)
+        y = _forward_gemm(x2, weight, k_shards)
         ctx.save_for_backward(x2, weight)
         ctx.x_shape = x.shape
         return y.reshape(*x.shape[:-1], weight.shape[0])
@@ -48,17 +69,20 @@ class _DetLinearFn(torch.autograd.Function):
         if ctx.needs_input_grad[1]:
             dw32 = det_gemm(g.t(), x2.t(), check_finite=False)        # [out, in], K = T
             dw = _to_dtype(dw32, weight.dtype)
-        return dx, dw
+        return dx, dw, None
 
 
 class DetLinear(torch.nn.Module):
     """y = x W^T with exact accumulation; W is [out_features, in_features]."""
 
     def __init__(self, in_features: int, out_features: int, bias: bool = False,
-                 device=None, dtype=torch.float32):
+                 device=None, dtype=torch.float32, k_shards: int = 1):
         super().__init__()
         if bias:
             raise ValueError("DetLinear has no bias")
+        if k_shards < 1:
+            raise ValueError("k_shards must be >= 1")
+        self.k_shards = k_shards
         if dtype not in (torch.float32, torch.bfloat16):
             raise ValueError("DetLinear supports float32 and bfloat16 parameters")
         self.in_features, self.out_features = in_features, out_features
@@ -72,7 +96,8 @@ class DetLinear(torch.nn.Module):
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         if x.dtype != self.weight.dtype:
             raise ValueError(f"input dtype {x.dtype} differs from weight dtype {self.weight.dtype}")
-        return _DetLinearFn.apply(x, self.weight)
+        return _DetLinearFn.apply(x, self.weight, self.k_shards)
 
     def extra_repr(self) -> str:
-        return f"in_features={self.in_features}, out_features={self.out_features}, bias=False"
+        return (f"in_features={self.in_features}, out_features={self.out_features}, bias=False"
+                + (f", k_shards={self.k_shards}" if self.k_shards > 1 else ""))

@@ -121,6 +121,19 @@ def test_python_layer_validates_before_launch():
         det.det_finalize(torch.empty(3, 17, dtype=torch.int64))
     with pytest.raises(ValueError):
         det.DetLinear(4, 4, bias=True)
+    with pytest.raises(ValueError):
+        det.DetLinear(4, 4, k_shards=0)
+
+
+def test_shard_bounds_cover_k_once():
+    from bitwise_deterministic_exact_amd.linear import shard_bounds
+    for k in (1, 3, 4, 7, 192, 4096):
+        for s in (1, 2, 3, 4, 16):
+            b = shard_bounds(k, s)
+            assert b[0][0] == 0 and b[-1][1] == k
+            assert all(lo < hi for lo, hi in b)
+            assert all(b[i][1] == b[i + 1][0] for i in range(len(b) - 1))
+            assert len(b) == min(s, k)
 
 
 def test_no_cpu_fallback_in_the_product():
