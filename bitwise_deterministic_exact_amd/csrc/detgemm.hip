@@ -139,6 +139,9 @@ struct GemmArgs {
   const uint16_t* wexp;               // k_gemm: 16-bit exponent words [Kp/16][Np/64][2][64][8]
   const uint32_t* wexp32;             // k_gemm8: 32-bit words [Kp/16][Np/64][4][64][4]
   int64_t wld;                        // Np * 16, the chunk pitch of all three
+  const int32_t* xsig;                // pre-decoded x of this K block: significands [Mp][xld]
+  const uint32_t* xword;              // pre-decoded x: exponent / address words [Mp][xld]
+  int64_t xld;                        // row pitch of both: the block's K padded to 16
   int64_t* acc;                       // digits [M][N][18]: the partial's output, or scratch
   float* y; int64_t y_sm, y_sn;       // gemm: fp32 out
   int epi;                            // epilogue, see EPI_* below
@@ -360,25 +363,34 @@ __global__ __launch_bounds__(64 * W, WPE) void k_partial(GemmArgs a, const void*
     xrow[r] = min(m0 + r, a.M - 1) * a.x_sm;
   }
   const int xj = lane & 15;
+  const uint32_t xj4 = static_cast<uint32_t>(xj) * 4u;
   const uint32_t lane_off = static_cast<uint32_t>(lane * 4);
   const int32_t* const wsl = a.wsig + n0 * V_KC + lane * 4;     // the lane's sub-block 0 of chunk 0
   const uint16_t* const wel = a.wexp + n0 * V_KC + lane * 8;
 
   const int64_t nchunks = (a.K + V_KC - 1) / V_KC;
-  uint32_t wq[2][V_KC], wbq[2][V_KC / 2], xq[2][R];
+  uint32_t wq[2][V_KC], wbq[2][V_KC / 2], xq[2][R], xwq[2][R];
 #pragma unroll
   for (int i = 0; i < V_KC / 2; ++i) { wbq[0][i] = 0u; wbq[1][i] = 0u; }
 #pragma unroll
-  for (int r = 0; r < R; ++r) xq[0][r] = xq[1][r] = 0u;
+  for (int r = 0; r < R; ++r) xq[0][r] = xq[1][r] = xwq[0][r] = xwq[1][r] = 0u;
   constexpr int64_t ESZ = DT == DET_F32 ? 4 : 2;
   const char* const xp = static_cast<const char*>(xg) + (xrow[0] + xj * a.x_sk) * ESZ;
   const int64_t xstep = V_KC * a.x_sk * ESZ, xrstep = a.x_sm * ESZ;
   const bool rows_in = m0 + R <= a.M;
-  auto load = [&](int64_t c, uint32_t (&w)[V_KC], uint32_t (&we)[V_KC / 2], uint32_t (&x)[R]) {
+  auto load = [&](int64_t c, uint32_t (&w)[V_KC], uint32_t (&we)[V_KC / 2], uint32_t (&x)[R], uint32_t (&xw)[R]) {
     const int64_t k0 = c * V_KC;
     if (PRE) load_w_pre(a, wsl, wel, k0, w, we);
     else load_w_chunk<DT>(a, wg, wrow, n_ok, k0, w);
-    if (k0 + V_KC <= a.K && rows_in) {
+    if (PRE) {                                    // decoded x: padded, no masking
+      const char* const xb = reinterpret_cast<const char*>(a.xsig + m0 * a.xld + k0);
+      const char* const wb = reinterpret_cast<const char*>(a.xword + m0 * a.xld + k0);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        x[r] = *reinterpret_cast<const uint32_t*>(xb + r * a.xld * 4 + xj4);
+        xw[r] = *reinterpret_cast<const uint32_t*>(wb + r * a.xld * 4 + xj4);
+      }
+    } else if (k0 + V_KC <= a.K && rows_in) {
       const char* const p = xp + c * xstep;
 #pragma unroll
       for (int r = 0; r < R; ++r) x[r] = load_elem<DT>(p + r * xrstep, 0);
@@ -388,7 +400,7 @@ __global__ __launch_bounds__(64 * W, WPE) void k_partial(GemmArgs a, const void*
       for (int r = 0; r < R; ++r) x[r] = load_elem<DT>(xg, xrow[r] + k * a.x_sk);
     }
   };
-  if (wave < nchunks) load(wave, wq[0], wbq[0], xq[0]);
+  if (wave < nchunks) load(wave, wq[0], wbq[0], xq[0], xwq[0]);
 
   // this wave's chunks: wave, wave + W, ...; in pairs so that the ring slot of
   // each is static
@@ -397,14 +409,15 @@ __global__ __launch_bounds__(64 * W, WPE) void k_partial(GemmArgs a, const void*
     for (int sl = 0; sl < 2; ++sl) {
       const int64_t c = c0 + sl * W;
       if (c >= nchunks) break;
-      if (c + W < nchunks) load(c + W, wq[sl ^ 1], wbq[sl ^ 1], xq[sl ^ 1]);
+      if (c + W < nchunks) load(c + W, wq[sl ^ 1], wbq[sl ^ 1], xq[sl ^ 1], xwq[sl ^ 1]);
       const bool kin = c * V_KC + xj < a.K;
       int xm[R], xe[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         int32_t m;
         uint32_t e;
-        decode<DT, false, 0, EXP_SHIFT>(kin && row_ok[r] ? xq[sl][r] : 0u, m, e);
+        if (PRE) { m = static_cast<int32_t>(xq[sl][r]); e = xwq[sl][r]; }
+        else decode<DT, false, 0, EXP_SHIFT>(kin && row_ok[r] ? xq[sl][r] : 0u, m, e);
         xm[r] = m;
         xe[r] = static_cast<int>(e);
       }
@@ -465,6 +478,8 @@ __global__ __launch_bounds__(64 * W, WPE) void k_partial(GemmArgs a, const void*
 
 template <int DT, int R>
 struct Cells8 {
+  static constexpr int ROWS = R;
+  static constexpr bool XPACK = false;          // decoded x: separate significand and word arrays
   static constexpr int NCELL = 64;              // cells that products reach
   static constexpr int FIRST = DT == DET_F32 ? 0 : 4;     // first reachable cell (bf16: offset >= 32)
   static constexpr int BITS = 8;
@@ -501,6 +516,16 @@ struct Cells8 {
 
 template <int R>
 struct Cells4 {
+  static constexpr int ROWS = R;
+  // decoded x packs the 12-bit shifted significand and the address word
+  // (< 2^17) into one 32-bit word: one load per row and chunk, two
+  // instructions to unpack
+  static constexpr bool XPACK = true;
+  __device__ static uint32_t pack_x(int32_t m, uint32_t e) { return (e << 12) | (static_cast<uint32_t>(m) & 0xFFFu); }
+  __device__ static void unpack_x(uint32_t w, int32_t& m, uint32_t& e) {
+    m = static_cast<int32_t>(w << 20) >> 20;
+    e = w >> 12;
+  }
   static constexpr int NCELL = 128;
   static constexpr int FIRST = 7;                         // offsets >= 32 -> cells >= 7
   static constexpr int BITS = 4;
@@ -538,6 +563,11 @@ struct Cells4 {
     atomicAdd(reinterpret_cast<int*>(cbase + (xe + we)), __mul24(xm, wm));
   }
 };
+
+template <class G>
+__device__ __forceinline__ void unpack_packed(uint32_t w, int32_t& m, uint32_t& e) {
+  if constexpr (G::XPACK) G::unpack_x(w, m, e);
+}
 
 // the lane's pre-decoded w chunk for k_gemm8: 16 significands and 16 32-bit
 // words, both laid out like load_w_pre's 32-bit words
@@ -653,6 +683,7 @@ __global__ __launch_bounds__(64 * W, WPE) void k_gemm8(GemmArgs a, const void* _
     xrow[r] = min(m0 + r, a.M - 1) * a.x_sm;
   }
   const int xj = lane & 15;
+  const uint32_t xj4 = static_cast<uint32_t>(xj) * 4u;
   const uint32_t lane_off = static_cast<uint32_t>(lane * G::ES);
 
   int64_t dg[R][WD];
@@ -662,11 +693,11 @@ __global__ __launch_bounds__(64 * W, WPE) void k_gemm8(GemmArgs a, const void* _
     for (int j = 0; j < WD; ++j) dg[r][j] = 0;
 
   const int64_t nchunks = (a.K + V_KC - 1) / V_KC;
-  uint32_t wq[2][V_KC], weq[2][V_KC], xq[2][R];
+  uint32_t wq[2][V_KC], weq[2][V_KC], xq[2][R], xwq[2][R];
 #pragma unroll
   for (int i = 0; i < V_KC; ++i) { weq[0][i] = 0u; weq[1][i] = 0u; }
 #pragma unroll
-  for (int r = 0; r < R; ++r) xq[0][r] = xq[1][r] = 0u;
+  for (int r = 0; r < R; ++r) xq[0][r] = xq[1][r] = xwq[0][r] = xwq[1][r] = 0u;
   // x element k0 + xj of each row: a per-lane pointer plus a wave-uniform
   // chunk offset, clamped into the row only in the last, partial chunk
   constexpr int64_t ESZ = DT == DET_F32 ? 4 : 2;
@@ -675,11 +706,19 @@ __global__ __launch_bounds__(64 * W, WPE) void k_gemm8(GemmArgs a, const void* _
   const bool rows_in = m0 + R <= a.M;             // all R rows exist: rows are x_sm apart
   const int32_t* const wsl = a.wsig + n0 * V_KC + lane * 4;       // the lane's sub-block 0 of chunk 0
   const uint32_t* const wel = a.wexp32 + n0 * V_KC + lane * 4;
-  auto load = [&](int64_t c, uint32_t (&w)[V_KC], uint32_t (&we)[V_KC], uint32_t (&x)[R]) {
+  auto load = [&](int64_t c, uint32_t (&w)[V_KC], uint32_t (&we)[V_KC], uint32_t (&x)[R], uint32_t (&xw)[R]) {
     const int64_t k0 = c * V_KC;
     if (PRE) load_w_pre8(a, wsl, wel, k0, w, we);
     else load_w_chunk<DT>(a, wg, wrow, n_ok, k0, w);
-    if (k0 + V_KC <= a.K && rows_in) {
+    if (PRE) {                                    // decoded x: padded, no masking
+      const char* const xb = reinterpret_cast<const char*>(a.xsig + m0 * a.xld + k0);
+      const char* const wb = reinterpret_cast<const char*>(a.xword + m0 * a.xld + k0);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        x[r] = *reinterpret_cast<const uint32_t*>(xb + r * a.xld * 4 + xj4);
+        if (!G::XPACK) xw[r] = *reinterpret_cast<const uint32_t*>(wb + r * a.xld * 4 + xj4);
+      }
+    } else if (k0 + V_KC <= a.K && rows_in) {
       const char* const p = xp + c * xstep;
 #pragma unroll
       for (int r = 0; r < R; ++r) x[r] = load_elem<DT>(p + r * xrstep, 0);
@@ -689,7 +728,7 @@ __global__ __launch_bounds__(64 * W, WPE) void k_gemm8(GemmArgs a, const void* _
       for (int r = 0; r < R; ++r) x[r] = load_elem<DT>(xg, xrow[r] + k * a.x_sk);
     }
   };
-  if (wave < nchunks) load(wave, wq[0], weq[0], xq[0]);
+  if (wave < nchunks) load(wave, wq[0], weq[0], xq[0], xwq[0]);
 
   // this wave's cells: CW consecutive cells from cell FIRST + wave * CW
   char* const my_cells = cells + (G::ALLOC - G::NCELL + wave * CW) * G::CS + lane * G::ES;
@@ -705,14 +744,16 @@ __global__ __launch_bounds__(64 * W, WPE) void k_gemm8(GemmArgs a, const void* _
     for (int sl = 0; sl < 2; ++sl) {
       const int64_t c = e0 + wave + (i2 + sl) * W;
       if (c < nchunks) {
-        if (c + W < nchunks) load(c + W, wq[sl ^ 1], weq[sl ^ 1], xq[sl ^ 1]);
+        if (c + W < nchunks) load(c + W, wq[sl ^ 1], weq[sl ^ 1], xq[sl ^ 1], xwq[sl ^ 1]);
         const bool kin = c * V_KC + xj < a.K;
         int xm[R], xe[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           int32_t m;
           uint32_t e;
-          G::decode_x(kin && row_ok[r] ? xq[sl][r] : 0u, r, m, e);
+          if (PRE && G::XPACK) unpack_packed<G>(xq[sl][r], m, e);
+          else if (PRE) { m = static_cast<int32_t>(xq[sl][r]); e = xwq[sl][r]; }
+          else G::decode_x(kin && row_ok[r] ? xq[sl][r] : 0u, r, m, e);
           xm[r] = m;
           xe[r] = static_cast<int>(e);
         }
@@ -825,6 +866,45 @@ __global__ __launch_bounds__(256) void k_predecode_w8(PredecodeArgs a) {
   }
 }
 
+// x of one K block [M][K] (any strides) -> the x side's significands and
+// words, [Mp][Kp] row-major with M padded to the tile's rows and K to the
+// chunk, the padding holding the decode of +0; D::decode_x gives the words
+// (D::ROWS rows per tile: row m is row m mod ROWS of its tile).
+struct PredecodeXArgs {
+  const void* x; int64_t x_sm, x_sk;
+  int64_t M, K, Mp, Kp;
+  int32_t* xsig; uint32_t* xword;
+};
+
+template <class D, int DT>
+__global__ __launch_bounds__(256) void k_predecode_x(PredecodeXArgs a) {
+  const int64_t total = a.Mp * a.Kp;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int64_t m = i / a.Kp, k = i % a.Kp;
+    int32_t v;
+    uint32_t e;
+    D::decode_x(m < a.M && k < a.K ? load_elem<DT>(a.x, m * a.x_sm + k * a.x_sk) : 0u,
+                static_cast<int>(m % D::ROWS), v, e);
+    if constexpr (D::XPACK) {
+      a.xsig[i] = static_cast<int32_t>(D::pack_x(v, e));
+    } else {
+      a.xsig[i] = v;
+      a.xword[i] = e;
+    }
+  }
+}
+
+// the raw-digit kernel's x decode, in the form k_predecode_x takes
+template <int DT, int R>
+struct RawDecode {
+  static constexpr int ROWS = R;
+  static constexpr bool XPACK = false;
+  __device__ static void decode_x(uint32_t b, int /*r*/, int32_t& m, uint32_t& e) {
+    decode<DT, false, 0, EXP_SHIFT>(b, m, e);
+  }
+};
+
 // ---------------------------------------------------------------- combine / finalize
 struct CombineArgs {
   const int64_t* parts[COMBINE_MAX];
@@ -914,16 +994,34 @@ int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 // launches of this length that carry the exact digits between them.
 constexpr int64_t K_BLOCK = int64_t(1) << 15;
 
-// workspace: the pre-decoded w, then (det_gemm with K > K_BLOCK) int64
-// digit scratch for the output
-// (det_gemm's kernel takes 32-bit exponent words, the partial's 16-bit ones)
+// workspace: the pre-decoded w, the pre-decoded x of one K block (8 bytes
+// per element, rows padded to 2, K to 16), then (det_gemm with K > K_BLOCK)
+// int64 digit scratch for the output.  det_gemm's kernel takes 32-bit
+// exponent words for w, the partial's 16-bit ones.
+constexpr int TILE_ROWS = 2;
 int64_t predecode_bytes(int out_mode, int64_t N, int64_t K) {
   return round_up(N, V_BN) * round_up(K, V_KC) * (out_mode == 1 ? 4 + 4 : 4 + 2);
 }
+int64_t xdecode_bytes(int64_t M, int64_t K) {
+  return round_up(M, TILE_ROWS) * round_up(min(K, K_BLOCK), V_KC) * (4 + 4);
+}
 int64_t workspace_bytes(int out_mode, int64_t M, int64_t N, int64_t K) {
-  int64_t b = predecode_bytes(out_mode, N, K);
+  int64_t b = predecode_bytes(out_mode, N, K) + xdecode_bytes(M, K);
   if (out_mode == 1 && K > K_BLOCK) b += M * N * ND * 8;
   return b;
+}
+
+// decode x's K block [k0, k0 + kb) into the workspace region at `xr`
+template <class D, int DT>
+det_status predecode_x_block(GemmArgs& b, const void* xblock, char* xr, hipStream_t s) {
+  PredecodeXArgs p{};
+  p.x = xblock; p.x_sm = b.x_sm; p.x_sk = b.x_sk;
+  p.M = b.M; p.K = b.K; p.Mp = round_up(b.M, TILE_ROWS); p.Kp = round_up(b.K, V_KC);
+  p.xsig = reinterpret_cast<int32_t*>(xr);
+  p.xword = reinterpret_cast<uint32_t*>(xr + p.Mp * p.Kp * 4);
+  b.xsig = p.xsig; b.xword = p.xword; b.xld = p.Kp;
+  hipLaunchKernelGGL((k_predecode_x<D, DT>), dim3(grid_for(p.Mp * p.Kp, 256, 8192)), dim3(256), 0, s, p);
+  return hip_check(hipGetLastError(), "x predecode launch");
 }
 
 // Raw digits (det_gemm_partial): k_partial with two rows and 64 columns per
@@ -967,6 +1065,11 @@ det_status launch_partial(GemmArgs a, void* ws, hipStream_t s) {
     b.w_vec = a.w_vec && (reinterpret_cast<uintptr_t>(wb) % 16) == 0;
     if (pre) { b.wsig = a.wsig + k0 / V_KC * a.wld; b.wexp = a.wexp + k0 / V_KC * a.wld; }
     b.epi = ib == 0 ? EPI_STORE : EPI_ADD;
+    if (pre) {
+      det_status st = predecode_x_block<RawDecode<DT, R>, DT>(
+          b, xb, static_cast<char*>(ws) + predecode_bytes(0, a.N, a.K), s);
+      if (st != DET_OK) return st;
+    }
     if (pre) hipLaunchKernelGGL((k_partial<DT, true, R, W, WPE>), grid, block, 0, s, b, xb, wb);
     else hipLaunchKernelGGL((k_partial<DT, false, R, W, WPE>), grid, block, 0, s, b, xb, wb);
     det_status st = hip_check(hipGetLastError(), "gemm launch");
@@ -1007,7 +1110,9 @@ det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s) {
   // workspace, behind the decoded w
   const int64_t kblk = pre ? K_BLOCK : a.K;
   const int64_t nblk = a.K > 0 ? (a.K + kblk - 1) / kblk : 1;
-  if (nblk > 1) a.acc = reinterpret_cast<int64_t*>(static_cast<char*>(ws) + predecode_bytes(1, a.N, a.K));
+  if (nblk > 1)
+    a.acc = reinterpret_cast<int64_t*>(static_cast<char*>(ws) + predecode_bytes(1, a.N, a.K) +
+                                       xdecode_bytes(a.M, a.K));
   for (int64_t ib = 0; ib < nblk; ++ib) {
     GemmArgs b = a;
     const int64_t k0 = ib * kblk;
@@ -1016,6 +1121,10 @@ det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s) {
     if (pre) { b.wsig = a.wsig + k0 / V_KC * a.wld; b.wexp32 = a.wexp32 + k0 / V_KC * a.wld; }
     const bool first = ib == 0, last = ib + 1 == nblk;
     b.epi = nblk == 1 ? EPI_ROUND : first ? EPI_STORE : last ? EPI_ADD_ROUND : EPI_ADD;
+    if (pre) {
+      det_status st = predecode_x_block<G, DT>(b, xb, static_cast<char*>(ws) + predecode_bytes(1, a.N, a.K), s);
+      if (st != DET_OK) return st;
+    }
     if (pre) hipLaunchKernelGGL((k_gemm8<G, DT, true, R, W, WPE>), grid, block, 0, s, b, xb, a.w);
     else hipLaunchKernelGGL((k_gemm8<G, DT, false, R, W, WPE>), grid, block, 0, s, b, xb, a.w);
     det_status st = hip_check(hipGetLastError(), "gemm launch");

@@ -109,19 +109,21 @@ det_status det_gemm_partial(det_dtype dt, const void* x, int64_t x_sm, int64_t x
  * Workspace variants.  det_gemm_ws and det_gemm_partial_ws compute exactly
  * what det_gemm and det_gemm_partial compute (bit-identical results) but
  * use a caller-provided device workspace: w is decoded into it once
- * (significands and exponents, rows padded), which saves the GEMM kernel the
- * decode of every w element in every output tile, and a K range longer than
- * 2^15 is run in blocks of 2^15 whose exact digits are carried from block to
- * block (in `acc` for the partial, in the workspace for det_gemm), which
- * keeps each block's slice of w in the L2 caches.
+ * (significands and exponent words, rows padded), and x one K block at a
+ * time, which saves the GEMM kernels the decode of every element in every
+ * output tile; a K range longer than 2^15 is run in blocks of 2^15 whose
+ * exact digits are carried from block to block (in `acc` for the partial, in
+ * the workspace for det_gemm), which keeps each block's slice of w in the L2
+ * caches.
  *   workspace        device memory, 16-byte aligned, at least
  *                    det_gemm_workspace_bytes(dt, partial, M, N, K) bytes;
  *                    owned by the caller, overwritten by the call, and in use
  *                    until the call's work on `stream` has finished
  *   workspace_bytes  its size in bytes
  * det_gemm_workspace_bytes returns the size needed (0 when M, N or K is 0):
- * 6 * roundup(N, 64) * roundup(K, 16), plus 144 * M * N for det_gemm_ws
- * (partial = 0) when K > 2^15.
+ * (partial ? 6 : 8) * roundup(N, 64) * roundup(K, 16) for w, plus
+ * 8 * roundup(M, 2) * roundup(min(K, 2^15), 16) for x, plus 144 * M * N for
+ * det_gemm_ws (partial = 0) when K > 2^15.
  * Errors as for det_gemm, plus DET_EINVAL for a null, misaligned or too small
  * workspace.
  */

@@ -75,13 +75,15 @@ def test_workspace_size_and_checks():
     assert lib.det_gemm_workspace_bytes(0, 0, 3, 5, 0) == 0
     assert lib.det_gemm_workspace_bytes(0, 0, 0, 5, 5) == 0
     # decoded w: 4-byte significand and exponent word per element (det_gemm),
-    # 4 + 2 bytes (det_gemm_partial), rows padded to 64 and K to 16
-    assert lib.det_gemm_workspace_bytes(0, 0, 1, 1, 1) == 8 * 64 * 16
-    assert lib.det_gemm_workspace_bytes(1, 1, 9, 4096, 4096) == 6 * 4096 * 4096
-    assert lib.det_gemm_workspace_bytes(0, 0, 9, 65, 17) == 8 * 128 * 32
+    # 4 + 2 bytes (det_gemm_partial), rows padded to 64 and K to 16; decoded
+    # x of one K block (at most 2^15): 8 bytes per element, rows padded to 2
+    assert lib.det_gemm_workspace_bytes(0, 0, 1, 1, 1) == 8 * 64 * 16 + 8 * 2 * 16
+    assert lib.det_gemm_workspace_bytes(1, 1, 9, 4096, 4096) == 6 * 4096 * 4096 + 8 * 10 * 4096
+    assert lib.det_gemm_workspace_bytes(0, 0, 9, 65, 17) == 8 * 128 * 32 + 8 * 10 * 32
     # det_gemm with K beyond one block also carries 144 bytes of digits per output
-    assert lib.det_gemm_workspace_bytes(0, 0, 7, 64, 40000) == 8 * 64 * 40000 + 144 * 7 * 64
-    assert lib.det_gemm_workspace_bytes(0, 1, 7, 64, 40000) == 6 * 64 * 40000
+    assert (lib.det_gemm_workspace_bytes(0, 0, 7, 64, 40000)
+            == 8 * 64 * 40000 + 8 * 8 * 32768 + 144 * 7 * 64)
+    assert lib.det_gemm_workspace_bytes(0, 1, 7, 64, 40000) == 6 * 64 * 40000 + 8 * 8 * 32768
     vp = ctypes.c_void_p
     args = (0, vp(1 << 20), 4, 1, vp(1 << 20), 4, 1, 4, 4, 4, vp(1 << 20), 4, 1)
     need = lib.det_gemm_workspace_bytes(0, 0, 4, 4, 4)
