@@ -12,6 +12,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdetgemm.
 
 DET_OK, DET_EINVAL, DET_EKLIMIT, DET_EDTYPE, DET_EHIP = 0, 1, 2, 3, 5
 DET_F32, DET_BF16 = 0, 1
+DET_PATH_AUTO, DET_PATH_ACCUMULATOR, DET_PATH_SLICES = 0, 1, 2
 NUM_DIGITS = 18
 LSB_EXPONENT = -298
 K_MAX = 1 << 19
@@ -49,6 +50,9 @@ def load() -> ctypes.CDLL:
         "det_finalize": ([vp, vp, i64, vp], c_int),
         "det_round_f32_to_bf16": ([vp, vp, i64, vp], c_int),
         "det_check_finite": ([c_int, vp, i64, i64, i64, i64, vp, vp], c_int),
+        "det_set_gemm_path": ([c_int, c_int], c_int),
+        "det_last_gemm_plan": ([ctypes.POINTER(c_int), ctypes.POINTER(c_int), ctypes.POINTER(i64),
+                                ctypes.POINTER(i64)], None),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)

@@ -74,8 +74,9 @@ def _reject_nonfinite(x, w, check_finite):
 
 
 def _workspace(dt: int, partial: bool, M: int, N: int, K: int, device: torch.device, use: bool):
-    """Scratch for the decoded copy of w and, for long K, the carried digits
-    (torch's caching allocator provides it)."""
+    """Scratch for the decoded copy of w, for long K the carried digits, and
+    for det_gemm the digit arrays of the matrix-core path (torch's caching
+    allocator provides it)."""
     nbytes = _lib.load().det_gemm_workspace_bytes(dt, int(partial), M, N, K) if use else 0
     if nbytes <= 0:
         return None, 0
@@ -160,6 +161,49 @@ def det_finalize(acc: torch.Tensor) -> torch.Tensor:
     _lib.check(_lib.load().det_finalize(ctypes.c_void_p(acc.data_ptr()), ctypes.c_void_p(y.data_ptr()),
                                         y.numel(), _stream(acc.device)))
     return y
+
+
+_PATHS = {"auto": _lib.DET_PATH_AUTO, "accumulator": _lib.DET_PATH_ACCUMULATOR,
+          "slices": _lib.DET_PATH_SLICES}
+_PATH_NAMES = {v: k for k, v in _PATHS.items()}
+
+
+def set_gemm_path(path: str = "auto", slices: int = 0) -> None:
+    """Choose how det_gemm forms the exact sum (process-wide; see
+    det_set_gemm_path in include/detgemm.h): "auto" (default), "accumulator"
+    (the digit accumulator always) or "slices" (int8 digit GEMMs on the
+    matrix cores, with `slices` = 2..7 digits per operand or 0 to let the
+    call choose).  Every path gives the same bits."""
+    if path not in _PATHS:
+        raise ValueError(f"path must be one of {sorted(_PATHS)}")
+    _lib.check(_lib.load().det_set_gemm_path(_PATHS[path], int(slices)))
+
+
+def last_gemm_plan() -> dict:
+    """What this thread's last det_gemm call did: the path, the digits per
+    operand (0 on the accumulator path) and how many rows of x and of w the
+    accumulator recomputed after the matrix-core pass."""
+    path, slices = ctypes.c_int(), ctypes.c_int()
+    rows, cols = ctypes.c_int64(), ctypes.c_int64()
+    _lib.load().det_last_gemm_plan(ctypes.byref(path), ctypes.byref(slices), ctypes.byref(rows),
+                                   ctypes.byref(cols))
+    return {"path": _PATH_NAMES.get(path.value, str(path.value)), "slices": slices.value,
+            "fallback_rows": rows.value, "fallback_cols": cols.value}
+
+
+class gemm_path:
+    """Context manager: set_gemm_path(path, slices) inside, "auto" after."""
+
+    def __init__(self, path: str, slices: int = 0):
+        self.path, self.slices = path, slices
+
+    def __enter__(self):
+        set_gemm_path(self.path, self.slices)
+        return self
+
+    def __exit__(self, *exc):
+        set_gemm_path("auto", 0)
+        return False
 
 
 def round_f32_to_bf16(t: torch.Tensor) -> torch.Tensor:

@@ -18,6 +18,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "detgemm.h"
@@ -145,6 +146,11 @@ struct GemmArgs {
   int64_t* acc;                       // digits [M][N][18]: the partial's output, or scratch
   float* y; int64_t y_sm, y_sn;       // gemm: fp32 out
   int epi;                            // epilogue, see EPI_* below
+  // det_gemm on a subset (pre-decoded path only): row m of this GEMM is row
+  // xmap[m] of x and of y, column n is row wmap[n] of w and column wmap[n]
+  // of y; null maps are the identity
+  const int32_t* xmap;
+  const int32_t* wmap;
 };
 
 // Epilogues.  A K range longer than one block is run as several launches
@@ -798,7 +804,8 @@ __global__ __launch_bounds__(64 * W, WPE) void k_gemm8(GemmArgs a, const void* _
 #pragma unroll
     for (int j = 0; j < ND; ++j) dd[j] = acc[j];
   } else {
-    a.y[m * a.y_sm + n * a.y_sn] = __uint_as_float(round_digits_to_f32(acc));
+    const int64_t ym = a.xmap != nullptr ? a.xmap[m] : m, yn = a.wmap != nullptr ? a.wmap[n] : n;
+    a.y[ym * a.y_sm + yn * a.y_sn] = __uint_as_float(round_digits_to_f32(acc));
   }
 }
 
@@ -816,6 +823,7 @@ struct PredecodeArgs {
   const void* w; int64_t w_sn, w_sk;
   int64_t N, K, Np, Kp;
   int32_t* wsig; void* wexp;          // exponent words: uint16 (k_gemm) or uint32 (k_gemm8)
+  const int32_t* rmap;                // k_predecode_w8: decoded row n is row rmap[n] of w (null: n)
 };
 
 // Element i of a 32-bit array (layout [Kp/16][Np/64][4][64][4]) is (n, k);
@@ -859,7 +867,8 @@ __global__ __launch_bounds__(256) void k_predecode_w8(PredecodeArgs a) {
     subblock_nk(i, a.Np, n, k);
     int32_t m;
     uint32_t e;
-    G::decode_w(n < a.N && k < a.K ? load_elem<DT>(a.w, n * a.w_sn + k * a.w_sk) : 0u,
+    const int64_t src = n < a.N && a.rmap != nullptr ? a.rmap[n] : n;
+    G::decode_w(n < a.N && k < a.K ? load_elem<DT>(a.w, src * a.w_sn + k * a.w_sk) : 0u,
                 static_cast<uint32_t>(n & (V_BN - 1)), m, e);
     a.wsig[i] = m;
     static_cast<uint32_t*>(a.wexp)[i] = e;
@@ -874,6 +883,7 @@ struct PredecodeXArgs {
   const void* x; int64_t x_sm, x_sk;
   int64_t M, K, Mp, Kp;
   int32_t* xsig; uint32_t* xword;
+  const int32_t* rmap;                // decoded row m is row rmap[m] of x (null: m)
 };
 
 template <class D, int DT>
@@ -882,9 +892,10 @@ __global__ __launch_bounds__(256) void k_predecode_x(PredecodeXArgs a) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
     const int64_t m = i / a.Kp, k = i % a.Kp;
+    const int64_t src = m < a.M && a.rmap != nullptr ? a.rmap[m] : m;
     int32_t v;
     uint32_t e;
-    D::decode_x(m < a.M && k < a.K ? load_elem<DT>(a.x, m * a.x_sm + k * a.x_sk) : 0u,
+    D::decode_x(m < a.M && k < a.K ? load_elem<DT>(a.x, src * a.x_sm + k * a.x_sk) : 0u,
                 static_cast<int>(m % D::ROWS), v, e);
     if constexpr (D::XPACK) {
       a.xsig[i] = static_cast<int32_t>(D::pack_x(v, e));
@@ -965,6 +976,438 @@ __global__ __launch_bounds__(256) void k_check_finite(const void* __restrict__ p
   if (bad) *flag = 1;
 }
 
+// ---------------------------------------------------------------- det_gemm on the matrix cores
+//
+// det_gemm returns the exact sum rounded once, so how the exact sum is formed
+// is free.  When the nonzero elements of every row of x and of w lie within a
+// few binades of each other, it is formed with integer matrix products:
+//   * a row is scaled by 2^-b (b = the row's top bit position + 3 - 8S), so
+//     that each element becomes an integer V with |V| < 2^(8S-2), exactly as
+//     long as the element's lowest set bit lies at or above b;
+//   * V is cut into S balanced 8-bit digits, V = sum_s 2^(8s) V_s with V_s in
+//     [-128, 127] (each digit is the sign-extended low byte of what remains);
+//   * Z[i,j] = sum_k X[i,k] W[j,k] = sum_{s,t} 2^(8(s+t)) (X_s W_t^T)[i,j].
+//     Each X_s W_t^T is an int8 GEMM on the MFMA units with int32 sums; the
+//     products with the same s + t share one int32 sum over K blocks of
+//     2^14 (|sum| <= 7 * 2^14 * 2^14 < 2^31), which are then added in
+//     128-bit integers: |Z| < K 2^(16S-4) <= 2^127 for S <= 7, K <= 2^19;
+//   * y[i,j] = RNE(Z[i,j] * 2^(bx[i] + bw[j])), the exact sum rounded once.
+// A row of x (or of w) whose span needs more than S digits is recomputed on
+// the exact-accumulator path after the matrix-core pass, which overwrites
+// that row (column) of y; the pass's own values there are discarded.  The
+// host picks S, or the accumulator path alone, from a histogram of the spans.
+
+constexpr int SL_MIN = 2, SL_MAX = 7;     // digits per operand
+constexpr int SL_KB = 64;                 // K per MFMA step
+constexpr int64_t SL_FOLD = 256;          // MFMA steps (2^14 k) per int32 sum
+constexpr int SL_TOP_NONE = -1000;        // top of an all-zero row
+constexpr int SL_LOW_NONE = 1000;
+constexpr int SL_HIST = 16;               // histogram bins per operand: need 0..8
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// element bits -> sign, integer significand m and the exponent of its bit 0
+// (value = +-m * 2^ex; subnormals keep their raw fraction)
+template <int DT>
+__device__ __forceinline__ void split_elem(uint32_t b, bool& neg, uint32_t& m, int& ex) {
+  if (DT == DET_F32) {
+    const uint32_t E = (b >> 23) & 0xFFu;
+    m = (b & 0x7FFFFFu) | (min(E, 1u) << 23);
+    ex = static_cast<int>(max(E, 1u)) - 150;
+    neg = (b >> 31) != 0u;
+  } else {
+    const uint32_t E = (b >> 7) & 0xFFu;
+    m = (b & 0x7Fu) | (min(E, 1u) << 7);
+    ex = static_cast<int>(max(E, 1u)) - 134;
+    neg = ((b >> 15) & 1u) != 0u;
+  }
+}
+
+// Per row of an operand [R][K] (any strides): the top set bit position
+// (max of ex + bit length - 1) and the lowest (min of ex + trailing zeros)
+// over its nonzero elements, by atomic max / min into top[] and low[]
+// (initialised to SL_TOP_NONE / SL_LOW_NONE).
+struct SliceStatArgs {
+  const void* p; int64_t R, K, s_r, s_k;
+  int32_t* top; int32_t* low;
+};
+
+template <int DT>
+__device__ __forceinline__ void stat_elem(uint32_t b, int& top, int& low) {
+  bool neg;
+  uint32_t m;
+  int ex;
+  split_elem<DT>(b, neg, m, ex);
+  if (m != 0u) {
+    top = max(top, ex + 31 - __clz(static_cast<int>(m)));
+    low = min(low, ex + __ffs(static_cast<int>(m)) - 1);
+  }
+}
+
+// KMAJ (unit K stride): one wave per row and 1024-element K range, lanes
+// along K; otherwise one thread per row and 256-element K range, lanes along
+// the rows
+template <int DT, bool KMAJ>
+__global__ __launch_bounds__(256) void k_slice_stats(SliceStatArgs a) {
+  int top = SL_TOP_NONE, low = SL_LOW_NONE;
+  int64_t row;
+  bool lead;
+  if (KMAJ) {
+    const int64_t nkr = (a.K + 1023) / 1024;
+    const int64_t wid = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) >> 6;
+    const int lane = threadIdx.x & 63;
+    if (wid >= a.R * nkr) return;               // uniform per wave
+    row = wid / nkr;
+    const int64_t k0 = (wid % nkr) * 1024;
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+      const int64_t k = k0 + i * 64 + lane;
+      if (k < a.K) stat_elem<DT>(load_elem<DT>(a.p, row * a.s_r + k), top, low);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      top = max(top, __shfl_xor(top, o));
+      low = min(low, __shfl_xor(low, o));
+    }
+    lead = lane == 0;
+  } else {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t nkr = (a.K + 255) / 256;
+    if (t >= a.R * nkr) return;
+    row = t % a.R;
+    const int64_t k0 = (t / a.R) * 256, k1 = min(k0 + 256, a.K);
+    for (int64_t k = k0; k < k1; ++k) stat_elem<DT>(load_elem<DT>(a.p, row * a.s_r + k * a.s_k), top, low);
+    lead = true;
+  }
+  if (lead && top != SL_TOP_NONE) {
+    atomicMax(a.top + row, top);
+    atomicMin(a.low + row, low);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_slice_init(int32_t* top, int32_t* low, int64_t n, int32_t* hist) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+    top[i] = SL_TOP_NONE;
+    low[i] = SL_LOW_NONE;
+  }
+  if (blockIdx.x == 0 && threadIdx.x < 2 * SL_HIST) hist[threadIdx.x] = 0;
+}
+
+// digits each row needs: the smallest S with top - low + 1 <= 8S - 2
+// (0 for an all-zero row, 8 for more than SL_MAX), and their histogram
+__global__ __launch_bounds__(256) void k_slice_need(const int32_t* top, const int32_t* low, int64_t n,
+                                                    int32_t* need, int32_t* hist) {
+  __shared__ int32_t h[SL_HIST];
+  if (threadIdx.x < SL_HIST) h[threadIdx.x] = 0;
+  __syncthreads();
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const int nd = top[i] == SL_TOP_NONE ? 0 : min((top[i] - low[i] + 10) / 8, SL_MAX + 1);
+    need[i] = nd;
+    atomicAdd(&h[nd], 1);
+  }
+  __syncthreads();
+  if (threadIdx.x < SL_HIST && h[threadIdx.x] != 0) atomicAdd(hist + threadIdx.x, h[threadIdx.x]);
+}
+
+// list[] = the rows with need > S, in increasing order (one workgroup)
+__global__ __launch_bounds__(1024) void k_slice_list(const int32_t* need, int64_t n, int S, int32_t* list) {
+  __shared__ int32_t wsum[16];
+  __shared__ int64_t base;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (threadIdx.x == 0) base = 0;
+  __syncthreads();
+  for (int64_t r0 = 0; r0 < n; r0 += 1024) {
+    const int64_t r = r0 + threadIdx.x;
+    const bool flag = r < n && need[r] > S;
+    const unsigned long long bal = __ballot(flag);
+    const int pre = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wsum[wave] = __popcll(bal);
+    __syncthreads();
+    int64_t off = base;
+    for (int v = 0; v < wave; ++v) off += wsum[v];
+    if (flag) list[off + pre] = static_cast<int32_t>(r);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int64_t t = base;
+      for (int v = 0; v < 16; ++v) t += wsum[v];
+      base = t;
+    }
+    __syncthreads();
+  }
+}
+
+// The S digits of an operand [R][K], int8 in MFMA fragment order
+// [Rb][Kb][S][64][16]: lane l, byte j of fragment (rb, kb, s) holds digit s of
+// row 16 rb + (l mod 16), k = 64 kb + 16 (l div 16) + j, the A/B operand
+// layout of v_mfma_i32_16x16x64_i8.  A wave loads one fragment as one
+// contiguous KiB, and the S fragments of a step are adjacent.  Zero outside
+// R x K, for zero elements and for elements below the row's window.  VEC:
+// unit K stride with every 16-element run 16-byte aligned.
+struct SliceMakeArgs {
+  const void* p; int64_t R, K, s_r, s_k;
+  const int32_t* top;
+  int8_t* out;
+  int64_t Rb, Kb;                     // 16-row and 64-k blocks (padded)
+  int S;
+  int vec;
+};
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_slice_make(SliceMakeArgs a) {
+  const int64_t total = a.Rb * a.Kb * 64;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < total; t += stride) {
+    const int lane = static_cast<int>(t & 63);
+    const int64_t blk = t >> 6, rb = blk / a.Kb, kb = blk % a.Kb;
+    const int64_t row = rb * 16 + (lane & 15), k0 = kb * 64 + (lane >> 4) * 16;
+    uint32_t d[SL_MAX][4];
+#pragma unroll
+    for (int s = 0; s < SL_MAX; ++s) d[s][0] = d[s][1] = d[s][2] = d[s][3] = 0u;
+    if (row < a.R) {
+      const int base = a.top[row] + 3 - 8 * a.S;
+      uint32_t e[16];
+      if (a.vec && k0 + 16 <= a.K) {
+        if (DT == DET_F32) {
+          const uint4* q = reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(a.p) + row * a.s_r + k0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint4 v = q[i];
+            e[4 * i] = v.x; e[4 * i + 1] = v.y; e[4 * i + 2] = v.z; e[4 * i + 3] = v.w;
+          }
+        } else {
+          const uint4* q = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.p) + row * a.s_r + k0);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const uint4 v = q[i];
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) { e[8 * i + 2 * u] = w4[u] & 0xFFFFu; e[8 * i + 2 * u + 1] = w4[u] >> 16; }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          e[j] = k0 + j < a.K ? load_elem<DT>(a.p, row * a.s_r + (k0 + j) * a.s_k) : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        bool neg;
+        uint32_t m;
+        int ex;
+        split_elem<DT>(e[j], neg, m, ex);
+        const int sh = ex - base;
+        if (m == 0u || sh + __ffs(static_cast<int>(m)) - 1 < 0) continue;    // zero, or below the window
+        int64_t v = sh >= 0 ? static_cast<int64_t>(m) << sh : static_cast<int64_t>(m >> (-sh));
+        if (neg) v = -v;
+#pragma unroll
+        for (int s = 0; s < SL_MAX; ++s) {
+          if (s < a.S) {
+            const int64_t dig = static_cast<int8_t>(static_cast<uint8_t>(v & 0xFF));
+            v = (v - dig) >> 8;
+            d[s][j >> 2] |= (static_cast<uint32_t>(dig) & 0xFFu) << (8 * (j & 3));
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < SL_MAX; ++s)
+      if (s < a.S)
+        *reinterpret_cast<uint4*>(a.out + ((blk * a.S + s) * 64 + lane) * 16) =
+            make_uint4(d[s][0], d[s][1], d[s][2], d[s][3]);
+  }
+}
+
+// RNE(z * 2^e2) as binary32 bits (gradual underflow, overflow to inf; z = 0
+// gives +0)
+__device__ uint32_t round_i128_to_f32(__int128 z, int e2) {
+  if (z == 0) return 0u;
+  const bool neg = z < 0;
+  const unsigned __int128 A = neg ? -static_cast<unsigned __int128>(z) : static_cast<unsigned __int128>(z);
+  const uint64_t hi = static_cast<uint64_t>(A >> 64), lo = static_cast<uint64_t>(A);
+  const int n = hi != 0u ? 127 - __clzll(static_cast<long long>(hi)) : 63 - __clzll(static_cast<long long>(lo));
+  int q = max(n - 23, -149 - e2);                 // lowest kept bit of A
+  uint32_t r;
+  if (q <= 0) {
+    r = static_cast<uint32_t>(A << (-q));         // exact: A < 2^(24 + q)
+  } else if (q > 128) {
+    r = 0u;                                       // |value| < 2^-150
+  } else {
+    const unsigned __int128 one = 1;
+    const unsigned __int128 rr = q == 128 ? 0 : A >> q;
+    const unsigned __int128 rem = q == 128 ? A : A & ((one << q) - 1);
+    const unsigned __int128 half = one << (q - 1);
+    r = static_cast<uint32_t>(rr);
+    if (rem > half || (rem == half && (r & 1u))) r += 1u;
+    if (r == (1u << 24)) { r = 1u << 23; q += 1; }
+  }
+  uint32_t mag;
+  if (r < (1u << 23)) {
+    mag = r;                                      // subnormal or zero: q + e2 == -149
+  } else {
+    const int E = q + e2 + 150;
+    mag = E >= 255 ? 0x7F800000u : (static_cast<uint32_t>(E) << 23) | (r - (1u << 23));
+  }
+  return (neg ? 0x80000000u : 0u) | mag;
+}
+
+// The matrix-core pass (v_mfma_i32_16x16x64_i8).  A workgroup of 4 waves
+// owns 64 rows x 32 CB columns; wave (wr, wc) owns 32 rows x 16 CB columns:
+// 2 x CB blocks of 16 x 16, each with 2S-1 int32 sums (one per s + t).  Per
+// 64-k step the workgroup's (4 + 2 CB) S fragments (one KiB each: 4 row
+// blocks and 2 CB column blocks of x and w, S digits each) are copied from
+// the digit arrays into one of two LDS buffers with global_load_lds_dwordx4
+// (one instruction per fragment, no registers); each wave reads its 2S + CB S
+// fragments from LDS, starts the copy of the next step into the other
+// buffer (the last one repeats a step, so the copy is unconditional), and
+// runs its 2 CB S^2 MFMAs.  One barrier per step.  At most 256 registers per
+// lane and 2 x (4 + 2 CB) S KiB of LDS, so two workgroups share a CU (one for
+// S = 7) and each SIMD switches between two waves while one reads LDS.  One
+// launch covers at most 2^14 k; longer K runs as several launches that carry
+// each output's 128-bit sum in the workspace (epilogues as for the
+// accumulator path).
+struct SliceMmaArgs {
+  const int8_t* xs; const int8_t* ws;
+  int64_t Kb;                         // 64-k steps in the digit arrays
+  int64_t kb0, kb1;                   // the steps of this launch
+  int64_t M, N;
+  int64_t tiles_m, tiles_n;
+  const int32_t* topx; const int32_t* topw;
+  float* y; int64_t y_sm, y_sn;
+  int64_t* z;                         // 128-bit sums [M][N][2] (lo, hi) between launches
+  int epi;
+};
+
+template <int S, int CB>
+struct SliceTile {
+  static constexpr int NG = 2 * S - 1;
+  static constexpr int FA = 4 * S;              // x fragments per step (4 row blocks)
+  static constexpr int FT = FA + 2 * CB * S;    // all fragments per step
+  static constexpr int PER_WAVE = (FT + 3) / 4;  // copies per wave (the last may be idle)
+  static constexpr int LDS_BYTES = 2 * FT * 1024;
+};
+
+// this wave's copies of step kb into LDS buffer `buf`: fragment f = wave + 4j
+// from src[j] (the lane's 16 bytes land at 16 * lane of the fragment)
+template <int S, int CB>
+__device__ __forceinline__ void slice_copy(const int8_t* const (&src)[SliceTile<S, CB>::PER_WAVE], int8_t* lds,
+                                           int wave, int64_t kb, int buf) {
+  using T = SliceTile<S, CB>;
+#pragma unroll
+  for (int j = 0; j < T::PER_WAVE; ++j)
+    if (T::FT % 4 == 0 || j + 1 < T::PER_WAVE || wave + 4 * j < T::FT)     // uniform per wave
+      __builtin_amdgcn_global_load_lds(src[j] + kb * (S * 1024), lds + buf * (T::FT * 1024) + (wave + 4 * j) * 1024,
+                                       16, 0, 0);
+}
+
+// one 64-k step: product (s, t) of block (i, c) into its sum for s + t
+template <int S, int CB>
+__device__ __forceinline__ void slice_steps(const v4i (&fa)[S][2], const v4i (&fb)[S][CB],
+                                            v4i (&acc)[2 * S - 1][2][CB]) {
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int t = 0; t < S; ++t)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+          acc[s + t][i][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[s][i], fb[t][c], acc[s + t][i][c], 0, 0, 0);
+}
+
+template <int S, int CB>
+__global__ __launch_bounds__(256, 2) void k_slice_mma(SliceMmaArgs a) {
+  using T = SliceTile<S, CB>;
+  constexpr int NG = T::NG, FA = T::FA, FT = T::FT, PW = T::PER_WAVE;
+  __shared__ __align__(16) int8_t lds[T::LDS_BYTES];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wr = wave >> 1, wc = wave & 1;
+  const int64_t tile = xcd_tile();
+  const int64_t rbw = 4 * (tile % a.tiles_m);                  // the workgroup's first 16-row block
+  const int64_t cbw = 2 * CB * (tile / a.tiles_m);             // and first 16-column block
+  const int64_t fstep = a.Kb * (S * 1024);                     // bytes between 16-row blocks
+
+  // this wave copies fragments f = wave + 4 j of every step: x block rbw + f
+  // div S (f < FA) or w block cbw + (f - FA) div S, digit f mod S
+  const int8_t* src[PW];
+#pragma unroll
+  for (int j = 0; j < PW; ++j) {
+    const int f = min(wave + 4 * j, FT - 1);
+    src[j] = f < FA ? a.xs + (rbw + f / S) * fstep + (f % S) * 1024
+                    : a.ws + (cbw + (f - FA) / S) * fstep + ((f - FA) % S) * 1024;
+    src[j] += lane * 16;
+  }
+
+  v4i acc[NG][2][CB];
+#pragma unroll
+  for (int u = 0; u < NG; ++u)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int c = 0; c < CB; ++c) acc[u][i][c] = v4i{0, 0, 0, 0};
+
+  if (a.kb0 < a.kb1) slice_copy<S, CB>(src, lds, wave, a.kb0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int64_t kb = a.kb0; kb < a.kb1; ++kb) {
+    const int buf = static_cast<int>((kb - a.kb0) & 1);
+    const int8_t* const lb = lds + buf * (FT * 1024) + lane * 16;
+    // this wave's fragments, in the order the MFMAs first use them
+    v4i fa[S][2], fb[S][CB];
+#pragma unroll
+    for (int t = 0; t < S; ++t) {
+      if (t == 0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) fa[0][i] = *reinterpret_cast<const v4i*>(lb + ((2 * wr + i) * S) * 1024);
+      }
+#pragma unroll
+      for (int c = 0; c < CB; ++c)
+        fb[t][c] = *reinterpret_cast<const v4i*>(lb + (FA + (wc * CB + c) * S + t) * 1024);
+    }
+#pragma unroll
+    for (int s = 1; s < S; ++s)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) fa[s][i] = *reinterpret_cast<const v4i*>(lb + ((2 * wr + i) * S + s) * 1024);
+    __builtin_amdgcn_sched_barrier(0);
+    slice_copy<S, CB>(src, lds, wave, min(kb + 1, a.Kb - 1), buf ^ 1);   // into the buffer read one step ago
+    __builtin_amdgcn_sched_barrier(0);
+    slice_steps<S, CB>(fa, fb, acc);
+    __builtin_amdgcn_sched_barrier(0);                  // the wait and barrier stay behind the MFMAs
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");    // this wave's copies of step kb + 1 landed
+    __syncthreads();                                     // everyone's, and buffer buf is free
+  }
+
+  // output (row, col) of accumulator r of block (i, c): the MFMA's C layout
+#pragma unroll
+  for (int c = 0; c < CB; ++c) {
+    const int64_t col = (cbw + wc * CB + c) * 16 + (lane & 15);
+    if (col >= a.N) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = (rbw + 2 * wr + i) * 16 + 4 * (lane >> 4) + r;
+        if (row >= a.M) continue;
+        __int128 z = 0;
+#pragma unroll
+        for (int u = 0; u < NG; ++u) z += static_cast<__int128>(acc[u][i][c][r]) << (8 * u);
+        int64_t* const zp = a.z + (row * a.N + col) * 2;
+        if (a.epi == EPI_ADD || a.epi == EPI_ADD_ROUND)
+          z += (static_cast<__int128>(zp[1]) << 64) | static_cast<__int128>(static_cast<uint64_t>(zp[0]));
+        if (a.epi == EPI_STORE || a.epi == EPI_ADD) {
+          zp[0] = static_cast<int64_t>(z);
+          zp[1] = static_cast<int64_t>(z >> 64);
+        } else {
+          const int e2 = (a.topx[row] + 3 - 8 * S) + (a.topw[col] + 3 - 8 * S);
+          a.y[row * a.y_sm + col * a.y_sn] = __uint_as_float(round_i128_to_f32(z, e2));
+        }
+        asm volatile("" ::: "memory");          // one output at a time
+      }
+  }
+}
+
 // ---------------------------------------------------------------- host helpers
 det_status check_operands(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk, const void* w,
                           int64_t w_sn, int64_t w_sk, int64_t M, int64_t N, int64_t K) {
@@ -1019,6 +1462,7 @@ det_status predecode_x_block(GemmArgs& b, const void* xblock, char* xr, hipStrea
   p.M = b.M; p.K = b.K; p.Mp = round_up(b.M, TILE_ROWS); p.Kp = round_up(b.K, V_KC);
   p.xsig = reinterpret_cast<int32_t*>(xr);
   p.xword = reinterpret_cast<uint32_t*>(xr + p.Mp * p.Kp * 4);
+  p.rmap = b.xmap;
   b.xsig = p.xsig; b.xword = p.xword; b.xld = p.Kp;
   hipLaunchKernelGGL((k_predecode_x<D, DT>), dim3(grid_for(p.Mp * p.Kp, 256, 8192)), dim3(256), 0, s, p);
   return hip_check(hipGetLastError(), "x predecode launch");
@@ -1100,6 +1544,7 @@ det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s) {
     p.wsig = static_cast<int32_t*>(ws);
     p.wexp = static_cast<char*>(ws) + p.Np * p.Kp * 4;
     a.wsig = p.wsig; a.wexp32 = static_cast<const uint32_t*>(p.wexp); a.wld = p.Np * V_KC;
+    p.rmap = a.wmap;
     const dim3 pg(grid_for(p.Np * p.Kp, 256, 8192));
     hipLaunchKernelGGL((k_predecode_w8<G, DT>), pg, dim3(256), 0, s, p);
     det_status st = hip_check(hipGetLastError(), "predecode launch");
@@ -1131,6 +1576,192 @@ det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s) {
     if (st != DET_OK) return st;
   }
   return DET_OK;
+}
+
+// ---------------------------------------------------------------- det_gemm: the matrix-core path
+//
+// Workspace behind the accumulator path's: per-row stats of x then w (top,
+// low, need, fallback list; int32), the span histogram, then SL_MAX digit
+// planes of x (rows padded to 64) and of w (rows padded to 128), K padded to
+// 32, then for K > 2^14 the 128-bit sums [M][N] carried between launches.
+int64_t slice_rows_x(int64_t M) { return round_up(M, 64); }
+int64_t slice_rows_w(int64_t N) { return round_up(N, 128); }
+int64_t slice_stats_bytes(int64_t M, int64_t N) { return round_up(16 * (M + N) + 4 * 2 * SL_HIST, 256); }
+int64_t slice_bytes(int64_t M, int64_t N, int64_t K) {
+  const int64_t Kp = round_up(K, 2 * SL_KB);
+  return slice_stats_bytes(M, N) + SL_MAX * (slice_rows_x(M) + slice_rows_w(N)) * Kp +
+         (Kp / SL_KB > SL_FOLD ? 16 * M * N : 0);
+}
+
+// Host choice between the paths: estimated seconds from the accumulator
+// kernels' MAC rate and the int8 MAC rate of the slice pass (both measured
+// on MI355X), S^2 int8 MACs per MAC plus the fallback rows and columns.
+constexpr double RATE_ACC_F32 = 3.4e12, RATE_ACC_BF16 = 5.0e12, RATE_MMA = 1.2e15;
+constexpr double SLICE_MIN_MACS = 134217728.0;    // 2^27: below, the accumulator path alone
+
+std::atomic<int> g_path{DET_PATH_AUTO};
+std::atomic<int> g_forced_slices{0};
+thread_local det_path g_plan_path = DET_PATH_ACCUMULATOR;
+thread_local int g_plan_slices = 0;
+thread_local int64_t g_plan_rows = 0, g_plan_cols = 0;
+
+void record_plan(det_path p, int S, int64_t fx, int64_t fw) {
+  g_plan_path = p; g_plan_slices = S; g_plan_rows = fx; g_plan_cols = fw;
+}
+
+int choose_slices(det_dtype dt, int64_t M, int64_t N, int64_t K, const int32_t* hx, const int32_t* hw,
+                  bool only_slices, int forced, int64_t& fx, int64_t& fw) {
+  const double macs = static_cast<double>(M) * N * K;
+  const double rate_acc = dt == DET_F32 ? RATE_ACC_F32 : RATE_ACC_BF16;
+  double best = only_slices ? 1e300 : macs / rate_acc;
+  int best_s = 0;
+  for (int S = SL_MIN; S <= SL_MAX; ++S) {
+    if (forced != 0 && S != forced) continue;
+    int64_t cx = 0, cw = 0;
+    for (int n = S + 1; n <= SL_MAX + 1; ++n) { cx += hx[n]; cw += hw[n]; }
+    const double t = static_cast<double>(S) * S * macs / RATE_MMA +
+                     (static_cast<double>(cx) * N * K + static_cast<double>(cw) * M * K) / rate_acc;
+    if (t < best) { best = t; best_s = S; fx = cx; fw = cw; }
+  }
+  return best_s;
+}
+
+template <int S>
+det_status launch_mma(SliceMmaArgs m, hipStream_t s) {
+  constexpr int CB = S == 2 ? 4 : S <= 4 ? 2 : 1;    // 16-column blocks per wave
+  m.tiles_m = slice_rows_x(m.M) / 64;
+  m.tiles_n = (m.N + 32 * CB - 1) / (32 * CB);
+  const int64_t blocks = m.tiles_m * m.tiles_n;
+  if (blocks > 0x7FFFFFFF) return fail(DET_EINVAL, "too many output tiles");
+  const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+  // K blocks of 2^14 (SL_FOLD steps): each int32 sum stays below 2^31
+  const int64_t nblk = (m.Kb + SL_FOLD - 1) / SL_FOLD;
+  for (int64_t ib = 0; ib < nblk; ++ib) {
+    SliceMmaArgs b = m;
+    b.kb0 = ib * SL_FOLD;
+    b.kb1 = min(m.Kb, b.kb0 + SL_FOLD);
+    b.epi = nblk == 1 ? EPI_ROUND : ib == 0 ? EPI_STORE : ib + 1 == nblk ? EPI_ADD_ROUND : EPI_ADD;
+    hipLaunchKernelGGL((k_slice_mma<S, CB>), grid, block, 0, s, b);
+    det_status st = hip_check(hipGetLastError(), "slice mma launch");
+    if (st != DET_OK) return st;
+  }
+  return DET_OK;
+}
+
+template <int DT>
+det_status slice_stats(const void* p, int64_t R, int64_t K, int64_t s_r, int64_t s_k, int32_t* top,
+                       int32_t* low, hipStream_t s) {
+  SliceStatArgs a{p, R, K, s_r, s_k, top, low};
+  if (s_k == 1) {
+    const int64_t waves = R * ((K + 1023) / 1024);
+    hipLaunchKernelGGL((k_slice_stats<DT, true>), dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256), 0, s, a);
+  } else {
+    const int64_t threads = R * ((K + 255) / 256);
+    hipLaunchKernelGGL((k_slice_stats<DT, false>), dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256),
+                       0, s, a);
+  }
+  return hip_check(hipGetLastError(), "slice stats launch");
+}
+
+template <int DT>
+det_status slice_make(const void* p, int64_t R, int64_t K, int64_t s_r, int64_t s_k, const int32_t* top,
+                      int8_t* out, int64_t rows_padded, int S, hipStream_t s) {
+  const int64_t esz = DT == DET_F32 ? 4 : 2;
+  SliceMakeArgs a{};
+  a.p = p; a.R = R; a.K = K; a.s_r = s_r; a.s_k = s_k; a.top = top; a.out = out;
+  a.Rb = rows_padded / 16; a.Kb = round_up(K, 2 * SL_KB) / SL_KB;
+  a.S = S;
+  a.vec = s_k == 1 && (reinterpret_cast<uintptr_t>(p) % 16) == 0 && (s_r * esz) % 16 == 0;
+  hipLaunchKernelGGL((k_slice_make<DT>), dim3(grid_for(a.Rb * a.Kb * 64, 256, 16384)), dim3(256), 0, s, a);
+  return hip_check(hipGetLastError(), "slice make launch");
+}
+
+template <int DT>
+det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s);
+
+// det_gemm with the room for both paths in `ws`: span statistics, the
+// choice, then either the accumulator path or the matrix-core pass plus the
+// accumulator path on the rows and columns that did not fit.
+template <int DT>
+det_status launch_sliced(GemmArgs a, char* ws, bool only_slices, int forced, hipStream_t s) {
+  const int64_t M = a.M, N = a.N, K = a.K;
+  char* const sl = ws + workspace_bytes(1, M, N, K);
+  int32_t* const topx = reinterpret_cast<int32_t*>(sl);
+  int32_t* const topw = topx + M;
+  int32_t* const lowx = topw + N;
+  int32_t* const loww = lowx + M;
+  int32_t* const needx = loww + N;
+  int32_t* const needw = needx + M;
+  int32_t* const listx = needw + N;
+  int32_t* const listw = listx + M;
+  int32_t* const hist = listw + N;
+  int8_t* const planes = reinterpret_cast<int8_t*>(sl + slice_stats_bytes(M, N));
+  const int64_t Kp = round_up(K, 2 * SL_KB);
+  int8_t* const xs = planes;
+  int8_t* const wsl = planes + SL_MAX * slice_rows_x(M) * Kp;
+
+  hipLaunchKernelGGL(k_slice_init, dim3(grid_for(M + N, 256, 1024)), dim3(256), 0, s, topx, lowx, M + N, hist);
+  det_status st = hip_check(hipGetLastError(), "slice init launch");
+  if (st == DET_OK) st = slice_stats<DT>(a.x, M, K, a.x_sm, a.x_sk, topx, lowx, s);
+  if (st == DET_OK) st = slice_stats<DT>(a.w, N, K, a.w_sn, a.w_sk, topw, loww, s);
+  if (st != DET_OK) return st;
+  hipLaunchKernelGGL(k_slice_need, dim3(grid_for(M, 256, 256)), dim3(256), 0, s, topx, lowx, M, needx, hist);
+  hipLaunchKernelGGL(k_slice_need, dim3(grid_for(N, 256, 256)), dim3(256), 0, s, topw, loww, N, needw,
+                     hist + SL_HIST);
+  st = hip_check(hipGetLastError(), "slice need launch");
+  if (st != DET_OK) return st;
+  int32_t h[2 * SL_HIST];
+  st = hip_check(hipMemcpyAsync(h, hist, sizeof h, hipMemcpyDeviceToHost, s), "span histogram copy");
+  if (st == DET_OK) st = hip_check(hipStreamSynchronize(s), "span histogram sync");
+  if (st != DET_OK) return st;
+
+  int64_t fx = 0, fw = 0;
+  const int S = choose_slices(static_cast<det_dtype>(DT), M, N, K, h, h + SL_HIST, only_slices, forced, fx, fw);
+  if (S == 0) {
+    record_plan(DET_PATH_ACCUMULATOR, 0, 0, 0);
+    return launch_gemm8<DT>(a, ws, s);
+  }
+  record_plan(DET_PATH_SLICES, S, fx, fw);
+  st = slice_make<DT>(a.x, M, K, a.x_sm, a.x_sk, topx, xs, slice_rows_x(M), S, s);
+  if (st == DET_OK) st = slice_make<DT>(a.w, N, K, a.w_sn, a.w_sk, topw, wsl, slice_rows_w(N), S, s);
+  if (st != DET_OK) return st;
+  SliceMmaArgs m{};
+  m.xs = xs; m.ws = wsl;
+  m.Kb = Kp / SL_KB;
+  m.M = M; m.N = N;
+  m.topx = topx; m.topw = topw;
+  m.y = a.y; m.y_sm = a.y_sm; m.y_sn = a.y_sn;
+  m.z = reinterpret_cast<int64_t*>(planes + SL_MAX * (slice_rows_x(M) + slice_rows_w(N)) * Kp);
+  switch (S) {
+    case 2: st = launch_mma<2>(m, s); break;
+    case 3: st = launch_mma<3>(m, s); break;
+    case 4: st = launch_mma<4>(m, s); break;
+    case 5: st = launch_mma<5>(m, s); break;
+    case 6: st = launch_mma<6>(m, s); break;
+    default: st = launch_mma<7>(m, s); break;
+  }
+  if (st != DET_OK) return st;
+  // rows and columns beyond S digits: the accumulator path overwrites them
+  if (fx > 0) {
+    hipLaunchKernelGGL(k_slice_list, dim3(1), dim3(1024), 0, s, needx, M, S, listx);
+    st = hip_check(hipGetLastError(), "slice list launch");
+    if (st != DET_OK) return st;
+    GemmArgs b = a;
+    b.M = fx;
+    b.xmap = listx;
+    st = launch_gemm8<DT>(b, ws, s);
+    if (st != DET_OK) return st;
+  }
+  if (fw > 0) {
+    hipLaunchKernelGGL(k_slice_list, dim3(1), dim3(1024), 0, s, needw, N, S, listw);
+    st = hip_check(hipGetLastError(), "slice list launch");
+    if (st != DET_OK) return st;
+    GemmArgs b = a;
+    b.N = fw;
+    b.wmap = listw;
+    st = launch_gemm8<DT>(b, ws, s);
+  }
+  return st;
 }
 
 det_status launch_gemm(det_dtype dt, int out_mode, GemmArgs a, void* ws, hipStream_t s) {
@@ -1175,7 +1806,24 @@ det_status gemm_common(int out_mode, det_dtype dt, const void* x, int64_t x_sm, 
   a.M = M; a.N = N; a.K = K;
   a.y = y; a.y_sm = y_sm; a.y_sn = y_sn;
   a.acc = acc;
-  return launch_gemm(dt, out_mode, a, ws, static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (out_mode == 1 && ws != nullptr && M > 0 && N > 0 && K > 0) {
+    const int path = g_path.load();
+    const bool room = ws_bytes >= static_cast<size_t>(workspace_bytes(1, M, N, K) + slice_bytes(M, N, K));
+    if (path == DET_PATH_SLICES && !room)
+      return fail(DET_EINVAL, "the matrix-core path needs a workspace of %lld bytes",
+                  (long long)(workspace_bytes(1, M, N, K) + slice_bytes(M, N, K)));
+    const bool big = static_cast<double>(M) * N * K >= SLICE_MIN_MACS;
+    if (room && (path == DET_PATH_SLICES || (path == DET_PATH_AUTO && big))) {
+      const bool only = path == DET_PATH_SLICES;
+      const int forced = only ? g_forced_slices.load() : 0;
+      char* const w8 = static_cast<char*>(ws);
+      return dt == DET_F32 ? launch_sliced<DET_F32>(a, w8, only, forced, s)
+                           : launch_sliced<DET_BF16>(a, w8, only, forced, s);
+    }
+  }
+  if (out_mode == 1) record_plan(DET_PATH_ACCUMULATOR, 0, 0, 0);
+  return launch_gemm(dt, out_mode, a, ws, s);
 }
 
 }  // namespace
@@ -1183,7 +1831,25 @@ det_status gemm_common(int out_mode, det_dtype dt, const void* x, int64_t x_sm, 
 int64_t det_gemm_workspace_bytes(det_dtype dt, int partial, int64_t M, int64_t N, int64_t K) {
   (void)dt;
   if (M <= 0 || N <= 0 || K <= 0) return 0;
-  return workspace_bytes(partial ? 0 : 1, M, N, K);
+  if (partial) return workspace_bytes(0, M, N, K);
+  return workspace_bytes(1, M, N, K) + slice_bytes(M, N, K);
+}
+
+det_status det_set_gemm_path(det_path path, int slices) {
+  if (path != DET_PATH_AUTO && path != DET_PATH_ACCUMULATOR && path != DET_PATH_SLICES)
+    return fail(DET_EINVAL, "unknown path %d", static_cast<int>(path));
+  if (slices != 0 && (slices < SL_MIN || slices > SL_MAX))
+    return fail(DET_EINVAL, "slices must be 0 or %d..%d (got %d)", SL_MIN, SL_MAX, slices);
+  g_forced_slices.store(slices);
+  g_path.store(static_cast<int>(path));
+  return DET_OK;
+}
+
+void det_last_gemm_plan(int* path, int* slices, int64_t* fallback_rows, int64_t* fallback_cols) {
+  if (path) *path = static_cast<int>(g_plan_path);
+  if (slices) *slices = g_plan_slices;
+  if (fallback_rows) *fallback_rows = g_plan_rows;
+  if (fallback_cols) *fallback_cols = g_plan_cols;
 }
 
 det_status det_gemm(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk, const void* w, int64_t w_sn,

@@ -38,7 +38,9 @@
  *     sliced views (e.g. x[:, a:b] or x^T).  Operand elements must be
  *     naturally aligned (4 bytes for f32, 2 for bf16).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
- *     asynchronously and stream-ordered; nothing here synchronises.
+ *     asynchronously and stream-ordered.  The one exception is det_gemm_ws
+ *     when it considers the matrix-core path (see det_set_gemm_path): it
+ *     waits for `stream` once, to read a 128-byte histogram.
  *   - Argument errors are reported before anything is enqueued; on error
  *     nothing is written.  det_last_error() returns a message for the calling
  *     thread's most recent failure.
@@ -123,7 +125,12 @@ det_status det_gemm_partial(det_dtype dt, const void* x, int64_t x_sm, int64_t x
  * det_gemm_workspace_bytes returns the size needed (0 when M, N or K is 0):
  * (partial ? 6 : 8) * roundup(N, 64) * roundup(K, 16) for w, plus
  * 8 * roundup(M, 2) * roundup(min(K, 2^15), 16) for x, plus 144 * M * N for
- * det_gemm_ws (partial = 0) when K > 2^15.
+ * det_gemm_ws (partial = 0) when K > 2^15; for det_gemm_ws also the room of
+ * the matrix-core path: roundup(16 (M + N) + 128, 256) +
+ * 7 * (roundup(M, 64) + roundup(N, 128)) * roundup(K, 128), plus 16 * M * N
+ * when K > 2^14.  det_gemm_ws
+ * given only the accumulator path's size (the sum without that last term)
+ * runs the accumulator path.
  * Errors as for det_gemm, plus DET_EINVAL for a null, misaligned or too small
  * workspace.
  */
@@ -134,6 +141,44 @@ det_status det_gemm_ws(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk,
                        int64_t M, int64_t N, int64_t K,
                        float* y, int64_t y_sm, int64_t y_sn,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The matrix-core path of det_gemm_ws.  det_gemm only promises the exact sum
+ * rounded once ("Method"), so for operands whose rows each span few binades
+ * the sum may be formed with int8 matrix products instead of the digit
+ * accumulator: each row of x and of w is scaled by a power of two to
+ * integers below 2^(8S-2) in magnitude (S = 2..7), which are cut into S
+ * signed 8-bit digits; the S^2 digit GEMMs run on the MFMA units with int32
+ * sums, are added exactly in 128-bit integers and rounded once.  Rows of x
+ * or w whose nonzero elements span more than 8S - 3 binades are recomputed
+ * on the accumulator path.  The results are bit-identical to the
+ * accumulator path's for every input.
+ *
+ * det_set_gemm_path sets, for the whole process, which path det_gemm_ws
+ * takes:
+ *   DET_PATH_AUTO         (default) the matrix-core path is considered for
+ *                         M*N*K >= 2^27 when the workspace has its room: the
+ *                         call measures the spans (one pass over x and w),
+ *                         waits for the stream, and picks S, or the
+ *                         accumulator path, by estimated time
+ *   DET_PATH_ACCUMULATOR  always the digit accumulator
+ *   DET_PATH_SLICES       always the matrix-core path (a too small workspace
+ *                         is DET_EINVAL); `slices` = 2..7 fixes S, 0 lets the
+ *                         call pick it
+ * `slices` must be 0 or 2..7 (else DET_EINVAL); it is ignored by the other
+ * two paths.  det_gemm (no workspace) and the partials always use the
+ * accumulator.
+ *
+ * det_last_gemm_plan reports the calling thread's last det_gemm or
+ * det_gemm_ws call: the path taken (DET_PATH_ACCUMULATOR or DET_PATH_SLICES),
+ * S (0 for the accumulator) and how many rows of x and of w the accumulator
+ * recomputed.  Null pointers are skipped.
+ */
+typedef enum { DET_PATH_AUTO = 0, DET_PATH_ACCUMULATOR = 1, DET_PATH_SLICES = 2 } det_path;
+
+det_status det_set_gemm_path(det_path path, int slices);
+
+void det_last_gemm_plan(int* path, int* slices, int64_t* fallback_rows, int64_t* fallback_cols);
 
 det_status det_gemm_partial_ws(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk,
                                const void* w, int64_t w_sn, int64_t w_sk,

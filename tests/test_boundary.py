@@ -69,6 +69,16 @@ def test_c_abi_rejects_bad_arguments_without_a_gpu():
     assert lib.det_check_finite(9, None, 1, 1, 1, 1, None, None) == _lib.DET_EDTYPE
 
 
+def _ru(v, m):
+    return (v + m - 1) // m * m
+
+
+def _slice_room(M, N, K):
+    """det_gemm_ws's room for the matrix-core path, as include/detgemm.h states it."""
+    return (_ru(16 * (M + N) + 128, 256) + 7 * (_ru(M, 64) + _ru(N, 128)) * _ru(K, 128)
+            + (16 * M * N if K > (1 << 14) else 0))
+
+
 def test_workspace_size_and_checks():
     lib = _lib.load()
     assert lib.det_gemm_workspace_bytes(0, 0, 3, 0, 5) == 0
@@ -76,21 +86,52 @@ def test_workspace_size_and_checks():
     assert lib.det_gemm_workspace_bytes(0, 0, 0, 5, 5) == 0
     # decoded w: 4-byte significand and exponent word per element (det_gemm),
     # 4 + 2 bytes (det_gemm_partial), rows padded to 64 and K to 16; decoded
-    # x of one K block (at most 2^15): 8 bytes per element, rows padded to 2
-    assert lib.det_gemm_workspace_bytes(0, 0, 1, 1, 1) == 8 * 64 * 16 + 8 * 2 * 16
+    # x of one K block (at most 2^15): 8 bytes per element, rows padded to 2;
+    # det_gemm also reserves the matrix-core path's digit arrays
+    assert lib.det_gemm_workspace_bytes(0, 0, 1, 1, 1) == 8 * 64 * 16 + 8 * 2 * 16 + _slice_room(1, 1, 1)
     assert lib.det_gemm_workspace_bytes(1, 1, 9, 4096, 4096) == 6 * 4096 * 4096 + 8 * 10 * 4096
-    assert lib.det_gemm_workspace_bytes(0, 0, 9, 65, 17) == 8 * 128 * 32 + 8 * 10 * 32
+    assert (lib.det_gemm_workspace_bytes(0, 0, 9, 65, 17)
+            == 8 * 128 * 32 + 8 * 10 * 32 + _slice_room(9, 65, 17))
     # det_gemm with K beyond one block also carries 144 bytes of digits per output
     assert (lib.det_gemm_workspace_bytes(0, 0, 7, 64, 40000)
-            == 8 * 64 * 40000 + 8 * 8 * 32768 + 144 * 7 * 64)
+            == 8 * 64 * 40000 + 8 * 8 * 32768 + 144 * 7 * 64 + _slice_room(7, 64, 40000))
     assert lib.det_gemm_workspace_bytes(0, 1, 7, 64, 40000) == 6 * 64 * 40000 + 8 * 8 * 32768
     vp = ctypes.c_void_p
     args = (0, vp(1 << 20), 4, 1, vp(1 << 20), 4, 1, 4, 4, 4, vp(1 << 20), 4, 1)
     need = lib.det_gemm_workspace_bytes(0, 0, 4, 4, 4)
+    acc_need = need - _slice_room(4, 4, 4)              # the accumulator path alone
     assert lib.det_gemm_ws(*args, None, need, None) == _lib.DET_EINVAL
     assert lib.det_gemm_ws(*args, vp((1 << 20) + 8), need, None) == _lib.DET_EINVAL   # misaligned
-    assert lib.det_gemm_ws(*args, vp(1 << 20), need - 1, None) == _lib.DET_EINVAL    # too small
+    assert lib.det_gemm_ws(*args, vp(1 << 20), acc_need - 1, None) == _lib.DET_EINVAL  # too small
     assert "workspace" in _lib.last_error()
+    # the matrix-core path, forced, needs its room too
+    try:
+        assert lib.det_set_gemm_path(_lib.DET_PATH_SLICES, 0) == _lib.DET_OK
+        assert lib.det_gemm_ws(*args, vp(1 << 20), need - 1, None) == _lib.DET_EINVAL
+        assert "matrix-core" in _lib.last_error()
+    finally:
+        assert lib.det_set_gemm_path(_lib.DET_PATH_AUTO, 0) == _lib.DET_OK
+
+
+def test_gemm_path_settings():
+    lib = _lib.load()
+    assert lib.det_set_gemm_path(3, 0) == _lib.DET_EINVAL
+    for bad in (1, 8, -1):
+        assert lib.det_set_gemm_path(_lib.DET_PATH_SLICES, bad) == _lib.DET_EINVAL
+    assert "slices" in _lib.last_error()
+    for path in (_lib.DET_PATH_ACCUMULATOR, _lib.DET_PATH_SLICES, _lib.DET_PATH_AUTO):
+        for S in (0, 2, 7):
+            assert lib.det_set_gemm_path(path, S) == _lib.DET_OK
+    lib.det_set_gemm_path(_lib.DET_PATH_AUTO, 0)
+    lib.det_last_gemm_plan(None, None, None, None)       # null pointers are skipped
+    with pytest.raises(ValueError):
+        det.set_gemm_path("fast")
+    with pytest.raises(ValueError):
+        det.set_gemm_path("slices", 9)
+    with det.gemm_path("accumulator"):
+        pass
+    plan = det.last_gemm_plan()
+    assert set(plan) == {"path", "slices", "fallback_rows", "fallback_cols"}
 
 
 def test_c_abi_empty_problems_are_no_ops():

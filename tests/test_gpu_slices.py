@@ -1,0 +1,211 @@
+"""GPU parity of det_gemm's matrix-core path against the oracle, bit for bit.
+
+The path forms the exact sum from int8 digit GEMMs when the rows of x and w
+span few binades, and recomputes the rows and columns that do not fit on the
+digit accumulator; either way the result must be the oracle's correctly
+rounded exact sum.  The cases force the path (and the digit count S) so that
+small shapes reach it, and cover ragged tiles, K past one 2^14 block, the
+recomputed rows and columns (their counts checked against the rule stated in
+include/detgemm.h), strided views, all-zero rows, and results that overflow,
+underflow or round at ties."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import c_oracle
+from tests import pins
+from tests.gpu_util import announce, f32_bits, mismatch_report, to_device
+from workloads import f32_bits as np_f32_bits, random_operands, to_bf16_bits
+import bitwise_deterministic_exact_amd as det
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _auto_path_after():
+    yield
+    det.set_gemm_path("auto", 0)
+
+
+def _needs(bits: np.ndarray, dt: str) -> np.ndarray:
+    """Digits each row needs: the least S with (top bit - lowest set bit + 1)
+    <= 8S - 2 over the row's nonzero elements, 0 for an all-zero row."""
+    b = bits.astype(np.int64)
+    if dt == "f32":
+        E, F, hid, bias = (b >> 23) & 0xFF, b & 0x7FFFFF, 1 << 23, 150
+    else:
+        E, F, hid, bias = (b >> 7) & 0xFF, b & 0x7F, 1 << 7, 134
+    m = F | np.where(E > 0, hid, 0)
+    ex = np.maximum(E, 1) - bias
+    nz = m != 0
+    mm = np.where(nz, m, 1)
+    top = ex + np.floor(np.log2(mm)).astype(np.int64)
+    low = ex + np.log2(mm & -mm).astype(np.int64)
+    tops = np.where(nz, top, -10**6).max(axis=1)
+    lows = np.where(nz, low, 10**6).min(axis=1)
+    need = (tops - lows + 10) // 8
+    return np.where(nz.any(axis=1), np.minimum(need, 8), 0)
+
+
+def _run(xb, wb, dt, S, x=None, w=None):
+    x = to_device(xb, dt) if x is None else x
+    w = to_device(wb, dt) if w is None else w
+    det.set_gemm_path("slices", S)
+    y = f32_bits(det.det_gemm(x, w))
+    return y, det.last_gemm_plan()
+
+
+def _check(xb, wb, dt, S, label, **kw):
+    announce(f"slices {label} {dt} S={S} M={xb.shape[0]} N={wb.shape[0]} K={xb.shape[1]}")
+    got, plan = _run(xb, wb, dt, S, **kw)
+    want = c_oracle.gemm(xb, wb)
+    assert plan["path"] == "slices", plan
+    if S:
+        assert plan["slices"] == S, plan
+        assert plan["fallback_rows"] == int((_needs(xb, dt) > S).sum()), plan
+        assert plan["fallback_cols"] == int((_needs(wb, dt) > S).sum()), plan
+    assert np.array_equal(got, want), mismatch_report(got, want)
+    return plan
+
+
+SHAPES = [(1, 1, 1), (5, 3, 7), (32, 32, 32), (33, 31, 63), (64, 128, 64), (70, 130, 100),
+          (129, 65, 257), (200, 300, 96)]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("kind", ["normal", "uniform", "int"])
+def test_forced_digits_ragged_shapes(kind, dt):
+    rng = np.random.default_rng(500 + 3 * ["normal", "uniform", "int"].index(kind) + (dt == "bf16"))
+    for i, (M, N, K) in enumerate(SHAPES):
+        xb, wb = random_operands(rng, M, N, K, dt, kind)
+        S = 2 + (i % 6)
+        _check(xb, wb, dt, S, kind)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_every_digit_count_on_one_input(dt):
+    rng = np.random.default_rng(520 + (dt == "bf16"))
+    xb, wb = random_operands(rng, 96, 160, 200, dt, "normal")
+    for S in range(2, 8):
+        _check(xb, wb, dt, S, "normal")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_rows_and_columns_recomputed(dt):
+    # wide and special operands: most rows need more digits than S, so most of
+    # y comes from the accumulator pass over the listed rows and columns
+    rng = np.random.default_rng(530 + (dt == "bf16"))
+    for kind in ("wide", "special"):
+        xb, wb = random_operands(rng, 45, 77, 90, dt, kind)
+        for S in (2, 7):
+            _check(xb, wb, dt, S, kind)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_outlier_rows_and_columns(dt):
+    # rows and columns with one tiny element planted need more digits than S
+    # (f32 N(0,1) rows of 128 fit in 7 digits, bf16 ones in 4): those rows of
+    # x and of w go to the accumulator
+    rng = np.random.default_rng(540 + (dt == "bf16"))
+    M, N, K = 150, 260, 128
+    S = 7 if dt == "f32" else 4
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    w = rng.standard_normal((N, K), dtype=np.float32)
+    rows = rng.choice(M, 7, replace=False)
+    cols = rng.choice(N, 11, replace=False)
+    x[rows, rng.integers(0, K, rows.size)] = np.float32(3.0 * 2.0 ** -60)
+    w[cols, rng.integers(0, K, cols.size)] = np.float32(-(2.0 ** -70))
+    x[3, :] = 0.0                                   # an all-zero row
+    w[5, :] = 0.0                                   # an all-zero column
+    conv = np_f32_bits if dt == "f32" else to_bf16_bits
+    xb, wb = conv(x), conv(w)
+    nx, nw = _needs(xb, dt), _needs(wb, dt)
+    assert nx[3] == 0 and nw[5] == 0
+    assert all(nx[r] > S for r in rows if r != 3) and all(nw[c] > S for c in cols if c != 5)
+    plan = _check(xb, wb, dt, S, "outliers")
+    assert plan["fallback_rows"] >= len(set(rows.tolist()) - {3})
+    assert plan["fallback_cols"] >= len(set(cols.tolist()) - {5})
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_k_beyond_one_block(dt):
+    # K > 2^14: the 128-bit sums are carried between launches in the workspace
+    rng = np.random.default_rng(550 + (dt == "bf16"))
+    for K, S in ((16385, 4), (40000, 7 if dt == "f32" else 5)):
+        xb, wb = random_operands(rng, 35, 66, K, dt, "normal")
+        _check(xb, wb, dt, S, "long K")
+
+
+def test_chosen_digits_on_normal_data():
+    # slices = 0: the call picks S; on N(0,1) data it stays on the matrix cores
+    rng = np.random.default_rng(560)
+    for dt in ("f32", "bf16"):
+        xb, wb = random_operands(rng, 128, 192, 256, dt, "normal")
+        plan = _check(xb, wb, dt, 0, "chosen S")
+        assert 2 <= plan["slices"] <= 7
+
+
+def _row_scaled(rng, M, K, emin, emax, spread, dt):
+    """Rows of N(0,1)-like values with few significant bits, each row scaled
+    by its own power of two: narrow spans at extreme magnitudes."""
+    e = rng.integers(emin, emax + 1, size=(M, 1))
+    v = rng.integers(-(1 << spread), (1 << spread) + 1, size=(M, K)).astype(np.float64)
+    a = np.ldexp(v, e).astype(np.float32)
+    return np_f32_bits(a) if dt == "f32" else to_bf16_bits(a)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_overflow_underflow_and_ties(dt):
+    rng = np.random.default_rng(570 + (dt == "bf16"))
+    # products far above 2^128 and far below 2^-149: inf, subnormal, +-0
+    xb = _row_scaled(rng, 64, 40, -140, 100, 6, dt)
+    wb = _row_scaled(rng, 96, 40, -140, 100, 6, dt)
+    _check(xb, wb, dt, 3, "extreme rows")
+    # integer sums past 2^24 land on rounding ties
+    xb = _row_scaled(rng, 40, 300, 0, 0, 12, dt)
+    wb = _row_scaled(rng, 70, 300, 0, 0, 12, dt)
+    _check(xb, wb, dt, 3, "integer ties")
+
+
+def test_golden_rounding_fixtures_on_the_matrix_cores():
+    announce("golden rounding fixtures, matrix-core path")
+    det.set_gemm_path("slices", 0)
+    fails = pins.check_golden_rounding(lambda xb, wb, dt: f32_bits(det.det_gemm(to_device(xb, dt),
+                                                                                 to_device(wb, dt))))
+    assert fails == []
+
+
+def test_strided_and_transposed_views():
+    rng = np.random.default_rng(580)
+    for dt in ("f32", "bf16"):
+        xb, wb = random_operands(rng, 67, 90, 140, dt, "normal")
+        x, w = to_device(xb, dt), to_device(wb, dt)
+        xt = x.t().contiguous().t()                      # unit M stride
+        wt = w.t().contiguous().t()
+        xs = to_device(np.ascontiguousarray(np.pad(xb, ((0, 0), (5, 3)))), dt)[:, 5:-3]
+        for xx, ww in ((xt, w), (x, wt), (xt, wt), (xs, w)):
+            _check(xb, wb, dt, 4, "views", x=xx, w=ww)
+
+
+def test_auto_path_matches_accumulator_path():
+    # above 2^27 MACs, auto considers the matrix cores; the bits never change
+    rng = np.random.default_rng(590)
+    for dt, kind in (("bf16", "normal"), ("f32", "normal"), ("f32", "wide")):
+        announce(f"auto vs accumulator {dt} {kind} 512^3")
+        xb, wb = random_operands(rng, 512, 512, 512, dt, kind)
+        x, w = to_device(xb, dt), to_device(wb, dt)
+        det.set_gemm_path("accumulator")
+        ya = f32_bits(det.det_gemm(x, w))
+        assert det.last_gemm_plan()["path"] == "accumulator"
+        det.set_gemm_path("auto")
+        yb = f32_bits(det.det_gemm(x, w))
+        plan = det.last_gemm_plan()
+        announce(f"auto plan {plan}")
+        assert np.array_equal(ya, yb), mismatch_report(yb, ya)
+        rr, cc = np.meshgrid(np.arange(0, 512, 37), np.arange(3, 512, 41), indexing="ij")
+        want = c_oracle.gemm_pairs(xb, wb, rr.ravel(), cc.ravel())
+        assert np.array_equal(ya[rr.ravel(), cc.ravel()], want)
+        if kind == "normal":
+            assert plan["path"] == "slices"
+        else:
+            assert plan["path"] == "accumulator"
