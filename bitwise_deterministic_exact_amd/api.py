@@ -182,7 +182,7 @@ def set_gemm_path(path: str = "auto", slices: int = 0) -> None:
 def last_gemm_plan() -> dict:
     """What this thread's last det_gemm call did: the path, the digits per
     operand (0 on the accumulator path) and how many rows of x and of w the
-    accumulator recomputed after the matrix-core pass."""
+    matrix-core pass listed (rows that span more than S digits)."""
     path, slices = ctypes.c_int(), ctypes.c_int()
     rows, cols = ctypes.c_int64(), ctypes.c_int64()
     _lib.load().det_last_gemm_plan(ctypes.byref(path), ctypes.byref(slices), ctypes.byref(rows),

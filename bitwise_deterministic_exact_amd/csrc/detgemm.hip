@@ -20,6 +20,7 @@
 
 #include <atomic>
 #include <type_traits>
+#include <vector>
 
 #include "detgemm.h"
 
@@ -1111,8 +1112,10 @@ __global__ __launch_bounds__(256) void k_slice_need(const int32_t* top, const in
   if (threadIdx.x < SL_HIST && h[threadIdx.x] != 0) atomicAdd(hist + threadIdx.x, h[threadIdx.x]);
 }
 
-// list[] = the rows with need > S, in increasing order (one workgroup)
-__global__ __launch_bounds__(1024) void k_slice_list(const int32_t* need, int64_t n, int S, int32_t* list) {
+// list[] = the rows with need > S, in increasing order, and pos[r] = the
+// place of row r in list[] or -1 (one workgroup)
+__global__ __launch_bounds__(1024) void k_slice_list(const int32_t* need, int64_t n, int S, int32_t* list,
+                                                     int32_t* pos) {
   __shared__ int32_t wsum[16];
   __shared__ int64_t base;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1128,6 +1131,7 @@ __global__ __launch_bounds__(1024) void k_slice_list(const int32_t* need, int64_
     int64_t off = base;
     for (int v = 0; v < wave; ++v) off += wsum[v];
     if (flag) list[off + pre] = static_cast<int32_t>(r);
+    if (r < n) pos[r] = flag ? static_cast<int32_t>(off + pre) : -1;
     __syncthreads();
     if (threadIdx.x == 0) {
       int64_t t = base;
@@ -1135,6 +1139,187 @@ __global__ __launch_bounds__(1024) void k_slice_list(const int32_t* need, int64_
       base = t;
     }
     __syncthreads();
+  }
+}
+
+// ---- tails: the elements of a listed row below its window (lowest set bit
+// under top + 3 - 8S), whose products the matrix-core pass leaves out
+constexpr int SL_TAIL_CAP = 256;          // tails per row kept in a list; more: the row is recomputed
+constexpr int64_t SL_ZFIX_MAX = int64_t(1) << 22;   // listed outputs whose 128-bit sums are kept
+
+struct TailArgs {
+  const void* p; int64_t K, s_r, s_k;     // the operand
+  const int32_t* list; int64_t n;         // its listed rows
+  const int32_t* top; int S;
+  int32_t* cnt;                           // tails per listed row
+  const int32_t* off;                     // k_tail_fill: each row's place in tk (-1: not kept)
+  int32_t* tk;                            // k_tail_fill: the tails' k, row by row, increasing
+};
+
+template <int DT>
+__device__ __forceinline__ bool is_tail(uint32_t b, int base) {
+  bool neg;
+  uint32_t m;
+  int ex;
+  split_elem<DT>(b, neg, m, ex);
+  return m != 0u && ex + __ffs(static_cast<int>(m)) - 1 < base;
+}
+
+// one wave per listed row: count its tails (FILL: write their k in order)
+template <int DT, bool FILL>
+__global__ __launch_bounds__(256) void k_tail_scan(TailArgs a) {
+  const int64_t p = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (p >= a.n) return;                                   // uniform per wave
+  if (FILL && a.off[p] < 0) return;
+  const int64_t r = a.list[p];
+  const int base = a.top[r] + 3 - 8 * a.S;
+  int64_t c = 0;
+  for (int64_t k0 = 0; k0 < a.K; k0 += 64) {
+    const int64_t k = k0 + lane;
+    const bool t = k < a.K && is_tail<DT>(load_elem<DT>(a.p, r * a.s_r + k * a.s_k), base);
+    const unsigned long long bal = __ballot(t);
+    if (FILL && t) a.tk[a.off[p] + c + __popcll(bal & ((1ull << lane) - 1ull))] = static_cast<int32_t>(k);
+    c += __popcll(bal);
+  }
+  if (!FILL && lane == 0) a.cnt[p] = static_cast<int32_t>(c);
+}
+
+// off[p] = place of row p's tails in tk (rows with more than SL_TAIL_CAP get
+// -1), ovl[] = the original indices of those rows, in order (one workgroup)
+__global__ __launch_bounds__(1024) void k_tail_plan(const int32_t* cnt, const int32_t* list, int64_t n,
+                                                    int32_t* off, int32_t* ovl) {
+  __shared__ int64_t wsum[16], wover[16];
+  __shared__ int64_t base, obase;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (threadIdx.x == 0) base = obase = 0;
+  __syncthreads();
+  for (int64_t p0 = 0; p0 < n; p0 += 1024) {
+    const int64_t p = p0 + threadIdx.x;
+    const int c = p < n ? cnt[p] : 0;
+    const bool over = p < n && c > SL_TAIL_CAP;
+    const int64_t kept = over ? 0 : c;
+    // wave-level inclusive scan of kept tails
+    int64_t v = kept;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t u = __shfl_up(v, o);
+      if (lane >= o) v += u;
+    }
+    const unsigned long long bal = __ballot(over);
+    if (lane == 63) wsum[wave] = v;
+    if (lane == 0) wover[wave] = __popcll(bal);
+    __syncthreads();
+    int64_t b = base, ob = obase;
+    for (int w = 0; w < wave; ++w) { b += wsum[w]; ob += wover[w]; }
+    if (p < n) off[p] = over ? -1 : static_cast<int32_t>(b + v - kept);
+    if (over) ovl[ob + __popcll(bal & ((1ull << lane) - 1ull))] = list[p];
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int64_t t = base, ot = obase;
+      for (int w = 0; w < 16; ++w) { t += wsum[w]; ot += wover[w]; }
+      base = t;
+      obase = ot;
+    }
+    __syncthreads();
+  }
+}
+
+// dg += (-1)^neg * v * 2^(o - 298) for v < 2^128 (raw digits; the bits of
+// v * 2^o below 2^0 must be zero)
+__device__ __forceinline__ void add_u128(int64_t (&dg)[ND], bool neg, unsigned __int128 v, int o) {
+  if (o < 0) { v = o > -128 ? v >> -o : 0; o = 0; }
+  const int d = o >> 5, sh = o & 31;
+#pragma unroll
+  for (int t = 0; t < 5; ++t) {
+    const int bit = 32 * t - sh;                           // bit of v at the limb's bit 0
+    uint64_t limb;
+    if (bit < 0) limb = static_cast<uint64_t>(v << (-bit)) & 0xFFFFFFFFull;
+    else limb = bit < 128 ? static_cast<uint64_t>(v >> bit) & 0xFFFFFFFFull : 0ull;
+    if (limb != 0ull && d + t < ND) dg[d + t] += neg ? -static_cast<int64_t>(limb) : static_cast<int64_t>(limb);
+  }
+}
+
+// dg += the exact product of two elements
+template <int DT>
+__device__ __forceinline__ void add_product(int64_t (&dg)[ND], uint32_t xb, uint32_t wb) {
+  bool nx, nw;
+  uint32_t mx, mw;
+  int ex, ew;
+  split_elem<DT>(xb, nx, mx, ex);
+  split_elem<DT>(wb, nw, mw, ew);
+  if (mx == 0u || mw == 0u) return;
+  add_u128(dg, nx != nw, static_cast<unsigned __int128>(static_cast<uint64_t>(mx) * mw), ex + ew + 298);
+}
+
+// The listed outputs: row p of x's list with every column (zr, [nx][N]),
+// then column q of w's list with every row not in x's list (zc, [nw][M]).
+// Each adds its tail products to the matrix-core pass's exact sum Z and
+// rounds once: y = RNE(Z 2^(bx + bw) + sum over x's tails k of x w + sum
+// over w's tails k of x w where x[i,k] is not one of x's tails).  Rows
+// and columns with off = -1 are left to the accumulator pass.
+struct SliceFixArgs {
+  const void* x; int64_t x_sm, x_sk;
+  const void* w; int64_t w_sn, w_sk;
+  int64_t M, N;
+  int S;
+  const int32_t* topx; const int32_t* topw;
+  const int32_t* listx; const int32_t* listw;
+  const int32_t* posx; const int32_t* posw;
+  const int32_t* cntx; const int32_t* cntw;
+  const int32_t* offx; const int32_t* offw;
+  const int32_t* tkx; const int32_t* tkw;
+  const int64_t* zr; const int64_t* zc;
+  int64_t nx, nw;
+  float* y; int64_t y_sm, y_sn;
+};
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_slice_fix(SliceFixArgs a) {
+  const int64_t total = a.nx * a.N + a.nw * a.M;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < total; t += stride) {
+    int64_t i, j, p, q;
+    const int64_t* zp;
+    if (t < a.nx * a.N) {
+      p = t / a.N;
+      j = t % a.N;
+      i = a.listx[p];
+      q = a.posw[j];
+      zp = a.zr + 2 * t;
+    } else {
+      const int64_t u = t - a.nx * a.N;
+      q = u / a.M;
+      i = u % a.M;
+      p = a.posx[i];
+      if (p >= 0) continue;                       // done with x's list
+      j = a.listw[q];
+      zp = a.zc + 2 * u;
+    }
+    if ((p >= 0 && a.offx[p] < 0) || (q >= 0 && a.offw[q] < 0)) continue;    // recomputed later
+    const int bx = a.topx[i] + 3 - 8 * a.S, bw = a.topw[j] + 3 - 8 * a.S;
+    int64_t dg[ND];
+#pragma unroll
+    for (int d = 0; d < ND; ++d) dg[d] = 0;
+    const __int128 z = (static_cast<__int128>(zp[1]) << 64) | static_cast<__int128>(static_cast<uint64_t>(zp[0]));
+    if (z != 0) {
+      const bool neg = z < 0;
+      add_u128(dg, neg, neg ? -static_cast<unsigned __int128>(z) : static_cast<unsigned __int128>(z), bx + bw + 298);
+    }
+    const int64_t xr = i * a.x_sm, wr = j * a.w_sn;
+    if (p >= 0)
+      for (int e = 0; e < a.cntx[p]; ++e) {
+        const int64_t k = a.tkx[a.offx[p] + e];
+        add_product<DT>(dg, load_elem<DT>(a.x, xr + k * a.x_sk), load_elem<DT>(a.w, wr + k * a.w_sk));
+      }
+    if (q >= 0)
+      for (int e = 0; e < a.cntw[q]; ++e) {
+        const int64_t k = a.tkw[a.offw[q] + e];
+        const uint32_t xb = load_elem<DT>(a.x, xr + k * a.x_sk);
+        if (p >= 0 && is_tail<DT>(xb, bx)) continue;          // counted with x's tails
+        add_product<DT>(dg, xb, load_elem<DT>(a.w, wr + k * a.w_sk));
+      }
+    a.y[i * a.y_sm + j * a.y_sn] = __uint_as_float(round_digits_to_f32(dg));
   }
 }
 
@@ -1277,6 +1462,10 @@ struct SliceMmaArgs {
   float* y; int64_t y_sm, y_sn;
   int64_t* z;                         // 128-bit sums [M][N][2] (lo, hi) between launches
   int epi;
+  // listed rows and columns (null: none): their final sums go to zr
+  // [rows][N][2] (row in x's list) or zc [cols][M][2], not to y
+  const int32_t* posx; const int32_t* posw;
+  int64_t* zr; int64_t* zc;
 };
 
 template <int S, int CB>
@@ -1396,9 +1585,17 @@ __global__ __launch_bounds__(256, 2) void k_slice_mma(SliceMmaArgs a) {
         int64_t* const zp = a.z + (row * a.N + col) * 2;
         if (a.epi == EPI_ADD || a.epi == EPI_ADD_ROUND)
           z += (static_cast<__int128>(zp[1]) << 64) | static_cast<__int128>(static_cast<uint64_t>(zp[0]));
+        int64_t* zo = nullptr;
         if (a.epi == EPI_STORE || a.epi == EPI_ADD) {
-          zp[0] = static_cast<int64_t>(z);
-          zp[1] = static_cast<int64_t>(z >> 64);
+          zo = zp;
+        } else if (a.posx != nullptr) {
+          const int32_t px = a.posx[row], pw = a.posw[col];
+          if (px >= 0) zo = a.zr + (px * a.N + col) * 2;
+          else if (pw >= 0) zo = a.zc + (static_cast<int64_t>(pw) * a.M + row) * 2;
+        }
+        if (zo != nullptr) {
+          zo[0] = static_cast<int64_t>(z);
+          zo[1] = static_cast<int64_t>(z >> 64);
         } else {
           const int e2 = (a.topx[row] + 3 - 8 * S) + (a.topw[col] + 3 - 8 * S);
           a.y[row * a.y_sm + col * a.y_sn] = __uint_as_float(round_i128_to_f32(z, e2));
@@ -1580,17 +1777,20 @@ det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s) {
 
 // ---------------------------------------------------------------- det_gemm: the matrix-core path
 //
-// Workspace behind the accumulator path's: per-row stats of x then w (top,
-// low, need, fallback list; int32), the span histogram, then SL_MAX digit
-// planes of x (rows padded to 64) and of w (rows padded to 128), K padded to
-// 32, then for K > 2^14 the 128-bit sums [M][N] carried between launches.
+// Workspace behind the accumulator path's: 8 int32 arrays per row of x and
+// of w (top, low, need, list, pos, tail count, tail offset, recompute list)
+// and the span histogram; SL_MAX digits of x (rows padded to 64) and of w
+// (rows padded to 128), K padded to 128; for K > 2^14 the 128-bit sums
+// [M][N] carried between launches; the tails' k (SL_TAIL_CAP per row); the
+// listed outputs' 128-bit sums (at most SL_ZFIX_MAX, and 2MN).
 int64_t slice_rows_x(int64_t M) { return round_up(M, 64); }
 int64_t slice_rows_w(int64_t N) { return round_up(N, 128); }
-int64_t slice_stats_bytes(int64_t M, int64_t N) { return round_up(16 * (M + N) + 4 * 2 * SL_HIST, 256); }
+int64_t slice_stats_bytes(int64_t M, int64_t N) { return round_up(32 * (M + N) + 4 * 2 * SL_HIST, 256); }
+int64_t slice_zfix_outputs(int64_t M, int64_t N) { return min(SL_ZFIX_MAX, 2 * M * N); }
 int64_t slice_bytes(int64_t M, int64_t N, int64_t K) {
   const int64_t Kp = round_up(K, 2 * SL_KB);
   return slice_stats_bytes(M, N) + SL_MAX * (slice_rows_x(M) + slice_rows_w(N)) * Kp +
-         (Kp / SL_KB > SL_FOLD ? 16 * M * N : 0);
+         (Kp / SL_KB > SL_FOLD ? 16 * M * N : 0) + 4 * SL_TAIL_CAP * (M + N) + 16 * slice_zfix_outputs(M, N);
 }
 
 // Host choice between the paths: estimated seconds from the accumulator
@@ -1679,26 +1879,50 @@ det_status slice_make(const void* p, int64_t R, int64_t K, int64_t s_r, int64_t 
 template <int DT>
 det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s);
 
+// The accumulator path on a subset: rows `rows` of x (m = M), or the rows
+// `cols` of w (n = N), overwriting those outputs of y.
+template <int DT>
+det_status recompute(GemmArgs a, char* ws, const int32_t* rows, int64_t m, const int32_t* cols, int64_t n,
+                     hipStream_t s) {
+  if (m == 0 || n == 0) return DET_OK;
+  GemmArgs b = a;
+  b.M = m; b.N = n;
+  b.xmap = rows; b.wmap = cols;
+  return launch_gemm8<DT>(b, ws, s);
+}
+
 // det_gemm with the room for both paths in `ws`: span statistics, the
-// choice, then either the accumulator path or the matrix-core pass plus the
-// accumulator path on the rows and columns that did not fit.
+// choice, then either the accumulator path or the matrix-core pass.  Rows
+// whose span needs more than S digits ("listed") keep their matrix-core sums;
+// their tails' products are added one by one (k_slice_fix), or, for rows
+// with more than SL_TAIL_CAP tails or more listed outputs than the sums'
+// room, the accumulator path recomputes them.
 template <int DT>
 det_status launch_sliced(GemmArgs a, char* ws, bool only_slices, int forced, hipStream_t s) {
   const int64_t M = a.M, N = a.N, K = a.K;
   char* const sl = ws + workspace_bytes(1, M, N, K);
-  int32_t* const topx = reinterpret_cast<int32_t*>(sl);
-  int32_t* const topw = topx + M;
-  int32_t* const lowx = topw + N;
-  int32_t* const loww = lowx + M;
-  int32_t* const needx = loww + N;
-  int32_t* const needw = needx + M;
-  int32_t* const listx = needw + N;
-  int32_t* const listw = listx + M;
-  int32_t* const hist = listw + N;
-  int8_t* const planes = reinterpret_cast<int8_t*>(sl + slice_stats_bytes(M, N));
+  int32_t* q = reinterpret_cast<int32_t*>(sl);
+  auto take = [&](int64_t n) { int32_t* r = q; q += n; return r; };
+  int32_t* const topx = take(M); int32_t* const topw = take(N);      // top, then low: contiguous for init
+  int32_t* const lowx = take(M); int32_t* const loww = take(N);
+  int32_t* const needx = take(M); int32_t* const needw = take(N);
+  int32_t* const listx = take(M); int32_t* const listw = take(N);
+  int32_t* const posx = take(M); int32_t* const posw = take(N);
+  int32_t* const cntx = take(M); int32_t* const cntw = take(N);
+  int32_t* const offx = take(M); int32_t* const offw = take(N);
+  int32_t* const ovlx = take(M); int32_t* const ovlw = take(N);
+  int32_t* const hist = take(2 * SL_HIST);
   const int64_t Kp = round_up(K, 2 * SL_KB);
-  int8_t* const xs = planes;
-  int8_t* const wsl = planes + SL_MAX * slice_rows_x(M) * Kp;
+  char* r8 = sl + slice_stats_bytes(M, N);
+  int8_t* const xs = reinterpret_cast<int8_t*>(r8);
+  int8_t* const wsl = xs + SL_MAX * slice_rows_x(M) * Kp;
+  r8 += SL_MAX * (slice_rows_x(M) + slice_rows_w(N)) * Kp;
+  int64_t* const zcarry = reinterpret_cast<int64_t*>(r8);
+  if (Kp / SL_KB > SL_FOLD) r8 += 16 * M * N;
+  int32_t* const tkx = reinterpret_cast<int32_t*>(r8);
+  int32_t* const tkw = tkx + SL_TAIL_CAP * M;
+  r8 += 4 * SL_TAIL_CAP * (M + N);
+  int64_t* const zfix = reinterpret_cast<int64_t*>(r8);
 
   hipLaunchKernelGGL(k_slice_init, dim3(grid_for(M + N, 256, 1024)), dim3(256), 0, s, topx, lowx, M + N, hist);
   det_status st = hip_check(hipGetLastError(), "slice init launch");
@@ -1722,17 +1946,50 @@ det_status launch_sliced(GemmArgs a, char* ws, bool only_slices, int forced, hip
     return launch_gemm8<DT>(a, ws, s);
   }
   record_plan(DET_PATH_SLICES, S, fx, fw);
+  const bool listed = fx + fw > 0;
+  const bool tails = listed && fx * N + fw * M <= slice_zfix_outputs(M, N);
+  if (listed) {
+    hipLaunchKernelGGL(k_slice_list, dim3(1), dim3(1024), 0, s, needx, M, S, listx, posx);
+    hipLaunchKernelGGL(k_slice_list, dim3(1), dim3(1024), 0, s, needw, N, S, listw, posw);
+    st = hip_check(hipGetLastError(), "slice list launch");
+    if (st != DET_OK) return st;
+  }
+  // tails per listed row, read back while the matrix-core pass runs
+  std::vector<int32_t> cx(static_cast<size_t>(fx)), cw(static_cast<size_t>(fw));
+  hipEvent_t counted = nullptr;
+  if (tails) {
+    TailArgs t{};
+    t.S = S;
+    t.p = a.x; t.K = K; t.s_r = a.x_sm; t.s_k = a.x_sk; t.list = listx; t.n = fx; t.top = topx; t.cnt = cntx;
+    if (fx > 0) hipLaunchKernelGGL((k_tail_scan<DT, false>), dim3(grid_for(fx * 64, 256, 1u << 30)), dim3(256), 0, s, t);
+    t.p = a.w; t.s_r = a.w_sn; t.s_k = a.w_sk; t.list = listw; t.n = fw; t.top = topw; t.cnt = cntw;
+    if (fw > 0) hipLaunchKernelGGL((k_tail_scan<DT, false>), dim3(grid_for(fw * 64, 256, 1u << 30)), dim3(256), 0, s, t);
+    st = hip_check(hipGetLastError(), "tail count launch");
+    if (st == DET_OK && fx > 0)
+      st = hip_check(hipMemcpyAsync(cx.data(), cntx, 4 * fx, hipMemcpyDeviceToHost, s), "tail count copy");
+    if (st == DET_OK && fw > 0)
+      st = hip_check(hipMemcpyAsync(cw.data(), cntw, 4 * fw, hipMemcpyDeviceToHost, s), "tail count copy");
+    if (st == DET_OK) st = hip_check(hipEventCreateWithFlags(&counted, hipEventDisableTiming), "event create");
+    if (st == DET_OK) st = hip_check(hipEventRecord(counted, s), "event record");
+    if (st != DET_OK) {
+      if (counted) (void)hipEventDestroy(counted);
+      return st;
+    }
+  }
   st = slice_make<DT>(a.x, M, K, a.x_sm, a.x_sk, topx, xs, slice_rows_x(M), S, s);
   if (st == DET_OK) st = slice_make<DT>(a.w, N, K, a.w_sn, a.w_sk, topw, wsl, slice_rows_w(N), S, s);
-  if (st != DET_OK) return st;
   SliceMmaArgs m{};
   m.xs = xs; m.ws = wsl;
   m.Kb = Kp / SL_KB;
   m.M = M; m.N = N;
   m.topx = topx; m.topw = topw;
   m.y = a.y; m.y_sm = a.y_sm; m.y_sn = a.y_sn;
-  m.z = reinterpret_cast<int64_t*>(planes + SL_MAX * (slice_rows_x(M) + slice_rows_w(N)) * Kp);
-  switch (S) {
+  m.z = zcarry;
+  if (tails) {
+    m.posx = posx; m.posw = posw;
+    m.zr = zfix; m.zc = zfix + 2 * fx * N;
+  }
+  if (st == DET_OK) switch (S) {
     case 2: st = launch_mma<2>(m, s); break;
     case 3: st = launch_mma<3>(m, s); break;
     case 4: st = launch_mma<4>(m, s); break;
@@ -1740,27 +1997,42 @@ det_status launch_sliced(GemmArgs a, char* ws, bool only_slices, int forced, hip
     case 6: st = launch_mma<6>(m, s); break;
     default: st = launch_mma<7>(m, s); break;
   }
+  if (!listed) return st;
+  if (!tails) {
+    // too many listed outputs to keep their sums: recompute the rows and columns
+    if (st == DET_OK) st = recompute<DT>(a, ws, listx, fx, nullptr, N, s);
+    if (st == DET_OK) st = recompute<DT>(a, ws, nullptr, M, listw, fw, s);
+    return st;
+  }
+  // the tail counts have been copied (the matrix-core pass may still run)
+  det_status sync_st = hip_check(hipEventSynchronize(counted), "tail count sync");
+  (void)hipEventDestroy(counted);
+  if (st == DET_OK) st = sync_st;
   if (st != DET_OK) return st;
-  // rows and columns beyond S digits: the accumulator path overwrites them
-  if (fx > 0) {
-    hipLaunchKernelGGL(k_slice_list, dim3(1), dim3(1024), 0, s, needx, M, S, listx);
-    st = hip_check(hipGetLastError(), "slice list launch");
-    if (st != DET_OK) return st;
-    GemmArgs b = a;
-    b.M = fx;
-    b.xmap = listx;
-    st = launch_gemm8<DT>(b, ws, s);
-    if (st != DET_OK) return st;
-  }
-  if (fw > 0) {
-    hipLaunchKernelGGL(k_slice_list, dim3(1), dim3(1024), 0, s, needw, N, S, listw);
-    st = hip_check(hipGetLastError(), "slice list launch");
-    if (st != DET_OK) return st;
-    GemmArgs b = a;
-    b.N = fw;
-    b.wmap = listw;
-    st = launch_gemm8<DT>(b, ws, s);
-  }
+  int64_t ox = 0, ow = 0;
+  for (int32_t c : cx) ox += c > SL_TAIL_CAP;
+  for (int32_t c : cw) ow += c > SL_TAIL_CAP;
+  hipLaunchKernelGGL(k_tail_plan, dim3(1), dim3(1024), 0, s, cntx, listx, fx, offx, ovlx);
+  hipLaunchKernelGGL(k_tail_plan, dim3(1), dim3(1024), 0, s, cntw, listw, fw, offw, ovlw);
+  TailArgs t{};
+  t.S = S;
+  t.p = a.x; t.K = K; t.s_r = a.x_sm; t.s_k = a.x_sk; t.list = listx; t.n = fx; t.top = topx; t.off = offx; t.tk = tkx;
+  if (fx > 0) hipLaunchKernelGGL((k_tail_scan<DT, true>), dim3(grid_for(fx * 64, 256, 1u << 30)), dim3(256), 0, s, t);
+  t.p = a.w; t.s_r = a.w_sn; t.s_k = a.w_sk; t.list = listw; t.n = fw; t.top = topw; t.off = offw; t.tk = tkw;
+  if (fw > 0) hipLaunchKernelGGL((k_tail_scan<DT, true>), dim3(grid_for(fw * 64, 256, 1u << 30)), dim3(256), 0, s, t);
+  SliceFixArgs f{};
+  f.x = a.x; f.x_sm = a.x_sm; f.x_sk = a.x_sk;
+  f.w = a.w; f.w_sn = a.w_sn; f.w_sk = a.w_sk;
+  f.M = M; f.N = N; f.S = S;
+  f.topx = topx; f.topw = topw; f.listx = listx; f.listw = listw; f.posx = posx; f.posw = posw;
+  f.cntx = cntx; f.cntw = cntw; f.offx = offx; f.offw = offw; f.tkx = tkx; f.tkw = tkw;
+  f.zr = m.zr; f.zc = m.zc; f.nx = fx; f.nw = fw;
+  f.y = a.y; f.y_sm = a.y_sm; f.y_sn = a.y_sn;
+  hipLaunchKernelGGL((k_slice_fix<DT>), dim3(grid_for(fx * N + fw * M, 256, 4096)), dim3(256), 0, s, f);
+  st = hip_check(hipGetLastError(), "tail launch");
+  // rows and columns with too many tails
+  if (st == DET_OK) st = recompute<DT>(a, ws, ovlx, ox, nullptr, N, s);
+  if (st == DET_OK) st = recompute<DT>(a, ws, nullptr, M, ovlw, ow, s);
   return st;
 }
 

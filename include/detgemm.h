@@ -40,7 +40,8 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     asynchronously and stream-ordered.  The one exception is det_gemm_ws
  *     when it considers the matrix-core path (see det_set_gemm_path): it
- *     waits for `stream` once, to read a 128-byte histogram.
+ *     waits for `stream` once, to read a 128-byte histogram, and with listed
+ *     rows once more, for their tail counts.
  *   - Argument errors are reported before anything is enqueued; on error
  *     nothing is written.  det_last_error() returns a message for the calling
  *     thread's most recent failure.
@@ -126,9 +127,9 @@ det_status det_gemm_partial(det_dtype dt, const void* x, int64_t x_sm, int64_t x
  * (partial ? 6 : 8) * roundup(N, 64) * roundup(K, 16) for w, plus
  * 8 * roundup(M, 2) * roundup(min(K, 2^15), 16) for x, plus 144 * M * N for
  * det_gemm_ws (partial = 0) when K > 2^15; for det_gemm_ws also the room of
- * the matrix-core path: roundup(16 (M + N) + 128, 256) +
- * 7 * (roundup(M, 64) + roundup(N, 128)) * roundup(K, 128), plus 16 * M * N
- * when K > 2^14.  det_gemm_ws
+ * the matrix-core path: roundup(32 (M + N) + 128, 256) +
+ * 7 * (roundup(M, 64) + roundup(N, 128)) * roundup(K, 128) + 1024 (M + N) +
+ * 16 * min(2^22, 2 M N), plus 16 * M * N when K > 2^14.  det_gemm_ws
  * given only the accumulator path's size (the sum without that last term)
  * runs the accumulator path.
  * Errors as for det_gemm, plus DET_EINVAL for a null, misaligned or too small
@@ -149,10 +150,14 @@ det_status det_gemm_ws(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk,
  * accumulator: each row of x and of w is scaled by a power of two to
  * integers below 2^(8S-2) in magnitude (S = 2..7), which are cut into S
  * signed 8-bit digits; the S^2 digit GEMMs run on the MFMA units with int32
- * sums, are added exactly in 128-bit integers and rounded once.  Rows of x
- * or w whose nonzero elements span more than 8S - 3 binades are recomputed
- * on the accumulator path.  The results are bit-identical to the
- * accumulator path's for every input.
+ * sums, are added exactly in 128-bit integers and rounded once.  In a row
+ * of x or w whose nonzero elements span more than 8S - 3 binades ("listed"),
+ * the elements below the row's window ("tails") are left out of the digit
+ * GEMMs; the outputs of listed rows and columns keep their exact 128-bit
+ * sums, to which the tails' products are added one by one before the one
+ * rounding.  A row with more than 256 tails, or more listed outputs than
+ * 2^22, is recomputed on the accumulator path instead.  The results are
+ * bit-identical to the accumulator path's for every input.
  *
  * det_set_gemm_path sets, for the whole process, which path det_gemm_ws
  * takes:
@@ -160,7 +165,8 @@ det_status det_gemm_ws(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk,
  *                         M*N*K >= 2^27 when the workspace has its room: the
  *                         call measures the spans (one pass over x and w),
  *                         waits for the stream, and picks S, or the
- *                         accumulator path, by estimated time
+ *                         accumulator path, by estimated time; with listed
+ *                         rows it waits once more, for their tail counts
  *   DET_PATH_ACCUMULATOR  always the digit accumulator
  *   DET_PATH_SLICES       always the matrix-core path (a too small workspace
  *                         is DET_EINVAL); `slices` = 2..7 fixes S, 0 lets the
@@ -171,8 +177,8 @@ det_status det_gemm_ws(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk,
  *
  * det_last_gemm_plan reports the calling thread's last det_gemm or
  * det_gemm_ws call: the path taken (DET_PATH_ACCUMULATOR or DET_PATH_SLICES),
- * S (0 for the accumulator) and how many rows of x and of w the accumulator
- * recomputed.  Null pointers are skipped.
+ * S (0 for the accumulator) and how many rows of x and of w were listed.
+ * Null pointers are skipped.
  */
 typedef enum { DET_PATH_AUTO = 0, DET_PATH_ACCUMULATOR = 1, DET_PATH_SLICES = 2 } det_path;
 

@@ -75,8 +75,8 @@ def _ru(v, m):
 
 def _slice_room(M, N, K):
     """det_gemm_ws's room for the matrix-core path, as include/detgemm.h states it."""
-    return (_ru(16 * (M + N) + 128, 256) + 7 * (_ru(M, 64) + _ru(N, 128)) * _ru(K, 128)
-            + (16 * M * N if K > (1 << 14) else 0))
+    return (_ru(32 * (M + N) + 128, 256) + 7 * (_ru(M, 64) + _ru(N, 128)) * _ru(K, 128)
+            + 1024 * (M + N) + 16 * min(1 << 22, 2 * M * N) + (16 * M * N if K > (1 << 14) else 0))
 
 
 def test_workspace_size_and_checks():

@@ -128,6 +128,27 @@ def test_outlier_rows_and_columns(dt):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_many_tails_and_many_listed_outputs(dt):
+    rng = np.random.default_rng(545 + (dt == "bf16"))
+    # wide rows have far more than 256 tails: recomputed on the accumulator
+    xb, wb = random_operands(rng, 40, 70, 700, dt, "wide")
+    _check(xb, wb, dt, 2, "many tails")
+    # N(0,1) rows with some wide rows and some single outliers mixed in:
+    # tails added one by one next to rows recomputed whole
+    xn, wn = random_operands(rng, 90, 130, 400, dt, "normal")
+    xw, ww = random_operands(rng, 90, 130, 400, dt, "wide")
+    xb, wb = xn.copy(), wn.copy()
+    xb[::7], wb[::9] = xw[::7], ww[::9]
+    xb[3::11, 5] = xw[3::11, 5]
+    wb[4::13, 17] = ww[4::13, 17]
+    _check(xb, wb, dt, 4, "mixed tails")
+    # more listed outputs than 2^22: whole rows and columns recomputed
+    xb, wb = random_operands(rng, 2100, 2100, 64, dt, "normal")
+    plan = _check(xb, wb, dt, 2, "many listed")
+    assert plan["fallback_rows"] * 2100 + plan["fallback_cols"] * 2100 > (1 << 22)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_k_beyond_one_block(dt):
     # K > 2^14: the 128-bit sums are carried between launches in the workspace
     rng = np.random.default_rng(550 + (dt == "bf16"))
