@@ -1175,12 +1175,21 @@ __global__ __launch_bounds__(256) void k_tail_scan(TailArgs a) {
   const int64_t r = a.list[p];
   const int base = a.top[r] + 3 - 8 * a.S;
   int64_t c = 0;
-  for (int64_t k0 = 0; k0 < a.K; k0 += 64) {
-    const int64_t k = k0 + lane;
-    const bool t = k < a.K && is_tail<DT>(load_elem<DT>(a.p, r * a.s_r + k * a.s_k), base);
-    const unsigned long long bal = __ballot(t);
-    if (FILL && t) a.tk[a.off[p] + c + __popcll(bal & ((1ull << lane) - 1ull))] = static_cast<int32_t>(k);
-    c += __popcll(bal);
+  for (int64_t k0 = 0; k0 < a.K; k0 += 1024) {
+    uint32_t e[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int64_t k = k0 + 64 * u + lane;
+      e[u] = k < a.K ? load_elem<DT>(a.p, r * a.s_r + k * a.s_k) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const bool t = is_tail<DT>(e[u], base);
+      const unsigned long long bal = __ballot(t);
+      if (FILL && t)
+        a.tk[a.off[p] + c + __popcll(bal & ((1ull << lane) - 1ull))] = static_cast<int32_t>(k0 + 64 * u + lane);
+      c += __popcll(bal);
+    }
   }
   if (!FILL && lane == 0) a.cnt[p] = static_cast<int32_t>(c);
 }
@@ -1513,9 +1522,15 @@ __global__ __launch_bounds__(256, 2) void k_slice_mma(SliceMmaArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wr = wave >> 1, wc = wave & 1;
+  // tiles in groups of 8 rows of tiles, column by column within a group: the
+  // workgroups resident on one XCD (consecutive in its range) cover about
+  // 8 x 8 tiles, so each x and w fragment is fetched into that XCD's L2 once
+  // for 8 workgroups
   const int64_t tile = xcd_tile();
-  const int64_t rbw = 4 * (tile % a.tiles_m);                  // the workgroup's first 16-row block
-  const int64_t cbw = 2 * CB * (tile / a.tiles_m);             // and first 16-column block
+  const int64_t gsz = 8 * a.tiles_n, grp = tile / gsz, rows_g = min<int64_t>(8, a.tiles_m - 8 * grp);
+  const int64_t tm = 8 * grp + (tile % gsz) % rows_g, tn = (tile % gsz) / rows_g;
+  const int64_t rbw = 4 * tm;                                   // the workgroup's first 16-row block
+  const int64_t cbw = 2 * CB * tn;                              // and first 16-column block
   const int64_t fstep = a.Kb * (S * 1024);                     // bytes between 16-row blocks
 
   // this wave copies fragments f = wave + 4 j of every step: x block rbw + f
