@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 # wave64 instruction per SIMD every 4 clocks)
 VALU_PEAK_LANE_OPS = 256 * 64 * 2.4e9
 HBM_PEAK = 8.0e12
+INT8_MFMA_PEAK = 5.0e15             # dense int8 ops/s (2 per MAC)
 KERNEL_SOURCE = os.path.join(ROOT, "bitwise_deterministic_exact_amd", "csrc", "detgemm.hip")
 PROFILE_RECORD = os.path.join(ROOT, "profiles", "k_gemm8_f32_4096_wide.md")
 
@@ -95,9 +96,10 @@ def main() -> int:
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (calibrates HBM byte counters)")
     ap.add_argument("--workload", default="wide4096",
-                    choices=["wide4096", "bf16cancel", "ksharded", "detlinear"],
+                    choices=["wide4096", "bf16cancel", "ksharded", "detlinear", "matrixcore"],
                     help="wide4096 (default, the headline): f32 4096^3 wide range; the others time "
-                         "the bf16 1024^3, the 16-shard K=2^19 and the DetLinear configurations")
+                         "the bf16 1024^3, the 16-shard K=2^19 and the DetLinear configurations, "
+                         "and (matrixcore) det_gemm on the DetLinear forward shape")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -221,9 +223,10 @@ def main() -> int:
                            "GB/s": round((acc_bytes + M * N * 4) / (t_fin * 1e-3) / 1e9, 1),
                            "hbm_frac": round((acc_bytes + M * N * 4) / (t_fin * 1e-3) / HBM_PEAK, 4)}
         aux["sharded_equals_unsharded"] = same
+        del pa, pb, acc, yf
+        aux["matrix_core_bf16"] = matrix_core_aux(det, dev, timed)
         result["aux"] = aux
         log(f"aux: {aux}")
-        del pa, pb, acc, yf
 
     if args.copy_probe:
         # a plain copy of known size: 256 MiB read + 256 MiB written; its
@@ -244,6 +247,40 @@ def main() -> int:
 
     print(json.dumps(result), flush=True)
     return 0 if parity_ok else 1
+
+
+def matrix_core_aux(det, dev, timed) -> dict:
+    """det_gemm on the DetLinear forward shape (bf16 N(0,1), 8192 x 4096 x
+    4096), where the call picks the matrix-core path: time, the path it took,
+    the digit GEMMs' int8 rate against the dense int8 MFMA peak (the whole
+    call's time, so a lower bound on the kernel's), and the same outputs
+    compared bit for bit with the digit-accumulator path."""
+    import torch
+    import workloads as W
+    wl = W.c5_detlinear_bf16()
+    x = torch.from_numpy(wl.x.view(np.int16)).view(torch.bfloat16).to(dev)
+    w = torch.from_numpy(wl.w.view(np.int16)).view(torch.bfloat16).to(dev)
+    M, K = x.shape
+    N = w.shape[0]
+    t, y = timed(lambda: det.det_gemm(x, w, check_finite=False))
+    plan = det.last_gemm_plan()
+    det.set_gemm_path("accumulator")
+    try:
+        y_acc = det.det_gemm(x, w, check_finite=False)
+    finally:
+        det.set_gemm_path("auto")
+    S = plan["slices"]
+    ops = 2.0 * S * S * M * N * K
+    out = {"M": M, "N": N, "K": K, "ms": round(t, 3), "GMAC/s": round(M * N * K / (t * 1e-3) / 1e9, 1),
+           "plan": plan, "equals_accumulator_path": bool(torch.equal(y.view(torch.int32),
+                                                                     y_acc.view(torch.int32)))}
+    if S:
+        out["roofline"] = {"bound": "mfma", "kernel": f"k_slice_mma<{S}> (whole call timed)",
+                           "achieved": round(ops / (t * 1e-3) / 1e12, 1), "peak": INT8_MFMA_PEAK / 1e12,
+                           "unit": "TOP/s int8", "frac": round(ops / (t * 1e-3) / INT8_MFMA_PEAK, 4),
+                           "ops": "2 S^2 M N K int8 ops per call"}
+    del x, w, y, y_acc
+    return out
 
 
 def _timed(fn, steps, warmup):
@@ -282,7 +319,37 @@ def other_workload(args) -> int:
     def bits32(t):
         return t.cpu().contiguous().view(torch.int32).numpy().view(np.uint32)
 
-    if args.workload == "bf16cancel":
+    if args.workload == "matrixcore":
+        steps, warmup = args.steps, args.warmup
+
+        def timed(fn):
+            for _ in range(max(1, warmup)):
+                fn()
+            torch.cuda.synchronize()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(steps):
+                out_ = fn()
+            e.record()
+            torch.cuda.synchronize()
+            return s.elapsed_time(e) / steps, out_
+
+        mc = matrix_core_aux(det, dev, timed)
+        wl = W.c5_detlinear_bf16()
+        x, w = to_dev(wl.x, "bf16"), to_dev(wl.w, "bf16")
+        y = det.det_gemm(x, w, check_finite=False)
+        rows, cols = rng.integers(0, 8192, 64), rng.integers(0, 4096, 64)
+        ok = bool(np.array_equal(bits32(y)[rows, cols],
+                                 c_oracle.gemm_pairs(wl.x, wl.w, rows, cols, nthreads=threads)))
+        ok = ok and mc["equals_accumulator_path"]
+        out.update(metric="exact-GEMM GMAC/s (bf16 8192x4096x4096 N(0,1), det_gemm's own path choice)",
+                   value=mc["GMAC/s"], unit="GMAC/s", ms_per_step=mc["ms"], dtype="int8",
+                   plan=mc["plan"], roofline=mc.get("roofline"),
+                   parity={"sampled_outputs": 64, "bit_exact": ok,
+                           "equals_accumulator_path": mc["equals_accumulator_path"]},
+                   config={"workload": wl.name + ", seed 4 (the DetLinear forward GEMM)",
+                           "M": 8192, "N": 4096, "K": 4096})
+    elif args.workload == "bf16cancel":
         wl = W.c2_bf16_cancel()
         xb, wb = wl.bits()
         x, w = to_dev(xb, "bf16"), to_dev(wb, "bf16")
