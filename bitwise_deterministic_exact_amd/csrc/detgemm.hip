@@ -1446,21 +1446,21 @@ __device__ uint32_t round_i128_to_f32(__int128 z, int e2) {
   return (neg ? 0x80000000u : 0u) | mag;
 }
 
-// The matrix-core pass (v_mfma_i32_16x16x64_i8).  A workgroup of 4 waves
-// owns 64 rows x 32 CB columns; wave (wr, wc) owns 32 rows x 16 CB columns:
-// 2 x CB blocks of 16 x 16, each with 2S-1 int32 sums (one per s + t).  Per
-// 64-k step the workgroup's (4 + 2 CB) S fragments (one KiB each: 4 row
-// blocks and 2 CB column blocks of x and w, S digits each) are copied from
-// the digit arrays into one of two LDS buffers with global_load_lds_dwordx4
-// (one instruction per fragment, no registers); each wave reads its 2S + CB S
-// fragments from LDS, starts the copy of the next step into the other
-// buffer (the last one repeats a step, so the copy is unconditional), and
-// runs its 2 CB S^2 MFMAs.  One barrier per step.  At most 256 registers per
-// lane and 2 x (4 + 2 CB) S KiB of LDS, so two workgroups share a CU (one for
-// S = 7) and each SIMD switches between two waves while one reads LDS.  One
-// launch covers at most 2^14 k; longer K runs as several launches that carry
-// each output's 128-bit sum in the workspace (epilogues as for the
-// accumulator path).
+// The matrix-core pass (v_mfma_i32_16x16x64_i8).  A workgroup of 2 WR waves
+// owns 32 WR rows x 32 CB columns; wave (wr, wc) owns 32 rows x 16 CB
+// columns: 2 x CB blocks of 16 x 16, each with 2S-1 int32 sums (one per
+// s + t).  Per 64-k step the workgroup's (2 WR + 2 CB) S fragments (one KiB
+// each: 2 WR row blocks and 2 CB column blocks of x and w, S digits each) are
+// copied from the digit arrays into one of NBUF LDS buffers with
+// global_load_lds_dwordx4 (one instruction per fragment, no registers), NBUF
+// - 1 steps ahead; each wave reads its 2S + CB S fragments from LDS, starts
+// the copy of step kb + NBUF - 1 into the buffer read one step ago (the last
+// ones repeat a step, so every copy is unconditional), and runs its 2 CB S^2
+// MFMAs.  One barrier per step.  At most 256 registers per lane, so a SIMD
+// switches between two waves while one reads LDS (two workgroups of 4 waves
+// or one of 8 per CU; one wave for S = 7).  One launch covers at most 2^14
+// k; longer K runs as several launches that carry each output's 128-bit sum
+// in the workspace (epilogues as for the accumulator path).
 struct SliceMmaArgs {
   const int8_t* xs; const int8_t* ws;
   int64_t Kb;                         // 64-k steps in the digit arrays
@@ -1477,25 +1477,39 @@ struct SliceMmaArgs {
   int64_t* zr; int64_t* zc;
 };
 
-template <int S, int CB>
+template <int S, int CB, int WR, int NBUF>
 struct SliceTile {
   static constexpr int NG = 2 * S - 1;
-  static constexpr int FA = 4 * S;              // x fragments per step (4 row blocks)
+  static constexpr int NW = 2 * WR;             // waves
+  static constexpr int FA = 2 * WR * S;         // x fragments per step
   static constexpr int FT = FA + 2 * CB * S;    // all fragments per step
-  static constexpr int PER_WAVE = (FT + 3) / 4;  // copies per wave (the last may be idle)
-  static constexpr int LDS_BYTES = 2 * FT * 1024;
+  static constexpr int PER_WAVE = (FT + NW - 1) / NW;   // copies per wave (the last may be idle)
+  static constexpr int LDS_BYTES = NBUF * FT * 1024;
 };
 
-// this wave's copies of step kb into LDS buffer `buf`: fragment f = wave + 4j
-// from src[j] (the lane's 16 bytes land at 16 * lane of the fragment)
-template <int S, int CB>
-__device__ __forceinline__ void slice_copy(const int8_t* const (&src)[SliceTile<S, CB>::PER_WAVE], int8_t* lds,
-                                           int wave, int64_t kb, int buf) {
-  using T = SliceTile<S, CB>;
+// s_waitcnt with vmcnt(n) and the other counters left alone (gfx9 encoding)
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Workgroup barrier without the release fence of __syncthreads (which would
+// wait for every outstanding copy into LDS, including those a step or two
+// ahead).  Callers first wait (vmcnt) for the copies the next step reads; the
+// LDS reads of the step are complete, since its MFMAs consumed them.  The
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void step_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// this wave's copies of step kb into LDS buffer `buf`: fragment f = wave +
+// NW j from src[j] (the lane's 16 bytes land at 16 * lane of the fragment)
+template <class T>
+__device__ __forceinline__ void slice_copy(const int8_t* const (&src)[T::PER_WAVE], int8_t* lds, int wave,
+                                           int64_t kb, int buf, int64_t step_bytes) {
 #pragma unroll
   for (int j = 0; j < T::PER_WAVE; ++j)
-    if (T::FT % 4 == 0 || j + 1 < T::PER_WAVE || wave + 4 * j < T::FT)     // uniform per wave
-      __builtin_amdgcn_global_load_lds(src[j] + kb * (S * 1024), lds + buf * (T::FT * 1024) + (wave + 4 * j) * 1024,
+    if (T::FT % T::NW == 0 || j + 1 < T::PER_WAVE || wave + T::NW * j < T::FT)     // uniform per wave
+      __builtin_amdgcn_global_load_lds(src[j] + kb * step_bytes, lds + buf * (T::FT * 1024) + (wave + T::NW * j) * 1024,
                                        16, 0, 0);
 }
 
@@ -1514,10 +1528,10 @@ __device__ __forceinline__ void slice_steps(const v4i (&fa)[S][2], const v4i (&f
           acc[s + t][i][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[s][i], fb[t][c], acc[s + t][i][c], 0, 0, 0);
 }
 
-template <int S, int CB>
-__global__ __launch_bounds__(256, 2) void k_slice_mma(SliceMmaArgs a) {
-  using T = SliceTile<S, CB>;
-  constexpr int NG = T::NG, FA = T::FA, FT = T::FT, PW = T::PER_WAVE;
+template <int S, int CB, int WR, int NBUF>
+__global__ __launch_bounds__(128 * WR, 2) void k_slice_mma(SliceMmaArgs a) {
+  using T = SliceTile<S, CB, WR, NBUF>;
+  constexpr int NG = T::NG, NW = T::NW, FA = T::FA, FT = T::FT, PW = T::PER_WAVE;
   __shared__ __align__(16) int8_t lds[T::LDS_BYTES];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1529,16 +1543,17 @@ __global__ __launch_bounds__(256, 2) void k_slice_mma(SliceMmaArgs a) {
   const int64_t tile = xcd_tile();
   const int64_t gsz = 8 * a.tiles_n, grp = tile / gsz, rows_g = min<int64_t>(8, a.tiles_m - 8 * grp);
   const int64_t tm = 8 * grp + (tile % gsz) % rows_g, tn = (tile % gsz) / rows_g;
-  const int64_t rbw = 4 * tm;                                   // the workgroup's first 16-row block
+  const int64_t rbw = 2 * WR * tm;                              // the workgroup's first 16-row block
   const int64_t cbw = 2 * CB * tn;                              // and first 16-column block
-  const int64_t fstep = a.Kb * (S * 1024);                     // bytes between 16-row blocks
+  const int64_t step_bytes = S * 1024;
+  const int64_t fstep = a.Kb * step_bytes;                      // bytes between 16-row blocks
 
-  // this wave copies fragments f = wave + 4 j of every step: x block rbw + f
+  // this wave copies fragments f = wave + NW j of every step: x block rbw + f
   // div S (f < FA) or w block cbw + (f - FA) div S, digit f mod S
   const int8_t* src[PW];
 #pragma unroll
   for (int j = 0; j < PW; ++j) {
-    const int f = min(wave + 4 * j, FT - 1);
+    const int f = min(wave + NW * j, FT - 1);
     src[j] = f < FA ? a.xs + (rbw + f / S) * fstep + (f % S) * 1024
                     : a.ws + (cbw + (f - FA) / S) * fstep + ((f - FA) % S) * 1024;
     src[j] += lane * 16;
@@ -1552,11 +1567,14 @@ __global__ __launch_bounds__(256, 2) void k_slice_mma(SliceMmaArgs a) {
 #pragma unroll
       for (int c = 0; c < CB; ++c) acc[u][i][c] = v4i{0, 0, 0, 0};
 
-  if (a.kb0 < a.kb1) slice_copy<S, CB>(src, lds, wave, a.kb0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  // steps kb0 .. kb0 + NBUF - 2 in flight; wait for the first
+  const int64_t last = a.Kb - 1;
+#pragma unroll
+  for (int b = 0; b + 1 < NBUF; ++b) slice_copy<T>(src, lds, wave, min(a.kb0 + b, last), b, step_bytes);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm((NBUF - 2) * PW));
+  step_barrier();
+  int buf = 0;
   for (int64_t kb = a.kb0; kb < a.kb1; ++kb) {
-    const int buf = static_cast<int>((kb - a.kb0) & 1);
     const int8_t* const lb = lds + buf * (FT * 1024) + lane * 16;
     // this wave's fragments, in the order the MFMAs first use them
     v4i fa[S][2], fb[S][CB];
@@ -1575,15 +1593,18 @@ __global__ __launch_bounds__(256, 2) void k_slice_mma(SliceMmaArgs a) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) fa[s][i] = *reinterpret_cast<const v4i*>(lb + ((2 * wr + i) * S + s) * 1024);
     __builtin_amdgcn_sched_barrier(0);
-    slice_copy<S, CB>(src, lds, wave, min(kb + 1, a.Kb - 1), buf ^ 1);   // into the buffer read one step ago
+    // into the buffer read one step ago (free since that step's barrier)
+    const int nb = buf == 0 ? NBUF - 1 : buf - 1;
+    slice_copy<T>(src, lds, wave, min(kb + NBUF - 1, last), nb, step_bytes);
     __builtin_amdgcn_sched_barrier(0);
     slice_steps<S, CB>(fa, fb, acc);
     __builtin_amdgcn_sched_barrier(0);                  // the wait and barrier stay behind the MFMAs
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");    // this wave's copies of step kb + 1 landed
-    __syncthreads();                                     // everyone's, and buffer buf is free
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NBUF - 2) * PW));   // this wave's copies of step kb + 1 landed
+    step_barrier();                                      // everyone's, and buffer buf is free
+    buf = buf + 1 == NBUF ? 0 : buf + 1;
   }
 
-  // output (row, col) of accumulator r of block (i, c): the MFMA's C layout
+// output (row, col) of accumulator r of block (i, c): the MFMA's C layout
 #pragma unroll
   for (int c = 0; c < CB; ++c) {
     const int64_t col = (cbw + wc * CB + c) * 16 + (lane & 15);
@@ -1794,11 +1815,11 @@ det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s) {
 //
 // Workspace behind the accumulator path's: 8 int32 arrays per row of x and
 // of w (top, low, need, list, pos, tail count, tail offset, recompute list)
-// and the span histogram; SL_MAX digits of x (rows padded to 64) and of w
+// and the span histogram; SL_MAX digits of x (rows padded to 128) and of w
 // (rows padded to 128), K padded to 128; for K > 2^14 the 128-bit sums
 // [M][N] carried between launches; the tails' k (SL_TAIL_CAP per row); the
 // listed outputs' 128-bit sums (at most SL_ZFIX_MAX, and 2MN).
-int64_t slice_rows_x(int64_t M) { return round_up(M, 64); }
+int64_t slice_rows_x(int64_t M) { return round_up(M, 128); }
 int64_t slice_rows_w(int64_t N) { return round_up(N, 128); }
 int64_t slice_stats_bytes(int64_t M, int64_t N) { return round_up(32 * (M + N) + 4 * 2 * SL_HIST, 256); }
 int64_t slice_zfix_outputs(int64_t M, int64_t N) { return min(SL_ZFIX_MAX, 2 * M * N); }
@@ -1841,14 +1862,25 @@ int choose_slices(det_dtype dt, int64_t M, int64_t N, int64_t K, const int32_t* 
   return best_s;
 }
 
+// tile shapes: 16-column blocks per wave, wave rows, LDS buffers
+template <int S> struct SliceShape;
+template <> struct SliceShape<2> { static constexpr int CB = 4, WR = 2, NBUF = 2; };
+template <> struct SliceShape<3> { static constexpr int CB = 2, WR = 2, NBUF = 2; };
+template <> struct SliceShape<4> { static constexpr int CB = 2, WR = 2, NBUF = 2; };
+template <> struct SliceShape<5> { static constexpr int CB = 1, WR = 2, NBUF = 2; };
+template <> struct SliceShape<6> { static constexpr int CB = 1, WR = 2, NBUF = 2; };
+template <> struct SliceShape<7> { static constexpr int CB = 1, WR = 2, NBUF = 2; };
+
 template <int S>
 det_status launch_mma(SliceMmaArgs m, hipStream_t s) {
-  constexpr int CB = S == 2 ? 4 : S <= 4 ? 2 : 1;    // 16-column blocks per wave
-  m.tiles_m = slice_rows_x(m.M) / 64;
+  using Sh = SliceShape<S>;
+  constexpr int CB = Sh::CB, WR = Sh::WR, NBUF = Sh::NBUF;
+  static_assert(SliceTile<S, CB, WR, NBUF>::LDS_BYTES <= 160 * 1024, "LDS");
+  m.tiles_m = slice_rows_x(m.M) / (32 * WR);
   m.tiles_n = (m.N + 32 * CB - 1) / (32 * CB);
   const int64_t blocks = m.tiles_m * m.tiles_n;
   if (blocks > 0x7FFFFFFF) return fail(DET_EINVAL, "too many output tiles");
-  const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(128 * WR);
   // K blocks of 2^14 (SL_FOLD steps): each int32 sum stays below 2^31
   const int64_t nblk = (m.Kb + SL_FOLD - 1) / SL_FOLD;
   for (int64_t ib = 0; ib < nblk; ++ib) {
@@ -1856,7 +1888,7 @@ det_status launch_mma(SliceMmaArgs m, hipStream_t s) {
     b.kb0 = ib * SL_FOLD;
     b.kb1 = min(m.Kb, b.kb0 + SL_FOLD);
     b.epi = nblk == 1 ? EPI_ROUND : ib == 0 ? EPI_STORE : ib + 1 == nblk ? EPI_ADD_ROUND : EPI_ADD;
-    hipLaunchKernelGGL((k_slice_mma<S, CB>), grid, block, 0, s, b);
+    hipLaunchKernelGGL((k_slice_mma<S, CB, WR, NBUF>), grid, block, 0, s, b);
     det_status st = hip_check(hipGetLastError(), "slice mma launch");
     if (st != DET_OK) return st;
   }

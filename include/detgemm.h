@@ -128,7 +128,7 @@ det_status det_gemm_partial(det_dtype dt, const void* x, int64_t x_sm, int64_t x
  * 8 * roundup(M, 2) * roundup(min(K, 2^15), 16) for x, plus 144 * M * N for
  * det_gemm_ws (partial = 0) when K > 2^15; for det_gemm_ws also the room of
  * the matrix-core path: roundup(32 (M + N) + 128, 256) +
- * 7 * (roundup(M, 64) + roundup(N, 128)) * roundup(K, 128) + 1024 (M + N) +
+ * 7 * (roundup(M, 128) + roundup(N, 128)) * roundup(K, 128) + 1024 (M + N) +
  * 16 * min(2^22, 2 M N), plus 16 * M * N when K > 2^14.  det_gemm_ws
  * given only the accumulator path's size (the sum without that last term)
  * runs the accumulator path.

@@ -75,7 +75,7 @@ def _ru(v, m):
 
 def _slice_room(M, N, K):
     """det_gemm_ws's room for the matrix-core path, as include/detgemm.h states it."""
-    return (_ru(32 * (M + N) + 128, 256) + 7 * (_ru(M, 64) + _ru(N, 128)) * _ru(K, 128)
+    return (_ru(32 * (M + N) + 128, 256) + 7 * (_ru(M, 128) + _ru(N, 128)) * _ru(K, 128)
             + 1024 * (M + N) + 16 * min(1 << 22, 2 * M * N) + (16 * M * N if K > (1 << 14) else 0))
 
 
