@@ -483,20 +483,25 @@ __global__ __launch_bounds__(64 * W, WPE) void k_partial(GemmArgs a, const void*
 // are added into one digit array per row in LDS and waves 0..R-1 finish the
 // rows (round to fp32, or carry the digits to the next K block).
 
-template <int DT, int R>
-struct Cells8 {
+// The grid of B-bit cells (B = 8: Cells8 above; B = 4 takes products below
+// 2^51, so a cell takes 4096 adds between folds instead of 256, in twice as
+// many cells).
+template <int DT, int R, int B>
+struct CellsG {
+  static_assert(B == 4 || B == 8, "cell grids of 4 or 8 bits");
   static constexpr int ROWS = R;
   static constexpr bool XPACK = false;          // decoded x: separate significand and word arrays
-  static constexpr int NCELL = 64;              // cells that products reach
-  static constexpr int FIRST = DT == DET_F32 ? 0 : 4;     // first reachable cell (bf16: offset >= 32)
-  static constexpr int BITS = 8;
+  static constexpr int NCELL = 512 / B;         // cells that products reach
+  static constexpr int FIRST = DT == DET_F32 ? 0 : 32 / B;   // first reachable cell (bf16: offset >= 32)
+  static constexpr int BITS = B;
   static constexpr int ES = DT == DET_F32 ? 8 : 4;        // bytes per cell
   static constexpr int RB = 64 * ES;                      // bytes between rows
   static constexpr uint32_t CS = R * RB;                  // bytes between cells
   static constexpr int ALLOC = FIRST + NCELL;             // cells allocated (the first FIRST unused)
-  static constexpr int64_t KFLUSH = 256;
-  static constexpr int NORM_EVERY = 8;                    // folds between carry passes
-  static constexpr uint32_t ESH = (DT == DET_F32 ? 6u : 5u) + (R == 4 ? 2u : R == 2 ? 1u : 0u);   // log2(CS / 8)
+  static constexpr int64_t KFLUSH = B == 8 ? 256 : 4096;  // adds between folds: |T| < 2^(47 + B)
+  static constexpr int NORM_EVERY = B == 8 ? 8 : 1;       // folds between carry passes
+  static constexpr uint32_t ESH = (DT == DET_F32 ? 9u : 8u) - (B == 8 ? 3u : 2u) +
+                                  (R == 4 ? 2u : R == 2 ? 1u : 0u);   // log2(CS / B)
   static_assert(R == 1 || R == 2 || R == 4, "the cell stride must be a power of two");
   using cell_t = typename std::conditional<DT == DET_F32, int64_t, int32_t>::type;
 
@@ -511,7 +516,7 @@ struct Cells8 {
                               uint32_t we) {
     const uint32_t o = xe + we;
     char* const p = cbase + ((o & ~(CS - 1u)) | (lane_off + r * RB));
-    const uint32_t sh = (o >> ESH) & 7u;
+    const uint32_t sh = (o >> ESH) & static_cast<uint32_t>(B - 1);
     if (DT == DET_F32) {
       const uint64_t T = static_cast<uint64_t>(static_cast<int64_t>(xm) * wm) << sh;
       atomicAdd(reinterpret_cast<unsigned long long*>(p), static_cast<unsigned long long>(T));
@@ -520,6 +525,9 @@ struct Cells8 {
     }
   }
 };
+
+template <int DT, int R>
+using Cells8 = CellsG<DT, R, 8>;
 
 template <int R>
 struct Cells4 {
@@ -1758,10 +1766,27 @@ det_status launch_partial(GemmArgs a, void* ws, hipStream_t s) {
 // det_gemm: k_gemm8 with two rows and 64 columns per workgroup, 64 KB of
 // cells (f32: Cells8, bf16: Cells4), so two workgroups share a CU: 8 waves
 // each, held to 128 VGPRs (WPE = 4 waves per SIMD) so that all 16 fit.
+// rows per workgroup, waves, waves per SIMD and the cell grid of k_gemm8.
+// f32: the 4-bit grid (4096 adds between folds) on 2 rows, 128 KB of cells
+// shared by 16 waves, one workgroup per CU: 3655 GMAC/s on the wide-range
+// 4096^3 workload against 3465 for the 8-bit grid (64 KB, 8 waves, two
+// workgroups per CU) and 3373 for the 4-bit grid on one row.  bf16 keeps two
+// 64 KB workgroups of 8 waves (four rows on 128 KB: 4570 against 5369).
+template <int DT> struct Gemm8Config;
+template <> struct Gemm8Config<DET_F32> {
+  static constexpr int R = 2, W = 16, WPE = 4;
+  using G = CellsG<DET_F32, R, 4>;
+};
+template <> struct Gemm8Config<DET_BF16> {
+  static constexpr int R = 2, W = 8, WPE = 4;
+  using G = Cells4<R>;
+};
+
 template <int DT>
 det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s) {
-  constexpr int R = 2, W = 8, WPE = 4;
-  using G = typename std::conditional<DT == DET_F32, Cells8<DET_F32, R>, Cells4<R>>::type;
+  using C = Gemm8Config<DT>;
+  constexpr int R = C::R, W = C::W, WPE = C::WPE;
+  using G = typename C::G;
   a.tiles_m = (a.M + R - 1) / R;
   a.tiles_n = (a.N + V_BN - 1) / V_BN;
   const int64_t blocks = a.tiles_m * a.tiles_n;
