@@ -187,7 +187,7 @@ def main() -> int:
                      "ops_per_mac": round(ops_per_mac, 3) if ops_per_mac else None,
                      "ops_source": "rocprofv3 SQ_INSTS_VALU x 64 per launch / MACs per launch",
                      "profile_current": bool(rec and rec["current"]),
-                     "kernel": "k_gemm8<f32, 2 rows, 8 waves>"},
+                     "kernel": "k_gemm8<f32, 4-bit cells, 2 rows, 16 waves>"},
         "parity": {"sampled_outputs": 256, "bit_exact": parity_ok},
     }
 

@@ -1770,8 +1770,11 @@ det_status launch_partial(GemmArgs a, void* ws, hipStream_t s) {
 // f32: the 4-bit grid (4096 adds between folds) on 2 rows, 128 KB of cells
 // shared by 16 waves, one workgroup per CU: 3655 GMAC/s on the wide-range
 // 4096^3 workload against 3465 for the 8-bit grid (64 KB, 8 waves, two
-// workgroups per CU) and 3373 for the 4-bit grid on one row.  bf16 keeps two
-// 64 KB workgroups of 8 waves (four rows on 128 KB: 4570 against 5369).
+// workgroups per CU), 3373 for the 4-bit grid on one row, and 3231 for a
+// 4-bit grid with the shift split between the operands at decode (three VALU
+// instructions per product instead of six, but 27-bit operands leave 512 adds
+// between folds: the LDS, not the VALU, binds).  bf16 keeps two 64 KB
+// workgroups of 8 waves (four rows on 128 KB: 4570 against 5369).
 template <int DT> struct Gemm8Config;
 template <> struct Gemm8Config<DET_F32> {
   static constexpr int R = 2, W = 16, WPE = 4;
