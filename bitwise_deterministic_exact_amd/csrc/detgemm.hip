@@ -701,11 +701,6 @@ __global__ __launch_bounds__(64 * W, WPE) void k_gemm8(GemmArgs a, const void* _
   const uint32_t xj4 = static_cast<uint32_t>(xj) * 4u;
   const uint32_t lane_off = static_cast<uint32_t>(lane * G::ES);
 
-  int64_t dg[R][WD];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int j = 0; j < WD; ++j) dg[r][j] = 0;
 
   const int64_t nchunks = (a.K + V_KC - 1) / V_KC;
   uint32_t wq[2][V_KC], weq[2][V_KC], xq[2][R], xwq[2][R];
@@ -751,8 +746,7 @@ __global__ __launch_bounds__(64 * W, WPE) void k_gemm8(GemmArgs a, const void* _
   // i*W, i < EPOCH/W, in pairs so that the ring slot of each is static.  The
   // barriers stay outside the unrolled pairs, so every wave meets each of
   // them once per epoch.
-  int64_t epoch = 0;
-  for (int64_t e0 = 0; e0 < nchunks; e0 += EPOCH, ++epoch) {
+  auto run_epoch = [&](int64_t e0) {
 #pragma unroll 1
     for (int i2 = 0; i2 < EPOCH / W; i2 += 2)
 #pragma unroll
@@ -775,6 +769,23 @@ __global__ __launch_bounds__(64 * W, WPE) void k_gemm8(GemmArgs a, const void* _
         steps8<G, DT, PRE, R, 0>(cells, static_cast<uint32_t>(lane), lane_off, wq[sl], weq[sl], xm, xe);
       }
     }
+  };
+  // The first epoch is peeled off: its fold defines the windows, so they
+  // hold no registers during its adds (with 16 waves per CU they would spill,
+  // and a 4096-long K is a single epoch on the 4-bit grid).
+  run_epoch(0);
+  __syncthreads();                                // the epoch's adds are in
+  int64_t dg[R][WD];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int j = 0; j < WD; ++j) dg[r][j] = 0;
+    fold8<G, CW, OFF, WD>(my_cells + r * G::RB, dg[r], G::NORM_EVERY == 1 || EPOCH >= nchunks);
+  }
+  __syncthreads();                                // cells clear before the next epoch
+  int64_t epoch = 1;
+  for (int64_t e0 = EPOCH; e0 < nchunks; e0 += EPOCH, ++epoch) {
+    run_epoch(e0);
     __syncthreads();                              // the epoch's adds are in
     const bool norm = (epoch % G::NORM_EVERY) == G::NORM_EVERY - 1 || e0 + EPOCH >= nchunks;
 #pragma unroll

@@ -75,11 +75,11 @@ def test_workspace_and_inkernel_decode_agree(dt):
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_long_k_counter_folds(dt):
-    # K long enough for many counter folds and digit carries inside the
-    # kernels (every 128 k on the 24-bit grid with a carry every 2048 k,
-    # every 2^15 k on the 16-bit grid), all signs and magnitudes
+    # K long enough for several epochs of cell folds and digit carries inside
+    # the kernels (f32: a fold every 4096 k; bf16: every 512 k; the partial's
+    # counters: a block every 2^15 k), all signs and magnitudes
     rng = np.random.default_rng(33 if dt == "f32" else 34)
-    for kind, K in (("wide", 5000), ("normal", 70001), ("special", 3000)):
+    for kind, K in (("wide", 5000), ("wide", 8200), ("normal", 9000), ("normal", 70001), ("special", 3000)):
         announce(f"long K {kind} {dt} K={K}")
         xb, wb = random_operands(rng, 5, 66, K, dt, kind)
         x, w = to_device(xb, dt), to_device(wb, dt)
