@@ -163,6 +163,49 @@ def det_finalize(acc: torch.Tensor) -> torch.Tensor:
     return y
 
 
+K_ANY_MAX = 1 << 30
+
+
+def gemm_any_k(x: torch.Tensor, w: torch.Tensor, *, check_finite: Optional[bool] = None) -> torch.Tensor:
+    """det_gemm for any K: up to 2^19 one call; beyond, K-slices of at most
+    2^19 as raw digits, added with det_combine and rounded once with
+    det_finalize ("Usage": the partials of K-slices compose into the whole
+    sum).  Bit-identical to one exact sum rounded once.  K up to 2^30, where
+    the added digits still fit det_combine's int64 bound."""
+    K = x.shape[1] if x.dim() == 2 else -1
+    if K <= _lib.K_MAX:
+        return det_gemm(x, w, check_finite=check_finite)
+    if w.dim() != 2 or w.shape[1] != K:
+        raise ValueError(f"K mismatch: x is {tuple(x.shape)}, w is {tuple(w.shape)}")
+    if K > K_ANY_MAX:
+        raise ValueError(f"K = {K} exceeds 2^30, the limit of composed K-slices")
+    _operands(x[:, :1], w[:, :1])
+    _reject_nonfinite(x, w, check_finite)
+    parts = [det_gemm_partial(x[:, a:min(a + _lib.K_MAX, K)], w[:, a:min(a + _lib.K_MAX, K)],
+                              check_finite=False)
+             for a in range(0, K, _lib.K_MAX)]
+    return det_finalize(det_combine(parts))
+
+
+def exact_dot(a: torch.Tensor, b: torch.Tensor, *, check_finite: Optional[bool] = None) -> torch.Tensor:
+    """sum_i a_i * b_i over all elements, every product exact and the sum
+    rounded once to fp32 (a 1 x 1 exact GEMM with K = numel); a 0-d float32
+    tensor.  a and b: same shape, both float32 or both bfloat16."""
+    if a.shape != b.shape:
+        raise ValueError("exact_dot needs operands of one shape")
+    a1, b1 = a.reshape(1, -1), b.reshape(1, -1)
+    if a1.shape[1] == 0:
+        return torch.zeros((), dtype=torch.float32, device=a.device)
+    return gemm_any_k(a1, b1, check_finite=check_finite).reshape(())
+
+
+def exact_sum_squares(y: torch.Tensor, *, check_finite: Optional[bool] = None) -> torch.Tensor:
+    """sum_i y_i^2 exactly, rounded once to fp32 (a loss such as mean(y^2)
+    is this divided by the element count: one more IEEE rounding, exact when
+    the count is a power of two and the result stays normal)."""
+    return exact_dot(y, y, check_finite=check_finite)
+
+
 _PATHS = {"auto": _lib.DET_PATH_AUTO, "accumulator": _lib.DET_PATH_ACCUMULATOR,
           "slices": _lib.DET_PATH_SLICES}
 _PATH_NAMES = {v: k for k, v in _PATHS.items()}

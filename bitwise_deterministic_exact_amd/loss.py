@@ -1,0 +1,70 @@
+"""Exact loss reductions: the sum over a whole tensor formed in the long
+accumulator, so the loss value does not depend on how the elements are split
+or ordered (det-train page, "Method": an exact sum is independent of its
+order; "Usage": the partials of K-slices compose into the whole sum).
+
+exact_mse_loss(y, t) = RNE32( sum_i (y_i - t_i)^2 ) / n
+
+The squared error is never rounded per element: with every product exact,
+sum (y - t)^2 = sum y*y + sum t*t + sum y*(-t) + sum y*(-t), one dot product
+of length 4n over [y | t | y | y] and [y | t | -t | -t] (negation is exact),
+which the library forms as a 1 x 1 exact GEMM and rounds once to fp32.  The
+division by n is one more IEEE fp32 division, correctly rounded, by n as an
+fp32 value (n itself rounded to fp32 above 2^24; the quotient is exact when n
+is a power of two and stays normal).  Without a target the loss is
+sum y^2 / n.
+
+The gradient 2 (y - t) / n is elementwise (no reduction, so no order to fix)
+and is formed with torch's elementwise ops.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from .api import exact_dot
+
+
+class _ExactMSE(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, y: torch.Tensor, t: Optional[torch.Tensor]) -> torch.Tensor:
+        yf = y.reshape(-1)
+        if t is None:
+            s = exact_dot(yf, yf, check_finite=False)
+        else:
+            tf = t.reshape(-1)
+            a = torch.cat([yf, tf, yf, yf])
+            b = torch.cat([yf, tf, -tf, -tf])
+            s = exact_dot(a, b, check_finite=False)
+        ctx.save_for_backward(y, t if t is not None else y)
+        ctx.has_target = t is not None
+        # a true fp32 division by a device tensor: torch turns a division by
+        # a host scalar into a product with its rounded reciprocal
+        n = torch.tensor(float(max(y.numel(), 1)), dtype=torch.float32, device=s.device)
+        return s / n
+
+    @staticmethod
+    def backward(ctx, g: torch.Tensor):
+        y, t = ctx.saved_tensors
+        n = max(y.numel(), 1)
+        d = y.to(torch.float32)
+        if ctx.has_target:
+            d = d - t.to(torch.float32)
+        gy = (d * (2.0 / n)) * g
+        dy = gy.to(y.dtype) if ctx.needs_input_grad[0] else None
+        dt = (-gy).to(t.dtype) if ctx.has_target and ctx.needs_input_grad[1] else None
+        return dy, dt
+
+
+def exact_mse_loss(y: torch.Tensor, target: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Mean squared error with the sum formed exactly; a 0-d float32 tensor.
+
+    y (and target, if given): float32 or bfloat16 GPU tensors of one shape
+    and dtype, finite, any number of elements."""
+    if target is not None:
+        if target.shape != y.shape or target.dtype != y.dtype:
+            raise ValueError("exact_mse_loss needs y and target of one shape and dtype")
+    if y.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("exact_mse_loss takes float32 or bfloat16 tensors")
+    return _ExactMSE.apply(y, target)

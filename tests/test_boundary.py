@@ -163,9 +163,30 @@ def test_python_layer_validates_before_launch():
     with pytest.raises(ValueError):
         det.det_finalize(torch.empty(3, 17, dtype=torch.int64))
     with pytest.raises(ValueError):
-        det.DetLinear(4, 4, bias=True)
-    with pytest.raises(ValueError):
         det.DetLinear(4, 4, k_shards=0)
+    # K-slice composition: up to 2^30, operands checked before any launch
+    with pytest.raises(ValueError, match="2\\^30"):
+        det.gemm_any_k(torch.empty(1, (1 << 30) + 1, **meta), torch.empty(1, (1 << 30) + 1, **meta))
+    with pytest.raises(ValueError, match="K mismatch"):
+        det.gemm_any_k(torch.empty(1, (1 << 19) + 5, **meta), torch.empty(1, (1 << 19) + 4, **meta))
+    with pytest.raises(ValueError, match="same GPU"):
+        det.gemm_any_k(torch.empty(2, (1 << 19) + 5, **meta), torch.empty(2, (1 << 19) + 5, **meta))
+    with pytest.raises(ValueError, match="one shape"):
+        det.exact_dot(torch.empty(3, **meta), torch.empty(4, **meta))
+    with pytest.raises(ValueError, match="one shape"):
+        det.exact_mse_loss(torch.empty(3, **meta), torch.empty(4, **meta))
+    with pytest.raises(ValueError, match="float32 or bfloat16"):
+        det.exact_mse_loss(torch.empty(3, dtype=torch.float16, **meta))
+
+
+def test_detlinear_bias_parameter():
+    layer = det.DetLinear(6, 5, bias=True)
+    assert layer.bias.shape == (5,) and layer.bias.dtype == torch.float32
+    assert "bias=True" in repr(layer)
+    assert all(abs(v) <= 1.0 / 6 ** 0.5 for v in layer.bias.tolist())
+    assert det.DetLinear(6, 5).bias is None
+    assert "bias=False" in repr(det.DetLinear(6, 5))
+    assert det.DetLinear(6, 5, bias=True, dtype=torch.bfloat16).bias.dtype == torch.bfloat16
 
 
 def test_shard_bounds_cover_k_once():

@@ -1,0 +1,195 @@
+"""GPU parity of the exact bias, the K-slice composition past 2^19 and the
+exact loss reduction against the oracle, bit for bit.
+
+A bias b is one more term of each output's exact sum: y = RNE32(sum_k x*w +
+1*b), which the oracle computes as the exact GEMM of [x | 1] and [W | b].
+The bias gradient is the exact column sum of dY, the GEMM of dY^T with a row
+of ones.  K past 2^19 runs as K-slices of raw digits composed by
+det_combine, which the oracle's single exact sum must equal.  The loss is
+the exact sum of squared errors rounded once, then divided by n in fp32."""
+import numpy as np
+import pytest
+import torch
+
+import bitwise_deterministic_exact_amd as det
+from oracle import c_oracle
+from oracle.exact import f32_bits_to_bf16_bits
+from tests.gpu_util import announce, f32_bits, mismatch_report, tensor_bits, to_device
+from workloads import random_operands
+
+pytestmark = pytest.mark.gpu
+
+ONE = {"f32": np.uint32(0x3F800000), "bf16": np.uint16(0x3F80)}
+NEG = {"f32": np.uint32(0x80000000), "bf16": np.uint16(0x8000)}
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _ones(shape, dt):
+    return np.full(shape, ONE[dt], dtype=ONE[dt].dtype)
+
+
+def _to_param_dtype(bits32: np.ndarray, dt: str) -> np.ndarray:
+    return bits32 if dt == "f32" else f32_bits_to_bf16_bits(bits32)
+
+
+def _layer(dt, IN, OUT, k_shards, Wb, bb):
+    layer = det.DetLinear(IN, OUT, bias=True, device="cuda", dtype=TORCH_DT[dt], k_shards=k_shards)
+    with torch.no_grad():
+        layer.weight.copy_(to_device(Wb, dt))
+        layer.bias.copy_(to_device(bb, dt))
+    return layer
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("k_shards", [1, 3])
+def test_detlinear_bias_forward_backward(dt, k_shards):
+    rng = np.random.default_rng(600 + 2 * k_shards + (dt == "bf16"))
+    T, IN, OUT = 37, 50, 29
+    for kind in ("normal", "wide"):
+        announce(f"DetLinear bias {dt} k_shards={k_shards} {kind} T={T} {IN}->{OUT}")
+        xb, Wb = random_operands(rng, T, OUT, IN, dt, kind)
+        bb = random_operands(rng, 1, OUT, 1, dt, kind)[1].reshape(OUT)
+        layer = _layer(dt, IN, OUT, k_shards, Wb, bb)
+        x = to_device(xb, dt).requires_grad_(True)
+        y = layer(x)
+        want = c_oracle.gemm(np.hstack([xb, _ones((T, 1), dt)]), np.hstack([Wb, bb.reshape(OUT, 1)]))
+        got = f32_bits(y)
+        assert np.array_equal(got, want), mismatch_report(got, want)
+        # backward with a given upstream gradient G; dY is G rounded to the
+        # parameter dtype
+        G = rng.standard_normal((T, OUT), dtype=np.float32)
+        gb = _to_param_dtype(G.view(np.uint32), dt)
+        y.backward(torch.from_numpy(G).cuda())
+        dx = c_oracle.gemm(gb, np.ascontiguousarray(Wb.T))
+        dw = c_oracle.gemm(np.ascontiguousarray(gb.T), np.ascontiguousarray(xb.T))
+        db = c_oracle.gemm(np.ascontiguousarray(gb.T), _ones((1, T), dt)).reshape(OUT)
+        for name, g, w32 in (("dx", x.grad, dx), ("dW", layer.weight.grad, dw), ("db", layer.bias.grad, db)):
+            want = _to_param_dtype(w32, dt)
+            got = tensor_bits(g)
+            assert np.array_equal(got, want), f"{name}: " + mismatch_report(got, want)
+
+
+def test_detlinear_bias_on_the_matrix_cores():
+    # 512 tokens, 512 -> 512 bf16: the forward (K = 513 with the bias term)
+    # is large enough for det_gemm to consider the matrix-core path
+    rng = np.random.default_rng(610)
+    T = IN = OUT = 512
+    xb, Wb = random_operands(rng, T, OUT, IN, "bf16", "normal")
+    bb = random_operands(rng, 1, OUT, 1, "bf16", "normal")[1].reshape(OUT)
+    layer = _layer("bf16", IN, OUT, 1, Wb, bb)
+    x = to_device(xb, "bf16")
+    announce("DetLinear bias bf16 512^3, auto path")
+    y = f32_bits(layer(x))
+    plan = det.last_gemm_plan()
+    with det.gemm_path("accumulator"):
+        ya = f32_bits(layer(x))
+    assert np.array_equal(y, ya), mismatch_report(y, ya)
+    rr, cc = np.meshgrid(np.arange(0, T, 29), np.arange(1, OUT, 31), indexing="ij")
+    xc = np.hstack([xb, _ones((T, 1), "bf16")])
+    wc = np.hstack([Wb, bb.reshape(OUT, 1)])
+    want = c_oracle.gemm_pairs(xc, wc, rr.ravel(), cc.ravel())
+    assert np.array_equal(y[rr.ravel(), cc.ravel()], want)
+    announce(f"plan {plan}")
+    assert plan["path"] == "slices"
+
+
+def _oracle_gemm_long(xb, wb):
+    """The oracle's exact sum for any K: its raw digits over K-thirds (each
+    within its 2^19 limit) added digit for digit, then rounded once."""
+    K = xb.shape[1]
+    cuts = [0, K // 3, (2 * K) // 3, K]
+    parts = [c_oracle.partial(np.ascontiguousarray(xb[:, a:b]), np.ascontiguousarray(wb[:, a:b]))
+             for a, b in zip(cuts[:-1], cuts[1:])]
+    return c_oracle.finalize(c_oracle.combine(parts))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_gemm_any_k_past_one_call(dt):
+    rng = np.random.default_rng(620 + (dt == "bf16"))
+    for K, kind in ((det.K_MAX + 3000, "wide"), (2 * det.K_MAX + 1, "normal"), (det.K_MAX, "special")):
+        announce(f"gemm_any_k {dt} {kind} 3 x 2 x {K}")
+        xb, wb = random_operands(rng, 3, 2, K, dt, kind)
+        got = f32_bits(det.gemm_any_k(to_device(xb, dt), to_device(wb, dt)))
+        want = _oracle_gemm_long(xb, wb)
+        assert np.array_equal(got, want), mismatch_report(got, want)
+
+
+def test_detlinear_weight_and_bias_gradients_past_2e19_tokens():
+    # T > 2^19 tokens: dW and db are K-slice compositions
+    rng = np.random.default_rng(630)
+    T, IN, OUT = det.K_MAX + 77, 4, 3
+    announce(f"DetLinear bias f32 T={T} {IN}->{OUT}")
+    xb, Wb = random_operands(rng, T, OUT, IN, "f32", "uniform")
+    bb = random_operands(rng, 1, OUT, 1, "f32", "uniform")[1].reshape(OUT)
+    layer = _layer("f32", IN, OUT, 1, Wb, bb)
+    x = to_device(xb, "f32")
+    y = layer(x)
+    G = rng.standard_normal((T, OUT), dtype=np.float32)
+    y.backward(torch.from_numpy(G).cuda())
+    gb = G.view(np.uint32)
+    dw = _oracle_gemm_long(np.ascontiguousarray(gb.T), np.ascontiguousarray(xb.T))
+    db = _oracle_gemm_long(np.ascontiguousarray(gb.T), _ones((1, T), "f32")).reshape(OUT)
+    assert np.array_equal(tensor_bits(layer.weight.grad), dw)
+    assert np.array_equal(tensor_bits(layer.bias.grad), db)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_exact_dot_and_sum_of_squares(dt):
+    rng = np.random.default_rng(640 + (dt == "bf16"))
+    for n, kind in ((1, "normal"), (1000, "wide"), (det.K_MAX + 5, "normal"), (4097, "special")):
+        announce(f"exact_dot {dt} {kind} n={n}")
+        ab, bb = random_operands(rng, 1, 1, n, dt, kind)
+        a, b = to_device(ab, dt), to_device(bb, dt)
+        dot = f32_bits(det.exact_dot(a.reshape(-1), b.reshape(-1)))
+        assert dot == _oracle_gemm_long(ab, bb)[0, 0]
+        got = f32_bits(det.exact_sum_squares(a))
+        assert got == _oracle_gemm_long(ab, ab)[0, 0]
+        # a 2-D view gives the same bits as the flat vector
+        if n % 2 == 0:
+            assert f32_bits(det.exact_dot(a.reshape(2, -1), b.reshape(2, -1))) == dot
+    z = torch.empty(0, device="cuda", dtype=TORCH_DT[dt])
+    assert f32_bits(det.exact_sum_squares(z)) == 0
+
+
+def _loss_oracle(yb, tb, dt):
+    neg = tb ^ NEG[dt]
+    s = c_oracle.gemm(np.hstack([yb, tb, yb, yb]).reshape(1, -1),
+                      np.hstack([yb, tb, neg, neg]).reshape(1, -1))[0, 0]
+    return np.float32(np.array([s], dtype=np.uint32).view(np.float32)[0] / np.float32(yb.size))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_exact_mse_loss(dt):
+    rng = np.random.default_rng(650 + (dt == "bf16"))
+    for n, kind in ((64, "normal"), (1000, "uniform"), (3 * 4096 + 5, "wide")):
+        announce(f"exact_mse_loss {dt} {kind} n={n}")
+        yb, tb = random_operands(rng, 1, 1, n, dt, kind)
+        yb, tb = yb.reshape(n), tb.reshape(n)
+        y = to_device(yb, dt).requires_grad_(True)
+        t = to_device(tb, dt)
+        loss = det.exact_mse_loss(y, t)
+        want = _loss_oracle(yb, tb, dt)
+        assert loss.dtype == torch.float32 and loss.dim() == 0
+        assert f32_bits(loss.reshape(1))[0] == want.view(np.uint32)
+        # the same elements in another order: the same bits
+        perm = torch.from_numpy(rng.permutation(n)).cuda()
+        assert torch.equal(det.exact_mse_loss(y.detach()[perm], t[perm]).view(torch.int32),
+                           loss.detach().view(torch.int32))
+        # the gradient 2 (y - t) / n, elementwise
+        loss.backward()
+        yf, tf = y.detach().float(), t.float()
+        want_g = ((yf - tf) * (2.0 / n)).to(y.dtype)
+        assert torch.equal(y.grad.view(torch.int16 if dt == "bf16" else torch.int32),
+                           want_g.view(torch.int16 if dt == "bf16" else torch.int32))
+    # the fp32 division of the rounded sum by n is correctly rounded
+    s32 = rng.standard_normal(4096).astype(np.float32) * np.float32(1e3)
+    for n in (3, 7, 1000, 12293, 8191, 1 << 20):
+        want = (s32 / np.float32(n)).astype(np.float32)
+        got = (torch.from_numpy(s32).cuda() / torch.tensor(float(n), device="cuda")).cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), n
+    # no target: sum y^2 / n
+    yb = random_operands(rng, 1, 1, 256, dt, "normal")[0].reshape(256)
+    y = to_device(yb, dt)
+    s = c_oracle.gemm(yb.reshape(1, -1), yb.reshape(1, -1))[0, 0]
+    want = np.float32(np.array([s], dtype=np.uint32).view(np.float32)[0] / np.float32(256))
+    assert f32_bits(det.exact_mse_loss(y).reshape(1))[0] == want.view(np.uint32)
