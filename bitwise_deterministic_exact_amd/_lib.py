@@ -50,6 +50,8 @@ def load() -> ctypes.CDLL:
         "det_finalize": ([vp, vp, i64, vp], c_int),
         "det_round_f32_to_bf16": ([vp, vp, i64, vp], c_int),
         "det_check_finite": ([c_int, vp, i64, i64, i64, i64, vp, vp], c_int),
+        "det_dot_partial": ([c_int, vp, i64, vp, i64, i64, vp, c_int, vp], c_int),
+        "det_sqdiff_partial": ([c_int, vp, i64, vp, i64, i64, vp, c_int, vp], c_int),
         "det_set_gemm_path": ([c_int, c_int], c_int),
         "det_last_gemm_plan": ([ctypes.POINTER(c_int), ctypes.POINTER(c_int), ctypes.POINTER(i64),
                                 ctypes.POINTER(i64)], None),

@@ -187,23 +187,69 @@ def gemm_any_k(x: torch.Tensor, w: torch.Tensor, *, check_finite: Optional[bool]
     return det_finalize(det_combine(parts))
 
 
-def exact_dot(a: torch.Tensor, b: torch.Tensor, *, check_finite: Optional[bool] = None) -> torch.Tensor:
-    """sum_i a_i * b_i over all elements, every product exact and the sum
-    rounded once to fp32 (a 1 x 1 exact GEMM with K = numel); a 0-d float32
-    tensor.  a and b: same shape, both float32 or both bfloat16."""
+DOT_MAX_PRODUCTS = 1 << 30
+
+
+def _vector(t: torch.Tensor, what: str):
+    """A tensor as (tensor, element increment) for the dot entry points: a
+    1-D view keeps its stride, anything else is flattened (a copy only when
+    its elements are not evenly spaced)."""
+    if t.dtype not in _DT:
+        raise ValueError(f"{what} must be float32 or bfloat16 (got {t.dtype})")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what} must be on a GPU")
+    if t.dim() != 1:
+        t = t.reshape(-1)
+    return t, (t.stride(0) if t.numel() > 1 else 1)
+
+
+def _dot_digits(fn, a: torch.Tensor, b: Optional[torch.Tensor], check_finite) -> torch.Tensor:
+    va, ia = _vector(a, "a")
+    vb, ib = _vector(b, "b") if b is not None else (None, 0)
+    if vb is not None and vb.dtype != va.dtype:
+        raise ValueError("a and b must share a dtype")
+    if _want_check(check_finite) and va.numel():
+        if has_nonfinite(va) or (vb is not None and has_nonfinite(vb)):
+            raise ValueError("a or b holds Inf or NaN; the exact accumulator takes finite inputs only")
+    acc = torch.empty(_lib.NUM_DIGITS, dtype=torch.int64, device=va.device)
+    bp = ctypes.c_void_p(vb.data_ptr()) if vb is not None else None
+    _lib.check(fn(_DT[va.dtype], ctypes.c_void_p(va.data_ptr()), ia, bp, ib, va.numel(),
+                  ctypes.c_void_p(acc.data_ptr()), 0, _stream(va.device)))
+    return acc
+
+
+def exact_dot_digits(a: torch.Tensor, b: torch.Tensor, *, check_finite: Optional[bool] = None) -> torch.Tensor:
+    """Raw digits (int64 [18]) of sum_i a_i * b_i, every product exact: the
+    digits det_gemm_partial gives for the 1 x 1 GEMM of the flattened
+    operands, so they compose with det_combine and round with det_finalize."""
     if a.shape != b.shape:
         raise ValueError("exact_dot needs operands of one shape")
-    a1, b1 = a.reshape(1, -1), b.reshape(1, -1)
-    if a1.shape[1] == 0:
-        return torch.zeros((), dtype=torch.float32, device=a.device)
-    return gemm_any_k(a1, b1, check_finite=check_finite).reshape(())
+    if a.numel() > DOT_MAX_PRODUCTS:
+        raise ValueError(f"{a.numel()} elements exceed 2^30 products per accumulator")
+    return _dot_digits(_lib.load().det_dot_partial, a, b, check_finite)
+
+
+def exact_dot(a: torch.Tensor, b: torch.Tensor, *, check_finite: Optional[bool] = None) -> torch.Tensor:
+    """sum_i a_i * b_i over all elements, every product exact and the sum
+    rounded once to fp32; a 0-d float32 tensor.  a and b: same shape, both
+    float32 or both bfloat16, at most 2^30 elements."""
+    return det_finalize(exact_dot_digits(a, b, check_finite=check_finite)).reshape(())
+
+
+def exact_sqdiff_digits(a: torch.Tensor, b: Optional[torch.Tensor] = None, *,
+                        check_finite: Optional[bool] = None) -> torch.Tensor:
+    """Raw digits (int64 [18]) of sum_i (a_i - b_i)^2 with no rounding of the
+    differences (sum_i a_i^2 without b)."""
+    if b is not None and a.shape != b.shape:
+        raise ValueError("a and b must have one shape")
+    if a.numel() > DOT_MAX_PRODUCTS // (3 if b is not None else 1):
+        raise ValueError(f"{a.numel()} elements exceed 2^30 products per accumulator")
+    return _dot_digits(_lib.load().det_sqdiff_partial, a, b, check_finite)
 
 
 def exact_sum_squares(y: torch.Tensor, *, check_finite: Optional[bool] = None) -> torch.Tensor:
-    """sum_i y_i^2 exactly, rounded once to fp32 (a loss such as mean(y^2)
-    is this divided by the element count: one more IEEE rounding, exact when
-    the count is a power of two and the result stays normal)."""
-    return exact_dot(y, y, check_finite=check_finite)
+    """sum_i y_i^2 exactly, rounded once to fp32; a 0-d float32 tensor."""
+    return det_finalize(exact_sqdiff_digits(y, check_finite=check_finite)).reshape(())
 
 
 _PATHS = {"auto": _lib.DET_PATH_AUTO, "accumulator": _lib.DET_PATH_ACCUMULATOR,

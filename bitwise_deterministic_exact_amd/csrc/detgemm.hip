@@ -1660,6 +1660,143 @@ __global__ __launch_bounds__(128 * WR, 2) void k_slice_mma(SliceMmaArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- exact dot products
+//
+// The raw digits of one long sum of exact products (det_dot_partial,
+// det_sqdiff_partial): the reduction of a whole tensor into a single
+// accumulator, e.g. a loss.  Each lane keeps 19 private int64 slots in LDS,
+// one per digit (the last only ever receives the zero limbs that lie past
+// digit 17 for finite inputs), and adds each product's three base-2^32 limbs
+// into the slots of the digits they fall in: one LDS atomic per limb, no
+// contention (the slots are the lane's own) and no bank conflicts (a wave's
+// 64 slots of one digit row are 512 contiguous bytes, and rows lie 512 bytes
+// apart, so the bank of a lane's slot depends on the lane alone).  At the end
+// the workgroup adds its lanes' slots digit by digit and adds each digit into
+// the output with one 64-bit global atomic.  Integer addition is exact and
+// commutative, so the digits do not depend on the order of the atomics.
+// The loop reads both operands once, 16 bytes per lane per load when they
+// are contiguous and 16-byte aligned: the kernel is bound by HBM bandwidth.
+
+constexpr int DOT_W = 4;                  // waves per workgroup
+constexpr int DOT_SLOTS = ND + 1;         // digit slots per lane
+constexpr int DOT_U = 4;                  // 16-byte loads in flight per operand and lane
+constexpr int64_t DOT_MAX_PRODUCTS = int64_t(1) << 30;
+
+enum { DOT_PLAIN = 0, DOT_SQDIFF = 1, DOT_SQUARE = 2 };
+
+struct DotArgs {
+  const void* a; int64_t inc_a;
+  const void* b; int64_t inc_b;
+  int64_t n;
+  int64_t* acc;                           // 18 digits
+};
+
+// slot += (-1)^neg * m1 * m2 * 2^(o - 298), o >= 0 the exponent of the
+// product's bit 0 plus 298; `slot` is the lane's slot for digit 0, the slot
+// of digit d lies 64 int64 further per digit
+__device__ __forceinline__ void dot_add(unsigned long long* slot, uint32_t m1, uint32_t m2, int o, bool neg) {
+  const uint64_t P = static_cast<uint64_t>(m1) * m2;               // < 2^48
+  const int d = o >> 5, sh = o & 31;
+  const uint64_t lo = P << sh;
+  const uint64_t hi = sh ? (P >> (64 - sh)) : 0ull;                 // < 2^15
+  uint64_t l0 = lo & 0xFFFFFFFFull, l1 = lo >> 32, l2 = hi;
+  if (neg) { l0 = 0ull - l0; l1 = 0ull - l1; l2 = 0ull - l2; }
+  unsigned long long* p = slot + d * 64;
+  __hip_atomic_fetch_add(p, l0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  __hip_atomic_fetch_add(p + 64, l1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  __hip_atomic_fetch_add(p + 128, l2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// the products of one element pair (mode: a*b, (a-b)^2 = a*a + b*b - 2 a*b,
+// or a*a)
+template <int DT, int MODE>
+__device__ __forceinline__ void dot_elem(unsigned long long* slot, uint32_t ab, uint32_t bb) {
+  bool na, nb;
+  uint32_t ma, mb;
+  int ea, eb;
+  split_elem<DT>(ab, na, ma, ea);
+  if (MODE == DOT_SQUARE) {
+    dot_add(slot, ma, ma, 2 * ea + 298, false);
+    return;
+  }
+  split_elem<DT>(bb, nb, mb, eb);
+  if (MODE == DOT_PLAIN) {
+    dot_add(slot, ma, mb, ea + eb + 298, na != nb);
+  } else {
+    dot_add(slot, ma, ma, 2 * ea + 298, false);
+    dot_add(slot, mb, mb, 2 * eb + 298, false);
+    dot_add(slot, ma, mb, ea + eb + 299, na == nb);
+  }
+}
+
+// element e of a 16-byte load (4 f32 or 8 bf16 bit patterns); e is a
+// compile-time index after unrolling
+template <int DT>
+__device__ __forceinline__ uint32_t dot_word_elem(const uint4& v, int e) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  if (DT == DET_F32) return w[e];
+  return (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu);
+}
+
+template <int DT, int MODE, bool VEC>
+__global__ __launch_bounds__(64 * DOT_W) void k_dot(DotArgs a) {
+  __shared__ unsigned long long slots[DOT_W * DOT_SLOTS * 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  unsigned long long* const my = slots + wave * DOT_SLOTS * 64 + lane;
+#pragma unroll
+  for (int j = 0; j < DOT_SLOTS; ++j) my[j * 64] = 0ull;
+  // no barrier needed here: a lane touches only its own slots until the end
+  const int64_t nthreads = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  constexpr int EPV = DT == DET_F32 ? 4 : 8;         // elements per 16-byte load
+  int64_t done = 0;
+  if (VEC) {
+    const uint4* const va = static_cast<const uint4*>(a.a);
+    const uint4* const vb = static_cast<const uint4*>(a.b);
+    const int64_t nv = a.n / EPV;
+    for (int64_t c0 = tid; c0 < nv; c0 += nthreads * DOT_U) {
+      uint4 ra[DOT_U], rb[DOT_U];
+#pragma unroll
+      for (int u = 0; u < DOT_U; ++u) {
+        const int64_t c = min(c0 + u * nthreads, nv - 1);            // clamped: always in bounds
+        ra[u] = va[c];
+        if (MODE != DOT_SQUARE) rb[u] = vb[c];
+      }
+#pragma unroll
+      for (int u = 0; u < DOT_U; ++u) {
+        if (c0 + u * nthreads >= nv) break;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e)
+          dot_elem<DT, MODE>(my, dot_word_elem<DT>(ra[u], e),
+                             MODE != DOT_SQUARE ? dot_word_elem<DT>(rb[u], e) : 0u);
+      }
+    }
+    done = nv * EPV;
+  }
+  for (int64_t i = done + tid; i < a.n; i += nthreads) {
+    const uint32_t x = load_elem<DT>(a.a, i * a.inc_a);
+    const uint32_t y = MODE != DOT_SQUARE ? load_elem<DT>(a.b, i * a.inc_b) : 0u;
+    dot_elem<DT, MODE>(my, x, y);
+  }
+  __syncthreads();
+  // digit j: lane l adds the slots of lane l of every wave, then the wave
+  // adds its 64 lanes; digit 18 holds only zeros for finite inputs
+  for (int j = wave; j < ND; j += DOT_W) {
+    int64_t s = 0;
+#pragma unroll
+    for (int w = 0; w < DOT_W; ++w) s += static_cast<int64_t>(slots[(w * DOT_SLOTS + j) * 64 + lane]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+    if (lane == 0 && s != 0)
+      __hip_atomic_fetch_add(reinterpret_cast<unsigned long long*>(a.acc + j), static_cast<unsigned long long>(s),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+__global__ __launch_bounds__(64) void k_zero_digits(int64_t* acc) {
+  if (threadIdx.x < ND) acc[threadIdx.x] = 0;
+}
+
 // ---------------------------------------------------------------- host helpers
 det_status check_operands(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk, const void* w,
                           int64_t w_sn, int64_t w_sk, int64_t M, int64_t N, int64_t K) {
@@ -1682,6 +1819,50 @@ unsigned grid_for(int64_t n, int64_t per_block, unsigned cap) {
 }
 
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+template <int DT, int MODE>
+void launch_dot(const DotArgs& a, bool vec, hipStream_t s) {
+  constexpr int EPV = DT == DET_F32 ? 4 : 8;
+  const int64_t per_block = static_cast<int64_t>(64) * DOT_W * (vec ? EPV * DOT_U : 4);
+  const dim3 grid(grid_for(a.n, per_block, 2048)), block(64 * DOT_W);
+  if (vec) hipLaunchKernelGGL((k_dot<DT, MODE, true>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((k_dot<DT, MODE, false>), grid, block, 0, s, a);
+}
+
+det_status dot_common(int mode, det_dtype dt, const void* a, int64_t inc_a, const void* b, int64_t inc_b,
+                      int64_t n, int64_t* acc, int accumulate, void* stream) {
+  if (dt != DET_F32 && dt != DET_BF16) return fail(DET_EDTYPE, "unknown dtype %d", static_cast<int>(dt));
+  if (n < 0 || inc_a < 0 || inc_b < 0) return fail(DET_EINVAL, "negative count or increment");
+  const int64_t per = mode == DOT_SQDIFF ? 3 : 1;
+  if (n > DOT_MAX_PRODUCTS / per)
+    return fail(DET_EKLIMIT, "%lld elements exceed the limit of 2^30 products per accumulator", (long long)n);
+  if (acc == nullptr) return fail(DET_EINVAL, "null accumulator");
+  if (reinterpret_cast<uintptr_t>(acc) & 7u) return fail(DET_EINVAL, "accumulator must be 8-byte aligned");
+  if (n > 0 && (a == nullptr || (mode != DOT_SQUARE && b == nullptr))) return fail(DET_EINVAL, "null operand");
+  const uintptr_t align = dt == DET_F32 ? 4u : 2u;
+  if ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b)) & (align - 1))
+    return fail(DET_EINVAL, "operands must be aligned to their element size");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!accumulate) {
+    hipLaunchKernelGGL(k_zero_digits, dim3(1), dim3(64), 0, s, acc);
+    det_status st = hip_check(hipGetLastError(), "dot zero launch");
+    if (st != DET_OK) return st;
+  }
+  if (n == 0) return DET_OK;
+  DotArgs d{a, inc_a, mode == DOT_SQUARE ? a : b, mode == DOT_SQUARE ? inc_a : inc_b, n, acc};
+  const bool vec = d.inc_a == 1 && d.inc_b == 1 &&
+                   ((reinterpret_cast<uintptr_t>(d.a) | reinterpret_cast<uintptr_t>(d.b)) & 15u) == 0u;
+  if (dt == DET_F32) {
+    if (mode == DOT_PLAIN) launch_dot<DET_F32, DOT_PLAIN>(d, vec, s);
+    else if (mode == DOT_SQDIFF) launch_dot<DET_F32, DOT_SQDIFF>(d, vec, s);
+    else launch_dot<DET_F32, DOT_SQUARE>(d, vec, s);
+  } else {
+    if (mode == DOT_PLAIN) launch_dot<DET_BF16, DOT_PLAIN>(d, vec, s);
+    else if (mode == DOT_SQDIFF) launch_dot<DET_BF16, DOT_SQDIFF>(d, vec, s);
+    else launch_dot<DET_BF16, DOT_SQUARE>(d, vec, s);
+  }
+  return hip_check(hipGetLastError(), "dot launch");
+}
 
 // K per launch.  With a longer K range the waves resident on one XCD drift
 // apart in k and stop sharing their slice of w in L2 (measured: 2400 GMAC/s at
@@ -2271,6 +2452,16 @@ det_status det_finalize(const int64_t* acc, float* y, int64_t n_outputs, void* s
   hipLaunchKernelGGL(k_finalize, dim3(static_cast<unsigned>((n_outputs + 255) / 256)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), acc, y, n_outputs);
   return hip_check(hipGetLastError(), "finalize launch");
+}
+
+det_status det_dot_partial(det_dtype dt, const void* a, int64_t inc_a, const void* b, int64_t inc_b, int64_t n,
+                           int64_t* acc, int accumulate, void* stream) {
+  return dot_common(DOT_PLAIN, dt, a, inc_a, b, inc_b, n, acc, accumulate, stream);
+}
+
+det_status det_sqdiff_partial(det_dtype dt, const void* a, int64_t inc_a, const void* b, int64_t inc_b,
+                              int64_t n, int64_t* acc, int accumulate, void* stream) {
+  return dot_common(b == nullptr ? DOT_SQUARE : DOT_SQDIFF, dt, a, inc_a, b, inc_b, n, acc, accumulate, stream);
 }
 
 det_status det_round_f32_to_bf16(const float* in, uint16_t* out, int64_t n, void* stream) {

@@ -6,13 +6,12 @@ order; "Usage": the partials of K-slices compose into the whole sum).
 exact_mse_loss(y, t) = RNE32( sum_i (y_i - t_i)^2 ) / n
 
 The squared error is never rounded per element: with every product exact,
-sum (y - t)^2 = sum y*y + sum t*t + sum y*(-t) + sum y*(-t), one dot product
-of length 4n over [y | t | y | y] and [y | t | -t | -t] (negation is exact),
-which the library forms as a 1 x 1 exact GEMM and rounds once to fp32.  The
-division by n is one more IEEE fp32 division, correctly rounded, by n as an
-fp32 value (n itself rounded to fp32 above 2^24; the quotient is exact when n
-is a power of two and stays normal).  Without a target the loss is
-sum y^2 / n.
+sum (y - t)^2 = sum y*y + sum t*t - sum 2*y*t, three exact products per
+element added into one accumulator (det_sqdiff_partial), rounded once to
+fp32 (det_finalize).  The division by n is one more IEEE fp32 division,
+correctly rounded, by n as an fp32 value (n itself rounded to fp32 above
+2^24; the quotient is exact when n is a power of two and stays normal).
+Without a target the loss is sum y^2 / n.
 
 The gradient 2 (y - t) / n is elementwise (no reduction, so no order to fix)
 and is formed with torch's elementwise ops.
@@ -23,20 +22,13 @@ from typing import Optional
 
 import torch
 
-from .api import exact_dot
+from .api import det_finalize, exact_sqdiff_digits
 
 
 class _ExactMSE(torch.autograd.Function):
     @staticmethod
     def forward(ctx, y: torch.Tensor, t: Optional[torch.Tensor]) -> torch.Tensor:
-        yf = y.reshape(-1)
-        if t is None:
-            s = exact_dot(yf, yf, check_finite=False)
-        else:
-            tf = t.reshape(-1)
-            a = torch.cat([yf, tf, yf, yf])
-            b = torch.cat([yf, tf, -tf, -tf])
-            s = exact_dot(a, b, check_finite=False)
+        s = det_finalize(exact_sqdiff_digits(y, t, check_finite=False)).reshape(())
         ctx.save_for_backward(y, t if t is not None else y)
         ctx.has_target = t is not None
         # a true fp32 division by a device tensor: torch turns a division by
@@ -61,7 +53,8 @@ def exact_mse_loss(y: torch.Tensor, target: Optional[torch.Tensor] = None) -> to
     """Mean squared error with the sum formed exactly; a 0-d float32 tensor.
 
     y (and target, if given): float32 or bfloat16 GPU tensors of one shape
-    and dtype, finite, any number of elements."""
+    and dtype, finite; at most 2^30 / 3 elements with a target, 2^30
+    without."""
     if target is not None:
         if target.shape != y.shape or target.dtype != y.dtype:
             raise ValueError("exact_mse_loss needs y and target of one shape and dtype")

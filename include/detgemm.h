@@ -214,6 +214,39 @@ det_status det_combine(const int64_t* const* parts, int nparts, int64_t* out,
 det_status det_finalize(const int64_t* acc, float* y, int64_t n_outputs, void* stream);
 
 /*
+ * det_dot_partial -- raw digits of one exact dot product, for reductions of a
+ * whole tensor such as a loss ("Method": every product exact, the sum in the
+ * digits of one accumulator; the page's accumulator applied to one output).
+ *   a, b         device operands of n elements each (bit patterns of dtype
+ *                dt), element i at a[i * inc_a] and b[i * inc_b]
+ *   inc_a, inc_b element increments (>= 0; 0 repeats one element)
+ *   n            element count (>= 0)
+ *   acc          device pointer to 18 int64 digits (8-byte aligned)
+ *   accumulate   0: acc = the digits of sum_i a_i b_i; 1: acc += them
+ * The digits are the same raw digits det_gemm_partial writes for the 1 x 1
+ * GEMM of a and b (for n <= 2^19), so det_combine and det_finalize apply.
+ * The digits are added into acc with 64-bit integer atomics: acc is in use
+ * until the call's work on `stream` has finished, and calls that add into one
+ * acc on different streams must not overlap.  At most 2^30 products may be
+ * added into one acc over all calls (a dot product adds n): then every digit
+ * stays within +-2^62.  Inputs must be finite (not checked).
+ * Returns DET_OK, DET_EINVAL, DET_EKLIMIT (more than 2^30 products in one
+ * call), DET_EDTYPE or DET_EHIP.
+ */
+det_status det_dot_partial(det_dtype dt, const void* a, int64_t inc_a, const void* b, int64_t inc_b,
+                           int64_t n, int64_t* acc, int accumulate, void* stream);
+
+/*
+ * det_sqdiff_partial -- raw digits of sum_i (a_i - b_i)^2, exactly: the
+ * differences are never rounded, the sum is formed from the exact products
+ * a_i a_i + b_i b_i - 2 a_i b_i (3 products per element).  b == NULL gives
+ * sum_i a_i^2 (1 product per element; inc_b is ignored).  Arguments, digits,
+ * limits and errors as for det_dot_partial.
+ */
+det_status det_sqdiff_partial(det_dtype dt, const void* a, int64_t inc_a, const void* b, int64_t inc_b,
+                              int64_t n, int64_t* acc, int accumulate, void* stream);
+
+/*
  * det_round_f32_to_bf16 -- round fp32 values to bf16 (nearest, ties to even),
  * used by the DetLinear backward of the "Usage" section to hand dY to a bf16
  * exact GEMM.  in: n fp32, out: n bf16 bit patterns; contiguous.  NaN stays NaN.

@@ -67,6 +67,17 @@ def test_c_abi_rejects_bad_arguments_without_a_gpu():
     assert lib.det_finalize(None, None, -1, None) == _lib.DET_EINVAL
     assert lib.det_round_f32_to_bf16(None, None, 3, None) == _lib.DET_EINVAL
     assert lib.det_check_finite(9, None, 1, 1, 1, 1, None, None) == _lib.DET_EDTYPE
+    # exact dot products: 2^30 products per accumulator, 3 per squared difference
+    v, acc = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 21)
+    assert lib.det_dot_partial(0, v, 1, v, 1, (1 << 30) + 1, acc, 0, None) == _lib.DET_EKLIMIT
+    assert lib.det_sqdiff_partial(0, v, 1, v, 1, (1 << 30) // 3 + 1, acc, 0, None) == _lib.DET_EKLIMIT
+    assert lib.det_sqdiff_partial(0, v, 1, None, 0, (1 << 30) + 1, acc, 0, None) == _lib.DET_EKLIMIT
+    assert lib.det_dot_partial(0, v, 1, v, 1, 8, None, 0, None) == _lib.DET_EINVAL
+    assert lib.det_dot_partial(0, v, 1, v, 1, 8, ctypes.c_void_p((1 << 21) + 4), 0, None) == _lib.DET_EINVAL
+    assert lib.det_dot_partial(0, v, -1, v, 1, 8, acc, 0, None) == _lib.DET_EINVAL
+    assert lib.det_dot_partial(0, v, 1, None, 1, 8, acc, 0, None) == _lib.DET_EINVAL
+    assert lib.det_dot_partial(0, ctypes.c_void_p((1 << 20) + 2), 1, v, 1, 8, acc, 0, None) == _lib.DET_EINVAL
+    assert lib.det_dot_partial(5, v, 1, v, 1, 8, acc, 0, None) == _lib.DET_EDTYPE
 
 
 def _ru(v, m):

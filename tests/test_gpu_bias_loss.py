@@ -133,22 +133,81 @@ def test_detlinear_weight_and_bias_gradients_past_2e19_tokens():
     assert np.array_equal(tensor_bits(layer.bias.grad), db)
 
 
+def _oracle_digits(ab, bb):
+    """The oracle's raw digits of sum_i a_i b_i (1-D bit arrays), over slices
+    of 400000 when longer than its 2^19 limit (raw digits add, so the split
+    does not change them)."""
+    a, b = ab.reshape(1, -1), bb.reshape(1, -1)
+    if a.shape[1] <= det.K_MAX:
+        return c_oracle.partial(a, b).reshape(-1)
+    K = a.shape[1]
+    cuts = list(range(0, K, 400_000)) + [K]
+    parts = [c_oracle.partial(np.ascontiguousarray(a[:, p:q]), np.ascontiguousarray(b[:, p:q]))
+             for p, q in zip(cuts[:-1], cuts[1:])]
+    return c_oracle.combine(parts).reshape(-1)
+
+
+def _value(digits):
+    return sum(int(d) << (32 * j) for j, d in enumerate(np.asarray(digits).tolist()))
+
+
+DOT_CASES = [(0, "normal"), (1, "normal"), (3, "special"), (7, "wide"), (8, "normal"), (1000, "wide"),
+             (4097, "special"), (det.K_MAX + 5, "normal"), (3_000_003, "wide")]
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_exact_dot_and_sum_of_squares(dt):
+def test_exact_dot_digits_equal_the_oracles(dt):
     rng = np.random.default_rng(640 + (dt == "bf16"))
-    for n, kind in ((1, "normal"), (1000, "wide"), (det.K_MAX + 5, "normal"), (4097, "special")):
+    for n, kind in DOT_CASES:
         announce(f"exact_dot {dt} {kind} n={n}")
-        ab, bb = random_operands(rng, 1, 1, n, dt, kind)
+        ab, bb = (v.reshape(n) for v in random_operands(rng, 1, 1, n, dt, kind))
         a, b = to_device(ab, dt), to_device(bb, dt)
-        dot = f32_bits(det.exact_dot(a.reshape(-1), b.reshape(-1)))
-        assert dot == _oracle_gemm_long(ab, bb)[0, 0]
-        got = f32_bits(det.exact_sum_squares(a))
-        assert got == _oracle_gemm_long(ab, ab)[0, 0]
-        # a 2-D view gives the same bits as the flat vector
-        if n % 2 == 0:
-            assert f32_bits(det.exact_dot(a.reshape(2, -1), b.reshape(2, -1))) == dot
-    z = torch.empty(0, device="cuda", dtype=TORCH_DT[dt])
-    assert f32_bits(det.exact_sum_squares(z)) == 0
+        want = _oracle_digits(ab, bb)
+        got = det.exact_dot_digits(a, b).cpu().numpy()
+        assert np.array_equal(got, want), (got, want)
+        assert f32_bits(det.exact_dot(a, b).reshape(1))[0] == c_oracle.finalize(want.reshape(1, 18))[0]
+        if 0 < n <= det.K_MAX:       # the same raw digits as the 1 x 1 GEMM partial
+            assert torch.equal(det.det_gemm_partial(a.reshape(1, n), b.reshape(1, n)).reshape(-1),
+                               det.exact_dot_digits(a, b))
+        # sum of squares: the digits' value is the exact sum of a_i^2
+        got = det.exact_sqdiff_digits(a).cpu().numpy()
+        assert _value(got) == _value(_oracle_digits(ab, ab))
+        assert f32_bits(det.exact_sum_squares(a).reshape(1))[0] == \
+            c_oracle.finalize(_oracle_digits(ab, ab).reshape(1, 18))[0]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_exact_dot_strided_unaligned_and_broadcast(dt):
+    rng = np.random.default_rng(660 + (dt == "bf16"))
+    M, K = 300, 257
+    xb, wb = random_operands(rng, M, 2, K, dt, "normal")
+    x, w = to_device(xb, dt), to_device(wb, dt)
+    cases = [
+        ("column", x[:, 5], xb[:, 5], x[:, 9], xb[:, 9]),                 # increment K
+        ("unaligned", x[3, 1:], xb[3, 1:], x[4, 1:], xb[4, 1:]),          # 1 element off 16 B
+        ("matrix", x[:, :64], xb[:, :64], x[:, 64:128], xb[:, 64:128]),   # 2-D, flattened
+        ("broadcast", w[0], wb[0], w[1, :1].expand(K), np.repeat(wb[1, :1], K)),   # increment 0
+    ]
+    for name, a, ab, b, bbits in cases:
+        announce(f"exact_dot {dt} {name}")
+        ab, bbits = np.ascontiguousarray(ab).reshape(-1), np.ascontiguousarray(bbits).reshape(-1)
+        got = det.exact_dot_digits(a, b).cpu().numpy()
+        assert np.array_equal(got, _oracle_digits(ab, bbits)), name
+
+
+def test_dot_digits_accumulate_across_calls():
+    # accumulate = 1 adds into the digits of an earlier call: the digits of
+    # both halves equal the digits of the whole
+    rng = np.random.default_rng(670)
+    ab, bb = (v.reshape(-1) for v in random_operands(rng, 1, 1, 10001, "f32", "wide"))
+    a, b = to_device(ab, "f32"), to_device(bb, "f32")
+    lib = det._lib.load()
+    acc = torch.empty(18, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    for lo, hi, accumulate in ((0, 4000, 0), (4000, 10001, 1)):
+        det._lib.check(lib.det_dot_partial(0, a[lo:].data_ptr(), 1, b[lo:].data_ptr(), 1, hi - lo,
+                                           acc.data_ptr(), accumulate, stream))
+    assert np.array_equal(acc.cpu().numpy(), _oracle_digits(ab, bb))
 
 
 def _loss_oracle(yb, tb, dt):
