@@ -96,10 +96,11 @@ def main() -> int:
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (calibrates HBM byte counters)")
     ap.add_argument("--workload", default="wide4096",
-                    choices=["wide4096", "bf16cancel", "ksharded", "detlinear", "matrixcore"],
+                    choices=["wide4096", "bf16cancel", "ksharded", "detlinear", "matrixcore", "loss"],
                     help="wide4096 (default, the headline): f32 4096^3 wide range; the others time "
                          "the bf16 1024^3, the 16-shard K=2^19 and the DetLinear configurations, "
-                         "and (matrixcore) det_gemm on the DetLinear forward shape")
+                         "(matrixcore) det_gemm on the DetLinear forward shape and (loss) the exact "
+                         "mean-squared-error reduction of a DetLinear output")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -283,6 +284,72 @@ def matrix_core_aux(det, dev, timed) -> dict:
     return out
 
 
+def _digits_of(v: int) -> np.ndarray:
+    """18 digits (base 2^32, the top one signed) holding the integer v."""
+    d = [(v >> (32 * j)) & 0xFFFFFFFF for j in range(17)] + [v >> (32 * 17)]
+    return np.array(d, dtype=np.int64).reshape(1, 18)
+
+
+def loss_workload(det, c_oracle, dev, steps, warmup) -> dict:
+    """exact_mse_loss of a DetLinear-sized f32 output (8192 x 4096, N(0,1))
+    against an N(0,1) target: the time of the whole loss, the squared-
+    difference kernel's share against the HBM roofline (its algorithmic bytes
+    are the two operands, read once), and the loss's bits against the
+    oracle's exact sum (sum y^2 + sum t^2 - 2 sum y t, formed from the
+    oracle's digits of the three dot products, rounded by the oracle)."""
+    import torch
+    rng = np.random.default_rng(8)
+    n = 8192 * 4096
+    yb = rng.standard_normal(n, dtype=np.float32).view(np.uint32)
+    tb = rng.standard_normal(n, dtype=np.float32).view(np.uint32)
+    y = torch.from_numpy(yb.view(np.float32)).to(dev)
+    t = torch.from_numpy(tb.view(np.float32)).to(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        for _ in range(max(1, warmup)):
+            fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        for _ in range(steps):
+            fn()
+        e.record(stream)
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / steps
+
+    ms_loss = timed(lambda: det.exact_mse_loss(y, t))
+    ms_digits = timed(lambda: det.exact_sqdiff_digits(y, t, check_finite=False))
+    ms_dot = timed(lambda: det.exact_dot_digits(y, t, check_finite=False))
+    loss = det.exact_mse_loss(y, t)
+    got = int(loss.reshape(1).cpu().view(torch.int32).numpy().view(np.uint32)[0])
+
+    def value(a, b):
+        total = 0
+        for lo in range(0, n, 400_000):
+            d = c_oracle.partial(a[lo:lo + 400_000].reshape(1, -1), b[lo:lo + 400_000].reshape(1, -1))
+            total += sum(int(v) << (32 * j) for j, v in enumerate(d.reshape(-1).tolist()))
+        return total
+
+    exact = value(yb, yb) + value(tb, tb) - 2 * value(yb, tb)
+    s32 = np.array([c_oracle.finalize(_digits_of(exact))[0]], dtype=np.uint32).view(np.float32)[0]
+    want = int(np.array([np.float32(s32) / np.float32(n)], dtype=np.float32).view(np.uint32)[0])
+    nbytes = 2 * 4 * n
+    return dict(metric="exact MSE loss, GB/s of operands (f32 8192x4096 prediction and target)",
+                value=round(nbytes / (ms_loss * 1e-3) / 1e9, 1), unit="GB/s", ms_per_step=round(ms_loss, 4),
+                dtype="int64",
+                roofline={"bound": "hbm", "kernel": "k_dot<f32, squared difference> (+ the digit clear)",
+                          "achieved": round(nbytes / (ms_digits * 1e-3) / 1e9, 1), "peak": HBM_PEAK / 1e9,
+                          "unit": "GB/s", "frac": round(nbytes / (ms_digits * 1e-3) / HBM_PEAK, 4),
+                          "traffic": None, "bytes": "8 n: both operands read once"},
+                dot={"kernel": "k_dot<f32, a*b>", "ms": round(ms_dot, 4),
+                     "GB/s": round(nbytes / (ms_dot * 1e-3) / 1e9, 1),
+                     "frac": round(nbytes / (ms_dot * 1e-3) / HBM_PEAK, 4)},
+                parity={"loss_bits": got, "oracle_bits": want, "bit_exact": got == want},
+                config={"workload": "exact_mse_loss of an 8192x4096 f32 output, N(0,1) prediction and "
+                                    "target, seed 8", "n": n})
+
+
 def _timed(fn, steps, warmup):
     import torch
     for _ in range(warmup):
@@ -349,6 +416,8 @@ def other_workload(args) -> int:
                            "equals_accumulator_path": mc["equals_accumulator_path"]},
                    config={"workload": wl.name + ", seed 4 (the DetLinear forward GEMM)",
                            "M": 8192, "N": 4096, "K": 4096})
+    elif args.workload == "loss":
+        out.update(loss_workload(det, c_oracle, dev, args.steps, args.warmup))
     elif args.workload == "bf16cancel":
         wl = W.c2_bf16_cancel()
         xb, wb = wl.bits()

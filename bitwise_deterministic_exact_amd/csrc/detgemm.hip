@@ -1664,22 +1664,26 @@ __global__ __launch_bounds__(128 * WR, 2) void k_slice_mma(SliceMmaArgs a) {
 //
 // The raw digits of one long sum of exact products (det_dot_partial,
 // det_sqdiff_partial): the reduction of a whole tensor into a single
-// accumulator, e.g. a loss.  Each lane keeps 19 private int64 slots in LDS,
-// one per digit (the last only ever receives the zero limbs that lie past
-// digit 17 for finite inputs), and adds each product's three base-2^32 limbs
-// into the slots of the digits they fall in: one LDS atomic per limb, no
-// contention (the slots are the lane's own) and no bank conflicts (a wave's
-// 64 slots of one digit row are 512 contiguous bytes, and rows lie 512 bytes
-// apart, so the bank of a lane's slot depends on the lane alone).  At the end
-// the workgroup adds its lanes' slots digit by digit and adds each digit into
-// the output with one 64-bit global atomic.  Integer addition is exact and
-// commutative, so the digits do not depend on the order of the atomics.
-// The loop reads both operands once, 16 bytes per lane per load when they
-// are contiguous and 16-byte aligned: the kernel is bound by HBM bandwidth.
+// accumulator, e.g. a loss.  Each lane keeps two private sets of 18 int64
+// slots in LDS, one slot per digit, for its positive and its negative
+// products, and adds each product's base-2^32 limbs (three for f32, two for
+// bf16) into the slots of the digits they fall in: one LDS atomic per limb,
+// no contention (the slots are the lane's own) and no bank conflicts (a
+// wave's 64 slots of one digit are 512 contiguous bytes and slot rows lie 512
+// bytes apart, so the bank of a lane's slot depends on the lane alone).  The
+// sign picks the set, so no limb is ever negated.  Every finite or
+// non-finite bit pattern keeps its limbs within the 18 digits.  At the end
+// the workgroup adds its lanes' slots digit by digit (positive minus
+// negative) and adds each digit into the output with one 64-bit global
+// atomic; integer addition is exact and commutative, so the digits do not
+// depend on the order of the atomics.  The loop reads both operands once,
+// 16 bytes per lane per load when they are contiguous and 16-byte aligned,
+// with the next loads issued before the current elements are added: the
+// kernel is bound by HBM bandwidth.
 
-constexpr int DOT_W = 4;                  // waves per workgroup
-constexpr int DOT_SLOTS = ND + 1;         // digit slots per lane
-constexpr int DOT_U = 4;                  // 16-byte loads in flight per operand and lane
+constexpr int DOT_W = 4;                  // waves per workgroup (two workgroups per CU)
+constexpr int DOT_U = 4;                  // 16-byte loads per operand and lane per step
+constexpr int DOT_SET = ND * 64;          // int64 slots of one sign of one wave
 constexpr int64_t DOT_MAX_PRODUCTS = int64_t(1) << 30;
 
 enum { DOT_PLAIN = 0, DOT_SQDIFF = 1, DOT_SQUARE = 2 };
@@ -1691,41 +1695,69 @@ struct DotArgs {
   int64_t* acc;                           // 18 digits
 };
 
-// slot += (-1)^neg * m1 * m2 * 2^(o - 298), o >= 0 the exponent of the
-// product's bit 0 plus 298; `slot` is the lane's slot for digit 0, the slot
-// of digit d lies 64 int64 further per digit
-__device__ __forceinline__ void dot_add(unsigned long long* slot, uint32_t m1, uint32_t m2, int o, bool neg) {
-  const uint64_t P = static_cast<uint64_t>(m1) * m2;               // < 2^48
-  const int d = o >> 5, sh = o & 31;
-  const uint64_t lo = P << sh;
-  const uint64_t hi = sh ? (P >> (64 - sh)) : 0ull;                 // < 2^15
-  uint64_t l0 = lo & 0xFFFFFFFFull, l1 = lo >> 32, l2 = hi;
-  if (neg) { l0 = 0ull - l0; l1 = 0ull - l1; l2 = 0ull - l2; }
-  unsigned long long* p = slot + d * 64;
-  __hip_atomic_fetch_add(p, l0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  __hip_atomic_fetch_add(p + 64, l1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  __hip_atomic_fetch_add(p + 128, l2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+// an element as its integer significand and biased exponent max(E, 1): the
+// value is +-m * 2^(Ez - 150) for f32, 2^(Ez - 134) for bf16
+template <int DT>
+__device__ __forceinline__ void dot_split(uint32_t b, uint32_t& m, uint32_t& ez) {
+  if (DT == DET_F32) {
+    const uint32_t E = (b >> 23) & 0xFFu;
+    m = (b & 0x7FFFFFu) | (min(E, 1u) << 23);
+    ez = max(E, 1u);
+  } else {
+    const uint32_t E = (b >> 7) & 0xFFu;
+    m = (b & 0x7Fu) | (min(E, 1u) << 7);
+    ez = max(E, 1u);
+  }
+}
+
+// the product m1 * m2 * 2^(o - 298) added into the lane's slots of one sign;
+// o >= 0 is the bit of the fixed-point accumulator that the product's bit 0
+// lands on, `set` the lane's slot for digit 0 of that sign
+template <int DT>
+__device__ __forceinline__ void dot_add(unsigned long long* set, uint32_t m1, uint32_t m2, uint32_t o) {
+  unsigned long long* const p = set + (o >> 5) * 64;
+  const uint32_t sh = o & 31u;
+  if (DT == DET_F32) {
+    const uint64_t P = static_cast<uint64_t>(m1) * m2;                       // < 2^48
+    const uint64_t lo = P << sh;                                             // limbs 0 and 1
+    const uint32_t l2 = static_cast<uint32_t>(((P >> 32) << sh) >> 32);     // limb 2, < 2^15
+    __hip_atomic_fetch_add(p, static_cast<unsigned long long>(static_cast<uint32_t>(lo)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_fetch_add(p + 64, static_cast<unsigned long long>(lo >> 32), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_fetch_add(p + 128, static_cast<unsigned long long>(l2), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
+  } else {
+    const uint64_t lo = static_cast<uint64_t>(m1 * m2) << sh;               // < 2^47: two limbs
+    __hip_atomic_fetch_add(p, static_cast<unsigned long long>(static_cast<uint32_t>(lo)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_fetch_add(p + 64, static_cast<unsigned long long>(lo >> 32), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
 }
 
 // the products of one element pair (mode: a*b, (a-b)^2 = a*a + b*b - 2 a*b,
-// or a*a)
+// or a*a); `pos` is the lane's positive set, the negative set follows it
 template <int DT, int MODE>
-__device__ __forceinline__ void dot_elem(unsigned long long* slot, uint32_t ab, uint32_t bb) {
-  bool na, nb;
-  uint32_t ma, mb;
-  int ea, eb;
-  split_elem<DT>(ab, na, ma, ea);
+__device__ __forceinline__ void dot_elem(unsigned long long* pos, uint32_t ab, uint32_t bb) {
+  // o = (Ez_a - bias) + (Ez_b - bias) + 298: 298 - 300 for f32, 298 - 268 for bf16
+  constexpr uint32_t OFF = DT == DET_F32 ? uint32_t(-2) : 30u;
+  uint32_t ma, ea;
+  dot_split<DT>(ab, ma, ea);
   if (MODE == DOT_SQUARE) {
-    dot_add(slot, ma, ma, 2 * ea + 298, false);
+    dot_add<DT>(pos, ma, ma, 2 * ea + OFF);
     return;
   }
-  split_elem<DT>(bb, nb, mb, eb);
+  uint32_t mb, eb;
+  dot_split<DT>(bb, mb, eb);
+  const uint32_t sa = DT == DET_F32 ? ab >> 31 : (ab >> 15) & 1u;
+  const uint32_t sb = DT == DET_F32 ? bb >> 31 : (bb >> 15) & 1u;
   if (MODE == DOT_PLAIN) {
-    dot_add(slot, ma, mb, ea + eb + 298, na != nb);
+    dot_add<DT>(pos + (sa ^ sb) * DOT_SET, ma, mb, ea + eb + OFF);
   } else {
-    dot_add(slot, ma, ma, 2 * ea + 298, false);
-    dot_add(slot, mb, mb, 2 * eb + 298, false);
-    dot_add(slot, ma, mb, ea + eb + 299, na == nb);
+    dot_add<DT>(pos, ma, ma, 2 * ea + OFF);
+    dot_add<DT>(pos, mb, mb, 2 * eb + OFF);
+    dot_add<DT>(pos + (1u ^ sa ^ sb) * DOT_SET, ma, mb, ea + eb + OFF + 1u);     // -2 a b
   }
 }
 
@@ -1738,14 +1770,25 @@ __device__ __forceinline__ uint32_t dot_word_elem(const uint4& v, int e) {
   return (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu);
 }
 
-template <int DT, int MODE, bool VEC>
-__global__ __launch_bounds__(64 * DOT_W) void k_dot(DotArgs a) {
-  __shared__ unsigned long long slots[DOT_W * DOT_SLOTS * 64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  unsigned long long* const my = slots + wave * DOT_SLOTS * 64 + lane;
+template <int DT, int MODE>
+__device__ __forceinline__ void dot_load(const uint4* va, const uint4* vb, int64_t c, int64_t step, int64_t last,
+                                         uint4 (&ra)[DOT_U], uint4 (&rb)[DOT_U]) {
 #pragma unroll
-  for (int j = 0; j < DOT_SLOTS; ++j) my[j * 64] = 0ull;
-  // no barrier needed here: a lane touches only its own slots until the end
+  for (int u = 0; u < DOT_U; ++u) {
+    const int64_t i = min(c + u * step, last);                   // clamped: always in bounds
+    ra[u] = va[i];
+    if (MODE != DOT_SQUARE) rb[u] = vb[i];
+  }
+}
+
+template <int DT, int MODE, bool VEC>
+__global__ __launch_bounds__(64 * DOT_W, 2) void k_dot(DotArgs a) {
+  __shared__ unsigned long long slots[DOT_W * 2 * DOT_SET];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  unsigned long long* const pos = slots + wave * 2 * DOT_SET + lane;
+#pragma unroll
+  for (int j = 0; j < 2 * ND; ++j) pos[j * 64] = 0ull;
+  // no barrier here: a lane touches only its own slots until the end
   const int64_t nthreads = static_cast<int64_t>(gridDim.x) * blockDim.x;
   const int64_t tid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   constexpr int EPV = DT == DET_F32 ? 4 : 8;         // elements per 16-byte load
@@ -1753,22 +1796,24 @@ __global__ __launch_bounds__(64 * DOT_W) void k_dot(DotArgs a) {
   if (VEC) {
     const uint4* const va = static_cast<const uint4*>(a.a);
     const uint4* const vb = static_cast<const uint4*>(a.b);
-    const int64_t nv = a.n / EPV;
-    for (int64_t c0 = tid; c0 < nv; c0 += nthreads * DOT_U) {
+    const int64_t nv = a.n / EPV, jump = nthreads * DOT_U;
+    if (tid < nv) {
       uint4 ra[DOT_U], rb[DOT_U];
+      dot_load<DT, MODE>(va, vb, tid, nthreads, nv - 1, ra, rb);
+      for (int64_t c = tid; c < nv; c += jump) {
+        uint4 na[DOT_U], nb[DOT_U];
+        dot_load<DT, MODE>(va, vb, c + jump, nthreads, nv - 1, na, nb);
 #pragma unroll
-      for (int u = 0; u < DOT_U; ++u) {
-        const int64_t c = min(c0 + u * nthreads, nv - 1);            // clamped: always in bounds
-        ra[u] = va[c];
-        if (MODE != DOT_SQUARE) rb[u] = vb[c];
-      }
+        for (int u = 0; u < DOT_U; ++u) {
+          if (c + u * nthreads < nv) {
 #pragma unroll
-      for (int u = 0; u < DOT_U; ++u) {
-        if (c0 + u * nthreads >= nv) break;
+            for (int e = 0; e < EPV; ++e)
+              dot_elem<DT, MODE>(pos, dot_word_elem<DT>(ra[u], e),
+                                 MODE != DOT_SQUARE ? dot_word_elem<DT>(rb[u], e) : 0u);
+          }
+        }
 #pragma unroll
-        for (int e = 0; e < EPV; ++e)
-          dot_elem<DT, MODE>(my, dot_word_elem<DT>(ra[u], e),
-                             MODE != DOT_SQUARE ? dot_word_elem<DT>(rb[u], e) : 0u);
+        for (int u = 0; u < DOT_U; ++u) { ra[u] = na[u]; rb[u] = nb[u]; }
       }
     }
     done = nv * EPV;
@@ -1776,15 +1821,18 @@ __global__ __launch_bounds__(64 * DOT_W) void k_dot(DotArgs a) {
   for (int64_t i = done + tid; i < a.n; i += nthreads) {
     const uint32_t x = load_elem<DT>(a.a, i * a.inc_a);
     const uint32_t y = MODE != DOT_SQUARE ? load_elem<DT>(a.b, i * a.inc_b) : 0u;
-    dot_elem<DT, MODE>(my, x, y);
+    dot_elem<DT, MODE>(pos, x, y);
   }
   __syncthreads();
-  // digit j: lane l adds the slots of lane l of every wave, then the wave
-  // adds its 64 lanes; digit 18 holds only zeros for finite inputs
+  // digit j: lane l adds slot j of lane l of every wave (positive minus
+  // negative), then the wave adds its 64 lanes
   for (int j = wave; j < ND; j += DOT_W) {
     int64_t s = 0;
 #pragma unroll
-    for (int w = 0; w < DOT_W; ++w) s += static_cast<int64_t>(slots[(w * DOT_SLOTS + j) * 64 + lane]);
+    for (int w = 0; w < DOT_W; ++w) {
+      const unsigned long long* const q = slots + w * 2 * DOT_SET + j * 64 + lane;
+      s += static_cast<int64_t>(q[0]) - static_cast<int64_t>(q[DOT_SET]);
+    }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
     if (lane == 0 && s != 0)
@@ -1824,7 +1872,7 @@ template <int DT, int MODE>
 void launch_dot(const DotArgs& a, bool vec, hipStream_t s) {
   constexpr int EPV = DT == DET_F32 ? 4 : 8;
   const int64_t per_block = static_cast<int64_t>(64) * DOT_W * (vec ? EPV * DOT_U : 4);
-  const dim3 grid(grid_for(a.n, per_block, 2048)), block(64 * DOT_W);
+  const dim3 grid(grid_for(a.n, per_block, 512)), block(64 * DOT_W);     // two per CU
   if (vec) hipLaunchKernelGGL((k_dot<DT, MODE, true>), grid, block, 0, s, a);
   else hipLaunchKernelGGL((k_dot<DT, MODE, false>), grid, block, 0, s, a);
 }

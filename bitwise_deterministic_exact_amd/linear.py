@@ -86,7 +86,7 @@ class _DetLinearFn(torch.autograd.Function):
         db = None
         if ctx.has_bias and ctx.needs_input_grad[2]:
             ones = torch.ones((1, g.shape[0]), dtype=g.dtype, device=g.device)
-            db32 = gemm_any_k(g.t(), ones, check_finite=False)        # [out, 1], K = T
+            db32 = gemm_any_k(ones, g.t(), check_finite=False)        # [1, out], K = T
             db = _to_dtype(db32.reshape(-1), weight.dtype)
         return dx, dw, db, None
 

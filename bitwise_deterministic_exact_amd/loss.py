@@ -33,7 +33,7 @@ class _ExactMSE(torch.autograd.Function):
         ctx.has_target = t is not None
         # a true fp32 division by a device tensor: torch turns a division by
         # a host scalar into a product with its rounded reciprocal
-        n = torch.tensor(float(max(y.numel(), 1)), dtype=torch.float32, device=s.device)
+        n = torch.full((), float(max(y.numel(), 1)), dtype=torch.float32, device=s.device)
         return s / n
 
     @staticmethod
