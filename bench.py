@@ -41,16 +41,17 @@ KERNEL_SOURCE = os.path.join(ROOT, "bitwise_deterministic_exact_amd", "csrc", "d
 PROFILE_RECORD = os.path.join(ROOT, "profiles", "k_gemm8_f32_4096_wide.md")
 
 
-def profile_record():
-    """The GEMM kernel's per-launch counters from the committed rocprofv3
-    summary (its `profile-record:` line): VALU instructions, FETCH_SIZE and
-    WRITE_SIZE with the copy calibration, and whether the kernel source is
-    still the one they were taken on.  None if there is no record."""
+def profile_record(path: str = PROFILE_RECORD, kernel: str = None):
+    """A kernel's per-launch counters from a committed rocprofv3 summary (its
+    `profile-record:` line, the first one or the one naming `kernel`): VALU
+    instructions, FETCH_SIZE and WRITE_SIZE with the copy calibration, and
+    whether the kernel source is still the one they were taken on.  None if
+    there is no record."""
     import hashlib
     try:
-        with open(PROFILE_RECORD) as f:
-            line = next(l for l in f if l.startswith("profile-record:"))
-        rec = json.loads(line.split(":", 1)[1])
+        with open(path) as f:
+            recs = [json.loads(l.split(":", 1)[1]) for l in f if l.startswith("profile-record:")]
+        rec = next(r for r in recs if kernel is None or r["kernel"] == kernel)
         with open(KERNEL_SOURCE, "rb") as f:
             rec["current"] = hashlib.sha256(f.read()).hexdigest() == rec["source_sha256"]
         return rec
@@ -335,13 +336,18 @@ def loss_workload(det, c_oracle, dev, steps, warmup) -> dict:
     s32 = np.array([c_oracle.finalize(_digits_of(exact))[0]], dtype=np.uint32).view(np.float32)[0]
     want = int(np.array([np.float32(s32) / np.float32(n)], dtype=np.float32).view(np.uint32)[0])
     nbytes = 2 * 4 * n
+    rec = profile_record(os.path.join(ROOT, "profiles", "k_dot_f32_loss_8192x4096.md"),
+                         "k_dot<f32, squared difference>")
+    traffic = (int((rec["fetch_kib"] * rec["fetch_scale"] + rec["write_kib"] * rec["write_scale"]) * 1024)
+               if rec and rec["current"] and rec["bytes"] == nbytes else None)
     return dict(metric="exact MSE loss, GB/s of operands (f32 8192x4096 prediction and target)",
                 value=round(nbytes / (ms_loss * 1e-3) / 1e9, 1), unit="GB/s", ms_per_step=round(ms_loss, 4),
                 dtype="int64",
                 roofline={"bound": "hbm", "kernel": "k_dot<f32, squared difference> (+ the digit clear)",
                           "achieved": round(nbytes / (ms_digits * 1e-3) / 1e9, 1), "peak": HBM_PEAK / 1e9,
                           "unit": "GB/s", "frac": round(nbytes / (ms_digits * 1e-3) / HBM_PEAK, 4),
-                          "traffic": None, "bytes": "8 n: both operands read once"},
+                          "traffic": traffic, "bytes": "8 n: both operands read once",
+                          "profile_current": bool(rec and rec["current"])},
                 dot={"kernel": "k_dot<f32, a*b>", "ms": round(ms_dot, 4),
                      "GB/s": round(nbytes / (ms_dot * 1e-3) / 1e9, 1),
                      "frac": round(nbytes / (ms_dot * 1e-3) / HBM_PEAK, 4)},
