@@ -1066,7 +1066,7 @@ __device__ __forceinline__ void stat_elem(uint32_t b, int& top, int& low) {
 
 // KMAJ (unit K stride): one wave per row and 1024-element K range, lanes
 // along K; otherwise one thread per row and 256-element K range, lanes along
-// the rows
+// the rows (coalesced for a transposed view), 16 loads in flight
 template <int DT, bool KMAJ>
 __global__ __launch_bounds__(256) void k_slice_stats(SliceStatArgs a) {
   int top = SL_TOP_NONE, low = SL_LOW_NONE;
@@ -1096,7 +1096,14 @@ __global__ __launch_bounds__(256) void k_slice_stats(SliceStatArgs a) {
     if (t >= a.R * nkr) return;
     row = t % a.R;
     const int64_t k0 = (t / a.R) * 256, k1 = min(k0 + 256, a.K);
-    for (int64_t k = k0; k < k1; ++k) stat_elem<DT>(load_elem<DT>(a.p, row * a.s_r + k * a.s_k), top, low);
+    for (int64_t kb = k0; kb < k1; kb += 16) {
+      uint32_t e[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)            // clamped: a repeated element leaves max and min as they are
+        e[u] = load_elem<DT>(a.p, row * a.s_r + min(kb + u, k1 - 1) * a.s_k);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) stat_elem<DT>(e[u], top, low);
+    }
     lead = true;
   }
   if (lead && top != SL_TOP_NONE) {
@@ -1171,8 +1178,7 @@ struct TailArgs {
   const int32_t* list; int64_t n;         // its listed rows
   const int32_t* top; int S;
   int32_t* cnt;                           // tails per listed row
-  const int32_t* off;                     // k_tail_fill: each row's place in tk (-1: not kept)
-  int32_t* tk;                            // k_tail_fill: the tails' k, row by row, increasing
+  int32_t* tk;                            // listed row p's first SL_TAIL_CAP tails' k at p * SL_TAIL_CAP
 };
 
 template <int DT>
@@ -1184,14 +1190,15 @@ __device__ __forceinline__ bool is_tail(uint32_t b, int base) {
   return m != 0u && ex + __ffs(static_cast<int>(m)) - 1 < base;
 }
 
-// one wave per listed row: count its tails (FILL: write their k in order)
-template <int DT, bool FILL>
+// one wave per listed row: count its tails and write the k of the first
+// SL_TAIL_CAP of them, in increasing order, into the row's slot of tk
+template <int DT>
 __global__ __launch_bounds__(256) void k_tail_scan(TailArgs a) {
   const int64_t p = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) >> 6;
   const int lane = threadIdx.x & 63;
   if (p >= a.n) return;                                   // uniform per wave
-  if (FILL && a.off[p] < 0) return;
   const int64_t r = a.list[p];
+  int32_t* const tk = a.tk + p * SL_TAIL_CAP;
   const int base = a.top[r] + 3 - 8 * a.S;
   int64_t c = 0;
   for (int64_t k0 = 0; k0 < a.K; k0 += 1024) {
@@ -1205,48 +1212,38 @@ __global__ __launch_bounds__(256) void k_tail_scan(TailArgs a) {
     for (int u = 0; u < 16; ++u) {
       const bool t = is_tail<DT>(e[u], base);
       const unsigned long long bal = __ballot(t);
-      if (FILL && t)
-        a.tk[a.off[p] + c + __popcll(bal & ((1ull << lane) - 1ull))] = static_cast<int32_t>(k0 + 64 * u + lane);
+      const int64_t at = c + __popcll(bal & ((1ull << lane) - 1ull));
+      if (t && at < SL_TAIL_CAP) tk[at] = static_cast<int32_t>(k0 + 64 * u + lane);
       c += __popcll(bal);
     }
   }
-  if (!FILL && lane == 0) a.cnt[p] = static_cast<int32_t>(c);
+  if (lane == 0) a.cnt[p] = static_cast<int32_t>(c);
 }
 
-// off[p] = place of row p's tails in tk (rows with more than SL_TAIL_CAP get
-// -1), ovl[] = the original indices of those rows, in order (one workgroup)
+// off[p] = place of listed row p's tails in tk (its fixed slot; -1 for rows
+// with more than SL_TAIL_CAP tails), ovl[] = the original indices of those
+// rows, in order (one workgroup)
 __global__ __launch_bounds__(1024) void k_tail_plan(const int32_t* cnt, const int32_t* list, int64_t n,
                                                     int32_t* off, int32_t* ovl) {
-  __shared__ int64_t wsum[16], wover[16];
-  __shared__ int64_t base, obase;
+  __shared__ int64_t wover[16];
+  __shared__ int64_t obase;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (threadIdx.x == 0) base = obase = 0;
+  if (threadIdx.x == 0) obase = 0;
   __syncthreads();
   for (int64_t p0 = 0; p0 < n; p0 += 1024) {
     const int64_t p = p0 + threadIdx.x;
-    const int c = p < n ? cnt[p] : 0;
-    const bool over = p < n && c > SL_TAIL_CAP;
-    const int64_t kept = over ? 0 : c;
-    // wave-level inclusive scan of kept tails
-    int64_t v = kept;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int64_t u = __shfl_up(v, o);
-      if (lane >= o) v += u;
-    }
+    const bool over = p < n && cnt[p] > SL_TAIL_CAP;
     const unsigned long long bal = __ballot(over);
-    if (lane == 63) wsum[wave] = v;
     if (lane == 0) wover[wave] = __popcll(bal);
     __syncthreads();
-    int64_t b = base, ob = obase;
-    for (int w = 0; w < wave; ++w) { b += wsum[w]; ob += wover[w]; }
-    if (p < n) off[p] = over ? -1 : static_cast<int32_t>(b + v - kept);
+    int64_t ob = obase;
+    for (int w = 0; w < wave; ++w) ob += wover[w];
+    if (p < n) off[p] = over ? -1 : static_cast<int32_t>(p * SL_TAIL_CAP);
     if (over) ovl[ob + __popcll(bal & ((1ull << lane) - 1ull))] = list[p];
     __syncthreads();
     if (threadIdx.x == 0) {
-      int64_t t = base, ot = obase;
-      for (int w = 0; w < 16; ++w) { t += wsum[w]; ot += wover[w]; }
-      base = t;
+      int64_t ot = obase;
+      for (int w = 0; w < 16; ++w) ot += wover[w];
       obase = ot;
     }
     __syncthreads();
@@ -2276,9 +2273,11 @@ det_status launch_sliced(GemmArgs a, char* ws, bool only_slices, int forced, hip
     TailArgs t{};
     t.S = S;
     t.p = a.x; t.K = K; t.s_r = a.x_sm; t.s_k = a.x_sk; t.list = listx; t.n = fx; t.top = topx; t.cnt = cntx;
-    if (fx > 0) hipLaunchKernelGGL((k_tail_scan<DT, false>), dim3(grid_for(fx * 64, 256, 1u << 30)), dim3(256), 0, s, t);
+    t.tk = tkx;
+    if (fx > 0) hipLaunchKernelGGL((k_tail_scan<DT>), dim3(grid_for(fx * 64, 256, 1u << 30)), dim3(256), 0, s, t);
     t.p = a.w; t.s_r = a.w_sn; t.s_k = a.w_sk; t.list = listw; t.n = fw; t.top = topw; t.cnt = cntw;
-    if (fw > 0) hipLaunchKernelGGL((k_tail_scan<DT, false>), dim3(grid_for(fw * 64, 256, 1u << 30)), dim3(256), 0, s, t);
+    t.tk = tkw;
+    if (fw > 0) hipLaunchKernelGGL((k_tail_scan<DT>), dim3(grid_for(fw * 64, 256, 1u << 30)), dim3(256), 0, s, t);
     st = hip_check(hipGetLastError(), "tail count launch");
     if (st == DET_OK && fx > 0)
       st = hip_check(hipMemcpyAsync(cx.data(), cntx, 4 * fx, hipMemcpyDeviceToHost, s), "tail count copy");
@@ -2329,12 +2328,6 @@ det_status launch_sliced(GemmArgs a, char* ws, bool only_slices, int forced, hip
   for (int32_t c : cw) ow += c > SL_TAIL_CAP;
   hipLaunchKernelGGL(k_tail_plan, dim3(1), dim3(1024), 0, s, cntx, listx, fx, offx, ovlx);
   hipLaunchKernelGGL(k_tail_plan, dim3(1), dim3(1024), 0, s, cntw, listw, fw, offw, ovlw);
-  TailArgs t{};
-  t.S = S;
-  t.p = a.x; t.K = K; t.s_r = a.x_sm; t.s_k = a.x_sk; t.list = listx; t.n = fx; t.top = topx; t.off = offx; t.tk = tkx;
-  if (fx > 0) hipLaunchKernelGGL((k_tail_scan<DT, true>), dim3(grid_for(fx * 64, 256, 1u << 30)), dim3(256), 0, s, t);
-  t.p = a.w; t.s_r = a.w_sn; t.s_k = a.w_sk; t.list = listw; t.n = fw; t.top = topw; t.off = offw; t.tk = tkw;
-  if (fw > 0) hipLaunchKernelGGL((k_tail_scan<DT, true>), dim3(grid_for(fw * 64, 256, 1u << 30)), dim3(256), 0, s, t);
   SliceFixArgs f{};
   f.x = a.x; f.x_sm = a.x_sm; f.x_sk = a.x_sk;
   f.w = a.w; f.w_sn = a.w_sn; f.w_sk = a.w_sk;
