@@ -20,7 +20,6 @@
 
 #include <atomic>
 #include <type_traits>
-#include <vector>
 
 #include "detgemm.h"
 
@@ -964,21 +963,32 @@ __global__ __launch_bounds__(256) void k_finalize(const int64_t* __restrict__ ac
   y[i] = __uint_as_float(round_digits_to_f32(dg));
 }
 
+__device__ __forceinline__ uint32_t round_bits_bf16(uint32_t b) {
+  if ((b & 0x7F800000u) == 0x7F800000u && (b & 0x7FFFFFu))
+    return (b >> 16) | 0x40u;                                // NaN stays a (quiet) NaN
+  // nearest-even on the bit pattern: add half an ulp minus one, plus the
+  // lowest kept bit, then truncate; exact for every finite value and carries
+  // into the exponent (up to Inf) where it must
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// VEC: 8 elements per thread (two 16-byte loads, one 16-byte store; both
+// pointers 16-byte aligned), the last n mod 8 by the scalar form
+template <bool VEC>
 __global__ __launch_bounds__(256) void k_round_bf16(const uint32_t* __restrict__ in, uint16_t* __restrict__ out,
                                                      int64_t n) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const uint32_t b = in[i];
-  uint16_t r;
-  if ((b & 0x7F800000u) == 0x7F800000u && (b & 0x7FFFFFu)) {
-    r = static_cast<uint16_t>((b >> 16) | 0x40u);            // NaN stays a (quiet) NaN
+  if (VEC) {
+    if (i >= n / 8) return;
+    const uint4 a = reinterpret_cast<const uint4*>(in)[2 * i];
+    const uint4 b = reinterpret_cast<const uint4*>(in)[2 * i + 1];
+    reinterpret_cast<uint4*>(out)[i] =
+        make_uint4(round_bits_bf16(a.x) | (round_bits_bf16(a.y) << 16), round_bits_bf16(a.z) | (round_bits_bf16(a.w) << 16),
+                   round_bits_bf16(b.x) | (round_bits_bf16(b.y) << 16), round_bits_bf16(b.z) | (round_bits_bf16(b.w) << 16));
   } else {
-    // nearest-even on the bit pattern: add half an ulp minus one, plus the
-    // lowest kept bit, then truncate; exact for every finite value and
-    // carries into the exponent (up to Inf) where it must
-    r = static_cast<uint16_t>((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+    if (i >= n) return;
+    out[i] = static_cast<uint16_t>(round_bits_bf16(in[i]));
   }
-  out[i] = r;
 }
 
 template <int DT>
@@ -1112,11 +1122,13 @@ __global__ __launch_bounds__(256) void k_slice_stats(SliceStatArgs a) {
   }
 }
 
-__global__ __launch_bounds__(256) void k_slice_init(int32_t* top, int32_t* low, int64_t n, int32_t* hist) {
+__global__ __launch_bounds__(256) void k_slice_init(int32_t* top, int32_t* low, int32_t* cnt, int64_t n,
+                                                    int32_t* hist) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
     top[i] = SL_TOP_NONE;
     low[i] = SL_LOW_NONE;
+    cnt[i] = 0;
   }
   if (blockIdx.x == 0 && threadIdx.x < 2 * SL_HIST) hist[threadIdx.x] = 0;
 }
@@ -1190,34 +1202,45 @@ __device__ __forceinline__ bool is_tail(uint32_t b, int base) {
   return m != 0u && ex + __ffs(static_cast<int>(m)) - 1 < base;
 }
 
-// one wave per listed row: count its tails and write the k of the first
-// SL_TAIL_CAP of them, in increasing order, into the row's slot of tk
+// one wave per listed row and 1024-element K range: count the range's tails
+// into the row's count (zeroed by k_slice_init) and write their k into the
+// row's slot of tk at the places one atomic add reserved, as long as they
+// fall within its first SL_TAIL_CAP (a row with more is recomputed whole,
+// and the order of its tails does not matter to the exact sum)
 template <int DT>
 __global__ __launch_bounds__(256) void k_tail_scan(TailArgs a) {
-  const int64_t p = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) >> 6;
+  const int64_t wid = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) >> 6;
   const int lane = threadIdx.x & 63;
-  if (p >= a.n) return;                                   // uniform per wave
+  const int64_t nkr = (a.K + 1023) / 1024;
+  if (wid >= a.n * nkr) return;                           // uniform per wave
+  const int64_t p = wid / nkr, k0 = (wid % nkr) * 1024;
   const int64_t r = a.list[p];
-  int32_t* const tk = a.tk + p * SL_TAIL_CAP;
   const int base = a.top[r] + 3 - 8 * a.S;
-  int64_t c = 0;
-  for (int64_t k0 = 0; k0 < a.K; k0 += 1024) {
-    uint32_t e[16];
+  uint32_t e[16];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int64_t k = k0 + 64 * u + lane;
-      e[u] = k < a.K ? load_elem<DT>(a.p, r * a.s_r + k * a.s_k) : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const bool t = is_tail<DT>(e[u], base);
-      const unsigned long long bal = __ballot(t);
-      const int64_t at = c + __popcll(bal & ((1ull << lane) - 1ull));
-      if (t && at < SL_TAIL_CAP) tk[at] = static_cast<int32_t>(k0 + 64 * u + lane);
-      c += __popcll(bal);
-    }
+  for (int u = 0; u < 16; ++u) {
+    const int64_t k = k0 + 64 * u + lane;
+    e[u] = k < a.K ? load_elem<DT>(a.p, r * a.s_r + k * a.s_k) : 0u;
   }
-  if (lane == 0) a.cnt[p] = static_cast<int32_t>(c);
+  unsigned long long bal[16];
+  int total = 0;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    bal[u] = __ballot(is_tail<DT>(e[u], base));
+    total += __popcll(bal[u]);
+  }
+  if (total == 0) return;                                 // uniform per wave
+  int at0 = 0;
+  if (lane == 0) at0 = atomicAdd(a.cnt + p, total);
+  int64_t c = __shfl(at0, 0);
+  int32_t* const tk = a.tk + p * SL_TAIL_CAP;
+  const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int64_t at = c + __popcll(bal[u] & below);
+    if (((bal[u] >> lane) & 1ull) && at < SL_TAIL_CAP) tk[at] = static_cast<int32_t>(k0 + 64 * u + lane);
+    c += __popcll(bal[u]);
+  }
 }
 
 // off[p] = place of listed row p's tails in tk (its fixed slot; -1 for rows
@@ -1364,6 +1387,42 @@ struct SliceMakeArgs {
   int vec;
 };
 
+// the S balanced 8-bit digits of 16 elements of one row (window bottom
+// `base`), packed four to a word: digit s of element j in byte j mod 4 of
+// d[s][j div 4]
+template <int DT>
+__device__ __forceinline__ void slice_digits(const uint32_t (&e)[16], int base, int S, uint32_t (&d)[SL_MAX][4]) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    bool neg;
+    uint32_t m;
+    int ex;
+    split_elem<DT>(e[j], neg, m, ex);
+    const int sh = ex - base;
+    if (m == 0u || sh + __ffs(static_cast<int>(m)) - 1 < 0) continue;    // zero, or below the window
+    int64_t v = sh >= 0 ? static_cast<int64_t>(m) << sh : static_cast<int64_t>(m >> (-sh));
+    if (neg) v = -v;
+#pragma unroll
+    for (int s = 0; s < SL_MAX; ++s) {
+      if (s < S) {
+        const int64_t dig = static_cast<int8_t>(static_cast<uint8_t>(v & 0xFF));
+        v = (v - dig) >> 8;
+        d[s][j >> 2] |= (static_cast<uint32_t>(dig) & 0xFFu) << (8 * (j & 3));
+      }
+    }
+  }
+}
+
+// fragment `blk` of the output, the lane's 16 bytes of each digit
+__device__ __forceinline__ void slice_store(const SliceMakeArgs& a, int64_t blk, int lane,
+                                            const uint32_t (&d)[SL_MAX][4]) {
+#pragma unroll
+  for (int s = 0; s < SL_MAX; ++s)
+    if (s < a.S)
+      *reinterpret_cast<uint4*>(a.out + ((blk * a.S + s) * 64 + lane) * 16) =
+          make_uint4(d[s][0], d[s][1], d[s][2], d[s][3]);
+}
+
 template <int DT>
 __global__ __launch_bounds__(256) void k_slice_make(SliceMakeArgs a) {
   const int64_t total = a.Rb * a.Kb * 64;
@@ -1401,32 +1460,46 @@ __global__ __launch_bounds__(256) void k_slice_make(SliceMakeArgs a) {
         for (int j = 0; j < 16; ++j)
           e[j] = k0 + j < a.K ? load_elem<DT>(a.p, row * a.s_r + (k0 + j) * a.s_k) : 0u;
       }
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        bool neg;
-        uint32_t m;
-        int ex;
-        split_elem<DT>(e[j], neg, m, ex);
-        const int sh = ex - base;
-        if (m == 0u || sh + __ffs(static_cast<int>(m)) - 1 < 0) continue;    // zero, or below the window
-        int64_t v = sh >= 0 ? static_cast<int64_t>(m) << sh : static_cast<int64_t>(m >> (-sh));
-        if (neg) v = -v;
-#pragma unroll
-        for (int s = 0; s < SL_MAX; ++s) {
-          if (s < a.S) {
-            const int64_t dig = static_cast<int8_t>(static_cast<uint8_t>(v & 0xFF));
-            v = (v - dig) >> 8;
-            d[s][j >> 2] |= (static_cast<uint32_t>(dig) & 0xFFu) << (8 * (j & 3));
-          }
-        }
-      }
+      slice_digits<DT>(e, base, a.S, d);
     }
-#pragma unroll
-    for (int s = 0; s < SL_MAX; ++s)
-      if (s < a.S)
-        *reinterpret_cast<uint4*>(a.out + ((blk * a.S + s) * 64 + lane) * 16) =
-            make_uint4(d[s][0], d[s][1], d[s][2], d[s][3]);
+    slice_store(a, blk, lane, d);
   }
+}
+
+// The same digits for an operand with unit row stride and K stride > 1 (a
+// transposed view): a workgroup takes 64 rows (four 16-row blocks) by 64 k,
+// reads them with the 64 rows along the lanes of a wave (one contiguous run
+// per load), and hands each wave its block's elements through LDS.  The tile's rows are padded to 65 words,
+// so the 16 k-runs a wave reads lie in four different bank quarters.
+template <int DT>
+__global__ __launch_bounds__(256) void k_slice_make_t(SliceMakeArgs a) {
+  __shared__ uint32_t tile[64][65];
+  const int64_t rb4 = blockIdx.x / a.Kb, kb = blockIdx.x % a.Kb;
+  const int t = threadIdx.x;
+  {
+    const int rl = t & 63, kq = t >> 6;                   // row of the tile (lane), quarter of its k
+    const int64_t row = rb4 * 64 + rl;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kl = kq * 16 + i;
+      const int64_t k = kb * 64 + kl;
+      tile[kl][rl] = row < a.R && k < a.K ? load_elem<DT>(a.p, row + k * a.s_k) : 0u;
+    }
+  }
+  __syncthreads();
+  const int lane = t & 63, wave = t >> 6;
+  const int rl = wave * 16 + (lane & 15), k0 = (lane >> 4) * 16;
+  const int64_t rb = rb4 * 4 + wave, row = rb * 16 + (lane & 15);
+  uint32_t d[SL_MAX][4];
+#pragma unroll
+  for (int s = 0; s < SL_MAX; ++s) d[s][0] = d[s][1] = d[s][2] = d[s][3] = 0u;
+  if (row < a.R) {
+    uint32_t e[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) e[j] = tile[k0 + j][rl];
+    slice_digits<DT>(e, a.top[row] + 3 - 8 * a.S, a.S, d);
+  }
+  slice_store(a, rb * a.Kb + kb, lane, d);
 }
 
 // RNE(z * 2^e2) as binary32 bits (gradual underflow, overflow to inf; z = 0
@@ -2102,6 +2175,41 @@ constexpr double SLICE_MIN_MACS = 134217728.0;    // 2^27: below, the accumulato
 
 std::atomic<int> g_path{DET_PATH_AUTO};
 std::atomic<int> g_forced_slices{0};
+// Pinned host buffers for the matrix-core path's two readbacks (the span
+// histogram and the tail counts), per calling thread, grown on demand and
+// kept until the process ends: a copy into pinned memory is asynchronous,
+// while one into pageable memory makes the host wait for it.  Every call has
+// waited for its own copies before it returns, so a buffer is never replaced
+// while a copy into it is in flight.
+struct Pinned {
+  int32_t* p = nullptr;
+  size_t n = 0;
+};
+thread_local Pinned g_pin_hist, g_pin_cnt;
+
+int32_t* pinned(Pinned& b, size_t n) {
+  if (b.n < n) {
+    if (b.p != nullptr) (void)hipHostFree(b.p);
+    b.p = nullptr;
+    b.n = 0;
+    void* q = nullptr;
+    if (hipHostMalloc(&q, n * sizeof(int32_t), hipHostMallocDefault) != hipSuccess) return nullptr;
+    b.p = static_cast<int32_t*>(q);
+    b.n = n;
+  }
+  return b.p;
+}
+
+// wait for an event by polling it: the readbacks are short and each one
+// holds up the launches that follow it
+det_status poll_event(hipEvent_t ev, const char* what) {
+  for (;;) {
+    const hipError_t q = hipEventQuery(ev);
+    if (q == hipSuccess) return DET_OK;
+    if (q != hipErrorNotReady) return hip_check(q, what);
+  }
+}
+
 thread_local det_path g_plan_path = DET_PATH_ACCUMULATOR;
 thread_local int g_plan_slices = 0;
 thread_local int64_t g_plan_rows = 0, g_plan_cols = 0;
@@ -2184,7 +2292,10 @@ det_status slice_make(const void* p, int64_t R, int64_t K, int64_t s_r, int64_t 
   a.Rb = rows_padded / 16; a.Kb = round_up(K, 2 * SL_KB) / SL_KB;
   a.S = S;
   a.vec = s_k == 1 && (reinterpret_cast<uintptr_t>(p) % 16) == 0 && (s_r * esz) % 16 == 0;
-  hipLaunchKernelGGL((k_slice_make<DT>), dim3(grid_for(a.Rb * a.Kb * 64, 256, 16384)), dim3(256), 0, s, a);
+  if (s_r == 1 && s_k > 1)      // a transposed view: through LDS (Rb is a multiple of 8)
+    hipLaunchKernelGGL((k_slice_make_t<DT>), dim3(static_cast<unsigned>(a.Rb / 4 * a.Kb)), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_slice_make<DT>), dim3(grid_for(a.Rb * a.Kb * 64, 256, 16384)), dim3(256), 0, s, a);
   return hip_check(hipGetLastError(), "slice make launch");
 }
 
@@ -2236,7 +2347,8 @@ det_status launch_sliced(GemmArgs a, char* ws, bool only_slices, int forced, hip
   r8 += 4 * SL_TAIL_CAP * (M + N);
   int64_t* const zfix = reinterpret_cast<int64_t*>(r8);
 
-  hipLaunchKernelGGL(k_slice_init, dim3(grid_for(M + N, 256, 1024)), dim3(256), 0, s, topx, lowx, M + N, hist);
+  hipLaunchKernelGGL(k_slice_init, dim3(grid_for(M + N, 256, 1024)), dim3(256), 0, s, topx, lowx, cntx, M + N,
+                     hist);
   det_status st = hip_check(hipGetLastError(), "slice init launch");
   if (st == DET_OK) st = slice_stats<DT>(a.x, M, K, a.x_sm, a.x_sk, topx, lowx, s);
   if (st == DET_OK) st = slice_stats<DT>(a.w, N, K, a.w_sn, a.w_sk, topw, loww, s);
@@ -2246,9 +2358,15 @@ det_status launch_sliced(GemmArgs a, char* ws, bool only_slices, int forced, hip
                      hist + SL_HIST);
   st = hip_check(hipGetLastError(), "slice need launch");
   if (st != DET_OK) return st;
-  int32_t h[2 * SL_HIST];
-  st = hip_check(hipMemcpyAsync(h, hist, sizeof h, hipMemcpyDeviceToHost, s), "span histogram copy");
-  if (st == DET_OK) st = hip_check(hipStreamSynchronize(s), "span histogram sync");
+  int32_t* const h = pinned(g_pin_hist, 2 * SL_HIST);
+  if (h == nullptr) return fail(DET_EHIP, "pinned host buffer for the span histogram");
+  hipEvent_t ready = nullptr;
+  st = hip_check(hipMemcpyAsync(h, hist, 2 * SL_HIST * sizeof(int32_t), hipMemcpyDeviceToHost, s),
+                 "span histogram copy");
+  if (st == DET_OK) st = hip_check(hipEventCreateWithFlags(&ready, hipEventDisableTiming), "event create");
+  if (st == DET_OK) st = hip_check(hipEventRecord(ready, s), "event record");
+  if (st == DET_OK) st = poll_event(ready, "span histogram wait");
+  if (ready != nullptr) (void)hipEventDestroy(ready);
   if (st != DET_OK) return st;
 
   int64_t fx = 0, fw = 0;
@@ -2267,26 +2385,30 @@ det_status launch_sliced(GemmArgs a, char* ws, bool only_slices, int forced, hip
     if (st != DET_OK) return st;
   }
   // tails per listed row, read back while the matrix-core pass runs
-  std::vector<int32_t> cx(static_cast<size_t>(fx)), cw(static_cast<size_t>(fw));
+  int32_t* const cx = tails ? pinned(g_pin_cnt, static_cast<size_t>(fx + fw)) : nullptr;
+  int32_t* const cw = cx != nullptr ? cx + fx : nullptr;
+  if (tails && cx == nullptr) return fail(DET_EHIP, "pinned host buffer for the tail counts");
   hipEvent_t counted = nullptr;
   if (tails) {
     TailArgs t{};
     t.S = S;
     t.p = a.x; t.K = K; t.s_r = a.x_sm; t.s_k = a.x_sk; t.list = listx; t.n = fx; t.top = topx; t.cnt = cntx;
     t.tk = tkx;
-    if (fx > 0) hipLaunchKernelGGL((k_tail_scan<DT>), dim3(grid_for(fx * 64, 256, 1u << 30)), dim3(256), 0, s, t);
+    const int64_t nkr = (K + 1023) / 1024;
+    if (fx > 0) hipLaunchKernelGGL((k_tail_scan<DT>), dim3(grid_for(fx * nkr * 64, 256, 1u << 30)), dim3(256), 0, s, t);
     t.p = a.w; t.s_r = a.w_sn; t.s_k = a.w_sk; t.list = listw; t.n = fw; t.top = topw; t.cnt = cntw;
     t.tk = tkw;
-    if (fw > 0) hipLaunchKernelGGL((k_tail_scan<DT>), dim3(grid_for(fw * 64, 256, 1u << 30)), dim3(256), 0, s, t);
+    if (fw > 0) hipLaunchKernelGGL((k_tail_scan<DT>), dim3(grid_for(fw * nkr * 64, 256, 1u << 30)), dim3(256), 0, s, t);
     st = hip_check(hipGetLastError(), "tail count launch");
     if (st == DET_OK && fx > 0)
-      st = hip_check(hipMemcpyAsync(cx.data(), cntx, 4 * fx, hipMemcpyDeviceToHost, s), "tail count copy");
+      st = hip_check(hipMemcpyAsync(cx, cntx, 4 * fx, hipMemcpyDeviceToHost, s), "tail count copy");
     if (st == DET_OK && fw > 0)
-      st = hip_check(hipMemcpyAsync(cw.data(), cntw, 4 * fw, hipMemcpyDeviceToHost, s), "tail count copy");
+      st = hip_check(hipMemcpyAsync(cw, cntw, 4 * fw, hipMemcpyDeviceToHost, s), "tail count copy");
     if (st == DET_OK) st = hip_check(hipEventCreateWithFlags(&counted, hipEventDisableTiming), "event create");
     if (st == DET_OK) st = hip_check(hipEventRecord(counted, s), "event record");
     if (st != DET_OK) {
       if (counted) (void)hipEventDestroy(counted);
+      (void)hipStreamSynchronize(s);              // no copy into the pinned buffer outlives the call
       return st;
     }
   }
@@ -2319,13 +2441,13 @@ det_status launch_sliced(GemmArgs a, char* ws, bool only_slices, int forced, hip
     return st;
   }
   // the tail counts have been copied (the matrix-core pass may still run)
-  det_status sync_st = hip_check(hipEventSynchronize(counted), "tail count sync");
+  det_status sync_st = poll_event(counted, "tail count wait");
   (void)hipEventDestroy(counted);
   if (st == DET_OK) st = sync_st;
   if (st != DET_OK) return st;
   int64_t ox = 0, ow = 0;
-  for (int32_t c : cx) ox += c > SL_TAIL_CAP;
-  for (int32_t c : cw) ow += c > SL_TAIL_CAP;
+  for (int64_t i = 0; i < fx; ++i) ox += cx[i] > SL_TAIL_CAP;
+  for (int64_t i = 0; i < fw; ++i) ow += cw[i] > SL_TAIL_CAP;
   hipLaunchKernelGGL(k_tail_plan, dim3(1), dim3(1024), 0, s, cntx, listx, fx, offx, ovlx);
   hipLaunchKernelGGL(k_tail_plan, dim3(1), dim3(1024), 0, s, cntw, listw, fw, offw, ovlw);
   SliceFixArgs f{};
@@ -2509,8 +2631,17 @@ det_status det_round_f32_to_bf16(const float* in, uint16_t* out, int64_t n, void
   if (n < 0) return fail(DET_EINVAL, "negative count");
   if (n == 0) return DET_OK;
   if (in == nullptr || out == nullptr) return fail(DET_EINVAL, "null pointer");
-  hipLaunchKernelGGL(k_round_bf16, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), reinterpret_cast<const uint32_t*>(in), out, n);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint32_t* const b = reinterpret_cast<const uint32_t*>(in);
+  int64_t done = 0;
+  if (((reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out)) & 15u) == 0u && n >= 8) {
+    hipLaunchKernelGGL(k_round_bf16<true>, dim3(static_cast<unsigned>((n / 8 + 255) / 256)), dim3(256), 0, s, b,
+                       out, n);
+    done = n / 8 * 8;
+  }
+  if (done < n)
+    hipLaunchKernelGGL(k_round_bf16<false>, dim3(static_cast<unsigned>((n - done + 255) / 256)), dim3(256), 0, s,
+                       b + done, out + done, n - done);
   return hip_check(hipGetLastError(), "round launch");
 }
 

@@ -33,7 +33,10 @@
  * Conventions for every entry point:
  *   - All data pointers are DEVICE pointers owned by the caller.  The library
  *     allocates no device memory and keeps none between calls (the _ws
- *     variants use memory the caller passes in).
+ *     variants use memory the caller passes in).  The one host-side state
+ *     is two small pinned host buffers per calling thread, for the two
+ *     readbacks of det_gemm_ws's matrix-core path (128 bytes, and 4 bytes
+ *     per listed row); they grow on demand and live until the process ends.
  *   - Strides are in elements, must be >= 0, and may describe transposed or
  *     sliced views (e.g. x[:, a:b] or x^T).  Operand elements must be
  *     naturally aligned (4 bytes for f32, 2 for bf16).
@@ -41,7 +44,8 @@
  *     asynchronously and stream-ordered.  The one exception is det_gemm_ws
  *     when it considers the matrix-core path (see det_set_gemm_path): it
  *     waits for `stream` once, to read a 128-byte histogram, and with listed
- *     rows once more, for their tail counts.
+ *     rows once more, for their tail counts.  Both waits poll an event, so
+ *     the calling thread keeps a CPU core busy while it waits.
  *   - Argument errors are reported before anything is enqueued; on error
  *     nothing is written.  det_last_error() returns a message for the calling
  *     thread's most recent failure.

@@ -215,8 +215,15 @@ def test_round_f32_to_bf16_kernel():
         ((rng.integers(0, 2 ** 16, 4000, dtype=np.uint32) << 16) | 0x8000).view(np.float32),
         np.array([0.0, -0.0, 2.0 ** -149, 3.3895e38, 3.4e38, np.inf, -np.inf], dtype=np.float32)])
     v = v[~np.isnan(v)]
-    got = tensor_bits(det.round_f32_to_bf16(torch.from_numpy(v).cuda()))
-    assert np.array_equal(got, oracle.f32_bits_to_bf16_bits(v.view(np.uint32)))
+    want = oracle.f32_bits_to_bf16_bits(v.view(np.uint32))
+    t = torch.from_numpy(v).cuda()
+    got = tensor_bits(det.round_f32_to_bf16(t))
+    assert np.array_equal(got, want)
+    # 8 elements per thread on 16-byte aligned data, one at a time otherwise,
+    # and the last n mod 8 elements one at a time
+    for lo, hi in ((4, 4 + 8 * 1000), (1, 5003), (8, 15), (3, 4)):
+        got = tensor_bits(det.round_f32_to_bf16(t[lo:hi]))
+        assert np.array_equal(got, want[lo:hi]), (lo, hi)
 
 
 def test_nonfinite_inputs_rejected():
