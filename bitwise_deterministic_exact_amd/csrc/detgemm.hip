@@ -1602,10 +1602,20 @@ __device__ __forceinline__ void slice_copy(const int8_t* const (&src)[T::PER_WAV
                                        16, 0, 0);
 }
 
-// one 64-k step: product (s, t) of block (i, c) into its sum for s + t
+// one 64-k step: product (s, t) of block (i, c) into its sum for s + t.
+// The lowest digit plane holds only the bits of elements far below their
+// row's top, so its fragments are often all zero (on N(0,1) rows at S = 4,
+// most of them): a product with such a fragment adds nothing and is skipped.
+// The test is one ballot per fragment, uniform across the wave; a product
+// that ran anyway would add zero, so the sums never depend on it.
 template <int S, int CB>
 __device__ __forceinline__ void slice_steps(const v4i (&fa)[S][2], const v4i (&fb)[S][CB],
                                             v4i (&acc)[2 * S - 1][2][CB]) {
+  bool xa[2], wb[CB];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) xa[i] = __ballot((fa[0][i].x | fa[0][i].y | fa[0][i].z | fa[0][i].w) != 0) != 0ull;
+#pragma unroll
+  for (int c = 0; c < CB; ++c) wb[c] = __ballot((fb[0][c].x | fb[0][c].y | fb[0][c].z | fb[0][c].w) != 0) != 0ull;
 #pragma unroll
   for (int s = 0; s < S; ++s)
 #pragma unroll
@@ -1613,8 +1623,10 @@ __device__ __forceinline__ void slice_steps(const v4i (&fa)[S][2], const v4i (&f
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int c = 0; c < CB; ++c)
+        for (int c = 0; c < CB; ++c) {
+          if ((s == 0 && !xa[i]) || (t == 0 && !wb[c])) continue;
           acc[s + t][i][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[s][i], fb[t][c], acc[s + t][i][c], 0, 0, 0);
+        }
 }
 
 template <int S, int CB, int WR, int NBUF>
