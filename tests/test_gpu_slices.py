@@ -8,6 +8,8 @@ small shapes reach it, and cover ragged tiles, K past one 2^14 block, the
 recomputed rows and columns (their counts checked against the rule stated in
 include/detgemm.h), strided views, all-zero rows, and results that overflow,
 underflow or round at ties."""
+import threading
+
 import numpy as np
 import pytest
 import torch
@@ -230,3 +232,61 @@ def test_auto_path_matches_accumulator_path():
             assert plan["path"] == "slices"
         else:
             assert plan["path"] == "accumulator"
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_tails_spread_over_many_k_ranges(dt):
+    # listed rows whose tails lie in several 1024-long K ranges (each range's
+    # wave reserves its own places in the row's list), rows with just under
+    # and just over 256 tails, and the same for columns
+    rng = np.random.default_rng(600 + (dt == "bf16"))
+    M, N, K = 70, 90, 5000
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    w = rng.standard_normal((N, K), dtype=np.float32)
+    tiny = np.float32(2.0 ** -70)                      # below the window at S = 7 (f32) and 4 (bf16)
+    for r, n_t in ((3, 5), (10, 200), (11, 256), (12, 257), (40, 600)):
+        x[r, rng.choice(K, n_t, replace=False)] = tiny * rng.integers(1, 100, n_t)
+    for c, n_t in ((7, 9), (8, 250), (60, 300)):
+        w[c, rng.choice(K, n_t, replace=False)] = -tiny * rng.integers(1, 100, n_t)
+    conv = np_f32_bits if dt == "f32" else to_bf16_bits
+    xb, wb = conv(x), conv(w)
+    S = 7 if dt == "f32" else 4
+    plan = _check(xb, wb, dt, S, "spread tails")
+    assert plan["fallback_rows"] >= 5 and plan["fallback_cols"] >= 3
+
+
+def test_concurrent_calls_from_two_threads():
+    # each thread has its own readback buffers: two threads on their own
+    # streams, with different numbers of listed rows, get the oracle's bits
+    rng = np.random.default_rng(610)
+    cases = []
+    for t in range(2):
+        xb, wb = random_operands(rng, 300 + 50 * t, 260, 700, "bf16", "normal")
+        xw, _ = random_operands(rng, 300 + 50 * t, 260, 700, "bf16", "wide")
+        xb[:: 5 + 4 * t] = xw[:: 5 + 4 * t]                 # listed rows, some recomputed
+        cases.append((xb, wb))
+    want = [c_oracle.gemm(xb, wb) for xb, wb in cases]
+    det.set_gemm_path("slices", 4)
+    got = [[None] * 6, [None] * 6]
+    errors = []
+
+    def run(t):
+        try:
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                x, w = to_device(cases[t][0], "bf16"), to_device(cases[t][1], "bf16")
+                for i in range(6):
+                    got[t][i] = f32_bits(det.det_gemm(x, w))
+        except Exception as e:                              # reported below, in the main thread
+            errors.append(e)
+
+    announce("slices from two threads at once")
+    threads = [threading.Thread(target=run, args=(t,)) for t in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=120)
+    assert not errors, errors
+    for t in range(2):
+        for i in range(6):
+            assert np.array_equal(got[t][i], want[t]), (t, i, mismatch_report(got[t][i], want[t]))
