@@ -15,7 +15,13 @@ carries:
                 from the committed profile) over its time measured here
   cpu_baseline  the plain C oracle timed on the host cores over a bounded
                 block of output rows of the same workload
-  parity        sampled outputs compared bit for bit with the oracle
+  parity        sampled outputs compared bit for bit with the oracle's
+
+The oracle (oracle/, test infrastructure) runs only in this file's
+cpu_baseline leg: it is timed there on bounded samples of each workload, and
+the outputs it computes on them are the ones each line's parity compares the
+GPU's with.  `--workload` selects the other configurations; each prints one
+line with its own cpu_baseline.
   aux           det_gemm_partial, det_combine and det_finalize on the same
                 workload (the other rows of the hot path), with HBM rates
 """
@@ -63,28 +69,113 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(xb: np.ndarray, wb: np.ndarray, target_s: float = 15.0) -> dict:
+# ---------------------------------------------------------------- the cpu_baseline leg
+# The only code in this file that runs the oracle (oracle/, test
+# infrastructure, never on the timed GPU path).  It times the oracle on the
+# host over bounded samples of each workload; the outputs the oracle computes
+# on those samples are the ones the GPU's outputs are compared with.
+
+def host_threads() -> int:
+    return min(os.cpu_count() or 1, 16)
+
+
+def host_cpu() -> str:
+    """The host's CPU model and logical CPU count (Linux /proc/cpuinfo)."""
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    return f"{model}, {os.cpu_count()} logical CPUs"
+
+
+def baseline_entry(macs: float, seconds: float, threads: int, sample: str) -> dict:
+    return {"value": round(macs / max(seconds, 1e-9) / 1e9, 4), "unit": "GMAC/s", "cores": threads,
+            "kind": "oracle", "sample": f"{sample} ({macs:.3g} MAC, {seconds:.2f} s)", "host": host_cpu()}
+
+
+def cpu_baseline(xb: np.ndarray, wb: np.ndarray, target_s: float = 15.0, threads: int = 0) -> dict:
     """Time the plain C oracle on a block of whole output rows (all N columns,
     full K) sized for roughly ``target_s`` seconds of host work."""
     from oracle import c_oracle
-    threads = min(os.cpu_count() or 1, 16)
+    threads = threads or host_threads()
     K = xb.shape[1]
     N = wb.shape[0]
-    cal_rows = 2 * threads
+    cal_rows = min(2 * threads, xb.shape[0])
     t0 = time.perf_counter()
     c_oracle.partial(xb[:cal_rows], wb, nthreads=threads)
     rate = cal_rows * N * K / max(time.perf_counter() - t0, 1e-6)
     rows = int(max(threads, min(xb.shape[0], target_s * rate / (N * K))))
-    rows = (rows // threads) * threads or threads
+    rows = min(xb.shape[0], (rows // threads) * threads or threads)
     t0 = time.perf_counter()
     c_oracle.partial(xb[:rows], wb, nthreads=threads)
     dt = time.perf_counter() - t0
-    macs = rows * N * K
-    return {"value": round(macs / dt / 1e9, 4), "unit": "GMAC/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"plain C oracle (exact_oracle.c), raw digits of the first {rows} output rows "
-                      f"x all {N} columns at full K={K} ({macs:.3g} MAC, {dt:.1f} s)"}
+    return baseline_entry(rows * N * K, dt, threads,
+                          f"plain C oracle (exact_oracle.c), raw digits of the first {rows} output rows "
+                          f"x all {N} columns at full K={K}")
 
+
+def oracle_pairs(xb: np.ndarray, wb: np.ndarray, rows, cols) -> np.ndarray:
+    """The oracle's fp32 bits of the outputs (rows[i], cols[i])."""
+    from oracle import c_oracle
+    return c_oracle.gemm_pairs(xb, wb, rows, cols, nthreads=host_threads())
+
+
+def oracle_gemm(xb: np.ndarray, wb: np.ndarray):
+    """The oracle's fp32 bits of every output, and the seconds it took."""
+    from oracle import c_oracle
+    t0 = time.perf_counter()
+    y = c_oracle.gemm(xb, wb, nthreads=host_threads())
+    return y, time.perf_counter() - t0
+
+
+def oracle_digits(xb: np.ndarray, wb: np.ndarray, threads: int = 0):
+    """The oracle's raw digits of every output, and the seconds they took."""
+    from oracle import c_oracle
+    t0 = time.perf_counter()
+    d = c_oracle.partial(xb, wb, nthreads=threads or host_threads())
+    return d, time.perf_counter() - t0
+
+
+def oracle_python_digits(xb: np.ndarray, wb: np.ndarray, dtype: str):
+    """The plain Python (big-integer) oracle's raw digits, and its seconds."""
+    from oracle import exact
+    t0 = time.perf_counter()
+    d = exact.partial(xb, wb, dtype)
+    return d, time.perf_counter() - t0
+
+
+def oracle_combine_finalize(parts) -> np.ndarray:
+    from oracle import c_oracle
+    return c_oracle.finalize(c_oracle.combine(parts))
+
+
+def oracle_mse_bits(yb: np.ndarray, tb: np.ndarray):
+    """fp32 bits of RNE(sum (y - t)^2) / n from the oracle: the exact sum is
+    sum y y + sum t t - 2 sum y t, each from the oracle's raw digits over
+    K-slices within its 2^19 limit (raw digits add), rounded by the oracle,
+    then one IEEE fp32 division by n.  Also the seconds it took."""
+    from oracle import c_oracle
+    n = yb.size
+    t0 = time.perf_counter()
+
+    def value(a, b):
+        total = 0
+        for lo in range(0, n, 400_000):
+            d = c_oracle.partial(a[lo:lo + 400_000].reshape(1, -1), b[lo:lo + 400_000].reshape(1, -1))
+            total += sum(int(v) << (32 * j) for j, v in enumerate(d.reshape(-1).tolist()))
+        return total
+
+    exact = value(yb, yb) + value(tb, tb) - 2 * value(yb, tb)
+    digits = [(exact >> (32 * j)) & 0xFFFFFFFF for j in range(17)] + [exact >> (32 * 17)]
+    s32 = np.array([c_oracle.finalize(np.array(digits, dtype=np.int64).reshape(1, 18))[0]],
+                   dtype=np.uint32).view(np.float32)[0]
+    bits = int(np.array([np.float32(s32) / np.float32(n)], dtype=np.float32).view(np.uint32)[0])
+    return bits, time.perf_counter() - t0
+
+
+# ---------------------------------------------------------------- the GPU measurements
 
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
@@ -97,9 +188,10 @@ def main() -> int:
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (calibrates HBM byte counters)")
     ap.add_argument("--workload", default="wide4096",
-                    choices=["wide4096", "bf16cancel", "ksharded", "detlinear", "matrixcore", "loss"],
+                    choices=["wide4096", "small", "bf16cancel", "ksharded", "detlinear", "matrixcore", "loss"],
                     help="wide4096 (default, the headline): f32 4096^3 wide range; the others time "
-                         "the bf16 1024^3, the 16-shard K=2^19 and the DetLinear configurations, "
+                         "the f32 64x64x256, the bf16 1024^3, the 16-shard K=2^19 and the DetLinear "
+                         "configurations, "
                          "(matrixcore) det_gemm on the DetLinear forward shape and (loss) the exact "
                          "mean-squared-error reduction of a DetLinear output")
     args = ap.parse_args()
@@ -111,8 +203,7 @@ def main() -> int:
 
     import torch
     import bitwise_deterministic_exact_amd as det
-    from oracle import c_oracle
-    from workloads import c3_wide_f32, f32_bits
+    from workloads import c3_wide_f32
 
     if args.workload != "wide4096":
         return other_workload(args)
@@ -152,7 +243,7 @@ def main() -> int:
     rows = rng.integers(0, M, 256)
     cols = rng.integers(0, N, 256)
     got = y.cpu().numpy().view(np.uint32)[rows, cols]
-    want = c_oracle.gemm_pairs(xb, wb, rows, cols, nthreads=min(os.cpu_count() or 1, 16))
+    want = oracle_pairs(xb, wb, rows, cols)
     parity_ok = bool(np.array_equal(got, want))
     log(f"parity on 256 sampled outputs: {'bit-exact' if parity_ok else 'MISMATCH'}")
 
@@ -285,13 +376,7 @@ def matrix_core_aux(det, dev, timed) -> dict:
     return out
 
 
-def _digits_of(v: int) -> np.ndarray:
-    """18 digits (base 2^32, the top one signed) holding the integer v."""
-    d = [(v >> (32 * j)) & 0xFFFFFFFF for j in range(17)] + [v >> (32 * 17)]
-    return np.array(d, dtype=np.int64).reshape(1, 18)
-
-
-def loss_workload(det, c_oracle, dev, steps, warmup) -> dict:
+def loss_workload(det, dev, steps, warmup) -> dict:
     """exact_mse_loss of a DetLinear-sized f32 output (8192 x 4096, N(0,1))
     against an N(0,1) target: the time of the whole loss, the squared-
     difference kernel's share against the HBM roofline (its algorithmic bytes
@@ -324,17 +409,7 @@ def loss_workload(det, c_oracle, dev, steps, warmup) -> dict:
     ms_dot = timed(lambda: det.exact_dot_digits(y, t, check_finite=False))
     loss = det.exact_mse_loss(y, t)
     got = int(loss.reshape(1).cpu().view(torch.int32).numpy().view(np.uint32)[0])
-
-    def value(a, b):
-        total = 0
-        for lo in range(0, n, 400_000):
-            d = c_oracle.partial(a[lo:lo + 400_000].reshape(1, -1), b[lo:lo + 400_000].reshape(1, -1))
-            total += sum(int(v) << (32 * j) for j, v in enumerate(d.reshape(-1).tolist()))
-        return total
-
-    exact = value(yb, yb) + value(tb, tb) - 2 * value(yb, tb)
-    s32 = np.array([c_oracle.finalize(_digits_of(exact))[0]], dtype=np.uint32).view(np.float32)[0]
-    want = int(np.array([np.float32(s32) / np.float32(n)], dtype=np.float32).view(np.uint32)[0])
+    want, t_oracle = oracle_mse_bits(yb, tb)
     nbytes = 2 * 4 * n
     rec = profile_record(os.path.join(ROOT, "profiles", "k_dot_f32_loss_8192x4096.md"),
                          "k_dot<f32, squared difference>")
@@ -352,8 +427,49 @@ def loss_workload(det, c_oracle, dev, steps, warmup) -> dict:
                      "GB/s": round(nbytes / (ms_dot * 1e-3) / 1e9, 1),
                      "frac": round(nbytes / (ms_dot * 1e-3) / HBM_PEAK, 4)},
                 parity={"loss_bits": got, "oracle_bits": want, "bit_exact": got == want},
+                cpu_baseline=baseline_entry(3 * n, t_oracle, 1,
+                                            "plain C oracle, the exact sum of the 3n products of the "
+                                            "whole loss (one output: one thread)"),
                 config={"workload": "exact_mse_loss of an 8192x4096 f32 output, N(0,1) prediction and "
                                     "target, seed 8", "n": n})
+
+
+def small_workload(det, dev, steps, warmup) -> dict:
+    """The f32 64x64x256 configuration (launch-bound): det_gemm and its
+    two-shard composition at k = 100, every output and every digit against
+    the oracle, and the oracle's time on the whole workload with one host
+    thread, with all of them, and for the plain Python (big-integer) oracle."""
+    import torch
+    import workloads as W
+    wl = W.c1_small_f32()
+    xb, wb = wl.bits()
+    x = torch.from_numpy(wl.x).to(dev)
+    w = torch.from_numpy(wl.w).to(dev)
+    y = torch.empty(64, 64, dtype=torch.float32, device=dev)
+    ms = _timed(lambda: det.det_gemm(x, w, check_finite=False, out=y), steps, warmup)
+    c = wl.cuts[0]
+    parts = [det.det_gemm_partial(x[:, :c], w[:, :c], check_finite=False),
+             det.det_gemm_partial(x[:, c:], w[:, c:], check_finite=False)]
+    whole = det.det_gemm_partial(x, w, check_finite=False)
+    y_s = det.det_finalize(det.det_combine(parts))
+    digits, t_all = oracle_digits(xb, wb)
+    digits_1, t_one = oracle_digits(xb, wb, threads=1)
+    digits_py, t_py = oracle_python_digits(xb, wb, "f32")
+    want = oracle_combine_finalize([digits])
+    got = y.cpu().view(torch.int32).numpy().view(np.uint32)
+    ok = (np.array_equal(got, want) and np.array_equal(whole.cpu().numpy(), digits)
+          and torch.equal(y_s.view(torch.int32), y.view(torch.int32))
+          and np.array_equal(digits_1, digits) and np.array_equal(digits_py, digits))
+    macs = 64 * 64 * 256
+    return dict(metric="exact-GEMM GMAC/s (f32 64x64x256, launch-bound)",
+                value=round(macs / (ms * 1e-3) / 1e9, 3), unit="GMAC/s", ms_per_step=round(ms, 4),
+                dtype="int64",
+                parity={"outputs": "all 64^2, fp32 and raw digits", "shards_compose": True, "bit_exact": bool(ok)},
+                cpu_baseline=baseline_entry(macs, t_all, host_threads(), "plain C oracle, every output"),
+                cpu_baseline_1thread=baseline_entry(macs, t_one, 1, "plain C oracle, every output"),
+                cpu_baseline_python=baseline_entry(macs, t_py, 1, "plain Python big-integer oracle, every output"),
+                config={"workload": wl.name + ", seed 0, shards [0,100) and [100,256)", "M": 64, "N": 64,
+                        "K": 256})
 
 
 def _timed(fn, steps, warmup):
@@ -371,15 +487,14 @@ def _timed(fn, steps, warmup):
 
 
 def other_workload(args) -> int:
-    """The other configurations: one JSON line each with their throughput and
-    a parity check (full or sampled) against the C oracle."""
+    """The other configurations: one JSON line each with their throughput, a
+    parity check (full or sampled) against the oracle and the oracle's own
+    rate on the host (cpu_baseline)."""
     import torch
     import bitwise_deterministic_exact_amd as det
-    from oracle import c_oracle
     import workloads as W
 
     dev = torch.device("cuda:0")
-    threads = min(os.cpu_count() or 1, 16)
     rng = np.random.default_rng(99)
     out = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "data": "synthetic"}
@@ -412,29 +527,35 @@ def other_workload(args) -> int:
         x, w = to_dev(wl.x, "bf16"), to_dev(wl.w, "bf16")
         y = det.det_gemm(x, w, check_finite=False)
         rows, cols = rng.integers(0, 8192, 64), rng.integers(0, 4096, 64)
-        ok = bool(np.array_equal(bits32(y)[rows, cols],
-                                 c_oracle.gemm_pairs(wl.x, wl.w, rows, cols, nthreads=threads)))
+        ok = bool(np.array_equal(bits32(y)[rows, cols], oracle_pairs(wl.x, wl.w, rows, cols)))
         ok = ok and mc["equals_accumulator_path"]
         out.update(metric="exact-GEMM GMAC/s (bf16 8192x4096x4096 N(0,1), det_gemm's own path choice)",
                    value=mc["GMAC/s"], unit="GMAC/s", ms_per_step=mc["ms"], dtype="int8",
                    plan=mc["plan"], roofline=mc.get("roofline"),
                    parity={"sampled_outputs": 64, "bit_exact": ok,
                            "equals_accumulator_path": mc["equals_accumulator_path"]},
+                   cpu_baseline=cpu_baseline(wl.x, wl.w, target_s=3.0),
                    config={"workload": wl.name + ", seed 4 (the DetLinear forward GEMM)",
                            "M": 8192, "N": 4096, "K": 4096})
     elif args.workload == "loss":
-        out.update(loss_workload(det, c_oracle, dev, args.steps, args.warmup))
+        out.update(loss_workload(det, dev, args.steps, args.warmup))
+    elif args.workload == "small":
+        out.update(small_workload(det, dev, args.steps, args.warmup))
     elif args.workload == "bf16cancel":
         wl = W.c2_bf16_cancel()
         xb, wb = wl.bits()
         x, w = to_dev(xb, "bf16"), to_dev(wb, "bf16")
         y = torch.empty(1024, 1024, dtype=torch.float32, device=dev)
         ms = _timed(lambda: det.det_gemm(x, w, check_finite=False, out=y), args.steps, args.warmup)
-        ok = bool(np.array_equal(bits32(y), c_oracle.gemm(xb, wb, nthreads=threads)))
+        want, t_oracle = oracle_gemm(xb, wb)
+        ok = bool(np.array_equal(bits32(y), want))
         macs = 1024 ** 3
         out.update(metric="exact-GEMM GMAC/s (bf16 1024^3, 10% negated w columns)",
                    value=round(macs / (ms * 1e-3) / 1e9, 2), unit="GMAC/s", ms_per_step=round(ms, 4),
                    dtype="int64", parity={"outputs": "all 1024^2", "bit_exact": ok},
+                   cpu_baseline=baseline_entry(macs, t_oracle, host_threads(),
+                                               "plain C oracle, every output of the workload"),
+                   cpu_baseline_1thread=cpu_baseline(xb, wb, target_s=2.0, threads=1),
                    config={"workload": wl.name + ", seed 1", "M": 1024, "N": 1024, "K": 1024})
     elif args.workload == "ksharded":
         wl = W.c4_ksharded_f32()
@@ -451,8 +572,7 @@ def other_workload(args) -> int:
         y_u = det.det_gemm(x, w, check_finite=False)
         same = bool(torch.equal(y_s.view(torch.int32), y_u.view(torch.int32)))
         rows, cols = rng.integers(0, 2048, 16), rng.integers(0, 2048, 16)
-        ok = same and bool(np.array_equal(bits32(y_u)[rows, cols],
-                                          c_oracle.gemm_pairs(xb, wb, rows, cols, nthreads=threads)))
+        ok = same and bool(np.array_equal(bits32(y_u)[rows, cols], oracle_pairs(xb, wb, rows, cols)))
         steps = max(1, min(args.steps, 3))
         ms_s = _timed(sharded, steps, 0)
         ms_u = _timed(lambda: det.det_gemm(x, w, check_finite=False), steps, 0)
@@ -462,6 +582,7 @@ def other_workload(args) -> int:
                    steps=steps, warmup=0, dtype="int64",
                    unsharded={"ms": round(ms_u, 3), "GMAC/s": round(macs / (ms_u * 1e-3) / 1e9, 2)},
                    parity={"sharded_equals_unsharded": same, "sampled_outputs": 16, "bit_exact": ok},
+                   cpu_baseline=cpu_baseline(xb, wb, target_s=3.0),
                    config={"workload": wl.name + ", seed 3", "M": 2048, "N": 2048, "K": K})
     else:
         wl = W.c5_detlinear_bf16()
@@ -478,13 +599,13 @@ def other_workload(args) -> int:
         ms = _timed(step, args.steps, args.warmup)
         y = layer(x).detach()
         rows, cols = rng.integers(0, 8192, 64), rng.integers(0, 4096, 64)
-        ok = bool(np.array_equal(bits32(y)[rows, cols],
-                                 c_oracle.gemm_pairs(wl.x, wl.w, rows, cols, nthreads=threads)))
+        ok = bool(np.array_equal(bits32(y)[rows, cols], oracle_pairs(wl.x, wl.w, rows, cols)))
         macs = 3 * 8192 * 4096 * 4096
         out.update(metric="DetLinear 4096->4096 bf16 fwd+bwd, 8192 tokens: exact-GEMM GMAC/s",
                    value=round(macs / (ms * 1e-3) / 1e9, 2), unit="GMAC/s", ms_per_step=round(ms, 3),
                    tokens_per_s=round(8192 / (ms * 1e-3), 1), dtype="int64",
                    parity={"sampled_forward_outputs": 64, "bit_exact": ok},
+                   cpu_baseline=cpu_baseline(wl.x, wl.w, target_s=3.0),
                    config={"workload": wl.name + ", seed 4", "tokens": 8192, "in": 4096, "out": 4096})
     print(json.dumps(out), flush=True)
     return 0 if out["parity"].get("bit_exact", False) else 1
