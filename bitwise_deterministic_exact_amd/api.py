@@ -31,6 +31,13 @@ def _stream(dev: torch.device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
+def _call(dev: torch.device, fn, *args) -> None:
+    """One library call with the operands' device current (the library's
+    launches, events and copies go to the calling thread's current device)."""
+    with torch.cuda.device(dev):
+        _lib.check(fn(*args))
+
+
 def _want_check(flag: Optional[bool]) -> bool:
     if flag is not None:
         return bool(flag)
@@ -61,9 +68,9 @@ def has_nonfinite(t: torch.Tensor) -> bool:
     if t2.dim() != 2:
         t2 = t2.reshape(-1, t2.shape[-1])
     flag = torch.zeros(1, dtype=torch.int32, device=t.device)
-    _lib.check(_lib.load().det_check_finite(
-        _DT[t.dtype], ctypes.c_void_p(t2.data_ptr()), t2.shape[0], t2.shape[1],
-        t2.stride(0), t2.stride(1), ctypes.c_void_p(flag.data_ptr()), _stream(t.device)))
+    _call(t.device, _lib.load().det_check_finite,
+          _DT[t.dtype], ctypes.c_void_p(t2.data_ptr()), t2.shape[0], t2.shape[1],
+          t2.stride(0), t2.stride(1), ctypes.c_void_p(flag.data_ptr()), _stream(t.device))
     return bool(flag.item())
 
 
@@ -103,9 +110,9 @@ def det_gemm(x: torch.Tensor, w: torch.Tensor, *, check_finite: Optional[bool] =
            ctypes.c_void_p(out.data_ptr()), out.stride(0), out.stride(1))
     ws, nbytes = _workspace(dt, False, M, N, K, x.device, workspace)
     if ws is None:
-        _lib.check(lib.det_gemm(*ops, _stream(x.device)))
+        _call(x.device, lib.det_gemm, *ops, _stream(x.device))
     else:
-        _lib.check(lib.det_gemm_ws(*ops, ctypes.c_void_p(ws.data_ptr()), nbytes, _stream(x.device)))
+        _call(x.device, lib.det_gemm_ws, *ops, ctypes.c_void_p(ws.data_ptr()), nbytes, _stream(x.device))
     return out
 
 
@@ -123,9 +130,10 @@ def det_gemm_partial(x: torch.Tensor, w: torch.Tensor, *, check_finite: Optional
            ctypes.c_void_p(acc.data_ptr()))
     ws, nbytes = _workspace(dt, True, M, N, K, x.device, workspace)
     if ws is None:
-        _lib.check(lib.det_gemm_partial(*ops, _stream(x.device)))
+        _call(x.device, lib.det_gemm_partial, *ops, _stream(x.device))
     else:
-        _lib.check(lib.det_gemm_partial_ws(*ops, ctypes.c_void_p(ws.data_ptr()), nbytes, _stream(x.device)))
+        _call(x.device, lib.det_gemm_partial_ws, *ops, ctypes.c_void_p(ws.data_ptr()), nbytes,
+              _stream(x.device))
     return acc
 
 
@@ -148,8 +156,8 @@ def det_combine(parts: Sequence[torch.Tensor]) -> torch.Tensor:
     parts = [p.contiguous() for p in parts]
     out = torch.empty_like(parts[0])
     ptrs = (ctypes.c_void_p * len(parts))(*[p.data_ptr() for p in parts])
-    _lib.check(_lib.load().det_combine(ptrs, len(parts), ctypes.c_void_p(out.data_ptr()),
-                                       out.numel() // _lib.NUM_DIGITS, _stream(out.device)))
+    _call(out.device, _lib.load().det_combine, ptrs, len(parts), ctypes.c_void_p(out.data_ptr()),
+          out.numel() // _lib.NUM_DIGITS, _stream(out.device))
     return out
 
 
@@ -158,8 +166,8 @@ def det_finalize(acc: torch.Tensor) -> torch.Tensor:
     _check_acc(acc, "det_finalize input")
     acc = acc.contiguous()
     y = torch.empty(acc.shape[:-1], dtype=torch.float32, device=acc.device)
-    _lib.check(_lib.load().det_finalize(ctypes.c_void_p(acc.data_ptr()), ctypes.c_void_p(y.data_ptr()),
-                                        y.numel(), _stream(acc.device)))
+    _call(acc.device, _lib.load().det_finalize, ctypes.c_void_p(acc.data_ptr()),
+          ctypes.c_void_p(y.data_ptr()), y.numel(), _stream(acc.device))
     return y
 
 
@@ -213,8 +221,8 @@ def _dot_digits(fn, a: torch.Tensor, b: Optional[torch.Tensor], check_finite) ->
             raise ValueError("a or b holds Inf or NaN; the exact accumulator takes finite inputs only")
     acc = torch.empty(_lib.NUM_DIGITS, dtype=torch.int64, device=va.device)
     bp = ctypes.c_void_p(vb.data_ptr()) if vb is not None else None
-    _lib.check(fn(_DT[va.dtype], ctypes.c_void_p(va.data_ptr()), ia, bp, ib, va.numel(),
-                  ctypes.c_void_p(acc.data_ptr()), 0, _stream(va.device)))
+    _call(va.device, fn, _DT[va.dtype], ctypes.c_void_p(va.data_ptr()), ia, bp, ib, va.numel(),
+          ctypes.c_void_p(acc.data_ptr()), 0, _stream(va.device))
     return acc
 
 
@@ -301,7 +309,6 @@ def round_f32_to_bf16(t: torch.Tensor) -> torch.Tensor:
         raise ValueError("round_f32_to_bf16 needs a float32 GPU tensor")
     t = t.contiguous()
     out = torch.empty(t.shape, dtype=torch.bfloat16, device=t.device)
-    _lib.check(_lib.load().det_round_f32_to_bf16(ctypes.c_void_p(t.data_ptr()),
-                                                 ctypes.c_void_p(out.data_ptr()), t.numel(),
-                                                 _stream(t.device)))
+    _call(t.device, _lib.load().det_round_f32_to_bf16, ctypes.c_void_p(t.data_ptr()),
+          ctypes.c_void_p(out.data_ptr()), t.numel(), _stream(t.device))
     return out

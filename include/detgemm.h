@@ -40,6 +40,8 @@
  *   - Strides are in elements, must be >= 0, and may describe transposed or
  *     sliced views (e.g. x[:, a:b] or x^T).  Operand elements must be
  *     naturally aligned (4 bytes for f32, 2 for bf16).
+ *   - The calling thread's current HIP device must be the device that holds
+ *     the pointers and owns `stream` (the Python layer makes it current).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     asynchronously and stream-ordered.  The one exception is det_gemm_ws
  *     when it considers the matrix-core path (see det_set_gemm_path): it
