@@ -175,3 +175,17 @@ def test_c5_detlinear_4096_bf16_8192_tokens():
     layer(x2).square().mean().backward()
     assert np.array_equal(tensor_bits(x2.grad), dx_bits)
     assert np.array_equal(tensor_bits(layer.weight.grad), dw_bits)
+    # the exact loss (the step bench.py times) gives the same gradients: its
+    # dY = 2 y / 2^25 is the same power-of-two scaling of y
+    x3 = to_device(xb, "bf16").requires_grad_(True)
+    layer.weight.grad = None
+    loss = det.exact_mse_loss(layer(x3))
+    loss.backward()
+    assert np.array_equal(tensor_bits(x3.grad), dx_bits)
+    assert np.array_equal(tensor_bits(layer.weight.grad), dw_bits)
+    flat = yb.reshape(-1)                          # sum y^2 over K-slices within the oracle's 2^19
+    parts = [c_oracle.partial(flat[a:a + 400_000].reshape(1, -1), flat[a:a + 400_000].reshape(1, -1))
+             for a in range(0, flat.size, 400_000)]
+    s_exact = c_oracle.finalize(c_oracle.combine(parts)).reshape(-1)[0]     # rounded once
+    want_loss = np.float32(np.array([s_exact], dtype=np.uint32).view(np.float32)[0] / np.float32(yb.size))
+    assert f32_bits(loss.reshape(1))[0] == want_loss.view(np.uint32)
