@@ -1103,6 +1103,7 @@ __device__ __forceinline__ void split_elem(uint32_t b, bool& neg, uint32_t& m, i
 struct SliceStatArgs {
   const void* p; int64_t R, K, s_r, s_k;
   int32_t* top; int32_t* low;
+  bool vec;                               // unit K stride, rows 16-byte aligned
 };
 
 template <int DT>
@@ -1132,10 +1133,30 @@ __global__ __launch_bounds__(256) void k_slice_stats(SliceStatArgs a) {
     if (wid >= a.R * nkr) return;               // uniform per wave
     row = wid / nkr;
     const int64_t k0 = (wid % nkr) * 1024;
+    constexpr int EPV = DT == DET_F32 ? 4 : 8;              // elements per 16-byte load
+    if (a.vec && k0 + 1024 <= a.K) {                         // lane: 16 consecutive elements
+      const uint4* const q = reinterpret_cast<const uint4*>(
+          static_cast<const char*>(a.p) + (row * a.s_r + k0 + lane * 16) * (DT == DET_F32 ? 4 : 2));
+#pragma unroll
+      for (int i = 0; i < 16 / EPV; ++i) {
+        const uint4 v = q[i];
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (DT == DET_F32) {
+            stat_elem<DT>(w4[u], top, low);
+          } else {
+            stat_elem<DT>(w4[u] & 0xFFFFu, top, low);
+            stat_elem<DT>(w4[u] >> 16, top, low);
+          }
+        }
+      }
+    } else {
 #pragma unroll 4
-    for (int i = 0; i < 16; ++i) {
-      const int64_t k = k0 + i * 64 + lane;
-      if (k < a.K) stat_elem<DT>(load_elem<DT>(a.p, row * a.s_r + k), top, low);
+      for (int i = 0; i < 16; ++i) {
+        const int64_t k = k0 + i * 64 + lane;
+        if (k < a.K) stat_elem<DT>(load_elem<DT>(a.p, row * a.s_r + k), top, low);
+      }
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
@@ -1433,8 +1454,8 @@ struct SliceMakeArgs {
 // the S balanced 8-bit digits of 16 elements of one row (window bottom
 // `base`), packed four to a word: digit s of element j in byte j mod 4 of
 // d[s][j div 4]
-template <int DT>
-__device__ __forceinline__ void slice_digits(const uint32_t (&e)[16], int base, int S, uint32_t (&d)[SL_MAX][4]) {
+template <int DT, typename V, int SMAX>
+__device__ __forceinline__ void slice_digits_in(const uint32_t (&e)[16], int base, int S, uint32_t (&d)[SL_MAX][4]) {
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     bool neg;
@@ -1443,17 +1464,24 @@ __device__ __forceinline__ void slice_digits(const uint32_t (&e)[16], int base, 
     split_elem<DT>(e[j], neg, m, ex);
     const int sh = ex - base;
     if (m == 0u || sh + __ffs(static_cast<int>(m)) - 1 < 0) continue;    // zero, or below the window
-    int64_t v = sh >= 0 ? static_cast<int64_t>(m) << sh : static_cast<int64_t>(m >> (-sh));
+    V v = sh >= 0 ? static_cast<V>(m) << sh : static_cast<V>(m >> (-sh));
     if (neg) v = -v;
 #pragma unroll
-    for (int s = 0; s < SL_MAX; ++s) {
+    for (int s = 0; s < SMAX; ++s) {
       if (s < S) {
-        const int64_t dig = static_cast<int8_t>(static_cast<uint8_t>(v & 0xFF));
+        const V dig = static_cast<int8_t>(static_cast<uint8_t>(v & 0xFF));
         v = (v - dig) >> 8;
         d[s][j >> 2] |= (static_cast<uint32_t>(dig) & 0xFFu) << (8 * (j & 3));
       }
     }
   }
+}
+
+// |V| < 2^(8S - 2): 32-bit arithmetic up to S = 4, 64-bit above
+template <int DT>
+__device__ __forceinline__ void slice_digits(const uint32_t (&e)[16], int base, int S, uint32_t (&d)[SL_MAX][4]) {
+  if (S <= 4) slice_digits_in<DT, int32_t, 4>(e, base, S, d);
+  else slice_digits_in<DT, int64_t, SL_MAX>(e, base, S, d);
 }
 
 // fragment `blk` of the output, the lane's 16 bytes of each digit
@@ -2336,7 +2364,9 @@ det_status launch_mma(SliceMmaArgs m, hipStream_t s) {
 template <int DT>
 det_status slice_stats(const void* p, int64_t R, int64_t K, int64_t s_r, int64_t s_k, int32_t* top,
                        int32_t* low, hipStream_t s) {
-  SliceStatArgs a{p, R, K, s_r, s_k, top, low};
+  SliceStatArgs a{p, R, K, s_r, s_k, top, low, false};
+  const int64_t esz = DT == DET_F32 ? 4 : 2;
+  a.vec = s_k == 1 && (reinterpret_cast<uintptr_t>(p) % 16) == 0 && (s_r * esz) % 16 == 0;
   if (s_k == 1) {
     const int64_t waves = R * ((K + 1023) / 1024);
     hipLaunchKernelGGL((k_slice_stats<DT, true>), dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256), 0, s, a);
