@@ -1122,13 +1122,13 @@ __device__ __forceinline__ void stat_elem(uint32_t b, int& top, int& low) {
 // along K; otherwise one thread per row and 256-element K range, lanes along
 // the rows (coalesced for a transposed view), 16 loads in flight
 template <int DT, bool KMAJ>
-__global__ __launch_bounds__(256) void k_slice_stats(SliceStatArgs a) {
+__device__ __forceinline__ void stats_body(const SliceStatArgs& a, int64_t blk) {
   int top = SL_TOP_NONE, low = SL_LOW_NONE;
   int64_t row;
   bool lead;
   if (KMAJ) {
     const int64_t nkr = (a.K + 1023) / 1024;
-    const int64_t wid = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) >> 6;
+    const int64_t wid = (blk * 256 + threadIdx.x) >> 6;
     const int lane = threadIdx.x & 63;
     if (wid >= a.R * nkr) return;               // uniform per wave
     row = wid / nkr;
@@ -1165,7 +1165,7 @@ __global__ __launch_bounds__(256) void k_slice_stats(SliceStatArgs a) {
     }
     lead = lane == 0;
   } else {
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t t = blk * 256 + threadIdx.x;
     const int64_t nkr = (a.K + 255) / 256;
     if (t >= a.R * nkr) return;
     row = t % a.R;
@@ -1186,6 +1186,20 @@ __global__ __launch_bounds__(256) void k_slice_stats(SliceStatArgs a) {
   }
 }
 
+// x's and w's span check in one launch: blocks [0, nb0) take op[0], the
+// rest op[1] (both operands need the same layout, KMAJ)
+struct SliceStatPair {
+  SliceStatArgs op[2];
+  int64_t nb0;
+};
+
+template <int DT, bool KMAJ>
+__global__ __launch_bounds__(256) void k_slice_stats(SliceStatPair p) {
+  const int64_t b = blockIdx.x;
+  if (b < p.nb0) stats_body<DT, KMAJ>(p.op[0], b);
+  else stats_body<DT, KMAJ>(p.op[1], b - p.nb0);
+}
+
 __global__ __launch_bounds__(256) void k_slice_init(int32_t* top, int32_t* low, int32_t* cnt, int64_t n,
                                                     int32_t* hist) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
@@ -1198,20 +1212,22 @@ __global__ __launch_bounds__(256) void k_slice_init(int32_t* top, int32_t* low, 
 }
 
 // digits each row needs: the smallest S with top - low + 1 <= 8S - 2
-// (0 for an all-zero row, 8 for more than SL_MAX), and their histogram
+// (0 for an all-zero row, 8 for more than SL_MAX), and their histograms
+// (x's rows [0, split) count into hist[0..SL_HIST), w's rows after them into
+// hist[SL_HIST..2 SL_HIST))
 __global__ __launch_bounds__(256) void k_slice_need(const int32_t* top, const int32_t* low, int64_t n,
-                                                    int32_t* need, int32_t* hist) {
-  __shared__ int32_t h[SL_HIST];
-  if (threadIdx.x < SL_HIST) h[threadIdx.x] = 0;
+                                                    int64_t split, int32_t* need, int32_t* hist) {
+  __shared__ int32_t h[2 * SL_HIST];
+  if (threadIdx.x < 2 * SL_HIST) h[threadIdx.x] = 0;
   __syncthreads();
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
     const int nd = top[i] == SL_TOP_NONE ? 0 : min((top[i] - low[i] + 10) / 8, SL_MAX + 1);
     need[i] = nd;
-    atomicAdd(&h[nd], 1);
+    atomicAdd(&h[(i < split ? 0 : SL_HIST) + nd], 1);
   }
   __syncthreads();
-  if (threadIdx.x < SL_HIST && h[threadIdx.x] != 0) atomicAdd(hist + threadIdx.x, h[threadIdx.x]);
+  if (threadIdx.x < 2 * SL_HIST && h[threadIdx.x] != 0) atomicAdd(hist + threadIdx.x, h[threadIdx.x]);
 }
 
 // list[] = the rows with need > S, in increasing order, and pos[r] = the
@@ -1495,10 +1511,10 @@ __device__ __forceinline__ void slice_store(const SliceMakeArgs& a, int64_t blk,
 }
 
 template <int DT>
-__global__ __launch_bounds__(256) void k_slice_make(SliceMakeArgs a) {
+__device__ __forceinline__ void make_body(const SliceMakeArgs& a, int64_t blk, int64_t nblk) {
   const int64_t total = a.Rb * a.Kb * 64;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < total; t += stride) {
+  const int64_t stride = nblk * blockDim.x;
+  for (int64_t t = blk * blockDim.x + threadIdx.x; t < total; t += stride) {
     const int lane = static_cast<int>(t & 63);
     const int64_t blk = t >> 6, rb = blk / a.Kb, kb = blk % a.Kb;
     const int64_t row = rb * 16 + (lane & 15), k0 = kb * 64 + (lane >> 4) * 16;
@@ -1543,9 +1559,9 @@ __global__ __launch_bounds__(256) void k_slice_make(SliceMakeArgs a) {
 // per load), and hands each wave its block's elements through LDS.  The tile's rows are padded to 65 words,
 // so the 16 k-runs a wave reads lie in four different bank quarters.
 template <int DT>
-__global__ __launch_bounds__(256) void k_slice_make_t(SliceMakeArgs a) {
+__device__ __forceinline__ void make_t_body(const SliceMakeArgs& a, int64_t blk) {
   __shared__ uint32_t tile[64][65];
-  const int64_t rb4 = blockIdx.x / a.Kb, kb = blockIdx.x % a.Kb;
+  const int64_t rb4 = blk / a.Kb, kb = blk % a.Kb;
   const int t = threadIdx.x;
   {
     const int rl = t & 63, kq = t >> 6;                   // row of the tile (lane), quarter of its k
@@ -1571,6 +1587,27 @@ __global__ __launch_bounds__(256) void k_slice_make_t(SliceMakeArgs a) {
     slice_digits<DT>(e, a.top[row] + 3 - 8 * a.S, a.S, d);
   }
   slice_store(a, rb * a.Kb + kb, lane, d);
+}
+
+// x's and w's digits in one launch: blocks [0, nb0) make op[0] (nb0 blocks),
+// the rest op[1] (nb1)
+struct SliceMakePair {
+  SliceMakeArgs op[2];
+  int64_t nb0, nb1;
+};
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_slice_make(SliceMakePair p) {
+  const int64_t b = blockIdx.x;
+  if (b < p.nb0) make_body<DT>(p.op[0], b, p.nb0);
+  else make_body<DT>(p.op[1], b - p.nb0, p.nb1);
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_slice_make_t(SliceMakePair p) {
+  const int64_t b = blockIdx.x;
+  if (b < p.nb0) make_t_body<DT>(p.op[0], b);
+  else make_t_body<DT>(p.op[1], b - p.nb0);
 }
 
 // RNE(z * 2^e2) as binary32 bits (gradual underflow, overflow to inf; z = 0
@@ -2361,36 +2398,75 @@ det_status launch_mma(SliceMmaArgs m, hipStream_t s) {
   return DET_OK;
 }
 
+// one operand's span-check arguments and its block count
 template <int DT>
-det_status slice_stats(const void* p, int64_t R, int64_t K, int64_t s_r, int64_t s_k, int32_t* top,
-                       int32_t* low, hipStream_t s) {
+SliceStatArgs stat_args(const void* p, int64_t R, int64_t K, int64_t s_r, int64_t s_k, int32_t* top, int32_t* low,
+                        int64_t& blocks) {
   SliceStatArgs a{p, R, K, s_r, s_k, top, low, false};
   const int64_t esz = DT == DET_F32 ? 4 : 2;
   a.vec = s_k == 1 && (reinterpret_cast<uintptr_t>(p) % 16) == 0 && (s_r * esz) % 16 == 0;
-  if (s_k == 1) {
-    const int64_t waves = R * ((K + 1023) / 1024);
-    hipLaunchKernelGGL((k_slice_stats<DT, true>), dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256), 0, s, a);
+  blocks = s_k == 1 ? (R * ((K + 1023) / 1024) + 3) / 4 : (R * ((K + 255) / 256) + 255) / 256;
+  return a;
+}
+
+// x's and w's span checks: one launch when both have the same layout
+template <int DT>
+det_status slice_stats(const GemmArgs& g, int32_t* topx, int32_t* lowx, int32_t* topw, int32_t* loww,
+                       hipStream_t s) {
+  int64_t bx, bw;
+  const SliceStatArgs ax = stat_args<DT>(g.x, g.M, g.K, g.x_sm, g.x_sk, topx, lowx, bx);
+  const SliceStatArgs aw = stat_args<DT>(g.w, g.N, g.K, g.w_sn, g.w_sk, topw, loww, bw);
+  auto launch = [&](const SliceStatArgs& a0, int64_t b0, const SliceStatArgs& a1, int64_t b1, bool kmaj) {
+    SliceStatPair p{{a0, a1}, b0};
+    const dim3 grid(static_cast<unsigned>(b0 + b1));
+    if (kmaj) hipLaunchKernelGGL((k_slice_stats<DT, true>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((k_slice_stats<DT, false>), grid, dim3(256), 0, s, p);
+  };
+  const bool kx = g.x_sk == 1, kw = g.w_sk == 1;
+  if (kx == kw) {
+    launch(ax, bx, aw, bw, kx);
   } else {
-    const int64_t threads = R * ((K + 255) / 256);
-    hipLaunchKernelGGL((k_slice_stats<DT, false>), dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256),
-                       0, s, a);
+    launch(ax, bx, ax, 0, kx);
+    launch(aw, bw, aw, 0, kw);
   }
   return hip_check(hipGetLastError(), "slice stats launch");
 }
 
+// one operand's digit-making arguments; `trans`: the LDS-transposing form
 template <int DT>
-det_status slice_make(const void* p, int64_t R, int64_t K, int64_t s_r, int64_t s_k, const int32_t* top,
-                      int8_t* out, int64_t rows_padded, int S, hipStream_t s) {
+SliceMakeArgs make_args(const void* p, int64_t R, int64_t K, int64_t s_r, int64_t s_k, const int32_t* top,
+                        int8_t* out, int64_t rows_padded, int S, bool& trans, int64_t& blocks) {
   const int64_t esz = DT == DET_F32 ? 4 : 2;
   SliceMakeArgs a{};
   a.p = p; a.R = R; a.K = K; a.s_r = s_r; a.s_k = s_k; a.top = top; a.out = out;
   a.Rb = rows_padded / 16; a.Kb = round_up(K, 2 * SL_KB) / SL_KB;
   a.S = S;
   a.vec = s_k == 1 && (reinterpret_cast<uintptr_t>(p) % 16) == 0 && (s_r * esz) % 16 == 0;
-  if (s_r == 1 && s_k > 1)      // a transposed view: through LDS (Rb is a multiple of 8)
-    hipLaunchKernelGGL((k_slice_make_t<DT>), dim3(static_cast<unsigned>(a.Rb / 4 * a.Kb)), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_slice_make<DT>), dim3(grid_for(a.Rb * a.Kb * 64, 256, 16384)), dim3(256), 0, s, a);
+  trans = s_r == 1 && s_k > 1;            // a transposed view: through LDS (Rb is a multiple of 8)
+  blocks = trans ? a.Rb / 4 * a.Kb : grid_for(a.Rb * a.Kb * 64, 256, 8192);
+  return a;
+}
+
+// x's and w's digits: one launch when both take the same form
+template <int DT>
+det_status slice_make(const GemmArgs& g, const int32_t* topx, const int32_t* topw, int8_t* xs, int8_t* wsl, int S,
+                      hipStream_t s) {
+  bool tx, tw;
+  int64_t bx, bw;
+  const SliceMakeArgs ax = make_args<DT>(g.x, g.M, g.K, g.x_sm, g.x_sk, topx, xs, slice_rows_x(g.M), S, tx, bx);
+  const SliceMakeArgs aw = make_args<DT>(g.w, g.N, g.K, g.w_sn, g.w_sk, topw, wsl, slice_rows_w(g.N), S, tw, bw);
+  auto launch = [&](const SliceMakeArgs& a0, int64_t b0, const SliceMakeArgs& a1, int64_t b1, bool trans) {
+    SliceMakePair p{{a0, a1}, b0, b1};
+    const dim3 grid(static_cast<unsigned>(b0 + b1));
+    if (trans) hipLaunchKernelGGL((k_slice_make_t<DT>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((k_slice_make<DT>), grid, dim3(256), 0, s, p);
+  };
+  if (tx == tw) {
+    launch(ax, bx, aw, bw, tx);
+  } else {
+    launch(ax, bx, ax, 0, tx);
+    launch(aw, bw, aw, 0, tw);
+  }
   return hip_check(hipGetLastError(), "slice make launch");
 }
 
@@ -2445,12 +2521,11 @@ det_status launch_sliced(GemmArgs a, char* ws, bool only_slices, int forced, hip
   hipLaunchKernelGGL(k_slice_init, dim3(grid_for(M + N, 256, 1024)), dim3(256), 0, s, topx, lowx, cntx, M + N,
                      hist);
   det_status st = hip_check(hipGetLastError(), "slice init launch");
-  if (st == DET_OK) st = slice_stats<DT>(a.x, M, K, a.x_sm, a.x_sk, topx, lowx, s);
-  if (st == DET_OK) st = slice_stats<DT>(a.w, N, K, a.w_sn, a.w_sk, topw, loww, s);
+  if (st == DET_OK) st = slice_stats<DT>(a, topx, lowx, topw, loww, s);
   if (st != DET_OK) return st;
-  hipLaunchKernelGGL(k_slice_need, dim3(grid_for(M, 256, 256)), dim3(256), 0, s, topx, lowx, M, needx, hist);
-  hipLaunchKernelGGL(k_slice_need, dim3(grid_for(N, 256, 256)), dim3(256), 0, s, topw, loww, N, needw,
-                     hist + SL_HIST);
+  // x's and w's tops, lows and needs are adjacent: one pass over M + N rows
+  hipLaunchKernelGGL(k_slice_need, dim3(grid_for(M + N, 256, 256)), dim3(256), 0, s, topx, lowx, M + N, M, needx,
+                     hist);
   st = hip_check(hipGetLastError(), "slice need launch");
   if (st != DET_OK) return st;
   int32_t* const h = pinned(g_pin_hist, 2 * SL_HIST);
@@ -2507,8 +2582,7 @@ det_status launch_sliced(GemmArgs a, char* ws, bool only_slices, int forced, hip
       return st;
     }
   }
-  st = slice_make<DT>(a.x, M, K, a.x_sm, a.x_sk, topx, xs, slice_rows_x(M), S, s);
-  if (st == DET_OK) st = slice_make<DT>(a.w, N, K, a.w_sn, a.w_sk, topw, wsl, slice_rows_w(N), S, s);
+  st = slice_make<DT>(a, topx, topw, xs, wsl, S, s);
   SliceMmaArgs m{};
   m.xs = xs; m.ws = wsl;
   m.Kb = Kp / SL_KB;
