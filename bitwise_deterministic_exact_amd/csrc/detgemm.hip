@@ -1104,6 +1104,7 @@ struct SliceStatArgs {
   const void* p; int64_t R, K, s_r, s_k;
   int32_t* top; int32_t* low;
   bool vec;                               // unit K stride, rows 16-byte aligned
+  bool direct;                            // one wave (one thread) takes a whole row: store, no atomics
 };
 
 template <int DT>
@@ -1180,43 +1181,47 @@ __device__ __forceinline__ void stats_body(const SliceStatArgs& a, int64_t blk) 
     }
     lead = true;
   }
-  if (lead && top != SL_TOP_NONE) {
+  if (lead && a.direct) {                 // the row's only writer: no initial values needed
+    a.top[row] = top;
+    a.low[row] = low;
+  } else if (lead && top != SL_TOP_NONE) {
     atomicMax(a.top + row, top);
     atomicMin(a.low + row, low);
   }
 }
 
 // x's and w's span check in one launch: blocks [0, nb0) take op[0], the
-// rest op[1] (both operands need the same layout, KMAJ)
+// rest op[1] (both operands need the same layout, KMAJ).  Block 0 also
+// clears the histograms (k_slice_need fills them next).
 struct SliceStatPair {
   SliceStatArgs op[2];
   int64_t nb0;
+  int32_t* hist;
 };
 
 template <int DT, bool KMAJ>
 __global__ __launch_bounds__(256) void k_slice_stats(SliceStatPair p) {
   const int64_t b = blockIdx.x;
+  if (b == 0 && threadIdx.x < 2 * SL_HIST && p.hist != nullptr) p.hist[threadIdx.x] = 0;
   if (b < p.nb0) stats_body<DT, KMAJ>(p.op[0], b);
   else stats_body<DT, KMAJ>(p.op[1], b - p.nb0);
 }
 
-__global__ __launch_bounds__(256) void k_slice_init(int32_t* top, int32_t* low, int32_t* cnt, int64_t n,
-                                                    int32_t* hist) {
+// initial tops and lows for rows that several waves share (atomics)
+__global__ __launch_bounds__(256) void k_slice_init(int32_t* top, int32_t* low, int64_t n) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
     top[i] = SL_TOP_NONE;
     low[i] = SL_LOW_NONE;
-    cnt[i] = 0;
   }
-  if (blockIdx.x == 0 && threadIdx.x < 2 * SL_HIST) hist[threadIdx.x] = 0;
 }
 
 // digits each row needs: the smallest S with top - low + 1 <= 8S - 2
 // (0 for an all-zero row, 8 for more than SL_MAX), and their histograms
 // (x's rows [0, split) count into hist[0..SL_HIST), w's rows after them into
-// hist[SL_HIST..2 SL_HIST))
+// hist[SL_HIST..2 SL_HIST)); also clears the rows' tail counts
 __global__ __launch_bounds__(256) void k_slice_need(const int32_t* top, const int32_t* low, int64_t n,
-                                                    int64_t split, int32_t* need, int32_t* hist) {
+                                                    int64_t split, int32_t* need, int32_t* hist, int32_t* cnt) {
   __shared__ int32_t h[2 * SL_HIST];
   if (threadIdx.x < 2 * SL_HIST) h[threadIdx.x] = 0;
   __syncthreads();
@@ -1224,6 +1229,7 @@ __global__ __launch_bounds__(256) void k_slice_need(const int32_t* top, const in
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
     const int nd = top[i] == SL_TOP_NONE ? 0 : min((top[i] - low[i] + 10) / 8, SL_MAX + 1);
     need[i] = nd;
+    cnt[i] = 0;
     atomicAdd(&h[(i < split ? 0 : SL_HIST) + nd], 1);
   }
   __syncthreads();
@@ -1283,7 +1289,7 @@ __device__ __forceinline__ bool is_tail(uint32_t b, int base) {
 }
 
 // one wave per listed row and 1024-element K range: count the range's tails
-// into the row's count (zeroed by k_slice_init) and write their k into the
+// into the row's count (zeroed by k_slice_need) and write their k into the
 // row's slot of tk at the places one atomic add reserved, as long as they
 // fall within its first SL_TAIL_CAP (a row with more is recomputed whole,
 // and the order of its tails does not matter to the exact sum)
@@ -2417,22 +2423,32 @@ det_status launch_mma(SliceMmaArgs m, hipStream_t s) {
 template <int DT>
 SliceStatArgs stat_args(const void* p, int64_t R, int64_t K, int64_t s_r, int64_t s_k, int32_t* top, int32_t* low,
                         int64_t& blocks) {
-  SliceStatArgs a{p, R, K, s_r, s_k, top, low, false};
+  SliceStatArgs a{p, R, K, s_r, s_k, top, low, false, false};
   const int64_t esz = DT == DET_F32 ? 4 : 2;
   a.vec = s_k == 1 && (reinterpret_cast<uintptr_t>(p) % 16) == 0 && (s_r * esz) % 16 == 0;
+  a.direct = K <= (s_k == 1 ? 1024 : 256);
   blocks = s_k == 1 ? (R * ((K + 1023) / 1024) + 3) / 4 : (R * ((K + 255) / 256) + 255) / 256;
   return a;
 }
 
-// x's and w's span checks: one launch when both have the same layout
+// x's and w's span checks: one launch when both have the same layout.  The
+// tops and lows of x then w are adjacent (topx, lowx hold M + N entries);
+// they need initial values only where several waves share a row.
 template <int DT>
 det_status slice_stats(const GemmArgs& g, int32_t* topx, int32_t* lowx, int32_t* topw, int32_t* loww,
-                       hipStream_t s) {
+                       int32_t* hist, hipStream_t s) {
   int64_t bx, bw;
   const SliceStatArgs ax = stat_args<DT>(g.x, g.M, g.K, g.x_sm, g.x_sk, topx, lowx, bx);
   const SliceStatArgs aw = stat_args<DT>(g.w, g.N, g.K, g.w_sn, g.w_sk, topw, loww, bw);
+  if (!ax.direct || !aw.direct) {
+    hipLaunchKernelGGL(k_slice_init, dim3(grid_for(g.M + g.N, 256, 1024)), dim3(256), 0, s, topx, lowx, g.M + g.N);
+    det_status st = hip_check(hipGetLastError(), "slice init launch");
+    if (st != DET_OK) return st;
+  }
+  bool first = true;
   auto launch = [&](const SliceStatArgs& a0, int64_t b0, const SliceStatArgs& a1, int64_t b1, bool kmaj) {
-    SliceStatPair p{{a0, a1}, b0};
+    SliceStatPair p{{a0, a1}, b0, first ? hist : nullptr};
+    first = false;
     const dim3 grid(static_cast<unsigned>(b0 + b1));
     if (kmaj) hipLaunchKernelGGL((k_slice_stats<DT, true>), grid, dim3(256), 0, s, p);
     else hipLaunchKernelGGL((k_slice_stats<DT, false>), grid, dim3(256), 0, s, p);
@@ -2533,14 +2549,11 @@ det_status launch_sliced(GemmArgs a, char* ws, bool only_slices, int forced, hip
   r8 += 4 * SL_TAIL_CAP * (M + N);
   int64_t* const zfix = reinterpret_cast<int64_t*>(r8);
 
-  hipLaunchKernelGGL(k_slice_init, dim3(grid_for(M + N, 256, 1024)), dim3(256), 0, s, topx, lowx, cntx, M + N,
-                     hist);
-  det_status st = hip_check(hipGetLastError(), "slice init launch");
-  if (st == DET_OK) st = slice_stats<DT>(a, topx, lowx, topw, loww, s);
+  det_status st = slice_stats<DT>(a, topx, lowx, topw, loww, hist, s);
   if (st != DET_OK) return st;
   // x's and w's tops, lows and needs are adjacent: one pass over M + N rows
   hipLaunchKernelGGL(k_slice_need, dim3(grid_for(M + N, 256, 256)), dim3(256), 0, s, topx, lowx, M + N, M, needx,
-                     hist);
+                     hist, cntx);
   st = hip_check(hipGetLastError(), "slice need launch");
   if (st != DET_OK) return st;
   int32_t* const h = pinned(g_pin_hist, 2 * SL_HIST);
