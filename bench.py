@@ -280,6 +280,11 @@ def main() -> int:
                      "ops_per_mac": round(ops_per_mac, 3) if ops_per_mac else None,
                      "ops_source": "rocprofv3 SQ_INSTS_VALU x 64 per launch / MACs per launch",
                      "profile_current": bool(rec and rec["current"]),
+                     # the same kernel's VALU-active share and average clock
+                     # from rocprofv3 counters (SQ_ACTIVE_INST_VALU over
+                     # GRBM_GUI_ACTIVE), from the committed profile
+                     "valu_active_counted": rec.get("valu_active") if rec else None,
+                     "clock_ghz_counted": rec.get("clock_ghz") if rec else None,
                      "kernel": "k_gemm8<f32, 4-bit cells, 2 rows, 16 waves>"},
         "parity": {"sampled_outputs": 256, "bit_exact": parity_ok},
     }
