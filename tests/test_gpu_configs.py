@@ -124,9 +124,13 @@ def test_c4_ksharded_2048_k2e19_fold_tree():
     y_sharded = det.det_finalize(folded)
     y = det.det_gemm(x, w, check_finite=False)
     assert torch.equal(y_sharded.view(torch.int32), y.view(torch.int32))
-    announce("C4 sampled outputs against the oracle")
-    rng = np.random.default_rng(41)
-    rows, cols = _sample(rng, 2048, 2048, 48)
+    # a seeded 1 % sample of the outputs (41943 of 2048^2, each with all 2^19
+    # products) against the oracle; the whole output is covered by the
+    # sharded == unsharded digit equality above
+    count = 2048 * 2048 // 100
+    announce(f"C4 {count} sampled outputs (1 %) against the oracle")
+    flat = np.random.default_rng(41).choice(2048 * 2048, count, replace=False)
+    rows, cols = flat // 2048, flat % 2048
     want_d = c_oracle.partial_pairs(xb, wb, rows, cols)
     got_d = whole[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()].cpu().numpy()
     assert np.array_equal(got_d, want_d), mismatch_report(got_d, want_d)
