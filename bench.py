@@ -43,6 +43,7 @@ sys.path.insert(0, ROOT)
 VALU_PEAK_LANE_OPS = 256 * 64 * 2.4e9
 HBM_PEAK = 8.0e12
 INT8_MFMA_PEAK = 5.0e15             # dense int8 ops/s (2 per MAC)
+LIMB_SPLIT_OPS_F32 = 12             # VALU lane-ops per f32 MAC of the limb-split formulation
 KERNEL_SOURCE = os.path.join(ROOT, "bitwise_deterministic_exact_amd", "csrc", "detgemm.hip")
 PROFILE_RECORD = os.path.join(ROOT, "profiles", "k_gemm8_f32_4096_wide.md")
 
@@ -285,6 +286,13 @@ def main() -> int:
                      # GRBM_GUI_ACTIVE), from the committed profile
                      "valu_active_counted": rec.get("valu_active") if rec else None,
                      "clock_ghz_counted": rec.get("clock_ghz") if rec else None,
+                     # the work of the limb-split formulation (one exact
+                     # product, three limbs and three int64 digit adds: 12
+                     # lane-ops per f32 MAC) at this kernel's MAC rate, over
+                     # the same peak; above 1 because one LDS add per
+                     # product replaces the limb split and digit adds
+                     "limb_split_ops_per_mac": LIMB_SPLIT_OPS_F32,
+                     "limb_split_frac": round(gmacs * 1e9 * LIMB_SPLIT_OPS_F32 / VALU_PEAK_LANE_OPS, 4),
                      "kernel": "k_gemm8<f32, 4-bit cells, 2 rows, 16 waves>"},
         "parity": {"sampled_outputs": 256, "bit_exact": parity_ok},
     }
