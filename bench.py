@@ -199,7 +199,8 @@ def main() -> int:
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the exact GEMM here has no multi-GPU path "
-              "(each GPU would run its own K- or output-shard; see DESIGN.md).", file=sys.stderr)
+              "(each GPU would run its own K- or output-shard of the GEMM, and the shards' raw "
+              "digits would be added with det_combine).", file=sys.stderr)
         return 2
 
     import torch

@@ -7,7 +7,7 @@ Source: the det-train page, "Method" section (digits, limbs, exact products,
 one rounding to fp32), "Usage" section (x is [M, K], w is [N, K], K-slices
 compose) and "Requirements and limits" section (K <= 2^19, bf16 and f32).
 
-Readings of points the page leaves open (each is listed in the design doc):
+Readings of points the page leaves open:
 
 * Digit layout: 18 signed int64 digits, digit j weighs 2^(32*j - 298).  Every
   fp32 (or bf16) product lies in [2^-298, 2^256); 18*32 = 576 bits leave 19+
