@@ -244,3 +244,25 @@ def check_partition(partial: Callable, combine: Callable, x, w, dt, rng) -> List
         if not np.array_equal(combine(parts), whole):
             fails.append(f"{nshards}-way n-ary combine changed the digits")
     return fails
+
+
+def check_combine_exact(combine: Callable, rng) -> List[str]:
+    """a6 (det-train page, "Method": partials of disjoint K ranges add digit by
+    digit): combine is the element-wise sum of all its parts.  Checked against
+    Python integers, which cannot wrap, for 1 to 40 parts of both signs and
+    several shapes, including a part count that is not a power of two and
+    arrays whose length is odd."""
+    fails = []
+    for nparts, shape in [(1, (2, 3, 18)), (2, (1, 18)), (3, (5, 18)), (7, (3, 1, 18)),
+                          (16, (2, 2, 18)), (33, (1, 18)), (40, (4, 18))]:
+        parts = [rng.integers(-(2 ** 56), 2 ** 56, size=shape, dtype=np.int64) for _ in range(nparts)]
+        parts[0].flat[0] = 2 ** 56 - 1                  # extremes of the drawn range
+        parts[-1].flat[-1] = -(2 ** 56)
+        got = combine(parts)
+        if got.shape != parts[0].shape or got.dtype != np.int64:
+            fails.append(f"{nparts} parts: result shape {got.shape} dtype {got.dtype}")
+            continue
+        want = [sum(int(p.flat[i]) for p in parts) for i in range(parts[0].size)]
+        if [int(v) for v in got.reshape(-1)] != want:
+            fails.append(f"{nparts} parts of shape {shape}: digit sums differ from the integer sums")
+    return fails

@@ -97,6 +97,19 @@ def test_partition_and_fold_invariance():
             assert pins.check_partition(oracle.partial, oracle.combine, x, w, dt, rng) == []
 
 
+def test_c_oracle_partition_and_combine():
+    # the C oracle's own partials and combine obey the same partition pin, and
+    # its combine equals exact integer sums
+    rng = np.random.default_rng(17)
+    for dt in ("f32", "bf16"):
+        for kind in ("wide", "normal", "special"):
+            x, w = random_operands(rng, 3, 4, 41, dt, kind)
+            part = lambda a, b, d: c_oracle.partial(a, b)
+            assert pins.check_partition(part, c_oracle.combine, x, w, dt, rng) == []
+    assert pins.check_combine_exact(c_oracle.combine, rng) == []
+    assert pins.check_combine_exact(oracle.combine, rng) == []
+
+
 def test_swap_and_negation():
     rng = np.random.default_rng(7)
     for dt in ("f32", "bf16"):
