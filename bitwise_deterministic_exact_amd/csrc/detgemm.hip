@@ -499,11 +499,13 @@ __global__ __launch_bounds__(64 * W, WPE) void k_partial(GemmArgs a, const void*
 // output weighs 2^(B*c - 298) and takes T = P * 2^s, P the product of the
 // (sign-applied) significands and s the product's bit offset o modulo B.
 // Two grids (the traits below):
-//   Cells8 (f32): B = 8, cell o div 8, s = o mod 8 applied per product;
-//     |P| < 2^48, so |T| < 2^55 and the cells are int64 (ds_add_u64), 256
-//     adds between folds, 64 cells (o <= 506).  Exponent words carry
-//     o * stride / 8, so the cell's byte offset is o & ~(stride - 1) (one
-//     and-or with the lane's offset) and s one bit-field extract.
+//   CellsG<f32, 2, 4> (f32, what det_gemm runs): B = 4, cell o div 4, s = o
+//     mod 4 applied per product; |P| < 2^48, so |T| < 2^51 and the cells are
+//     int64 (ds_add_u64), 4096 adds between folds, 128 cells (o <= 508).
+//     Exponent words carry o * stride / 4, so the cell's byte offset is
+//     o & ~(stride - 1) (one and-or with the lane's offset) and s one
+//     bit-field extract.  (CellsG with B = 8 is the 8-bit form: 256 adds
+//     between folds, 64 cells.)
 //   Cells4 (bf16): B = 4, and each side's exponent is split into a cell part
 //     and a 2-bit shift that is applied to that side's significand when it is
 //     decoded: ex = 4cx + sx, ew = 4cw + sw, x' = x_sig << sx, w' = w_sig <<
@@ -514,20 +516,19 @@ __global__ __launch_bounds__(64 * W, WPE) void k_partial(GemmArgs a, const void*
 //     instructions per product.  int32 cells, 512 adds between folds, 128
 //     cells (offsets 32..538 are cells 7..134).
 //
-// The cells of R x 64 outputs fill R x 32 KB: too much for one wave if the
-// CU is to hold enough waves to keep its VALUs busy, so W waves share them.
-// A workgroup owns rows m0..m0+R-1 and 64 columns; its waves take the
-// K-chunks in turn (wave v: chunks v, v + W, ...) and all add into the same
-// cells, which the LDS atomics keep exact.  At the end of every epoch (the
-// adds a cell can take) the workgroup meets at a barrier, each wave folds its
-// 1/W of the cells into a window of int64 digits in its registers and clears
-// them, and a second barrier opens the next epoch.  At the end the windows
-// are added into one digit array per row in LDS and waves 0..R-1 finish the
-// rows (round to fp32, or carry the digits to the next K block).
+// The cells of R x 64 outputs fill R x 64 KB (f32) or R x 32 KB (bf16): too
+// much for one wave if the CU is to hold enough waves to keep its VALUs busy,
+// so W waves share them (f32: 2 rows, 128 KB, 16 waves, one workgroup per
+// CU; bf16: 2 rows, 64 KB, 8 waves, two workgroups per CU).  A workgroup owns
+// rows m0..m0+R-1 and 64 columns; its waves take the K-chunks in turn (wave
+// v: chunks v, v + W, ...) and all add into the same cells, which the LDS
+// atomics keep exact.  At the end of every epoch (the adds a cell can take)
+// the workgroup meets at a barrier, each wave folds its 1/W of the cells into
+// a window of int64 digits in its registers and clears them, and a second
+// barrier opens the next epoch.  At the end the windows are added into one
+// digit array per row in LDS and waves 0..R-1 finish the rows (round to fp32,
+// or carry the digits to the next K block).
 
-// The grid of B-bit cells (B = 8: Cells8 above; B = 4 takes products below
-// 2^51, so a cell takes 4096 adds between folds instead of 256, in twice as
-// many cells).
 template <int DT, int R, int B>
 struct CellsG {
   static_assert(B == 4 || B == 8, "cell grids of 4 or 8 bits");
@@ -661,15 +662,22 @@ __device__ __forceinline__ void steps8(char* cbase, uint32_t lane, uint32_t lane
 }
 
 // dg += v * scale for a 32-bit v (unsigned or signed) and a power-of-two
-// scale, as one v_mad_u64_u32 / v_mad_i64_i32 (the compiler would otherwise
-// widen, shift and add in four instructions)
+// scale.  The compiler turns a multiply by a known power of two into a
+// widen, a 64-bit shift and an add; hiding only the scale's value (an empty
+// asm statement that emits no instruction) leaves it one v_mad_u64_u32 /
+// v_mad_i64_i32 per call.  Every instruction is the compiler's own, so its
+// hazard recognizer sees all of them: an earlier form issued these two mads
+// from inline assembly, whose VALU writes (64-bit VGPRs and an SGPR carry
+// pair) the recognizer cannot see.
+__device__ __forceinline__ uint32_t opaque_scale(uint32_t scale) {
+  asm("" : "+s"(scale));
+  return scale;
+}
 __device__ __forceinline__ void mad_u32(int64_t& dg, uint32_t v, uint32_t scale) {
-  uint64_t carry;
-  asm("v_mad_u64_u32 %0, %1, %2, %3, %0" : "+v"(dg), "=s"(carry) : "v"(v), "s"(scale));
+  dg = static_cast<int64_t>(static_cast<uint64_t>(dg) + static_cast<uint64_t>(v) * opaque_scale(scale));
 }
 __device__ __forceinline__ void mad_i32(int64_t& dg, int32_t v, uint32_t scale) {
-  uint64_t carry;
-  asm("v_mad_i64_i32 %0, %1, %2, %3, %0" : "+v"(dg), "=s"(carry) : "v"(v), "s"(scale));
+  dg += static_cast<int64_t>(v) * static_cast<int32_t>(opaque_scale(scale));
 }
 
 // Fold the CW cells this wave owns (CW consecutive cells of this lane and
@@ -2209,18 +2217,16 @@ det_status launch_partial(GemmArgs a, void* ws, hipStream_t s) {
   return DET_OK;
 }
 
-// det_gemm: k_gemm8 with two rows and 64 columns per workgroup, 64 KB of
-// cells (f32: Cells8, bf16: Cells4), so two workgroups share a CU: 8 waves
-// each, held to 128 VGPRs (WPE = 4 waves per SIMD) so that all 16 fit.
-// rows per workgroup, waves, waves per SIMD and the cell grid of k_gemm8.
-// f32: the 4-bit grid (4096 adds between folds) on 2 rows, 128 KB of cells
-// shared by 16 waves, one workgroup per CU: 3655 GMAC/s on the wide-range
-// 4096^3 workload against 3465 for the 8-bit grid (64 KB, 8 waves, two
-// workgroups per CU), 3373 for the 4-bit grid on one row, and 3231 for a
-// 4-bit grid with the shift split between the operands at decode (three VALU
-// instructions per product instead of six, but 27-bit operands leave 512 adds
-// between folds: the LDS, not the VALU, binds).  bf16 keeps two 64 KB
-// workgroups of 8 waves (four rows on 128 KB: 4570 against 5369).
+// det_gemm: k_gemm8's configuration per dtype: rows per workgroup, waves,
+// waves per SIMD and the cell grid.  f32: the 4-bit grid (4096 adds between
+// folds) on 2 rows, 128 KB of cells shared by 16 waves, one workgroup per CU:
+// 3655 GMAC/s on the wide-range 4096^3 workload when it was chosen, against
+// 3465 for the 8-bit grid (64 KB, 8 waves, two workgroups per CU), 3373 for
+// the 4-bit grid on one row, and 3231 for a 4-bit grid with the shift split
+// between the operands at decode (three VALU instructions per product instead
+// of six, but 27-bit operands leave 512 adds between folds: the LDS, not the
+// VALU, binds).  bf16 keeps two 64 KB workgroups of 8 waves (four rows on 128
+// KB: 4570 against 5369).
 template <int DT> struct Gemm8Config;
 template <> struct Gemm8Config<DET_F32> {
   static constexpr int R = 2, W = 16, WPE = 4;
@@ -2744,6 +2750,11 @@ det_status det_set_gemm_path(det_path path, int slices) {
   return DET_OK;
 }
 
+void det_get_gemm_path(det_path* path, int* slices) {
+  if (path) *path = static_cast<det_path>(g_path.load());
+  if (slices) *slices = g_forced_slices.load();
+}
+
 void det_last_gemm_plan(int* path, int* slices, int64_t* fallback_rows, int64_t* fallback_cols) {
   if (path) *path = static_cast<int>(g_plan_path);
   if (slices) *slices = g_plan_slices;
@@ -2788,16 +2799,38 @@ det_status det_combine(const int64_t* const* parts, int nparts, int64_t* out, in
   for (int p = 0; p < nparts; ++p)
     if (parts[p] == nullptr) return fail(DET_EINVAL, "null part %d", p);
   const int64_t n = n_outputs * ND;
+  // `out` may be one of the parts (the same pointer); any other overlap with
+  // a part is rejected.  Parts equal to `out` go into the first launch, which
+  // reads every element of its parts before it writes that element of `out`:
+  // later launches would read `out` after it holds the running sum.
+  const uintptr_t o0 = reinterpret_cast<uintptr_t>(out), o1 = o0 + static_cast<uintptr_t>(n) * 8u;
+  int aliased = 0;
+  for (int p = 0; p < nparts; ++p) {
+    const uintptr_t p0 = reinterpret_cast<uintptr_t>(parts[p]), p1 = p0 + static_cast<uintptr_t>(n) * 8u;
+    if (p0 == o0) ++aliased;
+    else if (p0 < o1 && o0 < p1) return fail(DET_EINVAL, "part %d overlaps out without being equal to it", p);
+  }
+  if (aliased > COMBINE_MAX)
+    return fail(DET_EINVAL, "%d parts are equal to out; at most %d may be", aliased, COMBINE_MAX);
   hipStream_t s = static_cast<hipStream_t>(stream);
   // more than COMBINE_MAX parts: fold them in groups, carrying the running sum
   // in `out` (integer addition: any grouping gives the same digits)
-  int done = 0;
+  int next_alias = 0, next_other = 0, done = 0;
+  auto take = [&]() -> const int64_t* {
+    while (next_alias < nparts && parts[next_alias] != out) ++next_alias;
+    if (next_alias < nparts) return parts[next_alias++];
+    while (parts[next_other] == out) ++next_other;
+    return parts[next_other++];
+  };
   while (done < nparts) {
     CombineArgs a{};
     a.out = out;
     a.n = n;
     if (done > 0) a.parts[a.nparts++] = out;
-    while (a.nparts < COMBINE_MAX && done < nparts) a.parts[a.nparts++] = parts[done++];
+    while (a.nparts < COMBINE_MAX && done < nparts) {
+      a.parts[a.nparts++] = take();
+      ++done;
+    }
     hipLaunchKernelGGL(k_combine, dim3(grid_for(n, 256, 65536)), dim3(256), 0, s, a);
     det_status st = hip_check(hipGetLastError(), "combine launch");
     if (st != DET_OK) return st;
