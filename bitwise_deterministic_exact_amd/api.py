@@ -288,18 +288,29 @@ def last_gemm_plan() -> dict:
             "fallback_rows": rows.value, "fallback_cols": cols.value}
 
 
+def get_gemm_path() -> tuple:
+    """The current process-wide (path, slices) setting of set_gemm_path."""
+    path, slices = ctypes.c_int(), ctypes.c_int()
+    _lib.load().det_get_gemm_path(ctypes.byref(path), ctypes.byref(slices))
+    return _PATH_NAMES.get(path.value, "auto"), slices.value
+
+
 class gemm_path:
-    """Context manager: set_gemm_path(path, slices) inside, "auto" after."""
+    """Context manager: set_gemm_path(path, slices) inside; the setting that
+    was in force before is restored on exit (contexts nest)."""
 
     def __init__(self, path: str, slices: int = 0):
         self.path, self.slices = path, slices
+        self._saved = []
 
     def __enter__(self):
+        self._saved.append(get_gemm_path())
         set_gemm_path(self.path, self.slices)
         return self
 
     def __exit__(self, *exc):
-        set_gemm_path("auto", 0)
+        path, slices = self._saved.pop()
+        set_gemm_path(path, slices)
         return False
 
 

@@ -190,6 +190,10 @@ typedef enum { DET_PATH_AUTO = 0, DET_PATH_ACCUMULATOR = 1, DET_PATH_SLICES = 2 
 
 det_status det_set_gemm_path(det_path path, int slices);
 
+/* det_get_gemm_path -- the current process-wide setting of det_set_gemm_path
+ * (path and slices); null pointers are skipped. */
+void det_get_gemm_path(det_path* path, int* slices);
+
 void det_last_gemm_plan(int* path, int* slices, int64_t* fallback_rows, int64_t* fallback_cols);
 
 det_status det_gemm_partial_ws(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk,
@@ -199,10 +203,13 @@ det_status det_gemm_partial_ws(det_dtype dt, const void* x, int64_t x_sm, int64_
 
 /*
  * det_combine -- digit-wise int64 sum of accumulator arrays ("Usage" and
- * "Method": sharded partials compose by adding digit arrays).
+ * "Method": the partials of disjoint K ranges add digit by digit).
  *   parts        HOST array of `nparts` >= 1 device pointers, each to
  *                n_outputs*18 int64 digits
- *   out          device pointer to n_outputs*18 int64; may alias a part
+ *   out          device pointer to n_outputs*18 int64.  `out` may be equal
+ *                to one or more of the parts (the same pointer; at most 32
+ *                of them); a part that overlaps `out` without being equal
+ *                to it is rejected with DET_EINVAL.
  *   n_outputs    number of accumulators (>= 0)
  * Precondition (not checked on the device): every digit sum fits int64 with
  * room for carries, i.e. |sum| <= 2^62; partials of GEMMs whose K values add

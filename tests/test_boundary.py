@@ -63,6 +63,15 @@ def test_c_abi_rejects_bad_arguments_without_a_gpu():
     assert lib.det_combine(None, 0, None, 4, None) == _lib.DET_EINVAL
     ptrs = (ctypes.c_void_p * 1)(None)
     assert lib.det_combine(ptrs, 1, ctypes.c_void_p(1 << 20), 4, None) == _lib.DET_EINVAL
+    # out may equal a part, but may not partly overlap one (n = 4 outputs = 576 bytes)
+    base = 1 << 30
+    ptrs = (ctypes.c_void_p * 2)(base, base + 8)
+    assert lib.det_combine(ptrs, 2, ctypes.c_void_p(base), 4, None) == _lib.DET_EINVAL
+    assert "overlaps" in _lib.last_error()
+    ptrs = (ctypes.c_void_p * 2)(base - 576 + 8, base + 4096)
+    assert lib.det_combine(ptrs, 2, ctypes.c_void_p(base), 4, None) == _lib.DET_EINVAL
+    ptrs = (ctypes.c_void_p * 33)(*([base] * 33))
+    assert lib.det_combine(ptrs, 33, ctypes.c_void_p(base), 4, None) == _lib.DET_EINVAL
     assert lib.det_finalize(None, None, 5, None) == _lib.DET_EINVAL
     assert lib.det_finalize(None, None, -1, None) == _lib.DET_EINVAL
     assert lib.det_round_f32_to_bf16(None, None, 3, None) == _lib.DET_EINVAL
@@ -139,8 +148,21 @@ def test_gemm_path_settings():
         det.set_gemm_path("fast")
     with pytest.raises(ValueError):
         det.set_gemm_path("slices", 9)
+    # contexts restore the setting that was in force before them, and nest
+    assert det.get_gemm_path() == ("auto", 0)
+    det.set_gemm_path("slices", 5)
     with det.gemm_path("accumulator"):
-        pass
+        assert det.get_gemm_path() == ("accumulator", 0)
+        with det.gemm_path("slices", 3):
+            assert det.get_gemm_path() == ("slices", 3)
+        assert det.get_gemm_path() == ("accumulator", 0)
+    assert det.get_gemm_path() == ("slices", 5)
+    with pytest.raises(KeyError):
+        with det.gemm_path("auto"):
+            raise KeyError("restored on an exception too")
+    assert det.get_gemm_path() == ("slices", 5)
+    det.set_gemm_path("auto")
+    assert det.get_gemm_path() == ("auto", 0)
     plan = det.last_gemm_plan()
     assert set(plan) == {"path", "slices", "fallback_rows", "fallback_cols"}
 

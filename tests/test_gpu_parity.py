@@ -3,6 +3,8 @@ bit, at sizes the oracle finishes in seconds (several 16x16 output tiles and
 16-wide K chunks, ragged tails, empty and degenerate shapes, strided views).
 
 Everything is called through the C ABI (via the thin Python binding)."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -13,6 +15,7 @@ from tests import pins
 from tests.gpu_util import announce, digest, f32_bits, mismatch_report, tensor_bits, to_device
 from workloads import random_operands, shard_bounds
 import bitwise_deterministic_exact_amd as det
+from bitwise_deterministic_exact_amd import _lib
 
 pytestmark = pytest.mark.gpu
 
@@ -187,6 +190,22 @@ def test_combine_many_parts_and_aliasing():
              for _ in range(70)]
     want = torch.stack([p.cpu() for p in parts]).sum(0)
     assert torch.equal(det.det_combine(parts).cpu(), want)
+    # through the C ABI, with out equal to a part that falls in a later group
+    # of 32 (parts[35] of 40), then equal to two parts (one in each group)
+    lib = _lib.load()
+    for nparts, alias in ((40, (35,)), (40, (3, 38)), (70, (69,))):
+        announce(f"combine of {nparts} parts, out == parts{list(alias)}")
+        ps = [p.clone() for p in parts[:nparts]]
+        for i in alias[1:]:
+            ps[i] = ps[alias[0]]
+        want = torch.stack([p.cpu() for p in ps]).sum(0)
+        out = ps[alias[0]]
+        ptrs = (ctypes.c_void_p * nparts)(*[p.data_ptr() for p in ps])
+        st = lib.det_combine(ptrs, nparts, ctypes.c_void_p(out.data_ptr()), 33,
+                             ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert st == _lib.DET_OK, _lib.last_error()
+        torch.cuda.synchronize()
+        assert torch.equal(out.cpu(), want)
 
 
 def test_finalize_random_digit_arrays():
