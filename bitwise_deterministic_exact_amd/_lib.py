@@ -44,6 +44,8 @@ def load() -> ctypes.CDLL:
         "det_gemm_workspace_bytes": ([c_int, c_int, i64, i64, i64], i64),
         "det_gemm_ws": ([c_int, vp, i64, i64, vp, i64, i64, i64, i64, i64, vp, i64, i64, vp, ctypes.c_size_t,
                          vp], c_int),
+        "det_gemm_noalloc": ([c_int, vp, i64, i64, vp, i64, i64, i64, i64, i64, vp, i64, i64, vp], c_int),
+        "det_gemm_noalloc_max_bytes": ([], ctypes.c_size_t),
         "det_gemm_partial_ws": ([c_int, vp, i64, i64, vp, i64, i64, i64, i64, i64, vp, vp, ctypes.c_size_t, vp],
                                 c_int),
         "det_combine": ([ctypes.POINTER(vp), c_int, vp, i64, vp], c_int),

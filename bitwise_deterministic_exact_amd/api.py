@@ -116,6 +116,24 @@ def det_gemm(x: torch.Tensor, w: torch.Tensor, *, check_finite: Optional[bool] =
     return out
 
 
+def det_gemm_noalloc(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
+    """det_gemm into a caller-provided float32 [M, N] ``out``, allocating
+    nothing: the library's static device scratch holds the decoded operands
+    (C ABI det_gemm_noalloc; sizes up to its 64 MiB).  Bit-identical to
+    det_gemm.  Inputs must be finite (not checked here: the check would
+    allocate).  Calls that overlap in time on one GPU race."""
+    dt = _operands(x, w)
+    M, K = x.shape
+    N = w.shape[0]
+    if out.shape != (M, N) or out.dtype != torch.float32 or out.device != x.device:
+        raise ValueError("out must be float32 [M, N] on the operands' device")
+    lib = _lib.load()
+    _call(x.device, lib.det_gemm_noalloc, dt, ctypes.c_void_p(x.data_ptr()), x.stride(0), x.stride(1),
+          ctypes.c_void_p(w.data_ptr()), w.stride(0), w.stride(1), M, N, K,
+          ctypes.c_void_p(out.data_ptr()), out.stride(0), out.stride(1), _stream(x.device))
+    return out
+
+
 def det_gemm_partial(x: torch.Tensor, w: torch.Tensor, *, check_finite: Optional[bool] = None,
                      workspace: bool = True) -> torch.Tensor:
     """Raw long-accumulator digits of x w^T: int64 [M, N, 18]."""

@@ -19,6 +19,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "detgemm.h"
@@ -2674,6 +2675,40 @@ det_status launch_gemm(det_dtype dt, int out_mode, GemmArgs a, void* ws, hipStre
   return dt == DET_F32 ? launch_gemm8<DET_F32>(a, ws, s) : launch_gemm8<DET_BF16>(a, ws, s);
 }
 
+// ---------------------------------------------------------------- static scratch
+//
+// det_gemm_noalloc keeps its workspace (w and x decoded, and the digits carried
+// between K blocks) in this file-scope array instead of memory the caller
+// brings in: every GPU the library runs on holds one copy until the process
+// ends, and every det_gemm_noalloc call on that GPU shares it.  In host code
+// `scratch` names a host-side stand-in, not device memory: the kernels get the
+// array's device address, looked up once per device.
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(64) << 20;
+static __device__ __align__(256) char scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES];
+
+// the current device's copy of `scratch` (its address is fixed for the life of
+// the process), looked up with that device current on first use
+det_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  det_status st = hip_check(hipGetDevice(&dev), "hipGetDevice");
+  if (st != DET_OK) return st;
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(DET_EINVAL, "device %d is beyond the %d supported", dev, MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    st = hip_check(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "scratch symbol address");
+    if (st != DET_OK) return st;
+    if (ptr == nullptr || (reinterpret_cast<uintptr_t>(ptr) & 255u)) return fail(DET_EHIP, "scratch address %p", ptr);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DET_OK;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- C ABI
@@ -2774,6 +2809,37 @@ det_status det_gemm_ws(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk, 
   if (workspace == nullptr && M > 0 && N > 0 && K > 0) return fail(DET_EINVAL, "null workspace");
   return gemm_common(1, dt, x, x_sm, x_sk, w, w_sn, w_sk, M, N, K, y, y_sm, y_sn, nullptr, workspace,
                      workspace_bytes, stream);
+}
+
+size_t det_gemm_noalloc_max_bytes(void) { return NOALLOC_SCRATCH_BYTES; }
+
+det_status det_gemm_noalloc(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk, const void* w,
+                            int64_t w_sn, int64_t w_sk, int64_t M, int64_t N, int64_t K, float* y,
+                            int64_t y_sm, int64_t y_sn, void* stream) {
+  det_status st = check_operands(dt, x, x_sm, x_sk, w, w_sn, w_sk, M, N, K);
+  if (st != DET_OK) return st;
+  if (M > 0 && N > 0 && y == nullptr) return fail(DET_EINVAL, "null output");
+  if (y_sm < 0 || y_sn < 0) return fail(DET_EINVAL, "negative output stride");
+  if (reinterpret_cast<uintptr_t>(y) & 3u) return fail(DET_EINVAL, "output must be 4-byte aligned");
+  // the accumulator path's workspace: decoded w, one K block of decoded x,
+  // and for K > 2^15 the digits carried between blocks
+  const double need = static_cast<double>(round_up(N, V_BN)) * round_up(K, V_KC) * 8 +
+                      static_cast<double>(round_up(M, TILE_ROWS)) * round_up(min(K, K_BLOCK), V_KC) * 8 +
+                      (K > K_BLOCK ? 144.0 * static_cast<double>(M) * static_cast<double>(N) : 0.0);
+  if (need > static_cast<double>(NOALLOC_SCRATCH_BYTES))
+    return fail(DET_EINVAL, "det_gemm_noalloc: M=%lld N=%lld K=%lld needs %.0f bytes of scratch, more than its %zu",
+                (long long)M, (long long)N, (long long)K, need, NOALLOC_SCRATCH_BYTES);
+  if (M == 0 || N == 0) return DET_OK;
+  void* ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st != DET_OK) return st;
+  GemmArgs a{};
+  a.x = x; a.x_sm = x_sm; a.x_sk = x_sk;
+  a.w = w; a.w_sn = w_sn; a.w_sk = w_sk;
+  a.M = M; a.N = N; a.K = K;
+  a.y = y; a.y_sm = y_sm; a.y_sn = y_sn;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return dt == DET_F32 ? launch_gemm8<DET_F32>(a, ws, s) : launch_gemm8<DET_BF16>(a, ws, s);
 }
 
 det_status det_gemm_partial(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk, const void* w,

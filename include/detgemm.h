@@ -202,6 +202,30 @@ det_status det_gemm_partial_ws(det_dtype dt, const void* x, int64_t x_sm, int64_
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * det_gemm_noalloc -- det_gemm for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, result and errors as det_gemm, bit for bit;
+ * it runs the pre-decoded digit accumulator of det_gemm_ws with the workspace
+ * in a static device array of det_gemm_noalloc_max_bytes() = 64 MiB that the
+ * library holds on every GPU it runs on until the process ends.  It allocates
+ * nothing (no hipMalloc, no allocating library call) and never waits for the
+ * device: the work is stream-ordered and asynchronous.
+ * Limit: 8 roundup(N, 64) roundup(K, 16) + 8 roundup(M, 2) roundup(min(K, 2^15),
+ * 16) (+ 144 M N when K > 2^15) must not exceed 64 MiB (for example
+ * M = N = K = 2048), else DET_EINVAL before anything is enqueued.
+ * All calls on one GPU share its array: calls whose work overlaps in time on
+ * one GPU (on different streams, or from different threads without ordering)
+ * race and give wrong results; the caller orders them.  No part of the array
+ * needs to start at zero.
+ */
+det_status det_gemm_noalloc(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk,
+                            const void* w, int64_t w_sn, int64_t w_sk,
+                            int64_t M, int64_t N, int64_t K,
+                            float* y, int64_t y_sm, int64_t y_sn, void* stream);
+
+size_t det_gemm_noalloc_max_bytes(void);
+
+/*
  * det_combine -- digit-wise int64 sum of accumulator arrays ("Usage" and
  * "Method": the partials of disjoint K ranges add digit by digit).
  *   parts        HOST array of `nparts` >= 1 device pointers, each to
