@@ -10,9 +10,11 @@ current stream), bracketed by device synchronisation.
 
 Besides the headline line this prints nothing on stdout.  The JSON line also
 carries:
-  roofline      the GEMM kernel against the VALU lane-op peak (bound "alu"):
-                the VALU lane-ops it issues per launch (rocprofv3 SQ_INSTS_VALU x 64,
-                from the committed profile) over its time measured here
+  roofline      the GEMM kernel against the unit that binds it, its LDS atomic
+                adds (one per MAC): atomic lane-ops per launch over the
+                launch's duration (HIP events the library records around the
+                kernel, on its stream), against the atomic rate a probe
+                kernel measures in the same run; the VALU shares beside it
   cpu_baseline  the plain C oracle timed on the host cores over a bounded
                 block of output rows of the same workload
   parity        sampled outputs compared bit for bit with the oracle's
@@ -43,9 +45,78 @@ sys.path.insert(0, ROOT)
 VALU_PEAK_LANE_OPS = 256 * 64 * 2.4e9
 HBM_PEAK = 8.0e12
 INT8_MFMA_PEAK = 5.0e15             # dense int8 ops/s (2 per MAC)
-LIMB_SPLIT_OPS_F32 = 12             # VALU lane-ops per f32 MAC of the limb-split formulation
+INT8_OPS_PER_MFMA = 2 * 16 * 16 * 64  # v_mfma_i32_16x16x64_i8, per wave instruction
+# the f32 det_gemm kernel's work per product (MAC): one 64-bit LDS atomic add
+# into a cell, and six VALU instructions (x broadcast, exponent add, cell
+# address, shift amount, 24x24-bit product, 64-bit shift)
+GEMM8_LDS_ATOMICS_PER_MAC = 1
+GEMM8_VALU_OPS_PER_MAC = 6
 KERNEL_SOURCE = os.path.join(ROOT, "bitwise_deterministic_exact_amd", "csrc", "detgemm.hip")
+PROBE_LIB = os.path.join(ROOT, "bitwise_deterministic_exact_amd", "liblds_probe.so")
 PROFILE_RECORD = os.path.join(ROOT, "profiles", "k_gemm8_f32_4096_wide.md")
+MC_PROFILE_RECORD = os.path.join(ROOT, "profiles", "k_slice_mma_bf16_8192x4096x4096.md")
+
+
+class KernelEvents:
+    """HIP events that libdetgemm.so records around the GEMM kernel of each
+    call (det_set_kernel_events): one start/stop pair per timed step, on the
+    stream the kernel runs on, read after the timed region."""
+
+    def __init__(self, lib, n: int):
+        import ctypes
+        self.ctypes = ctypes
+        # the HIP runtime torch loaded, which libdetgemm.so shares (same soname)
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.lib = lib
+        self.pairs = []
+        for _ in range(n):
+            a, b = ctypes.c_void_p(), ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(a)) or self.hip.hipEventCreate(ctypes.byref(b)):
+                raise RuntimeError("hipEventCreate failed")
+            self.pairs.append((a, b))
+
+    def arm(self, i: int) -> None:
+        self.lib.det_set_kernel_events(self.pairs[i][0], self.pairs[i][1])
+
+    def disarm(self) -> None:
+        self.lib.det_set_kernel_events(None, None)
+
+    def mean_ms(self) -> float:
+        """average start-to-stop time (call after the device has synchronised)"""
+        tot = 0.0
+        for a, b in self.pairs:
+            ms = self.ctypes.c_float()
+            if self.hip.hipEventElapsedTime(self.ctypes.byref(ms), a, b):
+                raise RuntimeError("hipEventElapsedTime failed")
+            tot += ms.value
+        return tot / len(self.pairs)
+
+    def close(self) -> None:
+        self.disarm()
+        for a, b in self.pairs:
+            self.hip.hipEventDestroy(a)
+            self.hip.hipEventDestroy(b)
+
+
+def lds_atomic_peak(bits: int, stream) -> dict:
+    """The measured rate of non-returning LDS atomic adds (64-bit for the f32
+    cells, 32-bit for bf16's) over all CUs, from the probe library
+    (csrc/lds_probe.hip): lane-atomics per second, and per CU per clock at
+    the 2.4 GHz peak engine clock."""
+    import ctypes
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.lds_probe_add_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.POINTER(ctypes.c_float)]
+    lib.lds_probe_lane_ops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.lds_probe_lane_ops.restype = ctypes.c_double
+    blocks, steps = 2048, 4096
+    ms = ctypes.c_float()
+    rc = lib.lds_probe_add_rate(bits, blocks, steps, ctypes.c_void_p(stream), ctypes.byref(ms))
+    if rc != 0:
+        raise RuntimeError(f"LDS probe failed ({rc})")
+    rate = lib.lds_probe_lane_ops(bits, blocks, steps) / (ms.value * 1e-3)
+    return {"rate": rate, "per_cu_clock": rate / 256 / 2.4e9, "ms": ms.value,
+            "probe": f"k_lds_add_rate<{bits}-bit>: {blocks} workgroups x {steps} adds per lane"}
 
 
 def profile_record(path: str = PROFILE_RECORD, kernel: str = None):
@@ -229,16 +300,24 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    kev = KernelEvents(det._lib.load(), args.steps)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
+    start.record(stream)
+    for i in range(args.steps):
+        kev.arm(i)
         step()
-    end.record()
+    end.record(stream)
+    kev.disarm()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
+    kernel_ms = kev.mean_ms()
+    kev.close()
     gmacs = macs / (ms * 1e-3) / 1e9
-    log(f"det_gemm {n}^3: {ms:.3f} ms/step, {gmacs:.1f} GMAC/s")
+    log(f"det_gemm {n}^3: {ms:.3f} ms/step, {gmacs:.1f} GMAC/s; GEMM kernel {kernel_ms:.3f} ms per launch")
+    peak = lds_atomic_peak(64, stream.cuda_stream)
+    log(f"LDS 64-bit atomic peak: {peak['rate'] / 1e12:.3f} T lane-ops/s ({peak['per_cu_clock']:.2f} per CU per clock)")
 
     # parity on sampled outputs (bit for bit against the C oracle)
     rng = np.random.default_rng(1234)
@@ -249,15 +328,18 @@ def main() -> int:
     parity_ok = bool(np.array_equal(got, want))
     log(f"parity on 256 sampled outputs: {'bit-exact' if parity_ok else 'MISMATCH'}")
 
-    # roofline: VALU lane-ops the GEMM kernel issues per MAC (rocprofv3,
-    # committed profile) times the MACs of one launch, over the launch time
-    # measured above (the step is one w pre-decode, 0.2% of it, and one GEMM
-    # launch); traffic only while the profile matches the kernel source
+    # roofline: the GEMM kernel is held to its LDS atomics (one 64-bit add per
+    # MAC) and its VALU (six instructions per MAC); the atomics bind.
+    # achieved = atomic lane-ops per launch / the launch's duration measured
+    # above with HIP events on its stream; peak = the atomic rate the probe
+    # measured just now on this GPU.  traffic only while the committed profile
+    # matches the kernel source.
     rec = profile_record()
-    ops_per_mac = rec["valu_insts"] * 64 / rec["macs"] if rec else None
-    achieved = ops_per_mac * macs / (ms * 1e-3) if rec else None
+    atomics = GEMM8_LDS_ATOMICS_PER_MAC * macs
+    achieved = atomics / (kernel_ms * 1e-3)
     traffic = (int((rec["fetch_kib"] * rec["fetch_scale"] + rec["write_kib"] * rec["write_scale"]) * 1024)
                if rec and rec["current"] and rec["macs"] == macs else None)
+    valu_issued = rec["valu_insts"] * 64 if rec and rec["current"] and rec["macs"] == macs else None
     result = {
         "metric": "exact-GEMM GMAC/s (f32 4096^3) + % VALU peak; bit-exact vs oracle",
         "value": round(gmacs, 2),
@@ -274,27 +356,25 @@ def main() -> int:
         "config": {"workload": f"det_gemm f32 M=N=K={n}, entries sign*m*2^e, m~U[1,2), "
                                f"e~U{{-70..70}}, 1% subnormal (e in [-149,-127]), seed 2",
                    "M": M, "N": N, "K": K, "inputs": "f32", "output": "f32"},
-        "roofline": {"bound": "alu",
-                     "achieved": round(achieved / 1e12, 3) if achieved else None,
-                     "peak": round(VALU_PEAK_LANE_OPS / 1e12, 3), "unit": "Tlane-op/s",
-                     "frac": round(achieved / VALU_PEAK_LANE_OPS, 4) if achieved else None,
+        "roofline": {"bound": "lds",
+                     "achieved": round(achieved / 1e12, 4),
+                     "peak": round(peak["rate"] / 1e12, 4), "unit": "T LDS-atomic lane-ops/s",
+                     "frac": round(achieved / peak["rate"], 4),
                      "traffic": traffic,
-                     "ops_per_mac": round(ops_per_mac, 3) if ops_per_mac else None,
-                     "ops_source": "rocprofv3 SQ_INSTS_VALU x 64 per launch / MACs per launch",
-                     "profile_current": bool(rec and rec["current"]),
-                     # the same kernel's VALU-active share and average clock
-                     # from rocprofv3 counters (SQ_ACTIVE_INST_VALU over
-                     # GRBM_GUI_ACTIVE), from the committed profile
-                     "valu_active_counted": rec.get("valu_active") if rec else None,
-                     "clock_ghz_counted": rec.get("clock_ghz") if rec else None,
-                     # the work of the limb-split formulation (one exact
-                     # product, three limbs and three int64 digit adds: 12
-                     # lane-ops per f32 MAC) at this kernel's MAC rate, over
-                     # the same peak; above 1 because one LDS add per
-                     # product replaces the limb split and digit adds
-                     "limb_split_ops_per_mac": LIMB_SPLIT_OPS_F32,
-                     "limb_split_frac": round(gmacs * 1e9 * LIMB_SPLIT_OPS_F32 / VALU_PEAK_LANE_OPS, 4),
-                     "kernel": "k_gemm8<f32, 4-bit cells, 2 rows, 16 waves>"},
+                     "kernel": "k_gemm8<f32, 4-bit cells, 2 rows, 16 waves>",
+                     "kernel_ms": round(kernel_ms, 4),
+                     "per_mac": f"{GEMM8_LDS_ATOMICS_PER_MAC} ds_add_u64 lane-op + "
+                                f"{GEMM8_VALU_OPS_PER_MAC} VALU lane-ops",
+                     "peak_source": f"measured in this run: {peak['probe']}, "
+                                    f"{peak['per_cu_clock']:.2f} lane-ops per CU per 2.4 GHz clock",
+                     # the other unit the kernel is held to, at the same
+                     # launch time: the VALU work per MAC over the VALU peak
+                     "valu_frac": round(GEMM8_VALU_OPS_PER_MAC * macs / (kernel_ms * 1e-3) / VALU_PEAK_LANE_OPS, 4),
+                     # VALU lane-ops issued per launch (rocprofv3
+                     # SQ_INSTS_VALU x 64, committed profile) over the peak
+                     "valu_issue_frac": (round(valu_issued / (kernel_ms * 1e-3) / VALU_PEAK_LANE_OPS, 4)
+                                         if valu_issued else None),
+                     "profile_current": bool(rec and rec["current"])},
         "parity": {"sampled_outputs": 256, "bit_exact": parity_ok},
     }
 
@@ -316,13 +396,26 @@ def main() -> int:
 
         h = K // 2
         t_part, pa = timed(lambda: det.det_gemm_partial(x[:, :h], w[:, :h], check_finite=False))
-        pb = det.det_gemm_partial(x[:, h:], w[:, h:], check_finite=False)
+        kev = KernelEvents(det._lib.load(), reps)
+        for i in range(reps):
+            kev.arm(i)
+            pb = det.det_gemm_partial(x[:, h:], w[:, h:], check_finite=False)
+        kev.disarm()
+        torch.cuda.synchronize()
+        part_kernel_ms = kev.mean_ms()
+        kev.close()
         t_comb, acc = timed(lambda: det.det_combine([pa, pb]))
         t_fin, yf = timed(lambda: det.det_finalize(acc))
         same = bool(torch.equal(yf.view(torch.int32), y.view(torch.int32)))
         acc_bytes = M * N * 18 * 8
+        # k_partial (f32): two 64-bit LDS atomic adds per product (four 16-bit
+        # fields, two to a counter), against the same measured atomic peak
+        part_atomics = 2 * M * N * (K - h)
         aux["partial_half_k"] = {"ms": round(t_part, 3),
-                                 "GMAC/s": round(M * N * h / (t_part * 1e-3) / 1e9, 2)}
+                                 "GMAC/s": round(M * N * h / (t_part * 1e-3) / 1e9, 2),
+                                 "kernel_ms": round(part_kernel_ms, 3),
+                                 "roofline": {"bound": "lds", "per_mac": "2 ds_add_u64 lane-ops",
+                                              "frac": round(part_atomics / (part_kernel_ms * 1e-3) / peak["rate"], 4)}}
         aux["combine_2"] = {"ms": round(t_comb, 3),
                             "GB/s": round(3 * acc_bytes / (t_comb * 1e-3) / 1e9, 1),
                             "hbm_frac": round(3 * acc_bytes / (t_comb * 1e-3) / HBM_PEAK, 4)}
@@ -371,6 +464,14 @@ def matrix_core_aux(det, dev, timed) -> dict:
     N = w.shape[0]
     t, y = timed(lambda: det.det_gemm(x, w, check_finite=False))
     plan = det.last_gemm_plan()
+    kev = KernelEvents(det._lib.load(), 3)
+    for i in range(3):
+        kev.arm(i)
+        det.det_gemm(x, w, check_finite=False)
+    kev.disarm()
+    torch.cuda.synchronize()
+    kms = kev.mean_ms()
+    kev.close()
     det.set_gemm_path("accumulator")
     try:
         y_acc = det.det_gemm(x, w, check_finite=False)
@@ -382,10 +483,19 @@ def matrix_core_aux(det, dev, timed) -> dict:
            "plan": plan, "equals_accumulator_path": bool(torch.equal(y.view(torch.int32),
                                                                      y_acc.view(torch.int32)))}
     if S:
-        out["roofline"] = {"bound": "mfma", "kernel": f"k_slice_mma<{S}> (whole call timed)",
-                           "achieved": round(ops / (t * 1e-3) / 1e12, 1), "peak": INT8_MFMA_PEAK / 1e12,
-                           "unit": "TOP/s int8", "frac": round(ops / (t * 1e-3) / INT8_MFMA_PEAK, 4),
-                           "ops": "2 S^2 M N K int8 ops per call"}
+        # executed MFMAs: rocprofv3 SQ_INSTS_MFMA per launch from the committed
+        # profile (products with an all-zero lowest-plane fragment are skipped)
+        rec = profile_record(MC_PROFILE_RECORD, f"k_slice_mma<{S}, 2>")
+        executed = (rec["mfma_insts"] * INT8_OPS_PER_MFMA
+                    if rec and rec["current"] and rec["int8_ops"] == ops else None)
+        out["roofline"] = {"bound": "mfma", "kernel": f"k_slice_mma<{S}>", "kernel_ms": round(kms, 4),
+                           "achieved": round(executed / (kms * 1e-3) / 1e12, 1) if executed else None,
+                           "peak": INT8_MFMA_PEAK / 1e12, "unit": "TOP/s int8",
+                           "frac": round(executed / (kms * 1e-3) / INT8_MFMA_PEAK, 4) if executed else None,
+                           "ops": "executed v_mfma_i32_16x16x64_i8 x 32768 int8 ops per launch",
+                           "dense_frac": round(ops / (kms * 1e-3) / INT8_MFMA_PEAK, 4),
+                           "dense_ops": "2 S^2 M N K int8 ops (skipped products counted as done)",
+                           "profile_current": bool(rec and rec["current"])}
     del x, w, y, y_acc
     return out
 

@@ -55,6 +55,7 @@ def load() -> ctypes.CDLL:
         "det_dot_partial": ([c_int, vp, i64, vp, i64, i64, vp, c_int, vp], c_int),
         "det_sqdiff_partial": ([c_int, vp, i64, vp, i64, i64, vp, c_int, vp], c_int),
         "det_set_gemm_path": ([c_int, c_int], c_int),
+        "det_set_kernel_events": ([vp, vp], None),
         "det_get_gemm_path": ([ctypes.POINTER(c_int), ctypes.POINTER(c_int)], None),
         "det_last_gemm_plan": ([ctypes.POINTER(c_int), ctypes.POINTER(c_int), ctypes.POINTER(i64),
                                 ctypes.POINTER(i64)], None),

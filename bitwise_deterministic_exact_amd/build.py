@@ -10,6 +10,9 @@ ROOT = os.path.dirname(PKG)
 SOURCES = [os.path.join(PKG, "csrc", "detgemm.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdetgemm.so")
+# the benchmark's LDS-atomic peak probe: its own library, never loaded by the package
+PROBE_SOURCES = [os.path.join(PKG, "csrc", "lds_probe.hip")]
+PROBE_LIB = os.path.join(PKG, "liblds_probe.so")
 ARCH = "gfx950"
 
 # -packed-fp32-ops off: no v_pk_{add,mul,fma}_f32 in any generated code
@@ -25,8 +28,8 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    cmd = [hipcc(), *HIPCC_FLAGS, "-o", LIB + ".tmp", *SOURCES]
+def _hipcc(sources, out: str, verbose: bool) -> str:
+    cmd = [hipcc(), *HIPCC_FLAGS, "-o", out + ".tmp", *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -36,8 +39,14 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err:
         print(err, file=sys.stderr)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Build libdetgemm.so and the benchmark's probe library."""
+    _hipcc(PROBE_SOURCES, PROBE_LIB, verbose)
+    return _hipcc(SOURCES, LIB, verbose)
 
 
 def device_asm(out_path: str) -> str:

@@ -44,6 +44,17 @@ det_status hip_check(hipError_t e, const char* what) {
   return DET_OK;
 }
 
+// Optional timing of a call's main GEMM kernel (det_set_kernel_events): the
+// calling thread's two events, recorded on the call's stream just before the
+// first and just after the last launch of the kernel that forms the call's
+// products (k_gemm8, k_slice_mma or k_partial).  Null: nothing is recorded.
+thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
+
+det_status mark_event(hipEvent_t ev, bool now, hipStream_t s) {
+  if (!now || ev == nullptr) return DET_OK;
+  return hip_check(hipEventRecord(ev, s), "kernel timing event");
+}
+
 // Packed exponent word (see decode below): the exponent offset sits at bits
 // 5..14 and, for raw digits, the sign at bit 15.
 constexpr uint32_t EXP_SHIFT = 5;
@@ -2210,9 +2221,12 @@ det_status launch_partial(GemmArgs a, void* ws, hipStream_t s) {
           b, xb, static_cast<char*>(ws) + predecode_bytes(0, a.N, a.K), s);
       if (st != DET_OK) return st;
     }
+    det_status st = mark_event(g_ev_start, ib == 0, s);
+    if (st != DET_OK) return st;
     if (pre) hipLaunchKernelGGL((k_partial<DT, true, R, PAIR, W, WPE>), grid, block, 0, s, b, xb, wb);
     else hipLaunchKernelGGL((k_partial<DT, false, R, PAIR, W, WPE>), grid, block, 0, s, b, xb, wb);
-    det_status st = hip_check(hipGetLastError(), "gemm launch");
+    st = hip_check(hipGetLastError(), "gemm launch");
+    if (st == DET_OK) st = mark_event(g_ev_stop, ib + 1 == nblk, s);
     if (st != DET_OK) return st;
   }
   return DET_OK;
@@ -2239,7 +2253,7 @@ template <> struct Gemm8Config<DET_BF16> {
 };
 
 template <int DT>
-det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s) {
+det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s, bool timed = true) {
   using C = Gemm8Config<DT>;
   constexpr int R = C::R, W = C::W, WPE = C::WPE;
   using G = typename C::G;
@@ -2284,9 +2298,12 @@ det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s) {
       det_status st = predecode_x_block<G, DT>(b, xb, static_cast<char*>(ws) + predecode_bytes(1, a.N, a.K), s);
       if (st != DET_OK) return st;
     }
+    det_status st = mark_event(g_ev_start, timed && first, s);
+    if (st != DET_OK) return st;
     if (pre) hipLaunchKernelGGL((k_gemm8<G, DT, true, R, W, WPE>), grid, block, 0, s, b, xb, a.w);
     else hipLaunchKernelGGL((k_gemm8<G, DT, false, R, W, WPE>), grid, block, 0, s, b, xb, a.w);
-    det_status st = hip_check(hipGetLastError(), "gemm launch");
+    st = hip_check(hipGetLastError(), "gemm launch");
+    if (st == DET_OK) st = mark_event(g_ev_stop, timed && last, s);
     if (st != DET_OK) return st;
   }
   return DET_OK;
@@ -2404,8 +2421,11 @@ det_status launch_mma_cb(SliceMmaArgs m, hipStream_t s) {
     b.kb0 = ib * SL_FOLD;
     b.kb1 = min(m.Kb, b.kb0 + SL_FOLD);
     b.epi = nblk == 1 ? EPI_ROUND : ib == 0 ? EPI_STORE : ib + 1 == nblk ? EPI_ADD_ROUND : EPI_ADD;
+    det_status st = mark_event(g_ev_start, ib == 0, s);
+    if (st != DET_OK) return st;
     hipLaunchKernelGGL((k_slice_mma<S, CB, WR, NBUF>), grid, block, 0, s, b);
-    det_status st = hip_check(hipGetLastError(), "slice mma launch");
+    st = hip_check(hipGetLastError(), "slice mma launch");
+    if (st == DET_OK) st = mark_event(g_ev_stop, ib + 1 == nblk, s);
     if (st != DET_OK) return st;
   }
   return DET_OK;
@@ -2509,7 +2529,7 @@ det_status slice_make(const GemmArgs& g, const int32_t* topx, const int32_t* top
 }
 
 template <int DT>
-det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s);
+det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s, bool timed);
 
 // The accumulator path on a subset: rows `rows` of x (m = M), or the rows
 // `cols` of w (n = N), overwriting those outputs of y.
@@ -2520,7 +2540,7 @@ det_status recompute(GemmArgs a, char* ws, const int32_t* rows, int64_t m, const
   GemmArgs b = a;
   b.M = m; b.N = n;
   b.xmap = rows; b.wmap = cols;
-  return launch_gemm8<DT>(b, ws, s);
+  return launch_gemm8<DT>(b, ws, s, false);
 }
 
 // det_gemm with the room for both paths in `ws`: span statistics, the
@@ -2809,6 +2829,11 @@ det_status det_gemm_ws(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk, 
   if (workspace == nullptr && M > 0 && N > 0 && K > 0) return fail(DET_EINVAL, "null workspace");
   return gemm_common(1, dt, x, x_sm, x_sk, w, w_sn, w_sk, M, N, K, y, y_sm, y_sn, nullptr, workspace,
                      workspace_bytes, stream);
+}
+
+void det_set_kernel_events(void* start, void* stop) {
+  g_ev_start = static_cast<hipEvent_t>(start);
+  g_ev_stop = static_cast<hipEvent_t>(stop);
 }
 
 size_t det_gemm_noalloc_max_bytes(void) { return NOALLOC_SCRATCH_BYTES; }

@@ -226,6 +226,20 @@ det_status det_gemm_noalloc(det_dtype dt, const void* x, int64_t x_sm, int64_t x
 size_t det_gemm_noalloc_max_bytes(void);
 
 /*
+ * det_set_kernel_events -- for callers that time the GEMM kernel itself (the
+ * benchmark): the calling thread's later det_gemm, det_gemm_ws,
+ * det_gemm_noalloc, det_gemm_partial and det_gemm_partial_ws calls record
+ * `start` (a hipEvent_t) on their stream just before the first launch of the
+ * kernel that forms the products (the digit accumulator, or on the
+ * matrix-core path the int8 digit GEMMs), and `stop` just after its last
+ * launch; with K > 2^15 the interval also holds the per-block x decodes
+ * between launches.  Calls that launch no such kernel (an empty M or N)
+ * record nothing.  The events stay owned by the caller; null for either
+ * turns its recording off.
+ */
+void det_set_kernel_events(void* start, void* stop);
+
+/*
  * det_combine -- digit-wise int64 sum of accumulator arrays ("Usage" and
  * "Method": the partials of disjoint K ranges add digit by digit).
  *   parts        HOST array of `nparts` >= 1 device pointers, each to
