@@ -14,7 +14,11 @@ correctly rounded, by n as an fp32 value (n itself rounded to fp32 above
 Without a target the loss is sum y^2 / n.
 
 The gradient 2 (y - t) / n is elementwise (no reduction, so no order to fix)
-and is formed with torch's elementwise ops.
+and is formed with torch's elementwise fp32 ops, each correctly rounded:
+  dy = RNE_dtype( RNE32( RNE32(y - t) * c ) * g ),  c = RNE32(2 / fp32(n)),
+with g the incoming gradient (1 when the loss is the output) and the last
+rounding only for bfloat16 y.  When n is a power of two (and nothing
+underflows) c is exact and the scaling adds no rounding.
 """
 from __future__ import annotations
 
@@ -39,11 +43,14 @@ class _ExactMSE(torch.autograd.Function):
     @staticmethod
     def backward(ctx, g: torch.Tensor):
         y, t = ctx.saved_tensors
-        n = max(y.numel(), 1)
+        # c = 2 / n as one IEEE fp32 division on the device (a Python scalar
+        # would reach the kernel as a double rounded to fp32: two roundings)
+        two = torch.full((), 2.0, dtype=torch.float32, device=y.device)
+        c = two / torch.full((), float(max(y.numel(), 1)), dtype=torch.float32, device=y.device)
         d = y.to(torch.float32)
         if ctx.has_target:
             d = d - t.to(torch.float32)
-        gy = (d * (2.0 / n)) * g
+        gy = (d * c) * g
         dy = gy.to(y.dtype) if ctx.needs_input_grad[0] else None
         dt = (-gy).to(t.dtype) if ctx.has_target and ctx.needs_input_grad[1] else None
         return dy, dt

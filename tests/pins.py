@@ -266,3 +266,30 @@ def check_combine_exact(combine: Callable, rng) -> List[str]:
         if [int(v) for v in got.reshape(-1)] != want:
             fails.append(f"{nparts} parts of shape {shape}: digit sums differ from the integer sums")
     return fails
+
+
+def rne_fraction(v: Fraction, p: int, emin: int = -126, emax: int = 127):
+    """The exact rational v rounded to the nearest binary float with a p-bit
+    significand (ties to even), gradual underflow below 2^emin, and values that
+    round to 2^(emax+1) or more returned as +-inf (a float); otherwise a
+    Fraction.  p = 24 is binary32, p = 8 bfloat16 (both emin -126, emax 127)."""
+    if v == 0:
+        return Fraction(0)
+    a = abs(v)
+    e = emin
+    if a >= Fraction(2) ** emin:                         # a in [2^e, 2^(e+1))
+        e = a.numerator.bit_length() - a.denominator.bit_length() - 1
+        while Fraction(2) ** (e + 1) <= a:
+            e += 1
+        while Fraction(2) ** e > a:
+            e -= 1
+    ulp = Fraction(2) ** (e - (p - 1))
+    q = a / ulp
+    r = q.numerator // q.denominator
+    rem = q - r
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and r % 2 == 1):
+        r += 1
+    out = r * ulp
+    if out >= Fraction(2) ** (emax + 1):
+        return float("inf") if v > 0 else float("-inf")
+    return out if v > 0 else -out

@@ -7,6 +7,7 @@ The bias gradient is the exact column sum of dY, the GEMM of dY^T with a row
 of ones.  K past 2^19 runs as K-slices of raw digits composed by
 det_combine, which the oracle's single exact sum must equal.  The loss is
 the exact sum of squared errors rounded once, then divided by n in fp32."""
+from fractions import Fraction
 import numpy as np
 import pytest
 import torch
@@ -14,6 +15,7 @@ import torch
 import bitwise_deterministic_exact_amd as det
 from oracle import c_oracle
 from oracle.exact import f32_bits_to_bf16_bits
+from tests import pins
 from tests.gpu_util import announce, f32_bits, mismatch_report, tensor_bits, to_device
 from workloads import random_operands
 
@@ -217,6 +219,33 @@ def _loss_oracle(yb, tb, dt):
     return np.float32(np.array([s], dtype=np.uint32).view(np.float32)[0] / np.float32(yb.size))
 
 
+def _mse_grad_reference(yb, tb, n, dt):
+    """The exact-MSE gradient's bits as the loss defines them:
+    RNE_dt(RNE32(RNE32(y - t) * RNE32(2 / fp32(n)))), from exact rationals: the
+    difference and the scale rounded to fp32 by pins.rne_fraction, their product
+    formed exactly in fp64 (two 24-bit significands), one IEEE cast to fp32,
+    and for bf16 rne_fraction to 8 bits."""
+    as_f32 = lambda b: float(np.array([b], dtype=np.uint32).view(np.float32)[0])
+    val = (lambda b: Fraction(as_f32(int(b)))) if dt == "f32" else (lambda b: Fraction(as_f32(int(b) << 16)))
+    c = pins.rne_fraction(Fraction(2) / Fraction(float(np.float32(n))), 24)
+    out = []
+    for yv, tv in zip(yb.tolist(), tb.tolist()):
+        d = pins.rne_fraction(val(yv) - val(tv), 24)
+        if d == 0:                                    # an exact zero keeps IEEE's sign: (-0) - (+0) = -0
+            d = (as_f32(int(yv)) if dt == "f32" else as_f32(int(yv) << 16)) - \
+                (as_f32(int(tv)) if dt == "f32" else as_f32(int(tv) << 16))
+        g = np.float32(np.float64(float(d)) * np.float64(float(c)))      # exact product, one rounding
+        if dt == "bf16":
+            gb = g if np.isinf(g) else np.float32(float(pins.rne_fraction(Fraction(float(g)), 8)))
+            bits = int(np.array([gb], dtype=np.float32).view(np.uint32)[0]) >> 16
+            if gb == 0 and np.signbit(g):             # a negative value rounded to zero is -0
+                bits = 0x8000
+            out.append(bits)
+        else:
+            out.append(int(np.array([g], dtype=np.float32).view(np.uint32)[0]))
+    return np.array(out, dtype=np.uint16 if dt == "bf16" else np.uint32)
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_exact_mse_loss(dt):
     rng = np.random.default_rng(650 + (dt == "bf16"))
@@ -234,12 +263,12 @@ def test_exact_mse_loss(dt):
         perm = torch.from_numpy(rng.permutation(n)).cuda()
         assert torch.equal(det.exact_mse_loss(y.detach()[perm], t[perm]).view(torch.int32),
                            loss.detach().view(torch.int32))
-        # the gradient 2 (y - t) / n, elementwise
+        # the gradient, elementwise: RNE_dt(RNE32(RNE32(y - t) * RNE32(2 / fp32(n)))),
+        # computed here from exact rationals and one IEEE cast
         loss.backward()
-        yf, tf = y.detach().float(), t.float()
-        want_g = ((yf - tf) * (2.0 / n)).to(y.dtype)
-        assert torch.equal(y.grad.view(torch.int16 if dt == "bf16" else torch.int32),
-                           want_g.view(torch.int16 if dt == "bf16" else torch.int32))
+        want_g = _mse_grad_reference(yb, tb, n, dt)
+        got_g = tensor_bits(y.grad)
+        assert np.array_equal(got_g, want_g), mismatch_report(got_g, want_g)
     # the fp32 division of the rounded sum by n is correctly rounded
     s32 = rng.standard_normal(4096).astype(np.float32) * np.float32(1e3)
     for n in (3, 7, 1000, 12293, 8191, 1 << 20):

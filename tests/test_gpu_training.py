@@ -15,7 +15,8 @@ import pytest
 import torch
 
 import bitwise_deterministic_exact_amd as det
-from tests.gpu_util import announce
+from oracle import c_oracle
+from tests.gpu_util import announce, mismatch_report
 
 pytestmark = pytest.mark.gpu
 
@@ -34,24 +35,62 @@ def _data(seed=7):
     return [torch.from_numpy(a).cuda() for a in (x, y, w1, w2)]
 
 
-def _train_det(k_shards):
+RECORD = (0, 80, STEPS - 1)       # steps whose GEMMs are checked against the oracle
+
+
+def _train_det(k_shards, record=()):
+    """Train; for the steps in `record` also keep what each layer's GEMMs
+    read and wrote: the layer inputs and weights of the step, the forward
+    outputs, the gradients arriving at the outputs (dY), the layer-2 input
+    gradient (dX) and the weight gradients."""
     x, y, w1, w2 = _data()
     l1 = det.DetLinear(IN, HID, device="cuda", k_shards=k_shards)
     l2 = det.DetLinear(HID, OUT, device="cuda", k_shards=k_shards)
     with torch.no_grad():
         l1.weight.copy_(w1)
         l2.weight.copy_(w2)
-    losses = []
-    for _ in range(STEPS):
-        h = torch.relu(l1(x))
-        loss = (l2(h) - y).square().mean()
+    losses, kept = [], {}
+    for step in range(STEPS):
+        y1 = l1(x)
+        h = torch.relu(y1)
+        h.retain_grad()
+        y2 = l2(h)
+        loss = (y2 - y).square().mean()
+        grads = {}
+        if step in record:
+            y1.register_hook(lambda g: grads.__setitem__("dy1", g.detach().clone()))
+            y2.register_hook(lambda g: grads.__setitem__("dy2", g.detach().clone()))
+            kept[step] = {"x": x, "w1": l1.weight.detach().clone(), "w2": l2.weight.detach().clone(),
+                          "y1": y1.detach().clone(), "h": h.detach().clone(), "y2": y2.detach().clone()}
         l1.weight.grad = l2.weight.grad = None
         loss.backward()
+        if step in record:
+            kept[step].update(grads, dh=h.grad.detach().clone(), dw1=l1.weight.grad.detach().clone(),
+                              dw2=l2.weight.grad.detach().clone())
         with torch.no_grad():
             l1.weight -= LR * l1.weight.grad
             l2.weight -= LR * l2.weight.grad
         losses.append(loss.detach())
-    return torch.stack(losses), l1.weight.detach().clone(), l2.weight.detach().clone()
+    out = (torch.stack(losses), l1.weight.detach().clone(), l2.weight.detach().clone())
+    return out + (kept,) if record else out
+
+
+def _np_bits(t):
+    return t.detach().contiguous().cpu().numpy().view(np.uint32)
+
+
+def _check_step_against_oracle(rec):
+    """Each of the step's five GEMMs, every output, against the oracle (f32
+    parameters: the results are the oracle's fp32 bits): y1 = x W1^T, y2 =
+    h W2^T, dh = dY2 W2 (K = 32), dW2 = dY2^T h and dW1 = dY1^T x (K =
+    the batch, 128)."""
+    b = {k: _np_bits(v) for k, v in rec.items()}
+    T = lambda a: np.ascontiguousarray(a.T)
+    cases = [("y1", b["x"], b["w1"]), ("y2", b["h"], b["w2"]), ("dh", b["dy2"], T(b["w2"])),
+             ("dw2", T(b["dy2"]), T(b["h"])), ("dw1", T(b["dy1"]), T(b["x"]))]
+    for name, xa, wa in cases:
+        want = c_oracle.gemm(xa, wa)
+        assert np.array_equal(b[name], want), f"{name}: " + mismatch_report(b[name].ravel(), want.ravel())
 
 
 def _linear_fp32(x, w, k_shards):
@@ -87,8 +126,13 @@ def _bits(t):
 
 def test_160_steps_unsharded_vs_4way_ksharded_identical_bytes():
     announce(f"training {STEPS} steps, DetLinear MLP {IN}-{HID}-{OUT}, k_shards 1 and 4")
-    loss1, a1, b1 = _train_det(1)
-    loss4, a4, b4 = _train_det(4)
+    loss1, a1, b1, kept1 = _train_det(1, RECORD)
+    loss4, a4, b4, kept4 = _train_det(4, RECORD)
+    # at steps 0, 80 and 159 every GEMM of both runs equals the oracle's
+    for step in RECORD:
+        announce(f"training step {step}: the five GEMMs of each run against the oracle")
+        _check_step_against_oracle(kept1[step])
+        _check_step_against_oracle(kept4[step])
     # it trains: the loss falls
     assert loss1[-1].item() < 0.5 * loss1[0].item()
     # exact accumulation: identical losses at every step and identical weights

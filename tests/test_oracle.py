@@ -251,3 +251,27 @@ def test_validation_errors():
         oracle.combine([a, a])
     with pytest.raises(ValueError):
         c_oracle.combine([a, a])
+
+
+def test_rne_fraction_matches_ieee_casts():
+    # the rational rounding the loss-gradient reference uses, against numpy's
+    # IEEE binary32 cast of exactly representable binary64 values: normals,
+    # subnormals, halfway ties, values that overflow, and exact zero
+    rng = np.random.default_rng(71)
+    vals = [0.0, 2.0 ** -149, 2.0 ** -150, 3 * 2.0 ** -151, 2.0 ** -126 * (1 - 2.0 ** -30),
+            float(np.finfo(np.float32).max), float(np.finfo(np.float32).max) * (1 + 2.0 ** -25),
+            float(np.finfo(np.float32).max) * (1 + 2.0 ** -24), 2.0 ** 128, 1 + 2.0 ** -24, 1 + 3 * 2.0 ** -24]
+    vals += list(rng.standard_normal(2000) * 2.0 ** rng.integers(-160, 130, 2000))
+    for v in vals:
+        for s in (1, -1):
+            x = s * v
+            want = np.float32(x)
+            got = pins.rne_fraction(Fraction(x), 24)
+            assert float(got) == float(want) and (np.signbit(want) == (x < 0) or want == 0), x
+    # bfloat16: 8-bit significand, against torch's CPU cast of float32 values
+    import torch
+    f = (rng.standard_normal(3000) * 2.0 ** rng.integers(-135, 128, 3000)).astype(np.float32)
+    f = f[np.isfinite(f)]
+    want = torch.from_numpy(f).to(torch.bfloat16).float().numpy()
+    for x, w in zip(f.tolist(), want.tolist()):
+        assert float(pins.rne_fraction(Fraction(x), 8)) == w, x
