@@ -10,7 +10,7 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdetgemm.so")
 
-DET_OK, DET_EINVAL, DET_EKLIMIT, DET_EDTYPE, DET_EHIP = 0, 1, 2, 3, 5
+DET_OK, DET_EINVAL, DET_EKLIMIT, DET_EDTYPE, DET_ENONFINITE, DET_EHIP, DET_ERANGE = 0, 1, 2, 3, 4, 5, 6
 DET_F32, DET_BF16 = 0, 1
 DET_PATH_AUTO, DET_PATH_ACCUMULATOR, DET_PATH_SLICES = 0, 1, 2
 NUM_DIGITS = 18
@@ -56,6 +56,8 @@ def load() -> ctypes.CDLL:
         "det_sqdiff_partial": ([c_int, vp, i64, vp, i64, i64, vp, c_int, vp], c_int),
         "det_set_gemm_path": ([c_int, c_int], c_int),
         "det_set_kernel_events": ([vp, vp], None),
+        "det_device_status": ([vp, c_int, ctypes.POINTER(c_int)], c_int),
+        "det_device_status_word": ([], vp),
         "det_get_gemm_path": ([ctypes.POINTER(c_int), ctypes.POINTER(c_int)], None),
         "det_last_gemm_plan": ([ctypes.POINTER(c_int), ctypes.POINTER(c_int), ctypes.POINTER(i64),
                                 ctypes.POINTER(i64)], None),

@@ -13,6 +13,9 @@ digits int64 [M, N, 18] (digit j weighs 2^(32j-298)).
 Non-finite inputs are rejected with ValueError when ``check_finite`` is true;
 its default comes from the environment variable DETGEMM_CHECK_FINITE ("1",
 the default, or "0").  The check costs one small kernel and a device sync.
+Unchecked calls still note an Inf or NaN operand (and combine and finalize a
+digit outside +-2^62) in the GPU's sticky device status, read with
+device_status().
 """
 from __future__ import annotations
 
@@ -120,8 +123,9 @@ def det_gemm_noalloc(x: torch.Tensor, w: torch.Tensor, out: torch.Tensor) -> tor
     """det_gemm into a caller-provided float32 [M, N] ``out``, allocating
     nothing: the library's static device scratch holds the decoded operands
     (C ABI det_gemm_noalloc; sizes up to its 64 MiB).  Bit-identical to
-    det_gemm.  Inputs must be finite (not checked here: the check would
-    allocate).  Calls that overlap in time on one GPU race."""
+    det_gemm.  Inputs must be finite; an Inf or NaN is not checked for here
+    (the check would allocate) but is noted in the device status (see
+    device_status).  Calls that overlap in time on one GPU race."""
     dt = _operands(x, w)
     M, K = x.shape
     N = w.shape[0]
@@ -330,6 +334,21 @@ class gemm_path:
         path, slices = self._saved.pop()
         set_gemm_path(path, slices)
         return False
+
+
+def device_status(device=None, clear: bool = True) -> set:
+    """The sticky device status of `device` (default: the current one) after
+    the work enqueued so far on its current stream: a set holding
+    "nonfinite" (an operand held Inf or NaN) and/or "range" (a digit outside
+    +-2^62 reached combine or finalize).  Waits for the stream; with `clear`
+    the status is reset after it is read (det_device_status)."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    flags = ctypes.c_int()
+    with torch.cuda.device(dev):
+        st = _lib.load().det_device_status(_stream(dev), int(bool(clear)), ctypes.byref(flags))
+    if st not in (_lib.DET_OK, _lib.DET_ENONFINITE, _lib.DET_ERANGE):
+        _lib.check(st)
+    return {name for bit, name in ((1, "nonfinite"), (2, "range")) if flags.value & bit}
 
 
 def round_f32_to_bf16(t: torch.Tensor) -> torch.Tensor:

@@ -55,6 +55,28 @@ det_status mark_event(hipEvent_t ev, bool now, hipStream_t s) {
   return hip_check(hipEventRecord(ev, s), "kernel timing event");
 }
 
+// Conditions only the kernels can see, kept per GPU until cleared (sticky,
+// like IEEE 754's exception flags): word 0 becomes 1 when an operand element
+// is Inf or NaN, word 1 when a digit handed to combine or finalize, or a
+// digit sum of combine, lies outside +-2^62.  Kernels store 1 and never 0;
+// only det_device_status clears the words.  In host code the array's name is
+// a host-side stand-in: host code uses the address status_words() looks up.
+static __device__ __align__(16) int32_t g_dev_status[4];
+
+template <int DT>
+__device__ __forceinline__ bool nonfinite_bits(uint32_t b) {
+  return DT == DET_F32 ? (b & 0x7F800000u) == 0x7F800000u : (b & 0x7F80u) == 0x7F80u;
+}
+__device__ __forceinline__ void note_nonfinite(bool bad) {
+  if (bad) g_dev_status[0] = 1;
+}
+__device__ __forceinline__ bool digit_in_range(int64_t v) {        // -2^62 <= v <= 2^62
+  return static_cast<uint64_t>(v) + (uint64_t(1) << 62) <= (uint64_t(1) << 63);
+}
+__device__ __forceinline__ void note_range(bool bad) {
+  if (bad) g_dev_status[1] = 1;
+}
+
 // Packed exponent word (see decode below): the exponent offset sits at bits
 // 5..14 and, for raw digits, the sign at bit 15.
 constexpr uint32_t EXP_SHIFT = 5;
@@ -970,6 +992,7 @@ __global__ __launch_bounds__(256) void k_predecode_w(PredecodeArgs a) {
   static_assert(sizeof(EW) == 2, "k_gemm's exponent words are 16-bit");
   const int64_t total = a.Np * a.Kp;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  bool bad = false;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
     int64_t n, k;
     subblock_nk(i, a.Np, n, k);
@@ -977,10 +1000,13 @@ __global__ __launch_bounds__(256) void k_predecode_w(PredecodeArgs a) {
     uint32_t e;
     // padding holds the decode of +0 (significand 0, exponent field 1), so
     // the exponent sums of padded products stay inside the counter range
-    decode<DT, TWOS, 1, ESH>(n < a.N && k < a.K ? load_elem<DT>(a.w, n * a.w_sn + k * a.w_sk) : 0u, m, e);
+    const uint32_t b = n < a.N && k < a.K ? load_elem<DT>(a.w, n * a.w_sn + k * a.w_sk) : 0u;
+    bad |= nonfinite_bits<DT>(b);
+    decode<DT, TWOS, 1, ESH>(b, m, e);
     a.wsig[i] = m;
     static_cast<EW*>(a.wexp)[exp16_index(n, k, a.Np)] = static_cast<EW>(e);
   }
+  note_nonfinite(bad);
 }
 
 // the same for k_gemm8: the grid's w-side words (32-bit), lane = n mod 64
@@ -988,17 +1014,20 @@ template <class G, int DT>
 __global__ __launch_bounds__(256) void k_predecode_w8(PredecodeArgs a) {
   const int64_t total = a.Np * a.Kp;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  bool bad = false;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
     int64_t n, k;
     subblock_nk(i, a.Np, n, k);
     int32_t m;
     uint32_t e;
     const int64_t src = n < a.N && a.rmap != nullptr ? a.rmap[n] : n;
-    G::decode_w(n < a.N && k < a.K ? load_elem<DT>(a.w, src * a.w_sn + k * a.w_sk) : 0u,
-                static_cast<uint32_t>(n & (V_BN - 1)), m, e);
+    const uint32_t b = n < a.N && k < a.K ? load_elem<DT>(a.w, src * a.w_sn + k * a.w_sk) : 0u;
+    bad |= nonfinite_bits<DT>(b);
+    G::decode_w(b, static_cast<uint32_t>(n & (V_BN - 1)), m, e);
     a.wsig[i] = m;
     static_cast<uint32_t*>(a.wexp)[i] = e;
   }
+  note_nonfinite(bad);
 }
 
 // x of one K block [M][K] (any strides) -> the x side's significands and
@@ -1016,13 +1045,15 @@ template <class D, int DT>
 __global__ __launch_bounds__(256) void k_predecode_x(PredecodeXArgs a) {
   const int64_t total = a.Mp * a.Kp;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  bool bad = false;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
     const int64_t m = i / a.Kp, k = i % a.Kp;
     const int64_t src = m < a.M && a.rmap != nullptr ? a.rmap[m] : m;
     int32_t v;
     uint32_t e;
-    D::decode_x(m < a.M && k < a.K ? load_elem<DT>(a.x, src * a.x_sm + k * a.x_sk) : 0u,
-                static_cast<int>(m % D::ROWS), v, e);
+    const uint32_t b = m < a.M && k < a.K ? load_elem<DT>(a.x, src * a.x_sm + k * a.x_sk) : 0u;
+    bad |= nonfinite_bits<DT>(b);
+    D::decode_x(b, static_cast<int>(m % D::ROWS), v, e);
     if constexpr (D::XPACK) {
       a.xsig[i] = static_cast<int32_t>(D::pack_x(v, e));
     } else {
@@ -1030,6 +1061,7 @@ __global__ __launch_bounds__(256) void k_predecode_x(PredecodeXArgs a) {
       a.xword[i] = e;
     }
   }
+  note_nonfinite(bad);
 }
 
 // the raw-digit kernel's x decode, in the form k_predecode_x takes
@@ -1052,11 +1084,21 @@ struct CombineArgs {
 
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  bool bad = false;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < a.n; i += stride) {
-    int64_t s = 0;
-    for (int p = 0; p < a.nparts; ++p) s += a.parts[p][i];
-    a.out[i] = s;
+    // a 128-bit sum: int64 partial sums may wrap although the total fits,
+    // and wrapped sums may look in range although the total does not
+    __int128 s = 0;
+    for (int p = 0; p < a.nparts; ++p) {
+      const int64_t v = a.parts[p][i];
+      bad |= !digit_in_range(v);
+      s += v;
+    }
+    const int64_t lo = static_cast<int64_t>(s);
+    bad |= static_cast<__int128>(lo) != s || !digit_in_range(lo);
+    a.out[i] = lo;
   }
+  note_range(bad);
 }
 
 __global__ __launch_bounds__(256) void k_finalize(const int64_t* __restrict__ acc, float* __restrict__ y,
@@ -1065,8 +1107,13 @@ __global__ __launch_bounds__(256) void k_finalize(const int64_t* __restrict__ ac
   if (i >= n) return;
   int64_t dg[ND];
   const int64_t* src = acc + i * ND;
+  bool bad = false;
 #pragma unroll
-  for (int j = 0; j < ND; ++j) dg[j] = src[j];
+  for (int j = 0; j < ND; ++j) {
+    dg[j] = src[j];
+    bad |= !digit_in_range(dg[j]);
+  }
+  note_range(bad);
   y[i] = __uint_as_float(round_digits_to_f32(dg));
 }
 
@@ -1107,10 +1154,10 @@ __global__ __launch_bounds__(256) void k_check_finite(const void* __restrict__ p
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
     const int64_t r = i / cols, c = i % cols;
     const int64_t idx = r * s_row + c * s_col;
-    if (DT == DET_F32) bad |= (static_cast<const uint32_t*>(p)[idx] & 0x7F800000u) == 0x7F800000u;
-    else bad |= (static_cast<const uint16_t*>(p)[idx] & 0x7F80u) == 0x7F80u;
+    if (DT == DET_F32) bad |= nonfinite_bits<DT>(static_cast<const uint32_t*>(p)[idx]);
+    else bad |= nonfinite_bits<DT>(static_cast<const uint16_t*>(p)[idx]);
   }
-  if (bad) *flag = 1;
+  if (bad) *(flag != nullptr ? flag : &g_dev_status[0]) = 1;
 }
 
 // ---------------------------------------------------------------- det_gemm on the matrix cores
@@ -1172,7 +1219,8 @@ struct SliceStatArgs {
 };
 
 template <int DT>
-__device__ __forceinline__ void stat_elem(uint32_t b, int& top, int& low) {
+__device__ __forceinline__ void stat_elem(uint32_t b, int& top, int& low, bool& bad) {
+  bad |= nonfinite_bits<DT>(b);
   bool neg;
   uint32_t m;
   int ex;
@@ -1189,6 +1237,7 @@ __device__ __forceinline__ void stat_elem(uint32_t b, int& top, int& low) {
 template <int DT, bool KMAJ>
 __device__ __forceinline__ void stats_body(const SliceStatArgs& a, int64_t blk) {
   int top = SL_TOP_NONE, low = SL_LOW_NONE;
+  bool bad = false;
   int64_t row;
   bool lead;
   if (KMAJ) {
@@ -1209,10 +1258,10 @@ __device__ __forceinline__ void stats_body(const SliceStatArgs& a, int64_t blk) 
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           if (DT == DET_F32) {
-            stat_elem<DT>(w4[u], top, low);
+            stat_elem<DT>(w4[u], top, low, bad);
           } else {
-            stat_elem<DT>(w4[u] & 0xFFFFu, top, low);
-            stat_elem<DT>(w4[u] >> 16, top, low);
+            stat_elem<DT>(w4[u] & 0xFFFFu, top, low, bad);
+            stat_elem<DT>(w4[u] >> 16, top, low, bad);
           }
         }
       }
@@ -1220,7 +1269,7 @@ __device__ __forceinline__ void stats_body(const SliceStatArgs& a, int64_t blk) 
 #pragma unroll 4
       for (int i = 0; i < 16; ++i) {
         const int64_t k = k0 + i * 64 + lane;
-        if (k < a.K) stat_elem<DT>(load_elem<DT>(a.p, row * a.s_r + k), top, low);
+        if (k < a.K) stat_elem<DT>(load_elem<DT>(a.p, row * a.s_r + k), top, low, bad);
       }
     }
 #pragma unroll
@@ -1241,10 +1290,11 @@ __device__ __forceinline__ void stats_body(const SliceStatArgs& a, int64_t blk) 
       for (int u = 0; u < 16; ++u)            // clamped: a repeated element leaves max and min as they are
         e[u] = load_elem<DT>(a.p, row * a.s_r + min(kb + u, k1 - 1) * a.s_k);
 #pragma unroll
-      for (int u = 0; u < 16; ++u) stat_elem<DT>(e[u], top, low);
+      for (int u = 0; u < 16; ++u) stat_elem<DT>(e[u], top, low, bad);
     }
     lead = true;
   }
+  note_nonfinite(bad);
   if (lead && a.direct) {                 // the row's only writer: no initial values needed
     a.top[row] = top;
     a.low[row] = low;
@@ -2004,7 +2054,8 @@ __device__ __forceinline__ void dot_add(unsigned long long* set, uint32_t m1, ui
 // the products of one element pair (mode: a*b, (a-b)^2 = a*a + b*b - 2 a*b,
 // or a*a); `pos` is the lane's positive set, the negative set follows it
 template <int DT, int MODE>
-__device__ __forceinline__ void dot_elem(unsigned long long* pos, uint32_t ab, uint32_t bb) {
+__device__ __forceinline__ void dot_elem(unsigned long long* pos, uint32_t ab, uint32_t bb, bool& bad) {
+  bad |= nonfinite_bits<DT>(ab) | (MODE != DOT_SQUARE && nonfinite_bits<DT>(bb));
   // o = (Ez_a - bias) + (Ez_b - bias) + 298: 298 - 300 for f32, 298 - 268 for bf16
   constexpr uint32_t OFF = DT == DET_F32 ? uint32_t(-2) : 30u;
   uint32_t ma, ea;
@@ -2058,6 +2109,7 @@ __global__ __launch_bounds__(64 * DOT_W, 2) void k_dot(DotArgs a) {
   const int64_t tid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   constexpr int EPV = DT == DET_F32 ? 4 : 8;         // elements per 16-byte load
   int64_t done = 0;
+  bool bad = false;
   if (VEC) {
     const uint4* const va = static_cast<const uint4*>(a.a);
     const uint4* const vb = static_cast<const uint4*>(a.b);
@@ -2074,7 +2126,7 @@ __global__ __launch_bounds__(64 * DOT_W, 2) void k_dot(DotArgs a) {
 #pragma unroll
             for (int e = 0; e < EPV; ++e)
               dot_elem<DT, MODE>(pos, dot_word_elem<DT>(ra[u], e),
-                                 MODE != DOT_SQUARE ? dot_word_elem<DT>(rb[u], e) : 0u);
+                                 MODE != DOT_SQUARE ? dot_word_elem<DT>(rb[u], e) : 0u, bad);
           }
         }
 #pragma unroll
@@ -2086,8 +2138,9 @@ __global__ __launch_bounds__(64 * DOT_W, 2) void k_dot(DotArgs a) {
   for (int64_t i = done + tid; i < a.n; i += nthreads) {
     const uint32_t x = load_elem<DT>(a.a, i * a.inc_a);
     const uint32_t y = MODE != DOT_SQUARE ? load_elem<DT>(a.b, i * a.inc_b) : 0u;
-    dot_elem<DT, MODE>(pos, x, y);
+    dot_elem<DT, MODE>(pos, x, y, bad);
   }
+  note_nonfinite(bad);
   __syncthreads();
   // digit j: lane l adds slot j of lane l of every wave (positive minus
   // negative), then the wave adds its 64 lanes
@@ -2222,6 +2275,18 @@ det_status predecode_x_block(GemmArgs& b, const void* xblock, char* xr, hipStrea
 // that reuses each w element matters more: the pair form was 10 % slower).
 // K runs in blocks of 2^15, with or without a workspace, so no counter can
 // overflow; the digits are carried in acc.
+// Without a workspace the GEMM kernels decode x and w themselves and no
+// pre-decode pass sees every element once: one checking pass per operand
+// notes an Inf or NaN in the device status instead.
+template <int DT>
+det_status note_raw_operands(const GemmArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_check_finite<DT>, dim3(grid_for(a.M * a.K, 256, 4096)), dim3(256), 0, s, a.x, a.M, a.K, a.x_sm,
+                     a.x_sk, nullptr);
+  hipLaunchKernelGGL(k_check_finite<DT>, dim3(grid_for(a.N * a.K, 256, 4096)), dim3(256), 0, s, a.w, a.N, a.K, a.w_sn,
+                     a.w_sk, nullptr);
+  return hip_check(hipGetLastError(), "operand check launch");
+}
+
 template <int DT>
 det_status launch_partial(GemmArgs a, void* ws, hipStream_t s) {
   constexpr bool PAIR = DT == DET_F32;
@@ -2235,6 +2300,10 @@ det_status launch_partial(GemmArgs a, void* ws, hipStream_t s) {
   const int64_t esz = DT == DET_F32 ? 4 : 2;
   a.w_vec = a.w_sk == 1 && (reinterpret_cast<uintptr_t>(a.w) % 16) == 0 && (a.w_sn * esz) % 16 == 0;
   const bool pre = ws != nullptr && a.K > 0;
+  if (!pre && a.K > 0) {
+    det_status st = note_raw_operands<DT>(a, s);
+    if (st != DET_OK) return st;
+  }
   if (pre) {
     PredecodeArgs p{};
     p.w = a.w; p.w_sn = a.w_sn; p.w_sk = a.w_sk;
@@ -2309,6 +2378,10 @@ det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s, bool timed = true) 
   const int64_t esz = DT == DET_F32 ? 4 : 2;
   a.w_vec = a.w_sk == 1 && (reinterpret_cast<uintptr_t>(a.w) % 16) == 0 && (a.w_sn * esz) % 16 == 0;
   const bool pre = ws != nullptr && a.K > 0;
+  if (!pre && a.K > 0) {
+    det_status st = note_raw_operands<DT>(a, s);
+    if (st != DET_OK) return st;
+  }
   if (pre) {
     PredecodeArgs p{};
     p.w = a.w; p.w_sn = a.w_sn; p.w_sk = a.w_sk;
@@ -2773,6 +2846,31 @@ det_status scratch_for_current_device(void** out) {
   return DET_OK;
 }
 
+// the current device's copy of g_dev_status, looked up once per device
+std::mutex g_status_mu;
+void* g_status_ptr[MAX_DEVICES];
+
+det_status status_words(void** out) {
+  int dev = -1;
+  det_status st = hip_check(hipGetDevice(&dev), "hipGetDevice");
+  if (st != DET_OK) return st;
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(DET_EINVAL, "device %d is beyond the %d supported", dev, MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_status_mu);
+  if (g_status_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    st = hip_check(hipGetSymbolAddress(&ptr, HIP_SYMBOL(g_dev_status)), "status symbol address");
+    if (st != DET_OK) return st;
+    if (ptr == nullptr) return fail(DET_EHIP, "status word address is null");
+    g_status_ptr[dev] = ptr;
+  }
+  *out = g_status_ptr[dev];
+  return DET_OK;
+}
+
+__global__ __launch_bounds__(64) void k_status_clear(int32_t* words) {
+  if (threadIdx.x < 4) words[threadIdx.x] = 0;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- C ABI
@@ -2873,6 +2971,33 @@ det_status det_gemm_ws(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk, 
   if (workspace == nullptr && M > 0 && N > 0 && K > 0) return fail(DET_EINVAL, "null workspace");
   return gemm_common(1, dt, x, x_sm, x_sk, w, w_sn, w_sk, M, N, K, y, y_sm, y_sn, nullptr, workspace,
                      workspace_bytes, stream);
+}
+
+det_status det_device_status(void* stream, int clear, int* flags) {
+  if (flags != nullptr) *flags = 0;
+  void* p = nullptr;
+  det_status st = status_words(&p);
+  if (st != DET_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t h[4] = {0, 0, 0, 0};
+  st = hip_check(hipMemcpyAsync(h, p, sizeof h, hipMemcpyDeviceToHost, s), "status copy");
+  if (st == DET_OK && clear) {
+    hipLaunchKernelGGL(k_status_clear, dim3(1), dim3(64), 0, s, static_cast<int32_t*>(p));
+    st = hip_check(hipGetLastError(), "status clear launch");
+  }
+  const det_status sync = hip_check(hipStreamSynchronize(s), "status wait");
+  if (st == DET_OK) st = sync;
+  if (st != DET_OK) return st;
+  const int f = (h[0] != 0 ? 1 : 0) | (h[1] != 0 ? 2 : 0);
+  if (flags != nullptr) *flags = f;
+  if (f & 1) return fail(DET_ENONFINITE, "an operand held Inf or NaN");
+  if (f & 2) return fail(DET_ERANGE, "a digit lay outside +-2^62");
+  return DET_OK;
+}
+
+int32_t* det_device_status_word(void) {
+  void* p = nullptr;
+  return status_words(&p) == DET_OK ? static_cast<int32_t*>(p) : nullptr;
 }
 
 void det_set_kernel_events(void* start, void* stop) {

@@ -32,8 +32,10 @@
  *
  * Conventions for every entry point:
  *   - All data pointers are DEVICE pointers owned by the caller.  The library
- *     allocates no device memory and keeps none between calls (the _ws
- *     variants use memory the caller passes in).  The one host-side state
+ *     allocates no device memory (the _ws variants use memory the caller
+ *     passes in); what it keeps on each GPU it runs on are two static device
+ *     arrays, det_gemm_noalloc's workspace and the 16-byte status word of
+ *     det_device_status, held until the process ends.  The one host-side state
  *     is two small pinned host buffers per calling thread, for the two
  *     readbacks of det_gemm_ws's matrix-core path (128 bytes, and 4 bytes
  *     per listed row); they grow on demand and live until the process ends.
@@ -51,9 +53,14 @@
  *   - Argument errors are reported before anything is enqueued; on error
  *     nothing is written.  det_last_error() returns a message for the calling
  *     thread's most recent failure.
- *   - Inputs must be finite.  Inf or NaN operands never cause an
- *     out-of-bounds access, but their results are unspecified; callers that
- *     cannot rule them out run det_check_finite first.
+ *   - Inputs must be finite (the page's limits name bf16 and f32 inputs and
+ *     no others; the digits cannot hold Inf or NaN).  Because calls are
+ *     asynchronous, an Inf or NaN operand is not an argument error: the
+ *     kernels that read the operands note it in the device status (see
+ *     det_device_status), which then reports DET_ENONFINITE, and the call's
+ *     results are unspecified; every access stays in bounds all the same.
+ *     Callers that want the check before any result is written run
+ *     det_check_finite first.
  */
 #ifndef DETGEMM_H
 #define DETGEMM_H
@@ -74,7 +81,9 @@ typedef enum {
   DET_EINVAL = 1,      /* bad pointer, size, stride or count */
   DET_EKLIMIT = 2,     /* K > 2^19 */
   DET_EDTYPE = 3,      /* unknown dtype */
-  DET_EHIP = 5         /* the HIP runtime reported an error */
+  DET_ENONFINITE = 4,  /* an operand held Inf or NaN (device status) */
+  DET_EHIP = 5,        /* the HIP runtime reported an error */
+  DET_ERANGE = 6       /* a digit outside +-2^62 (device status) */
 } det_status;
 
 typedef enum { DET_F32 = 0, DET_BF16 = 1 } det_dtype;
@@ -249,9 +258,13 @@ void det_set_kernel_events(void* start, void* stop);
  *                of them); a part that overlaps `out` without being equal
  *                to it is rejected with DET_EINVAL.
  *   n_outputs    number of accumulators (>= 0)
- * Precondition (not checked on the device): every digit sum fits int64 with
- * room for carries, i.e. |sum| <= 2^62; partials of GEMMs whose K values add
- * up to at most 2^30 always satisfy it.
+ * Precondition: every digit of every part, and every digit of the result,
+ * lies within +-2^62 (room for the carries of rounding); with more than 32
+ * parts the parts are added in groups of 32 and each group's running result
+ * is stored in `out`, so it must lie in that range too.  Partials of GEMMs
+ * whose K values add up to at most 2^30 always satisfy it.  A digit outside
+ * the range is noted in the device status (DET_ERANGE from
+ * det_device_status); the digits written are then unspecified.
  */
 det_status det_combine(const int64_t* const* parts, int nparts, int64_t* out,
                        int64_t n_outputs, void* stream);
@@ -261,6 +274,8 @@ det_status det_combine(const int64_t* const* parts, int nparts, int64_t* out,
  * rounded once to fp32).
  *   acc          n_outputs*18 int64 digits (any raw digits within +-2^62)
  *   y            n_outputs fp32 results, contiguous
+ * A digit outside +-2^62 is noted in the device status (DET_ERANGE from
+ * det_device_status); that output's value is then unspecified.
  */
 det_status det_finalize(const int64_t* acc, float* y, int64_t n_outputs, void* stream);
 
@@ -280,7 +295,8 @@ det_status det_finalize(const int64_t* acc, float* y, int64_t n_outputs, void* s
  * until the call's work on `stream` has finished, and calls that add into one
  * acc on different streams must not overlap.  At most 2^30 products may be
  * added into one acc over all calls (a dot product adds n): then every digit
- * stays within +-2^62.  Inputs must be finite (not checked).
+ * stays within +-2^62.  An Inf or NaN element is noted in the device
+ * status (DET_ENONFINITE from det_device_status); acc is then unspecified.
  * Returns DET_OK, DET_EINVAL, DET_EKLIMIT (more than 2^30 products in one
  * call), DET_EDTYPE or DET_EHIP.
  */
@@ -311,6 +327,38 @@ det_status det_round_f32_to_bf16(const float* in, uint16_t* out, int64_t n, void
  */
 det_status det_check_finite(det_dtype dt, const void* p, int64_t rows, int64_t cols,
                             int64_t s_row, int64_t s_col, int32_t* flag, void* stream);
+
+/*
+ * Device status -- conditions only the kernels can see, reported after the
+ * fact because every call is asynchronous.  Each GPU the library runs on
+ * keeps a status word of its own, set by any call on any stream of that GPU
+ * and cleared only here, like the sticky exception flags of IEEE 754:
+ *   DET_ENONFINITE  an operand of det_gemm, det_gemm_ws, det_gemm_noalloc,
+ *                   det_gemm_partial, det_gemm_partial_ws, det_dot_partial or
+ *                   det_sqdiff_partial held an Inf or a NaN
+ *   DET_ERANGE      a digit read by det_combine or det_finalize, or a digit
+ *                   det_combine computed, lay outside +-2^62
+ * The results of the call that set a condition are unspecified.
+ *
+ * det_device_status -- waits for `stream` (it blocks the calling thread),
+ * reads the current device's word and, if `clear` is nonzero, clears it in
+ * stream order after the read.  Returns DET_ENONFINITE if that condition is
+ * set, else DET_ERANGE if that one is, else DET_OK (or DET_EHIP).  *flags,
+ * unless null, gets 1 for non-finite plus 2 for range.  Work enqueued on
+ * other streams and not ordered before the read may set the word after it,
+ * and with `clear` a condition such work sets between the read and the
+ * clear is lost: callers that use several streams order them first.
+ *
+ * det_device_status_word -- the current device's status word, for callers
+ * that read it stream-ordered without waiting (a device copy, a kernel of
+ * their own): four int32, [0] nonzero after a non-finite operand, [1] nonzero
+ * after a digit out of range, [2] and [3] zero.  Null (see det_last_error) if
+ * the device cannot be queried.  The caller may read it; only
+ * det_device_status writes zeros to it.
+ */
+det_status det_device_status(void* stream, int clear, int* flags);
+
+int32_t* det_device_status_word(void);
 
 #ifdef __cplusplus
 }
