@@ -464,11 +464,14 @@ def matrix_core_aux(det, dev, timed) -> dict:
     N = w.shape[0]
     t, y = timed(lambda: det.det_gemm(x, w, check_finite=False))
     plan = det.last_gemm_plan()
+    # the kernel's own time, with the plan's S fixed: on the default path the
+    # events would also span the launches of the paths the plan did not pick
     kev = KernelEvents(det._lib.load(), 3)
-    for i in range(3):
-        kev.arm(i)
-        det.det_gemm(x, w, check_finite=False)
-    kev.disarm()
+    with det.gemm_path("slices", plan["slices"]) if plan["slices"] > 0 else det.gemm_path("auto"):
+        for i in range(3):
+            kev.arm(i)
+            det.det_gemm(x, w, check_finite=False)
+        kev.disarm()
     torch.cuda.synchronize()
     kms = kev.mean_ms()
     kev.close()

@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdetgemm.
 
 DET_OK, DET_EINVAL, DET_EKLIMIT, DET_EDTYPE, DET_ENONFINITE, DET_EHIP, DET_ERANGE = 0, 1, 2, 3, 4, 5, 6
 DET_F32, DET_BF16 = 0, 1
-DET_PATH_AUTO, DET_PATH_ACCUMULATOR, DET_PATH_SLICES = 0, 1, 2
+DET_PATH_AUTO, DET_PATH_ACCUMULATOR, DET_PATH_SLICES, DET_PATH_AUTO_HOST = 0, 1, 2, 3
 NUM_DIGITS = 18
 LSB_EXPONENT = -298
 K_MAX = 1 << 19

@@ -283,16 +283,18 @@ def exact_sum_squares(y: torch.Tensor, *, check_finite: Optional[bool] = None) -
 
 
 _PATHS = {"auto": _lib.DET_PATH_AUTO, "accumulator": _lib.DET_PATH_ACCUMULATOR,
-          "slices": _lib.DET_PATH_SLICES}
+          "slices": _lib.DET_PATH_SLICES, "auto_host": _lib.DET_PATH_AUTO_HOST}
 _PATH_NAMES = {v: k for k, v in _PATHS.items()}
 
 
 def set_gemm_path(path: str = "auto", slices: int = 0) -> None:
     """Choose how det_gemm forms the exact sum (process-wide; see
-    det_set_gemm_path in include/detgemm.h): "auto" (default), "accumulator"
-    (the digit accumulator always) or "slices" (int8 digit GEMMs on the
-    matrix cores, with `slices` = 2..7 digits per operand or 0 to let the
-    call choose).  Every path gives the same bits."""
+    det_set_gemm_path in include/detgemm.h): "auto" (default: the device
+    picks, the host never waits), "auto_host" (the host waits for the span
+    histogram and picks), "accumulator" (the digit accumulator always) or
+    "slices" (int8 digit GEMMs on the matrix cores, with `slices` = 2..7
+    digits per operand or 0 to let the call choose).  Every path gives the
+    same bits."""
     if path not in _PATHS:
         raise ValueError(f"path must be one of {sorted(_PATHS)}")
     _lib.check(_lib.load().det_set_gemm_path(_PATHS[path], int(slices)))
@@ -301,7 +303,8 @@ def set_gemm_path(path: str = "auto", slices: int = 0) -> None:
 def last_gemm_plan() -> dict:
     """What this thread's last det_gemm call did: the path, the digits per
     operand (0 on the accumulator path) and how many rows of x and of w the
-    matrix-core pass listed (rows that span more than S digits)."""
+    matrix-core pass listed (rows that span more than S digits).  Waits for
+    that call's plan when the device made it."""
     path, slices = ctypes.c_int(), ctypes.c_int()
     rows, cols = ctypes.c_int64(), ctypes.c_int64()
     _lib.load().det_last_gemm_plan(ctypes.byref(path), ctypes.byref(slices), ctypes.byref(rows),

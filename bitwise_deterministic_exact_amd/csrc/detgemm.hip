@@ -18,6 +18,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <type_traits>
@@ -54,6 +55,9 @@ det_status mark_event(hipEvent_t ev, bool now, hipStream_t s) {
   if (!now || ev == nullptr) return DET_OK;
   return hip_check(hipEventRecord(ev, s), "kernel timing event");
 }
+// which of the two events a launcher records (several launchers in one call
+// share the interval: the first records the start, the last the stop)
+constexpr int MARK_START = 1, MARK_STOP = 2, MARK_BOTH = 3;
 
 // Conditions only the kernels can see, kept per GPU until cleared (sticky,
 // like IEEE 754's exception flags): word 0 becomes 1 when an operand element
@@ -185,6 +189,13 @@ struct GemmArgs {
   // of y; null maps are the identity
   const int32_t* xmap;
   const int32_t* wmap;
+  // decided on the device (null: unused): the launch does nothing unless
+  // *gate != 0; the listed form of k_gemm8 takes M from *mcount and N from
+  // *ncount (M and N above are then their largest values)
+  const int32_t* gate;
+  const int32_t* mcount;
+  const int32_t* ncount;
+  int64_t tpw;                        // k_gemm8's looping form: consecutive tiles per workgroup
 };
 
 // Epilogues.  A K range longer than one block is run as several launches
@@ -751,9 +762,10 @@ __device__ __forceinline__ void fold8(char* c0, int64_t (&dg)[WD], bool norm) {
   }
 }
 
-template <class G, int DT, bool PRE, int R, int W, int WPE>
-__global__ __launch_bounds__(64 * W, WPE) void k_gemm8(GemmArgs a, const void* __restrict__ xg,
-                                                       const void* __restrict__ wg) {
+// One R x 64 output tile of det_gemm: the body of k_gemm8.
+template <class G, int DT, bool PRE, int R, int W>
+__device__ __forceinline__ void gemm8_tile(const GemmArgs& a, const void* __restrict__ xg,
+                                           const void* __restrict__ wg, int64_t tile, int tid, char* cells, int& claim) {
   constexpr int CW = G::NCELL / W;                          // cells each wave folds
   constexpr int OFF = (G::BITS * G::FIRST) & 31;            // bit of a wave's first cell within its digit
   // window digits: the window's value stays below 2^(OFF + B(CW-1) + cell
@@ -763,11 +775,8 @@ __global__ __launch_bounds__(64 * W, WPE) void k_gemm8(GemmArgs a, const void* _
   constexpr int WD = (OFF + G::BITS * (CW - 1) + VB + LOG2CW + 1 + 31) / 32;
   constexpr int64_t EPOCH = G::KFLUSH / V_KC;               // chunks per epoch, all waves together
   static_assert(CW * W == G::NCELL && EPOCH >= W && (G::BITS * CW) % 32 == 0, "epoch layout");
-  __shared__ __align__(16) char cells[G::ALLOC * G::CS];
-  __shared__ int claim;                           // the epoch's next unclaimed chunk (from e0)
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t tile = xcd_tile();
+  const int lane = tid & 63, wave = tid >> 6;
   const int64_t m0 = (tile % a.tiles_m) * R, n0 = (tile / a.tiles_m) * V_BN;
 
 
@@ -824,9 +833,9 @@ __global__ __launch_bounds__(64 * W, WPE) void k_gemm8(GemmArgs a, const void* _
   };
   // the first chunk's loads go out before the cells are cleared
   if (wave < nchunks) load(wave, wq[0], weq[0], xq[0], xwq[0]);
-  for (int q = threadIdx.x; q < G::ALLOC * static_cast<int>(G::CS) / 16; q += 64 * W)
+  for (int q = tid; q < G::ALLOC * static_cast<int>(G::CS) / 16; q += 64 * W)
     reinterpret_cast<uint4*>(cells)[q] = make_uint4(0u, 0u, 0u, 0u);
-  if (threadIdx.x == 0) claim = W;
+  if (tid == 0) claim = W;
   __syncthreads();
 
   // this wave's cells: CW consecutive cells from cell FIRST + wave * CW
@@ -899,7 +908,7 @@ __global__ __launch_bounds__(64 * W, WPE) void k_gemm8(GemmArgs a, const void* _
   // and a 4096-long K is a single epoch on the 4-bit grid).
   run_epoch(0);
   __syncthreads();                                // the epoch's adds are in
-  if (threadIdx.x == 0) claim = W;
+  if (tid == 0) claim = W;
   if (EPOCH + wave < nchunks) load(EPOCH + wave, wq[0], weq[0], xq[0], xwq[0]);
   int64_t dg[R][WD];
 #pragma unroll
@@ -913,7 +922,7 @@ __global__ __launch_bounds__(64 * W, WPE) void k_gemm8(GemmArgs a, const void* _
   for (int64_t e0 = EPOCH; e0 < nchunks; e0 += EPOCH, ++epoch) {
     run_epoch(e0);
     __syncthreads();                              // the epoch's adds are in
-    if (threadIdx.x == 0) claim = W;
+    if (tid == 0) claim = W;
     if (e0 + EPOCH + wave < nchunks) load(e0 + EPOCH + wave, wq[0], weq[0], xq[0], xwq[0]);
     const bool norm = (epoch % G::NORM_EVERY) == G::NORM_EVERY - 1 || e0 + EPOCH >= nchunks;
 #pragma unroll
@@ -957,6 +966,39 @@ __global__ __launch_bounds__(64 * W, WPE) void k_gemm8(GemmArgs a, const void* _
   }
 }
 
+// det_gemm: one workgroup per tile in the XCD-aware order.  LOOP: each
+// workgroup takes tpw consecutive tiles of that order, with M and N from the
+// device counts if given: the launches whose work the device decides (a
+// gated one, whose skipped workgroups then cost a tpw-th of a full grid's
+// dispatch, and the recompute of device-counted rows or columns).  Between
+// tiles a barrier: waves 0 and 1 read the digit array over the cells while
+// the others would clear them.
+template <class G, int DT, bool PRE, int R, int W, int WPE, bool LOOP>
+__global__ __launch_bounds__(64 * W, WPE) void k_gemm8(GemmArgs a, const void* __restrict__ xg,
+                                                       const void* __restrict__ wg) {
+  __shared__ __align__(16) char cells[G::ALLOC * G::CS];
+  __shared__ int claim;                           // the epoch's next unclaimed chunk (from e0)
+  if (a.gate != nullptr && *a.gate == 0) return;
+  if constexpr (!LOOP) {
+    gemm8_tile<G, DT, PRE, R, W>(a, xg, wg, xcd_tile(), threadIdx.x, cells, claim);
+  } else {
+    if (a.mcount != nullptr) a.M = *a.mcount;
+    if (a.ncount != nullptr) a.N = *a.ncount;
+    a.tiles_m = (a.M + R - 1) / R;
+    a.tiles_n = (a.N + V_BN - 1) / V_BN;
+    const int64_t tiles = a.tiles_m * a.tiles_n;
+    const int64_t t0 = xcd_tile() * a.tpw, t1 = min(t0 + a.tpw, tiles);
+    for (int64_t t = t0; t < t1; ++t) {
+      // the thread index, opaque to the compiler at each tile: nothing
+      // derived from it is hoisted out of the loop to hold registers
+      int tid = static_cast<int>(threadIdx.x);
+      asm volatile("" : "+v"(tid));
+      gemm8_tile<G, DT, PRE, R, W>(a, xg, wg, t, tid, cells, claim);
+      __syncthreads();
+    }
+  }
+}
+
 // ---------------------------------------------------------------- w pre-decode
 // w [N][K] (any strides) -> significands int32 and exponent words (uint16
 // for k_gemm, uint32 for k_gemm8), +0 outside N x K.  Layout: chunk-major
@@ -972,6 +1014,10 @@ struct PredecodeArgs {
   int64_t N, K, Np, Kp;
   int32_t* wsig; void* wexp;          // exponent words: uint16 (k_gemm) or uint32 (k_gemm8)
   const int32_t* rmap;                // k_predecode_w8: decoded row n is row rmap[n] of w (null: n)
+  // k_predecode_w8 decided on the device (null: unused): nothing unless
+  // *gate != 0; N rows from *ncount (Np stays the layout's pitch)
+  const int32_t* gate;
+  const int32_t* ncount;
 };
 
 // Element i of a 32-bit array (layout [Kp/16][Np/64][4][64][4]) is (n, k);
@@ -1012,10 +1058,15 @@ __global__ __launch_bounds__(256) void k_predecode_w(PredecodeArgs a) {
 // the same for k_gemm8: the grid's w-side words (32-bit), lane = n mod 64
 template <class G, int DT>
 __global__ __launch_bounds__(256) void k_predecode_w8(PredecodeArgs a) {
-  const int64_t total = a.Np * a.Kp;
+  if (a.gate != nullptr && *a.gate == 0) return;
+  if (a.ncount != nullptr) a.N = *a.ncount;
+  // with a device count only the chunks' first npd columns are decoded
+  const int64_t npd = a.ncount != nullptr ? (a.N + V_BN - 1) / V_BN * V_BN : a.Np;
+  const int64_t total = npd * a.Kp;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   bool bad = false;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
+  for (int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; j < total; j += stride) {
+    const int64_t i = npd == a.Np ? j : j / (npd * V_KC) * (a.Np * V_KC) + j % (npd * V_KC);
     int64_t n, k;
     subblock_nk(i, a.Np, n, k);
     int32_t m;
@@ -1039,10 +1090,20 @@ struct PredecodeXArgs {
   int64_t M, K, Mp, Kp;
   int32_t* xsig; uint32_t* xword;
   const int32_t* rmap;                // decoded row m is row rmap[m] of x (null: m)
+  // decided on the device (null: unused): nothing unless *gate != 0; M rows
+  // from *mcount, padded to `mround`
+  const int32_t* gate;
+  const int32_t* mcount;
+  int64_t mround;
 };
 
 template <class D, int DT>
 __global__ __launch_bounds__(256) void k_predecode_x(PredecodeXArgs a) {
+  if (a.gate != nullptr && *a.gate == 0) return;
+  if (a.mcount != nullptr) {
+    a.M = *a.mcount;
+    a.Mp = (a.M + a.mround - 1) / a.mround * a.mround;
+  }
   const int64_t total = a.Mp * a.Kp;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   bool bad = false;
@@ -1350,12 +1411,25 @@ __global__ __launch_bounds__(256) void k_slice_need(const int32_t* top, const in
   if (threadIdx.x < 2 * SL_HIST && h[threadIdx.x] != 0) atomicAdd(hist + threadIdx.x, h[threadIdx.x]);
 }
 
+// The plan of one call, made on the device (k_slice_plan) from the span
+// histogram, and read by every later kernel of the call: int32 words in the
+// workspace, behind the histograms.
+constexpr int PL_S = 0;                   // digits per operand of the matrix-core pass; 0: the accumulator path
+constexpr int PL_ACC = 1;                 // 1 when the accumulator path runs instead (its gate)
+constexpr int PL_PREF = 2;                // the S the cost model prefers (0: the accumulator path)
+constexpr int PL_TAILS = 3;               // 1: listed outputs keep their sums and get their tails added
+constexpr int PL_FX = 4, PL_FW = 5;       // listed rows of x, of w
+constexpr int PL_OX = 6, PL_OW = 7;       // rows of x, of w recomputed on the accumulator path
+constexpr int PL_WORDS = 8;
+
 // list[] = the rows with need > S, in increasing order, and pos[r] = the
 // place of row r in list[] or -1 (one workgroup)
-__global__ __launch_bounds__(1024) void k_slice_list(const int32_t* need, int64_t n, int S, int32_t* list,
-                                                     int32_t* pos) {
+__global__ __launch_bounds__(1024) void k_slice_list(const int32_t* need, int64_t n, const int32_t* plan,
+                                                     int32_t* list, int32_t* pos) {
   __shared__ int32_t wsum[16];
   __shared__ int64_t base;
+  const int S = plan[PL_S];
+  if (S == 0) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (threadIdx.x == 0) base = 0;
   __syncthreads();
@@ -1387,8 +1461,9 @@ constexpr int64_t SL_ZFIX_MAX = int64_t(1) << 22;   // listed outputs whose 128-
 
 struct TailArgs {
   const void* p; int64_t K, s_r, s_k;     // the operand
-  const int32_t* list; int64_t n;         // its listed rows
-  const int32_t* top; int S;
+  const int32_t* list;                    // its listed rows (plan[PL_FX + side] of them)
+  const int32_t* top;
+  const int32_t* plan; int side;          // side 0: x, 1: w
   int32_t* cnt;                           // tails per listed row
   int32_t* tk;                            // listed row p's first SL_TAIL_CAP tails' k at p * SL_TAIL_CAP
 };
@@ -1408,14 +1483,10 @@ __device__ __forceinline__ bool is_tail(uint32_t b, int base) {
 // fall within its first SL_TAIL_CAP (a row with more is recomputed whole,
 // and the order of its tails does not matter to the exact sum)
 template <int DT>
-__global__ __launch_bounds__(256) void k_tail_scan(TailArgs a) {
-  const int64_t wid = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) >> 6;
-  const int lane = threadIdx.x & 63;
-  const int64_t nkr = (a.K + 1023) / 1024;
-  if (wid >= a.n * nkr) return;                           // uniform per wave
+__device__ __forceinline__ void tail_scan_range(const TailArgs& a, int S, int64_t wid, int64_t nkr, int lane) {
   const int64_t p = wid / nkr, k0 = (wid % nkr) * 1024;
   const int64_t r = a.list[p];
-  const int base = a.top[r] + 3 - 8 * a.S;
+  const int base = a.top[r] + 3 - 8 * S;
   uint32_t e[16];
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
@@ -1443,13 +1514,33 @@ __global__ __launch_bounds__(256) void k_tail_scan(TailArgs a) {
   }
 }
 
+// the listed rows' ranges, the waves of a capped grid taking them in turn
+// (nothing when the plan keeps no tails)
+template <int DT>
+__global__ __launch_bounds__(256) void k_tail_scan(TailArgs a) {
+  const int S = a.plan[PL_S];
+  if (S == 0 || a.plan[PL_TAILS] == 0) return;
+  const int64_t nkr = (a.K + 1023) / 1024, ranges = a.plan[PL_FX + a.side] * nkr;
+  const int64_t waves = static_cast<int64_t>(gridDim.x) * 4;
+  for (int64_t wid = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) >> 6; wid < ranges; wid += waves)
+    tail_scan_range<DT>(a, S, wid, nkr, threadIdx.x & 63);
+}
+
 // off[p] = place of listed row p's tails in tk (its fixed slot; -1 for rows
 // with more than SL_TAIL_CAP tails), ovl[] = the original indices of those
-// rows, in order (one workgroup)
-__global__ __launch_bounds__(1024) void k_tail_plan(const int32_t* cnt, const int32_t* list, int64_t n,
+// rows, in order, and their count into the plan (one workgroup).  Without
+// tails every listed row is recomputed.
+__global__ __launch_bounds__(1024) void k_tail_plan(int32_t* plan, int side, const int32_t* cnt, const int32_t* list,
                                                     int32_t* off, int32_t* ovl) {
   __shared__ int64_t wover[16];
   __shared__ int64_t obase;
+  if (plan[PL_S] == 0) return;
+  const int64_t n = plan[PL_FX + side];
+  if (plan[PL_TAILS] == 0) {
+    for (int64_t p = threadIdx.x; p < n; p += 1024) ovl[p] = list[p];
+    if (threadIdx.x == 0) plan[PL_OX + side] = static_cast<int32_t>(n);
+    return;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (threadIdx.x == 0) obase = 0;
   __syncthreads();
@@ -1471,6 +1562,7 @@ __global__ __launch_bounds__(1024) void k_tail_plan(const int32_t* cnt, const in
     }
     __syncthreads();
   }
+  if (threadIdx.x == 0) plan[PL_OX + side] = static_cast<int32_t>(obase);
 }
 
 // dg += (-1)^neg * v * 2^(o - 298) for v < 2^128 (raw digits; the bits of
@@ -1520,10 +1612,16 @@ struct SliceFixArgs {
   const int64_t* zr; const int64_t* zc;
   int64_t nx, nw;
   float* y; int64_t y_sm, y_sn;
+  const int32_t* plan;                    // S, nx and nw are taken from the plan
 };
 
 template <int DT>
 __global__ __launch_bounds__(256) void k_slice_fix(SliceFixArgs a) {
+  a.S = a.plan[PL_S];
+  if (a.S == 0 || a.plan[PL_TAILS] == 0) return;
+  a.nx = a.plan[PL_FX];
+  a.nw = a.plan[PL_FW];
+  a.zc = a.zr + 2 * a.nx * a.N;                   // column sums follow the row sums
   const int64_t total = a.nx * a.N + a.nw * a.M;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < total; t += stride) {
@@ -1714,10 +1812,13 @@ __device__ __forceinline__ void make_t_body(const SliceMakeArgs& a, int64_t blk)
 struct SliceMakePair {
   SliceMakeArgs op[2];
   int64_t nb0, nb1;
+  const int32_t* plan;                    // S is the plan's (nothing when it is 0)
 };
 
 template <int DT>
 __global__ __launch_bounds__(256) void k_slice_make(SliceMakePair p) {
+  p.op[0].S = p.op[1].S = p.plan[PL_S];
+  if (p.op[0].S == 0) return;
   const int64_t b = blockIdx.x;
   if (b < p.nb0) make_body<DT>(p.op[0], b, p.nb0);
   else make_body<DT>(p.op[1], b - p.nb0, p.nb1);
@@ -1725,6 +1826,8 @@ __global__ __launch_bounds__(256) void k_slice_make(SliceMakePair p) {
 
 template <int DT>
 __global__ __launch_bounds__(256) void k_slice_make_t(SliceMakePair p) {
+  p.op[0].S = p.op[1].S = p.plan[PL_S];
+  if (p.op[0].S == 0) return;
   const int64_t b = blockIdx.x;
   if (b < p.nb0) make_t_body<DT>(p.op[0], b);
   else make_t_body<DT>(p.op[1], b - p.nb0);
@@ -1788,10 +1891,11 @@ struct SliceMmaArgs {
   float* y; int64_t y_sm, y_sn;
   int64_t* z;                         // 128-bit sums [M][N][2] (lo, hi) between launches
   int epi;
-  // listed rows and columns (null: none): their final sums go to zr
-  // [rows][N][2] (row in x's list) or zc [cols][M][2], not to y
+  // listed rows and columns, when the plan keeps tails: their final sums go
+  // to zr [rows][N][2] (row in x's list) or zc [cols][M][2], not to y
   const int32_t* posx; const int32_t* posw;
   int64_t* zr; int64_t* zc;
+  const int32_t* plan;                    // the launch does nothing unless the plan's S is this kernel's
 };
 
 template <int S, int CB, int WR, int NBUF>
@@ -1867,6 +1971,9 @@ __global__ __launch_bounds__(128 * WR, 2) void k_slice_mma(SliceMmaArgs a) {
   using T = SliceTile<S, CB, WR, NBUF>;
   constexpr int NG = T::NG, NW = T::NW, FA = T::FA, FT = T::FT, PW = T::PER_WAVE;
   __shared__ __align__(16) int8_t lds[T::LDS_BYTES];
+  if (a.plan[PL_S] != S) return;
+  const bool tails = a.plan[PL_TAILS] != 0;
+  a.zc = a.zr + 2 * static_cast<int64_t>(a.plan[PL_FX]) * a.N;      // column sums follow the row sums
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wr = wave >> 1, wc = wave & 1;
@@ -1958,7 +2065,7 @@ __global__ __launch_bounds__(128 * WR, 2) void k_slice_mma(SliceMmaArgs a) {
         int64_t* zo = nullptr;
         if (a.epi == EPI_STORE || a.epi == EPI_ADD) {
           zo = zp;
-        } else if (a.posx != nullptr) {
+        } else if (tails) {
           const int32_t px = a.posx[row], pw = a.posw[col];
           if (px >= 0) zo = a.zr + (px * a.N + col) * 2;
           else if (pw >= 0) zo = a.zc + (static_cast<int64_t>(pw) * a.M + row) * 2;
@@ -2262,6 +2369,7 @@ det_status predecode_x_block(GemmArgs& b, const void* xblock, char* xr, hipStrea
   p.xsig = reinterpret_cast<int32_t*>(xr);
   p.xword = reinterpret_cast<uint32_t*>(xr + p.Mp * p.Kp * 4);
   p.rmap = b.xmap;
+  p.gate = b.gate; p.mcount = b.mcount; p.mround = TILE_ROWS;
   b.xsig = p.xsig; b.xword = p.xword; b.xld = p.Kp;
   hipLaunchKernelGGL((k_predecode_x<D, DT>), dim3(grid_for(p.Mp * p.Kp, 256, 8192)), dim3(256), 0, s, p);
   return hip_check(hipGetLastError(), "x predecode launch");
@@ -2355,6 +2463,9 @@ det_status launch_partial(GemmArgs a, void* ws, hipStream_t s) {
 // of six, but 27-bit operands leave 512 adds between folds: the LDS, not the
 // VALU, binds).  bf16 keeps two 64 KB workgroups of 8 waves (four rows on 128
 // KB: 4570 against 5369).
+constexpr int64_t GEMM8_LIST_GRID = 1024;    // workgroups of a device-counted recompute
+constexpr int64_t GEMM8_GATED_TPW = 8;       // tiles per workgroup of a gated launch
+
 template <int DT> struct Gemm8Config;
 template <> struct Gemm8Config<DET_F32> {
   static constexpr int R = 2, W = 16, WPE = 4;
@@ -2366,7 +2477,7 @@ template <> struct Gemm8Config<DET_BF16> {
 };
 
 template <int DT>
-det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s, bool timed = true) {
+det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s, int marks = MARK_BOTH) {
   using C = Gemm8Config<DT>;
   constexpr int R = C::R, W = C::W, WPE = C::WPE;
   using G = typename C::G;
@@ -2390,12 +2501,19 @@ det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s, bool timed = true) 
     p.wexp = static_cast<char*>(ws) + p.Np * p.Kp * 4;
     a.wsig = p.wsig; a.wexp32 = static_cast<const uint32_t*>(p.wexp); a.wld = p.Np * V_KC;
     p.rmap = a.wmap;
+    p.gate = a.gate; p.ncount = a.ncount;
     const dim3 pg(grid_for(p.Np * p.Kp, 256, 8192));
     hipLaunchKernelGGL((k_predecode_w8<G, DT>), pg, dim3(256), 0, s, p);
     det_status st = hip_check(hipGetLastError(), "predecode launch");
     if (st != DET_OK) return st;
   }
-  const dim3 grid(static_cast<unsigned>(blocks)), block(64 * W);
+  // work the device decides: consecutive tiles per workgroup (a capped grid
+  // for device-counted rows or columns, GEMM8_GATED_TPW for a gated launch)
+  const bool listed = a.mcount != nullptr || a.ncount != nullptr;
+  const bool loop = listed || a.gate != nullptr;
+  if (loop && !pre) return fail(DET_EINVAL, "a launch decided on the device needs the workspace");
+  a.tpw = listed ? (blocks + GEMM8_LIST_GRID - 1) / GEMM8_LIST_GRID : loop ? GEMM8_GATED_TPW : 1;
+  const dim3 grid(static_cast<unsigned>((blocks + a.tpw - 1) / a.tpw)), block(64 * W);
   // K blocks; beyond one block the exact digits are carried in the
   // workspace, behind the decoded w
   const int64_t kblk = pre ? K_BLOCK : a.K;
@@ -2415,12 +2533,13 @@ det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s, bool timed = true) 
       det_status st = predecode_x_block<G, DT>(b, xb, static_cast<char*>(ws) + predecode_bytes(1, a.N, a.K), s);
       if (st != DET_OK) return st;
     }
-    det_status st = mark_event(g_ev_start, timed && first, s);
+    det_status st = mark_event(g_ev_start, (marks & MARK_START) && first, s);
     if (st != DET_OK) return st;
-    if (pre) hipLaunchKernelGGL((k_gemm8<G, DT, true, R, W, WPE>), grid, block, 0, s, b, xb, a.w);
-    else hipLaunchKernelGGL((k_gemm8<G, DT, false, R, W, WPE>), grid, block, 0, s, b, xb, a.w);
+    if (loop) hipLaunchKernelGGL((k_gemm8<G, DT, true, R, W, WPE, true>), grid, block, 0, s, b, xb, a.w);
+    else if (pre) hipLaunchKernelGGL((k_gemm8<G, DT, true, R, W, WPE, false>), grid, block, 0, s, b, xb, a.w);
+    else hipLaunchKernelGGL((k_gemm8<G, DT, false, R, W, WPE, false>), grid, block, 0, s, b, xb, a.w);
     st = hip_check(hipGetLastError(), "gemm launch");
-    if (st == DET_OK) st = mark_event(g_ev_stop, timed && last, s);
+    if (st == DET_OK) st = mark_event(g_ev_stop, (marks & MARK_STOP) && last, s);
     if (st != DET_OK) return st;
   }
   return DET_OK;
@@ -2429,14 +2548,14 @@ det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s, bool timed = true) 
 // ---------------------------------------------------------------- det_gemm: the matrix-core path
 //
 // Workspace behind the accumulator path's: 8 int32 arrays per row of x and
-// of w (top, low, need, list, pos, tail count, tail offset, recompute list)
-// and the span histogram; SL_MAX digits of x (rows padded to 128) and of w
+// of w (top, low, need, list, pos, tail count, tail offset, recompute list),
+// the span histogram and the plan's words; SL_MAX digits of x (rows padded to 128) and of w
 // (rows padded to 128), K padded to 128; for K > 2^14 the 128-bit sums
 // [M][N] carried between launches; the tails' k (SL_TAIL_CAP per row); the
 // listed outputs' 128-bit sums (at most SL_ZFIX_MAX, and 2MN).
 int64_t slice_rows_x(int64_t M) { return round_up(M, 128); }
 int64_t slice_rows_w(int64_t N) { return round_up(N, 128); }
-int64_t slice_stats_bytes(int64_t M, int64_t N) { return round_up(32 * (M + N) + 4 * 2 * SL_HIST, 256); }
+int64_t slice_stats_bytes(int64_t M, int64_t N) { return round_up(32 * (M + N) + 4 * (2 * SL_HIST + PL_WORDS), 256); }
 int64_t slice_zfix_outputs(int64_t M, int64_t N) { return min(SL_ZFIX_MAX, 2 * M * N); }
 int64_t slice_bytes(int64_t M, int64_t N, int64_t K) {
   const int64_t Kp = round_up(K, 2 * SL_KB);
@@ -2450,19 +2569,62 @@ int64_t slice_bytes(int64_t M, int64_t N, int64_t K) {
 constexpr double RATE_ACC_F32 = 3.4e12, RATE_ACC_BF16 = 5.0e12, RATE_MMA = 1.2e15;
 constexpr double SLICE_MIN_MACS = 134217728.0;    // 2^27: below, the accumulator path alone
 
+// The plan of one call on the device, from the span histograms: the S the
+// cost model prefers (the estimate above; `only`: no accumulator, `forced`:
+// that S alone), the S the call runs (`mode` > 0: that one, fixed by the
+// host; 0: the preferred one), the listed rows and whether their outputs
+// keep their sums (at most `zfix` of them).  One thread.
+struct PlanArgs {
+  const int32_t* hist;                    // x's bins, then w's
+  int32_t* plan;
+  int64_t M, N, K, zfix;
+  double rate_acc;
+  int mode, only, forced;
+};
+
+__global__ __launch_bounds__(64) void k_slice_plan(PlanArgs a) {
+  if (threadIdx.x != 0) return;
+  const int32_t* const hx = a.hist;
+  const int32_t* const hw = a.hist + SL_HIST;
+  const double macs = static_cast<double>(a.M) * a.N * a.K;
+  double best = a.only ? 1e300 : macs / a.rate_acc;
+  int pref = 0;
+  for (int S = SL_MIN; S <= SL_MAX; ++S) {
+    if (a.forced != 0 && S != a.forced) continue;
+    int64_t cx = 0, cw = 0;
+    for (int n = S + 1; n <= SL_MAX + 1; ++n) { cx += hx[n]; cw += hw[n]; }
+    const double t = static_cast<double>(S) * S * macs / RATE_MMA +
+                     (static_cast<double>(cx) * a.N * a.K + static_cast<double>(cw) * a.M * a.K) / a.rate_acc;
+    if (t < best) { best = t; pref = S; }
+  }
+  const int run = a.mode > 0 ? a.mode : pref;
+  int64_t fx = 0, fw = 0;
+  if (run > 0)
+    for (int n = run + 1; n <= SL_MAX + 1; ++n) { fx += hx[n]; fw += hw[n]; }
+  const bool tails = run > 0 && fx + fw > 0 && fx * a.N + fw * a.M <= a.zfix;
+  a.plan[PL_S] = run;
+  a.plan[PL_ACC] = run == 0;
+  a.plan[PL_PREF] = pref;
+  a.plan[PL_TAILS] = tails;
+  a.plan[PL_FX] = static_cast<int32_t>(fx);
+  a.plan[PL_FW] = static_cast<int32_t>(fw);
+  a.plan[PL_OX] = 0;
+  a.plan[PL_OW] = 0;
+}
+
 std::atomic<int> g_path{DET_PATH_AUTO};
 std::atomic<int> g_forced_slices{0};
-// Pinned host buffers for the matrix-core path's two readbacks (the span
-// histogram and the tail counts), per calling thread, grown on demand and
-// kept until the process ends: a copy into pinned memory is asynchronous,
-// while one into pageable memory makes the host wait for it.  Every call has
-// waited for its own copies before it returns, so a buffer is never replaced
-// while a copy into it is in flight.
+// Pinned host buffer for the span histogram that DET_PATH_AUTO_HOST reads
+// back, per calling thread, grown on demand and kept until the process ends:
+// a copy into pinned memory is asynchronous, while one into pageable memory
+// makes the host wait for it.  Every such call has waited for its copy
+// before it returns, so the buffer is never replaced while a copy into it is
+// in flight.
 struct Pinned {
   int32_t* p = nullptr;
   size_t n = 0;
 };
-thread_local Pinned g_pin_hist, g_pin_cnt;
+thread_local Pinned g_pin_hist;
 
 int32_t* pinned(Pinned& b, size_t n) {
   if (b.n < n) {
@@ -2487,12 +2649,70 @@ det_status poll_event(hipEvent_t ev, const char* what) {
   }
 }
 
-thread_local det_path g_plan_path = DET_PATH_ACCUMULATOR;
-thread_local int g_plan_slices = 0;
-thread_local int64_t g_plan_rows = 0, g_plan_cols = 0;
+// What the calling thread's last det_gemm call did, for det_last_gemm_plan.
+// A path the host chose is kept here; a plan made on the device is copied,
+// after its kernel, into one of four pinned slots per thread (a ring, so a
+// copy never lands in a slot whose previous copy may still be in flight: the
+// stream waits for that one first) and read when it is asked for.
+struct PlanLog {
+  int32_t* rec = nullptr;                 // pinned, 4 slots of PL_WORDS
+  hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+  int dev[4] = {-1, -1, -1, -1};
+  int next = 0;
+  int last = -1;                          // slot of the last call's device plan; -1: the host's below
+  det_path path = DET_PATH_ACCUMULATOR;
+  int slices = 0;
+  int64_t rows = 0, cols = 0;
+};
+thread_local PlanLog g_plan_log;
 
 void record_plan(det_path p, int S, int64_t fx, int64_t fw) {
-  g_plan_path = p; g_plan_slices = S; g_plan_rows = fx; g_plan_cols = fw;
+  PlanLog& l = g_plan_log;
+  l.last = -1;
+  l.path = p; l.slices = S; l.rows = fx; l.cols = fw;
+}
+
+// copy the device plan `plan` into the next slot, in stream order (not under
+// graph capture: the record is then unknown)
+det_status log_device_plan(const int32_t* plan, hipStream_t s) {
+  PlanLog& l = g_plan_log;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  det_status st0 = hip_check(hipStreamIsCapturing(s, &cs), "capture status");
+  if (st0 != DET_OK) return st0;
+  if (cs != hipStreamCaptureStatusNone) {
+    record_plan(DET_PATH_AUTO, -1, -1, -1);
+    return DET_OK;
+  }
+  if (l.rec == nullptr) {
+    void* q = nullptr;
+    det_status st = hip_check(hipHostMalloc(&q, 4 * PL_WORDS * sizeof(int32_t), hipHostMallocDefault),
+                              "pinned plan record");
+    if (st != DET_OK) return st;
+    l.rec = static_cast<int32_t*>(q);
+  }
+  int dev = -1;
+  det_status st = hip_check(hipGetDevice(&dev), "hipGetDevice");
+  if (st != DET_OK) return st;
+  const int i = l.next;
+  l.next = (i + 1) & 3;
+  if (l.ev[i] != nullptr && l.dev[i] != dev) {
+    (void)hipEventSynchronize(l.ev[i]);             // another device's copy: let it land, then drop its event
+    (void)hipEventDestroy(l.ev[i]);
+    l.ev[i] = nullptr;
+  }
+  if (l.ev[i] == nullptr) {
+    st = hip_check(hipEventCreateWithFlags(&l.ev[i], hipEventDisableTiming), "event create");
+    if (st != DET_OK) return st;
+    l.dev[i] = dev;
+  } else {
+    st = hip_check(hipStreamWaitEvent(s, l.ev[i], 0), "plan record order");
+    if (st != DET_OK) return st;
+  }
+  st = hip_check(hipMemcpyAsync(l.rec + i * PL_WORDS, plan, PL_WORDS * sizeof(int32_t), hipMemcpyDeviceToHost, s),
+                 "plan record copy");
+  if (st == DET_OK) st = hip_check(hipEventRecord(l.ev[i], s), "event record");
+  if (st == DET_OK) l.last = i;
+  return st;
 }
 
 int choose_slices(det_dtype dt, int64_t M, int64_t N, int64_t K, const int32_t* hx, const int32_t* hw,
@@ -2522,7 +2742,7 @@ template <> struct SliceShape<6> { static constexpr int CB = 1, WR = 2, NBUF = 2
 template <> struct SliceShape<7> { static constexpr int CB = 1, WR = 2, NBUF = 2; };
 
 template <int S, int CB>
-det_status launch_mma_cb(SliceMmaArgs m, hipStream_t s) {
+det_status launch_mma_cb(SliceMmaArgs m, hipStream_t s, int marks) {
   using Sh = SliceShape<S>;
   constexpr int WR = Sh::WR, NBUF = Sh::NBUF;
   static_assert(SliceTile<S, CB, WR, NBUF>::LDS_BYTES <= 160 * 1024, "LDS");
@@ -2538,11 +2758,11 @@ det_status launch_mma_cb(SliceMmaArgs m, hipStream_t s) {
     b.kb0 = ib * SL_FOLD;
     b.kb1 = min(m.Kb, b.kb0 + SL_FOLD);
     b.epi = nblk == 1 ? EPI_ROUND : ib == 0 ? EPI_STORE : ib + 1 == nblk ? EPI_ADD_ROUND : EPI_ADD;
-    det_status st = mark_event(g_ev_start, ib == 0, s);
+    det_status st = mark_event(g_ev_start, (marks & MARK_START) && ib == 0, s);
     if (st != DET_OK) return st;
     hipLaunchKernelGGL((k_slice_mma<S, CB, WR, NBUF>), grid, block, 0, s, b);
     st = hip_check(hipGetLastError(), "slice mma launch");
-    if (st == DET_OK) st = mark_event(g_ev_stop, ib + 1 == nblk, s);
+    if (st == DET_OK) st = mark_event(g_ev_stop, (marks & MARK_STOP) && ib + 1 == nblk, s);
     if (st != DET_OK) return st;
   }
   return DET_OK;
@@ -2554,13 +2774,13 @@ det_status launch_mma_cb(SliceMmaArgs m, hipStream_t s) {
 // 78 -> 70 us, 2048^3 203 -> 197 us; the 8192 x 4096 x 4096 shape is
 // faster with the regular tiles, 1.61 against 1.65 ms).
 template <int S>
-det_status launch_mma(SliceMmaArgs m, hipStream_t s) {
+det_status launch_mma(SliceMmaArgs m, hipStream_t s, int marks) {
   constexpr int CB = SliceShape<S>::CB, WR = SliceShape<S>::WR;
   const int64_t tiles = slice_rows_x(m.M) / (32 * WR) * ((m.N + 32 * CB - 1) / (32 * CB));
   if constexpr (CB > 1) {
-    if (tiles <= 1024) return launch_mma_cb<S, CB / 2>(m, s);
+    if (tiles <= 1024) return launch_mma_cb<S, CB / 2>(m, s, marks);
   }
-  return launch_mma_cb<S, CB>(m, s);
+  return launch_mma_cb<S, CB>(m, s, marks);
 }
 
 // one operand's span-check arguments and its block count
@@ -2624,14 +2844,14 @@ SliceMakeArgs make_args(const void* p, int64_t R, int64_t K, int64_t s_r, int64_
 
 // x's and w's digits: one launch when both take the same form
 template <int DT>
-det_status slice_make(const GemmArgs& g, const int32_t* topx, const int32_t* topw, int8_t* xs, int8_t* wsl, int S,
-                      hipStream_t s) {
+det_status slice_make(const GemmArgs& g, const int32_t* topx, const int32_t* topw, int8_t* xs, int8_t* wsl,
+                      const int32_t* plan, hipStream_t s) {
   bool tx, tw;
   int64_t bx, bw;
-  const SliceMakeArgs ax = make_args<DT>(g.x, g.M, g.K, g.x_sm, g.x_sk, topx, xs, slice_rows_x(g.M), S, tx, bx);
-  const SliceMakeArgs aw = make_args<DT>(g.w, g.N, g.K, g.w_sn, g.w_sk, topw, wsl, slice_rows_w(g.N), S, tw, bw);
+  const SliceMakeArgs ax = make_args<DT>(g.x, g.M, g.K, g.x_sm, g.x_sk, topx, xs, slice_rows_x(g.M), 0, tx, bx);
+  const SliceMakeArgs aw = make_args<DT>(g.w, g.N, g.K, g.w_sn, g.w_sk, topw, wsl, slice_rows_w(g.N), 0, tw, bw);
   auto launch = [&](const SliceMakeArgs& a0, int64_t b0, const SliceMakeArgs& a1, int64_t b1, bool trans) {
-    SliceMakePair p{{a0, a1}, b0, b1};
+    SliceMakePair p{{a0, a1}, b0, b1, plan};
     const dim3 grid(static_cast<unsigned>(b0 + b1));
     if (trans) hipLaunchKernelGGL((k_slice_make_t<DT>), grid, dim3(256), 0, s, p);
     else hipLaunchKernelGGL((k_slice_make<DT>), grid, dim3(256), 0, s, p);
@@ -2646,28 +2866,34 @@ det_status slice_make(const GemmArgs& g, const int32_t* topx, const int32_t* top
 }
 
 template <int DT>
-det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s, bool timed);
+det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s, int marks);
 
-// The accumulator path on a subset: rows `rows` of x (m = M), or the rows
-// `cols` of w (n = N), overwriting those outputs of y.
+// The accumulator path on a subset whose size the device decided: the
+// *count rows `rows` of x (and all of w), or the *count rows `cols` of w
+// (and all of x), overwriting those outputs of y; nothing when *count is 0.
 template <int DT>
-det_status recompute(GemmArgs a, char* ws, const int32_t* rows, int64_t m, const int32_t* cols, int64_t n,
+det_status recompute(GemmArgs a, char* ws, const int32_t* rows, const int32_t* cols, const int32_t* count,
                      hipStream_t s) {
-  if (m == 0 || n == 0) return DET_OK;
   GemmArgs b = a;
-  b.M = m; b.N = n;
   b.xmap = rows; b.wmap = cols;
-  return launch_gemm8<DT>(b, ws, s, false);
+  b.gate = count;
+  if (rows != nullptr) b.mcount = count;
+  else b.ncount = count;
+  return launch_gemm8<DT>(b, ws, s, 0);
 }
 
-// det_gemm with the room for both paths in `ws`: span statistics, the
-// choice, then either the accumulator path or the matrix-core pass.  Rows
-// whose span needs more than S digits ("listed") keep their matrix-core sums;
-// their tails' products are added one by one (k_slice_fix), or, for rows
-// with more than SL_TAIL_CAP tails or more listed outputs than the sums'
-// room, the accumulator path recomputes them.
+// det_gemm with the room for both paths in `ws`: span statistics, then the
+// plan, made on the device (k_slice_plan) so that the host never waits: the
+// kernels of every path the plan may pick are enqueued, each reading the
+// plan and doing nothing unless it is the one picked.  With `host_choice`
+// (DET_PATH_AUTO_HOST) the host instead waits for the histogram, picks, and
+// enqueues only that path.  Rows whose span needs more than S digits
+// ("listed") keep their matrix-core sums; their tails' products are added
+// one by one (k_slice_fix), or, for rows with more than SL_TAIL_CAP tails or
+// more listed outputs than the sums' room, the accumulator path recomputes
+// them (a grid that takes the device-counted rows in turn).
 template <int DT>
-det_status launch_sliced(GemmArgs a, char* ws, bool only_slices, int forced, hipStream_t s) {
+det_status launch_sliced(GemmArgs a, char* ws, bool only_slices, int forced, bool host_choice, hipStream_t s) {
   const int64_t M = a.M, N = a.N, K = a.K;
   char* const sl = ws + workspace_bytes(1, M, N, K);
   int32_t* q = reinterpret_cast<int32_t*>(sl);
@@ -2681,6 +2907,7 @@ det_status launch_sliced(GemmArgs a, char* ws, bool only_slices, int forced, hip
   int32_t* const offx = take(M); int32_t* const offw = take(N);
   int32_t* const ovlx = take(M); int32_t* const ovlw = take(N);
   int32_t* const hist = take(2 * SL_HIST);
+  int32_t* const plan = take(PL_WORDS);
   const int64_t Kp = round_up(K, 2 * SL_KB);
   char* r8 = sl + slice_stats_bytes(M, N);
   int8_t* const xs = reinterpret_cast<int8_t*>(r8);
@@ -2700,61 +2927,64 @@ det_status launch_sliced(GemmArgs a, char* ws, bool only_slices, int forced, hip
                      hist, cntx);
   st = hip_check(hipGetLastError(), "slice need launch");
   if (st != DET_OK) return st;
-  int32_t* const h = pinned(g_pin_hist, 2 * SL_HIST);
-  if (h == nullptr) return fail(DET_EHIP, "pinned host buffer for the span histogram");
-  hipEvent_t ready = nullptr;
-  st = hip_check(hipMemcpyAsync(h, hist, 2 * SL_HIST * sizeof(int32_t), hipMemcpyDeviceToHost, s),
-                 "span histogram copy");
-  if (st == DET_OK) st = hip_check(hipEventCreateWithFlags(&ready, hipEventDisableTiming), "event create");
-  if (st == DET_OK) st = hip_check(hipEventRecord(ready, s), "event record");
-  if (st == DET_OK) st = poll_event(ready, "span histogram wait");
-  if (ready != nullptr) (void)hipEventDestroy(ready);
-  if (st != DET_OK) return st;
 
-  int64_t fx = 0, fw = 0;
-  const int S = choose_slices(static_cast<det_dtype>(DT), M, N, K, h, h + SL_HIST, only_slices, forced, fx, fw);
-  if (S == 0) {
-    record_plan(DET_PATH_ACCUMULATOR, 0, 0, 0);
-    return launch_gemm8<DT>(a, ws, s);
-  }
-  record_plan(DET_PATH_SLICES, S, fx, fw);
-  const bool listed = fx + fw > 0;
-  const bool tails = listed && fx * N + fw * M <= slice_zfix_outputs(M, N);
-  if (listed) {
-    hipLaunchKernelGGL(k_slice_list, dim3(1), dim3(1024), 0, s, needx, M, S, listx, posx);
-    hipLaunchKernelGGL(k_slice_list, dim3(1), dim3(1024), 0, s, needw, N, S, listw, posw);
-    st = hip_check(hipGetLastError(), "slice list launch");
+  int mode = only_slices ? forced : 0;              // > 0: S fixed here
+  if (host_choice) {
+    int32_t* const h = pinned(g_pin_hist, 2 * SL_HIST);
+    if (h == nullptr) return fail(DET_EHIP, "pinned host buffer for the span histogram");
+    hipEvent_t ready = nullptr;
+    st = hip_check(hipMemcpyAsync(h, hist, 2 * SL_HIST * sizeof(int32_t), hipMemcpyDeviceToHost, s),
+                   "span histogram copy");
+    if (st == DET_OK) st = hip_check(hipEventCreateWithFlags(&ready, hipEventDisableTiming), "event create");
+    if (st == DET_OK) st = hip_check(hipEventRecord(ready, s), "event record");
+    if (st == DET_OK) st = poll_event(ready, "span histogram wait");
+    if (ready != nullptr) (void)hipEventDestroy(ready);
     if (st != DET_OK) return st;
-  }
-  // tails per listed row, read back while the matrix-core pass runs
-  int32_t* const cx = tails ? pinned(g_pin_cnt, static_cast<size_t>(fx + fw)) : nullptr;
-  int32_t* const cw = cx != nullptr ? cx + fx : nullptr;
-  if (tails && cx == nullptr) return fail(DET_EHIP, "pinned host buffer for the tail counts");
-  hipEvent_t counted = nullptr;
-  if (tails) {
-    TailArgs t{};
-    t.S = S;
-    t.p = a.x; t.K = K; t.s_r = a.x_sm; t.s_k = a.x_sk; t.list = listx; t.n = fx; t.top = topx; t.cnt = cntx;
-    t.tk = tkx;
-    const int64_t nkr = (K + 1023) / 1024;
-    if (fx > 0) hipLaunchKernelGGL((k_tail_scan<DT>), dim3(grid_for(fx * nkr * 64, 256, 1u << 30)), dim3(256), 0, s, t);
-    t.p = a.w; t.s_r = a.w_sn; t.s_k = a.w_sk; t.list = listw; t.n = fw; t.top = topw; t.cnt = cntw;
-    t.tk = tkw;
-    if (fw > 0) hipLaunchKernelGGL((k_tail_scan<DT>), dim3(grid_for(fw * nkr * 64, 256, 1u << 30)), dim3(256), 0, s, t);
-    st = hip_check(hipGetLastError(), "tail count launch");
-    if (st == DET_OK && fx > 0)
-      st = hip_check(hipMemcpyAsync(cx, cntx, 4 * fx, hipMemcpyDeviceToHost, s), "tail count copy");
-    if (st == DET_OK && fw > 0)
-      st = hip_check(hipMemcpyAsync(cw, cntw, 4 * fw, hipMemcpyDeviceToHost, s), "tail count copy");
-    if (st == DET_OK) st = hip_check(hipEventCreateWithFlags(&counted, hipEventDisableTiming), "event create");
-    if (st == DET_OK) st = hip_check(hipEventRecord(counted, s), "event record");
-    if (st != DET_OK) {
-      if (counted) (void)hipEventDestroy(counted);
-      (void)hipStreamSynchronize(s);              // no copy into the pinned buffer outlives the call
-      return st;
+    int64_t fx = 0, fw = 0;
+    mode = choose_slices(static_cast<det_dtype>(DT), M, N, K, h, h + SL_HIST, only_slices, forced, fx, fw);
+    if (mode == 0) {
+      record_plan(DET_PATH_ACCUMULATOR, 0, 0, 0);
+      return launch_gemm8<DT>(a, ws, s);
     }
   }
-  st = slice_make<DT>(a, topx, topw, xs, wsl, S, s);
+  PlanArgs pa{};
+  pa.hist = hist; pa.plan = plan;
+  pa.M = M; pa.N = N; pa.K = K; pa.zfix = slice_zfix_outputs(M, N);
+  pa.rate_acc = DT == DET_F32 ? RATE_ACC_F32 : RATE_ACC_BF16;
+  pa.mode = mode; pa.only = only_slices; pa.forced = forced;
+  hipLaunchKernelGGL(k_slice_plan, dim3(1), dim3(64), 0, s, pa);
+  st = hip_check(hipGetLastError(), "plan launch");
+  if (st == DET_OK) st = log_device_plan(plan, s);
+  if (st != DET_OK) return st;
+
+  // the accumulator path, if the plan may pick it (the kernel timing
+  // events then wrap its launches, picked or not)
+  const bool acc_alt = mode == 0 && !only_slices;
+  if (acc_alt) {
+    GemmArgs b = a;
+    b.gate = plan + PL_ACC;
+    st = launch_gemm8<DT>(b, ws, s, MARK_BOTH);
+    if (st != DET_OK) return st;
+  }
+  hipLaunchKernelGGL(k_slice_list, dim3(1), dim3(1024), 0, s, needx, M, plan, listx, posx);
+  hipLaunchKernelGGL(k_slice_list, dim3(1), dim3(1024), 0, s, needw, N, plan, listw, posw);
+  st = hip_check(hipGetLastError(), "slice list launch");
+  if (st != DET_OK) return st;
+  // tails per listed row (when the plan keeps tails)
+  {
+    const int64_t nkr = (K + 1023) / 1024;
+    TailArgs t{};
+    t.p = a.x; t.K = K; t.s_r = a.x_sm; t.s_k = a.x_sk; t.list = listx; t.top = topx; t.plan = plan; t.side = 0;
+    t.cnt = cntx; t.tk = tkx;
+    hipLaunchKernelGGL((k_tail_scan<DT>), dim3(grid_for(M * nkr * 64, 256, 2048)), dim3(256), 0, s, t);
+    t.p = a.w; t.s_r = a.w_sn; t.s_k = a.w_sk; t.list = listw; t.top = topw; t.side = 1;
+    t.cnt = cntw; t.tk = tkw;
+    hipLaunchKernelGGL((k_tail_scan<DT>), dim3(grid_for(N * nkr * 64, 256, 2048)), dim3(256), 0, s, t);
+    st = hip_check(hipGetLastError(), "tail count launch");
+    if (st != DET_OK) return st;
+  }
+  st = slice_make<DT>(a, topx, topw, xs, wsl, plan, s);
+  if (st != DET_OK) return st;
   SliceMmaArgs m{};
   m.xs = xs; m.ws = wsl;
   m.Kb = Kp / SL_KB;
@@ -2762,48 +2992,42 @@ det_status launch_sliced(GemmArgs a, char* ws, bool only_slices, int forced, hip
   m.topx = topx; m.topw = topw;
   m.y = a.y; m.y_sm = a.y_sm; m.y_sn = a.y_sn;
   m.z = zcarry;
-  if (tails) {
-    m.posx = posx; m.posw = posw;
-    m.zr = zfix; m.zc = zfix + 2 * fx * N;
+  m.posx = posx; m.posw = posw;
+  m.zr = zfix; m.zc = nullptr;                 // behind the listed rows' sums: set on the device
+  m.plan = plan;
+  // every S the plan may pick; without the accumulator's launches the
+  // timing interval runs from the first to the last
+  const int s_lo = mode > 0 ? mode : (forced != 0 ? forced : SL_MIN);
+  const int s_hi = mode > 0 ? mode : (forced != 0 ? forced : SL_MAX);
+  for (int S = s_lo; S <= s_hi && st == DET_OK; ++S) {
+    const int marks = acc_alt ? 0 : (S == s_lo ? MARK_START : 0) | (S == s_hi ? MARK_STOP : 0);
+    switch (S) {
+      case 2: st = launch_mma<2>(m, s, marks); break;
+      case 3: st = launch_mma<3>(m, s, marks); break;
+      case 4: st = launch_mma<4>(m, s, marks); break;
+      case 5: st = launch_mma<5>(m, s, marks); break;
+      case 6: st = launch_mma<6>(m, s, marks); break;
+      default: st = launch_mma<7>(m, s, marks); break;
+    }
   }
-  if (st == DET_OK) switch (S) {
-    case 2: st = launch_mma<2>(m, s); break;
-    case 3: st = launch_mma<3>(m, s); break;
-    case 4: st = launch_mma<4>(m, s); break;
-    case 5: st = launch_mma<5>(m, s); break;
-    case 6: st = launch_mma<6>(m, s); break;
-    default: st = launch_mma<7>(m, s); break;
-  }
-  if (!listed) return st;
-  if (!tails) {
-    // too many listed outputs to keep their sums: recompute the rows and columns
-    if (st == DET_OK) st = recompute<DT>(a, ws, listx, fx, nullptr, N, s);
-    if (st == DET_OK) st = recompute<DT>(a, ws, nullptr, M, listw, fw, s);
-    return st;
-  }
-  // the tail counts have been copied (the matrix-core pass may still run)
-  det_status sync_st = poll_event(counted, "tail count wait");
-  (void)hipEventDestroy(counted);
-  if (st == DET_OK) st = sync_st;
   if (st != DET_OK) return st;
-  int64_t ox = 0, ow = 0;
-  for (int64_t i = 0; i < fx; ++i) ox += cx[i] > SL_TAIL_CAP;
-  for (int64_t i = 0; i < fw; ++i) ow += cw[i] > SL_TAIL_CAP;
-  hipLaunchKernelGGL(k_tail_plan, dim3(1), dim3(1024), 0, s, cntx, listx, fx, offx, ovlx);
-  hipLaunchKernelGGL(k_tail_plan, dim3(1), dim3(1024), 0, s, cntw, listw, fw, offw, ovlw);
+  // which listed rows go to the accumulator path, and the tails of the others
+  hipLaunchKernelGGL(k_tail_plan, dim3(1), dim3(1024), 0, s, plan, 0, cntx, listx, offx, ovlx);
+  hipLaunchKernelGGL(k_tail_plan, dim3(1), dim3(1024), 0, s, plan, 1, cntw, listw, offw, ovlw);
   SliceFixArgs f{};
   f.x = a.x; f.x_sm = a.x_sm; f.x_sk = a.x_sk;
   f.w = a.w; f.w_sn = a.w_sn; f.w_sk = a.w_sk;
-  f.M = M; f.N = N; f.S = S;
+  f.M = M; f.N = N;
   f.topx = topx; f.topw = topw; f.listx = listx; f.listw = listw; f.posx = posx; f.posw = posw;
   f.cntx = cntx; f.cntw = cntw; f.offx = offx; f.offw = offw; f.tkx = tkx; f.tkw = tkw;
-  f.zr = m.zr; f.zc = m.zc; f.nx = fx; f.nw = fw;
+  f.zr = m.zr; f.zc = m.zc;
   f.y = a.y; f.y_sm = a.y_sm; f.y_sn = a.y_sn;
-  hipLaunchKernelGGL((k_slice_fix<DT>), dim3(grid_for(fx * N + fw * M, 256, 4096)), dim3(256), 0, s, f);
+  f.plan = plan;
+  hipLaunchKernelGGL((k_slice_fix<DT>), dim3(grid_for(slice_zfix_outputs(M, N), 256, 4096)), dim3(256), 0, s, f);
   st = hip_check(hipGetLastError(), "tail launch");
-  // rows and columns with too many tails
-  if (st == DET_OK) st = recompute<DT>(a, ws, ovlx, ox, nullptr, N, s);
-  if (st == DET_OK) st = recompute<DT>(a, ws, nullptr, M, ovlw, ow, s);
+  // rows and columns the accumulator path recomputes
+  if (st == DET_OK) st = recompute<DT>(a, ws, ovlx, nullptr, plan + PL_OX, s);
+  if (st == DET_OK) st = recompute<DT>(a, ws, nullptr, ovlw, plan + PL_OW, s);
   return st;
 }
 
@@ -2916,12 +3140,13 @@ det_status gemm_common(int out_mode, det_dtype dt, const void* x, int64_t x_sm, 
       return fail(DET_EINVAL, "the matrix-core path needs a workspace of %lld bytes",
                   (long long)(workspace_bytes(1, M, N, K) + slice_bytes(M, N, K)));
     const bool big = static_cast<double>(M) * N * K >= SLICE_MIN_MACS;
-    if (room && (path == DET_PATH_SLICES || (path == DET_PATH_AUTO && big))) {
-      const bool only = path == DET_PATH_SLICES;
+    const bool autop = path == DET_PATH_AUTO || path == DET_PATH_AUTO_HOST;
+    if (room && (path == DET_PATH_SLICES || (autop && big))) {
+      const bool only = path == DET_PATH_SLICES, host = path == DET_PATH_AUTO_HOST;
       const int forced = only ? g_forced_slices.load() : 0;
       char* const w8 = static_cast<char*>(ws);
-      return dt == DET_F32 ? launch_sliced<DET_F32>(a, w8, only, forced, s)
-                           : launch_sliced<DET_BF16>(a, w8, only, forced, s);
+      return dt == DET_F32 ? launch_sliced<DET_F32>(a, w8, only, forced, host, s)
+                           : launch_sliced<DET_BF16>(a, w8, only, forced, host, s);
     }
   }
   if (out_mode == 1) record_plan(DET_PATH_ACCUMULATOR, 0, 0, 0);
@@ -2938,7 +3163,8 @@ int64_t det_gemm_workspace_bytes(det_dtype dt, int partial, int64_t M, int64_t N
 }
 
 det_status det_set_gemm_path(det_path path, int slices) {
-  if (path != DET_PATH_AUTO && path != DET_PATH_ACCUMULATOR && path != DET_PATH_SLICES)
+  if (path != DET_PATH_AUTO && path != DET_PATH_ACCUMULATOR && path != DET_PATH_SLICES &&
+      path != DET_PATH_AUTO_HOST)
     return fail(DET_EINVAL, "unknown path %d", static_cast<int>(path));
   if (slices != 0 && (slices < SL_MIN || slices > SL_MAX))
     return fail(DET_EINVAL, "slices must be 0 or %d..%d (got %d)", SL_MIN, SL_MAX, slices);
@@ -2953,10 +3179,23 @@ void det_get_gemm_path(det_path* path, int* slices) {
 }
 
 void det_last_gemm_plan(int* path, int* slices, int64_t* fallback_rows, int64_t* fallback_cols) {
-  if (path) *path = static_cast<int>(g_plan_path);
-  if (slices) *slices = g_plan_slices;
-  if (fallback_rows) *fallback_rows = g_plan_rows;
-  if (fallback_cols) *fallback_cols = g_plan_cols;
+  PlanLog& l = g_plan_log;
+  if (l.last >= 0) {                              // made on the device: wait for its copy
+    const int32_t* r = l.rec + l.last * PL_WORDS;
+    if (hipEventSynchronize(l.ev[l.last]) == hipSuccess) {
+      l.path = r[PL_S] > 0 ? DET_PATH_SLICES : DET_PATH_ACCUMULATOR;
+      l.slices = r[PL_S];
+      l.rows = r[PL_S] > 0 ? r[PL_FX] : 0;
+      l.cols = r[PL_S] > 0 ? r[PL_FW] : 0;
+    } else {
+      l.path = DET_PATH_AUTO; l.slices = -1; l.rows = l.cols = -1;    // unknown
+    }
+    l.last = -1;
+  }
+  if (path) *path = static_cast<int>(l.path);
+  if (slices) *slices = l.slices;
+  if (fallback_rows) *fallback_rows = l.rows;
+  if (fallback_cols) *fallback_cols = l.cols;
 }
 
 det_status det_gemm(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk, const void* w, int64_t w_sn,

@@ -35,21 +35,20 @@
  *     allocates no device memory (the _ws variants use memory the caller
  *     passes in); what it keeps on each GPU it runs on are two static device
  *     arrays, det_gemm_noalloc's workspace and the 16-byte status word of
- *     det_device_status, held until the process ends.  The one host-side state
- *     is two small pinned host buffers per calling thread, for the two
- *     readbacks of det_gemm_ws's matrix-core path (128 bytes, and 4 bytes
- *     per listed row); they grow on demand and live until the process ends.
+ *     det_device_status, held until the process ends.  Host-side state, per
+ *     calling thread and kept until the process ends: a 128-byte pinned
+ *     buffer for the span histogram that DET_PATH_AUTO_HOST reads back, and
+ *     four 32-byte pinned records with their events for det_last_gemm_plan.
  *   - Strides are in elements, must be >= 0, and may describe transposed or
  *     sliced views (e.g. x[:, a:b] or x^T).  Operand elements must be
  *     naturally aligned (4 bytes for f32, 2 for bf16).
  *   - The calling thread's current HIP device must be the device that holds
  *     the pointers and owns `stream` (the Python layer makes it current).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
- *     asynchronously and stream-ordered.  The one exception is det_gemm_ws
- *     when it considers the matrix-core path (see det_set_gemm_path): it
- *     waits for `stream` once, to read a 128-byte histogram, and with listed
- *     rows once more, for their tail counts.  Both waits poll an event, so
- *     the calling thread keeps a CPU core busy while it waits.
+ *     asynchronously and stream-ordered; no call waits for the device except
+ *     the ones that say so: det_gemm_ws on the opt-in DET_PATH_AUTO_HOST,
+ *     det_last_gemm_plan, det_device_status.  So every other call can be
+ *     captured into a HIP graph.
  *   - Argument errors are reported before anything is enqueued; on error
  *     nothing is written.  det_last_error() returns a message for the calling
  *     thread's most recent failure.
@@ -142,7 +141,7 @@ det_status det_gemm_partial(det_dtype dt, const void* x, int64_t x_sm, int64_t x
  * (partial ? 6 : 8) * roundup(N, 64) * roundup(K, 16) for w, plus
  * 8 * roundup(M, 2) * roundup(min(K, 2^15), 16) for x, plus 144 * M * N for
  * det_gemm_ws (partial = 0) when K > 2^15; for det_gemm_ws also the room of
- * the matrix-core path: roundup(32 (M + N) + 128, 256) +
+ * the matrix-core path: roundup(32 (M + N) + 160, 256) +
  * 7 * (roundup(M, 128) + roundup(N, 128)) * roundup(K, 128) + 1024 (M + N) +
  * 16 * min(2^22, 2 M N), plus 16 * M * N when K > 2^14.  det_gemm_ws
  * given only the accumulator path's size (the sum without that last term)
@@ -174,28 +173,43 @@ det_status det_gemm_ws(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk,
  * 2^22, is recomputed on the accumulator path instead.  The results are
  * bit-identical to the accumulator path's for every input.
  *
+ * The choice between the paths, and of S, depends on the spans of the
+ * operands, which only the device sees; it is made on the device (a plan in
+ * the workspace that every later kernel of the call reads), so the host
+ * never waits: the call enqueues the kernels of every path the plan may
+ * pick, and those not picked exit at once (a gated launch of the
+ * accumulator takes 8 tiles per workgroup, so skipping it costs an eighth
+ * of a full grid's dispatch).  The rows the accumulator recomputes are
+ * counted on the device too.
+ *
  * det_set_gemm_path sets, for the whole process, which path det_gemm_ws
  * takes:
  *   DET_PATH_AUTO         (default) the matrix-core path is considered for
  *                         M*N*K >= 2^27 when the workspace has its room: the
- *                         call measures the spans (one pass over x and w),
- *                         waits for the stream, and picks S, or the
- *                         accumulator path, by estimated time; with listed
- *                         rows it waits once more, for their tail counts
+ *                         call measures the spans (one pass over x and w)
+ *                         and the device picks S, or the accumulator path,
+ *                         by estimated time
+ *   DET_PATH_AUTO_HOST    the same choice made by the host: the call waits
+ *                         for the stream to read the 128-byte span histogram
+ *                         (polling an event, so the thread keeps a CPU core
+ *                         busy) and enqueues only the path it picks; not for
+ *                         graph capture
  *   DET_PATH_ACCUMULATOR  always the digit accumulator
  *   DET_PATH_SLICES       always the matrix-core path (a too small workspace
  *                         is DET_EINVAL); `slices` = 2..7 fixes S, 0 lets the
- *                         call pick it
+ *                         device pick it
  * `slices` must be 0 or 2..7 (else DET_EINVAL); it is ignored by the other
- * two paths.  det_gemm (no workspace) and the partials always use the
+ * paths.  det_gemm (no workspace) and the partials always use the
  * accumulator.
  *
  * det_last_gemm_plan reports the calling thread's last det_gemm or
  * det_gemm_ws call: the path taken (DET_PATH_ACCUMULATOR or DET_PATH_SLICES),
  * S (0 for the accumulator) and how many rows of x and of w were listed.
- * Null pointers are skipped.
+ * When the device made the plan it waits for that call's plan to be copied
+ * back (an event wait); a call made under graph capture, or whose plan could
+ * not be read, reports DET_PATH_AUTO and -1.  Null pointers are skipped.
  */
-typedef enum { DET_PATH_AUTO = 0, DET_PATH_ACCUMULATOR = 1, DET_PATH_SLICES = 2 } det_path;
+typedef enum { DET_PATH_AUTO = 0, DET_PATH_ACCUMULATOR = 1, DET_PATH_SLICES = 2, DET_PATH_AUTO_HOST = 3 } det_path;
 
 det_status det_set_gemm_path(det_path path, int slices);
 
@@ -242,8 +256,12 @@ size_t det_gemm_noalloc_max_bytes(void);
  * kernel that forms the products (the digit accumulator, or on the
  * matrix-core path the int8 digit GEMMs), and `stop` just after its last
  * launch; with K > 2^15 the interval also holds the per-block x decodes
- * between launches.  Calls that launch no such kernel (an empty M or N)
- * record nothing.  The events stay owned by the caller; null for either
+ * between launches.  When the device picks the path (DET_PATH_AUTO on a
+ * product that may take the matrix cores, DET_PATH_SLICES with slices = 0)
+ * the interval wraps the accumulator's launches if the plan may pick that
+ * path, else every digit-GEMM launch, picked or not: to time one kernel, fix
+ * the path (DET_PATH_ACCUMULATOR, or DET_PATH_SLICES with S).  Calls that
+ * launch no such kernel (an empty M or N) record nothing.  The events stay owned by the caller; null for either
  * turns its recording off.
  */
 void det_set_kernel_events(void* start, void* stop);

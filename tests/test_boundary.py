@@ -95,7 +95,7 @@ def _ru(v, m):
 
 def _slice_room(M, N, K):
     """det_gemm_ws's room for the matrix-core path, as include/detgemm.h states it."""
-    return (_ru(32 * (M + N) + 128, 256) + 7 * (_ru(M, 128) + _ru(N, 128)) * _ru(K, 128)
+    return (_ru(32 * (M + N) + 160, 256) + 7 * (_ru(M, 128) + _ru(N, 128)) * _ru(K, 128)
             + 1024 * (M + N) + 16 * min(1 << 22, 2 * M * N) + (16 * M * N if K > (1 << 14) else 0))
 
 
@@ -135,11 +135,12 @@ def test_workspace_size_and_checks():
 
 def test_gemm_path_settings():
     lib = _lib.load()
-    assert lib.det_set_gemm_path(3, 0) == _lib.DET_EINVAL
+    assert lib.det_set_gemm_path(4, 0) == _lib.DET_EINVAL
+    assert lib.det_set_gemm_path(-1, 0) == _lib.DET_EINVAL
     for bad in (1, 8, -1):
         assert lib.det_set_gemm_path(_lib.DET_PATH_SLICES, bad) == _lib.DET_EINVAL
     assert "slices" in _lib.last_error()
-    for path in (_lib.DET_PATH_ACCUMULATOR, _lib.DET_PATH_SLICES, _lib.DET_PATH_AUTO):
+    for path in (_lib.DET_PATH_ACCUMULATOR, _lib.DET_PATH_SLICES, _lib.DET_PATH_AUTO, _lib.DET_PATH_AUTO_HOST):
         for S in (0, 2, 7):
             assert lib.det_set_gemm_path(path, S) == _lib.DET_OK
     lib.det_set_gemm_path(_lib.DET_PATH_AUTO, 0)
@@ -153,6 +154,8 @@ def test_gemm_path_settings():
     det.set_gemm_path("slices", 5)
     with det.gemm_path("accumulator"):
         assert det.get_gemm_path() == ("accumulator", 0)
+        with det.gemm_path("auto_host"):
+            assert det.get_gemm_path() == ("auto_host", 0)
         with det.gemm_path("slices", 3):
             assert det.get_gemm_path() == ("slices", 3)
         assert det.get_gemm_path() == ("accumulator", 0)
