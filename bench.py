@@ -47,10 +47,11 @@ HBM_PEAK = 8.0e12
 INT8_MFMA_PEAK = 5.0e15             # dense int8 ops/s (2 per MAC)
 INT8_OPS_PER_MFMA = 2 * 16 * 16 * 64  # v_mfma_i32_16x16x64_i8, per wave instruction
 # the f32 det_gemm kernel's work per product (MAC): one 64-bit LDS atomic add
-# into a cell, and six VALU instructions (x broadcast, exponent add, cell
-# address, shift amount, 24x24-bit product, 64-bit shift)
+# into a cell, and five VALU instructions (exponent-word add with the x word
+# broadcast, cell address, shift amount, 24x24-bit product with x's
+# significand from an SGPR, 64-bit shift)
 GEMM8_LDS_ATOMICS_PER_MAC = 1
-GEMM8_VALU_OPS_PER_MAC = 6
+GEMM8_VALU_OPS_PER_MAC = 5
 KERNEL_SOURCE = os.path.join(ROOT, "bitwise_deterministic_exact_amd", "csrc", "detgemm.hip")
 PROBE_LIB = os.path.join(ROOT, "bitwise_deterministic_exact_amd", "liblds_probe.so")
 PROFILE_RECORD = os.path.join(ROOT, "profiles", "k_gemm8_f32_4096_wide.md")

@@ -589,6 +589,10 @@ struct CellsG {
   static constexpr int64_t KFLUSH = B == 8 ? 256 : 4096;  // adds between folds: |T| < 2^(47 + B)
   static constexpr int NORM_EVERY = B == 8 ? 8 : 1;       // folds between carry passes
   static constexpr bool CLAIM = true;                     // waves claim chunks (one workgroup per CU)
+  // pre-decoded x significands through scalar loads: every lane multiplies
+  // the same x element, so it is an SGPR operand of the multiply and needs no
+  // broadcast (f32; bf16 packs significand and word in one word)
+  static constexpr bool SX = DT == DET_F32;
   static constexpr uint32_t ESH = (DT == DET_F32 ? 9u : 8u) - (B == 8 ? 3u : 2u) +
                                   (R == 4 ? 2u : R == 2 ? 1u : 0u);   // log2(CS / B)
   static_assert(R == 1 || R == 2 || R == 4, "the cell stride must be a power of two");
@@ -640,6 +644,7 @@ struct Cells4 {
   static constexpr int64_t KFLUSH = 512;
   static constexpr int NORM_EVERY = 1;
   static constexpr bool CLAIM = false;                    // fixed chunk shares (two workgroups per CU)
+  static constexpr bool SX = false;
   using cell_t = int32_t;
 
   // bf16 bits -> shifted significand and address word.  x: exponent offset
@@ -693,7 +698,8 @@ __device__ __forceinline__ void load_w_pre8(const GemmArgs& a, const int32_t* ws
 // of every 16-lane row) and the lane's w element J.
 template <class G, int DT, bool PRE, int R, int J>
 __device__ __forceinline__ void steps8(char* cbase, uint32_t lane, uint32_t lane_off, const uint32_t (&wa)[V_KC],
-                                       const uint32_t (&wb)[V_KC], const int (&xm)[R], const int (&xe)[R]) {
+                                       const uint32_t (&wb)[V_KC], const int (&xm)[R], const int (&xe)[R],
+                                       const uint32_t (&xs)[R][V_KC]) {
   int32_t wm;
   uint32_t we;
   if (PRE) {
@@ -704,8 +710,9 @@ __device__ __forceinline__ void steps8(char* cbase, uint32_t lane, uint32_t lane
   }
 #pragma unroll
   for (int r = 0; r < R; ++r)
-    G::step(cbase, lane_off, r, bcast<J>(xm[r]), static_cast<uint32_t>(bcast<J>(xe[r])), wm, we);
-  if constexpr (J + 1 < V_KC) steps8<G, DT, PRE, R, J + 1>(cbase, lane, lane_off, wa, wb, xm, xe);
+    G::step(cbase, lane_off, r, PRE && G::SX ? static_cast<int>(xs[r][J]) : bcast<J>(xm[r]),
+            static_cast<uint32_t>(bcast<J>(xe[r])), wm, we);
+  if constexpr (J + 1 < V_KC) steps8<G, DT, PRE, R, J + 1>(cbase, lane, lane_off, wa, wb, xm, xe, xs);
 }
 
 // dg += v * scale for a 32-bit v (unsigned or signed) and a power-of-two
@@ -818,7 +825,7 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, const void* __rest
       const char* const wb = reinterpret_cast<const char*>(a.xword + m0 * a.xld + k0);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        x[r] = *reinterpret_cast<const uint32_t*>(xb + r * a.xld * 4 + xj4);
+        if constexpr (!G::SX) x[r] = *reinterpret_cast<const uint32_t*>(xb + r * a.xld * 4 + xj4);
         if (!G::XPACK) xw[r] = *reinterpret_cast<const uint32_t*>(wb + r * a.xld * 4 + xj4);
       }
     } else if (k0 + V_KC <= a.K && rows_in) {
@@ -843,6 +850,7 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, const void* __rest
   // Epochs of EPOCH chunks.  The barriers stay outside the unrolled pairs of
   // ring slots, so every wave meets each of them once per epoch.
   // One chunk of products from ring slot sl.
+  // chunk c from ring slot sl
   auto compute = [&](int64_t c, int sl) {
     const bool kin = c * V_KC + xj < a.K;
     int xm[R], xe[R];
@@ -856,7 +864,20 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, const void* __rest
       xm[r] = m;
       xe[r] = static_cast<int>(e);
     }
-    steps8<G, DT, PRE, R, 0>(cells, static_cast<uint32_t>(lane), lane_off, wq[sl], weq[sl], xm, xe);
+    uint32_t xs[R][V_KC];
+    if constexpr (PRE && G::SX) {
+      // the chunk's x significands by scalar loads (the chunk index is the
+      // same in every lane), just before its products
+      const int64_t cu = __builtin_amdgcn_readfirstlane(static_cast<int>(c));
+      typedef const __attribute__((address_space(4))) uint32_t* cword;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const cword q = (cword)(a.xsig + (m0 + r) * a.xld + cu * V_KC);
+#pragma unroll
+        for (int i = 0; i < V_KC; ++i) xs[r][i] = q[i];
+      }
+    }
+    steps8<G, DT, PRE, R, 0>(cells, static_cast<uint32_t>(lane), lane_off, wq[sl], weq[sl], xm, xe, xs);
   };
   // An epoch's chunks e0 .. e0 + lim - 1: wave v starts with chunk e0 + v
   // (already in ring slot 0).  With G::CLAIM it then takes the next unclaimed
