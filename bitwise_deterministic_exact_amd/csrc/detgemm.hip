@@ -333,9 +333,10 @@ constexpr int NSLOT = NEG_SLOT + NF;        // slots per output
 // four fields take two 64-bit atomics (bf16: two fields, one atomic).  A half
 // takes at most 2^15 adds of a 16-bit field, so no carry crosses into the
 // other half.
-template <int DT, int R, bool PRE, bool PAIR, int J>
+template <int DT, int R, bool PRE, bool PAIR, bool SX, int J>
 __device__ __forceinline__ void steps_raw(char* cbase, uint32_t lane_off, const uint32_t (&wa)[V_KC],
-                                          const uint32_t (&wb)[V_KC / 2], const int (&xm)[R], const int (&xe)[R]) {
+                                          const uint32_t (&wb)[V_KC / 2], const int (&xm)[R], const int (&xe)[R],
+                                          const uint32_t (&xs)[R][V_KC]) {
   static_assert(R * 64 * (PAIR ? 8 : 4) == 512, "slot offsets come from bits 9..15 of the exponent sum");
   int32_t wm;
   uint32_t we;
@@ -356,10 +357,15 @@ __device__ __forceinline__ void steps_raw(char* cbase, uint32_t lane_off, const 
         return static_cast<unsigned long long>(v & 0xFFFFu) | (static_cast<unsigned long long>(v >> 16) << 32);
       };
       if (DT == DET_F32) {
-        const uint64_t T = (static_cast<uint64_t>(static_cast<uint32_t>(bcast<J>(xm[r]))) *
-                            static_cast<uint32_t>(wm)) << s16;
-        atomicAdd(q, pair(static_cast<uint32_t>(T)));
-        atomicAdd(q + 2 * FQ, pair(static_cast<uint32_t>(T >> 32)));
+        const uint32_t xv = SX ? xs[r][J] : static_cast<uint32_t>(bcast<J>(xm[r]));
+        const uint64_t T = (static_cast<uint64_t>(xv) * static_cast<uint32_t>(wm)) << s16;
+        // the halves as two opaque 32-bit values (an empty asm, no
+        // instruction): each pair is then one and and one shift, where the
+        // compiler otherwise rebuilds the fields with 64-bit shifts and moves
+        uint32_t lo = static_cast<uint32_t>(T), hi = static_cast<uint32_t>(T >> 32);
+        asm("" : "+v"(lo), "+v"(hi));
+        atomicAdd(q, pair(lo));
+        atomicAdd(q + 2 * FQ, pair(hi));
       } else {
         const uint32_t T = static_cast<uint32_t>(__umul24(static_cast<uint32_t>(bcast<J>(xm[r])),
                                                            static_cast<uint32_t>(wm))) << s16;
@@ -384,7 +390,7 @@ __device__ __forceinline__ void steps_raw(char* cbase, uint32_t lane_off, const 
       atomicAdd(p + F, static_cast<int>(T >> 16));
     }
   }
-  if constexpr (J + 1 < V_KC) steps_raw<DT, R, PRE, PAIR, J + 1>(cbase, lane_off, wa, wb, xm, xe);
+  if constexpr (J + 1 < V_KC) steps_raw<DT, R, PRE, PAIR, SX, J + 1>(cbase, lane_off, wa, wb, xm, xe, xs);
 }
 
 // the lane's pre-decoded w chunk: 16 significands and 16 exponent words
@@ -496,7 +502,21 @@ __global__ __launch_bounds__(64 * W, WPE) void k_partial(GemmArgs a, const void*
         xm[r] = m;
         xe[r] = static_cast<int>(e);
       }
-      steps_raw<DT, R, PRE, PAIR, 0>(cnt, lane_off, wq[sl], wbq[sl], xm, xe);
+      // f32, pre-decoded: x's significands by scalar loads (the chunk is the
+      // same in every lane), SGPR operands of the products (no broadcast)
+      constexpr bool SX = PRE && DT == DET_F32;
+      uint32_t xs[R][V_KC];
+      if constexpr (SX) {
+        const int64_t cu = __builtin_amdgcn_readfirstlane(static_cast<int>(c));
+        typedef const __attribute__((address_space(4))) uint32_t* cword;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const cword q = (cword)(a.xsig + (m0 + r) * a.xld + cu * V_KC);
+#pragma unroll
+          for (int i = 0; i < V_KC; ++i) xs[r][i] = q[i];
+        }
+      }
+      steps_raw<DT, R, PRE, PAIR, SX, 0>(cnt, lane_off, wq[sl], wbq[sl], xm, xe, xs);
     }
   }
   __syncthreads();
