@@ -1464,13 +1464,18 @@ constexpr int PL_OX = 6, PL_OW = 7;       // rows of x, of w recomputed on the a
 constexpr int PL_WORDS = 8;
 
 // list[] = the rows with need > S, in increasing order, and pos[r] = the
-// place of row r in list[] or -1 (one workgroup)
-__global__ __launch_bounds__(1024) void k_slice_list(const int32_t* need, int64_t n, const int32_t* plan,
+// place of row r in list[] or -1: workgroup 0 for x's M rows, workgroup 1 for
+// w's N rows (w's arrays follow x's)
+__global__ __launch_bounds__(1024) void k_slice_list(const int32_t* need, int64_t M, int64_t N, const int32_t* plan,
                                                      int32_t* list, int32_t* pos) {
   __shared__ int32_t wsum[16];
   __shared__ int64_t base;
   const int S = plan[PL_S];
   if (S == 0) return;
+  const int64_t n = blockIdx.x == 0 ? M : N, at = blockIdx.x == 0 ? 0 : M;
+  need += at;
+  list += at;
+  pos += at;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (threadIdx.x == 0) base = 0;
   __syncthreads();
@@ -1557,13 +1562,22 @@ __device__ __forceinline__ void tail_scan_range(const TailArgs& a, int S, int64_
 
 // the listed rows' ranges, the waves of a capped grid taking them in turn
 // (nothing when the plan keeps no tails)
+// x's and w's tail scans in one launch: workgroups [0, nb0) take x
+struct TailPair {
+  TailArgs op[2];
+  int64_t nb0;
+};
+
 template <int DT>
-__global__ __launch_bounds__(256) void k_tail_scan(TailArgs a) {
+__global__ __launch_bounds__(256) void k_tail_scan(TailPair p) {
+  const bool wside = blockIdx.x >= p.nb0;
+  const TailArgs& a = p.op[wside ? 1 : 0];
   const int S = a.plan[PL_S];
   if (S == 0 || a.plan[PL_TAILS] == 0) return;
+  const int64_t blk = wside ? blockIdx.x - p.nb0 : blockIdx.x, nb = wside ? gridDim.x - p.nb0 : p.nb0;
   const int64_t nkr = (a.K + 1023) / 1024, ranges = a.plan[PL_FX + a.side] * nkr;
-  const int64_t waves = static_cast<int64_t>(gridDim.x) * 4;
-  for (int64_t wid = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) >> 6; wid < ranges; wid += waves)
+  const int64_t waves = nb * 4;
+  for (int64_t wid = (blk * 256 + threadIdx.x) >> 6; wid < ranges; wid += waves)
     tail_scan_range<DT>(a, S, wid, nkr, threadIdx.x & 63);
 }
 
@@ -1571,11 +1585,18 @@ __global__ __launch_bounds__(256) void k_tail_scan(TailArgs a) {
 // with more than SL_TAIL_CAP tails), ovl[] = the original indices of those
 // rows, in order, and their count into the plan (one workgroup).  Without
 // tails every listed row is recomputed.
-__global__ __launch_bounds__(1024) void k_tail_plan(int32_t* plan, int side, const int32_t* cnt, const int32_t* list,
+__global__ __launch_bounds__(1024) void k_tail_plan(int32_t* plan, int64_t M, const int32_t* cnt, const int32_t* list,
                                                     int32_t* off, int32_t* ovl) {
   __shared__ int64_t wover[16];
   __shared__ int64_t obase;
   if (plan[PL_S] == 0) return;
+  // workgroup 0: x's listed rows, workgroup 1: w's (w's arrays follow x's)
+  const int side = blockIdx.x;
+  const int64_t at = side == 0 ? 0 : M;
+  cnt += at;
+  list += at;
+  off += at;
+  ovl += at;
   const int64_t n = plan[PL_FX + side];
   if (plan[PL_TAILS] == 0) {
     for (int64_t p = threadIdx.x; p < n; p += 1024) ovl[p] = list[p];
@@ -3007,20 +3028,23 @@ det_status launch_sliced(GemmArgs a, char* ws, bool only_slices, int forced, boo
     st = launch_gemm8<DT>(b, ws, s, MARK_BOTH);
     if (st != DET_OK) return st;
   }
-  hipLaunchKernelGGL(k_slice_list, dim3(1), dim3(1024), 0, s, needx, M, plan, listx, posx);
-  hipLaunchKernelGGL(k_slice_list, dim3(1), dim3(1024), 0, s, needw, N, plan, listw, posw);
+  hipLaunchKernelGGL(k_slice_list, dim3(2), dim3(1024), 0, s, needx, M, N, plan, listx, posx);
   st = hip_check(hipGetLastError(), "slice list launch");
   if (st != DET_OK) return st;
   // tails per listed row (when the plan keeps tails)
   {
     const int64_t nkr = (K + 1023) / 1024;
-    TailArgs t{};
+    TailPair tp{};
+    TailArgs& t = tp.op[0];
     t.p = a.x; t.K = K; t.s_r = a.x_sm; t.s_k = a.x_sk; t.list = listx; t.top = topx; t.plan = plan; t.side = 0;
     t.cnt = cntx; t.tk = tkx;
-    hipLaunchKernelGGL((k_tail_scan<DT>), dim3(grid_for(M * nkr * 64, 256, 2048)), dim3(256), 0, s, t);
-    t.p = a.w; t.s_r = a.w_sn; t.s_k = a.w_sk; t.list = listw; t.top = topw; t.side = 1;
-    t.cnt = cntw; t.tk = tkw;
-    hipLaunchKernelGGL((k_tail_scan<DT>), dim3(grid_for(N * nkr * 64, 256, 2048)), dim3(256), 0, s, t);
+    TailArgs& u = tp.op[1];
+    u = t;
+    u.p = a.w; u.s_r = a.w_sn; u.s_k = a.w_sk; u.list = listw; u.top = topw; u.side = 1;
+    u.cnt = cntw; u.tk = tkw;
+    tp.nb0 = grid_for(M * nkr * 64, 256, 1024);
+    const int64_t nb1 = grid_for(N * nkr * 64, 256, 1024);
+    hipLaunchKernelGGL((k_tail_scan<DT>), dim3(static_cast<unsigned>(tp.nb0 + nb1)), dim3(256), 0, s, tp);
     st = hip_check(hipGetLastError(), "tail count launch");
     if (st != DET_OK) return st;
   }
@@ -3053,8 +3077,7 @@ det_status launch_sliced(GemmArgs a, char* ws, bool only_slices, int forced, boo
   }
   if (st != DET_OK) return st;
   // which listed rows go to the accumulator path, and the tails of the others
-  hipLaunchKernelGGL(k_tail_plan, dim3(1), dim3(1024), 0, s, plan, 0, cntx, listx, offx, ovlx);
-  hipLaunchKernelGGL(k_tail_plan, dim3(1), dim3(1024), 0, s, plan, 1, cntw, listw, offw, ovlw);
+  hipLaunchKernelGGL(k_tail_plan, dim3(2), dim3(1024), 0, s, plan, M, cntx, listx, offx, ovlx);
   SliceFixArgs f{};
   f.x = a.x; f.x_sm = a.x_sm; f.x_sk = a.x_sk;
   f.w = a.w; f.w_sn = a.w_sn; f.w_sk = a.w_sk;
