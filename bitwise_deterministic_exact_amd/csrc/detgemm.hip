@@ -792,7 +792,8 @@ __device__ __forceinline__ void fold8(char* c0, int64_t (&dg)[WD], bool norm) {
 // One R x 64 output tile of det_gemm: the body of k_gemm8.
 template <class G, int DT, bool PRE, int R, int W>
 __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, const void* __restrict__ xg,
-                                           const void* __restrict__ wg, int64_t tile, int tid, char* cells, int& claim) {
+                                           const void* __restrict__ wg, int64_t tile, int tid, bool fresh, char* cells,
+                                           int& claim) {
   constexpr int CW = G::NCELL / W;                          // cells each wave folds
   constexpr int OFF = (G::BITS * G::FIRST) & 31;            // bit of a wave's first cell within its digit
   // window digits: the window's value stays below 2^(OFF + B(CW-1) + cell
@@ -858,9 +859,12 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, const void* __rest
       for (int r = 0; r < R; ++r) x[r] = load_elem<DT>(xg, xrow[r] + k * a.x_sk);
     }
   };
-  // the first chunk's loads go out before the cells are cleared
+  // the first chunk's loads go out before the cells are cleared.  After a
+  // tile of this workgroup (`fresh` false) the folds have zeroed every cell,
+  // and only the digit array laid over the first cells needs clearing.
   if (wave < nchunks) load(wave, wq[0], weq[0], xq[0], xwq[0]);
-  for (int q = tid; q < G::ALLOC * static_cast<int>(G::CS) / 16; q += 64 * W)
+  const int clear16 = fresh ? G::ALLOC * static_cast<int>(G::CS) / 16 : R * ND * 64 * 8 / 16;
+  for (int q = tid; q < clear16; q += 64 * W)
     reinterpret_cast<uint4*>(cells)[q] = make_uint4(0u, 0u, 0u, 0u);
   if (tid == 0) claim = W;
   __syncthreads();
@@ -1021,7 +1025,7 @@ __global__ __launch_bounds__(64 * W, WPE) void k_gemm8(GemmArgs a, const void* _
   __shared__ int claim;                           // the epoch's next unclaimed chunk (from e0)
   if (a.gate != nullptr && *a.gate == 0) return;
   if constexpr (!LOOP) {
-    gemm8_tile<G, DT, PRE, R, W>(a, xg, wg, xcd_tile(), threadIdx.x, cells, claim);
+    gemm8_tile<G, DT, PRE, R, W>(a, xg, wg, xcd_tile(), threadIdx.x, true, cells, claim);
   } else {
     if (a.mcount != nullptr) a.M = *a.mcount;
     if (a.ncount != nullptr) a.N = *a.ncount;
@@ -1034,7 +1038,7 @@ __global__ __launch_bounds__(64 * W, WPE) void k_gemm8(GemmArgs a, const void* _
       // derived from it is hoisted out of the loop to hold registers
       int tid = static_cast<int>(threadIdx.x);
       asm volatile("" : "+v"(tid));
-      gemm8_tile<G, DT, PRE, R, W>(a, xg, wg, t, tid, cells, claim);
+      gemm8_tile<G, DT, PRE, R, W>(a, xg, wg, t, tid, t == t0, cells, claim);
       __syncthreads();
     }
   }
