@@ -1317,6 +1317,8 @@ __device__ __forceinline__ void split_elem(uint32_t b, bool& neg, uint32_t& m, i
 // (max of ex + bit length - 1) and the lowest (min of ex + trailing zeros)
 // over its nonzero elements, by atomic max / min into top[] and low[]
 // (initialised to SL_TOP_NONE / SL_LOW_NONE).
+constexpr int64_t STAT_KR = 4096;         // K elements per wave of the K-major span check
+
 struct SliceStatArgs {
   const void* p; int64_t R, K, s_r, s_k;
   int32_t* top; int32_t* low;
@@ -1337,9 +1339,10 @@ __device__ __forceinline__ void stat_elem(uint32_t b, int& top, int& low, bool& 
   }
 }
 
-// KMAJ (unit K stride): one wave per row and 1024-element K range, lanes
-// along K; otherwise one thread per row and 256-element K range, lanes along
-// the rows (coalesced for a transposed view), 16 loads in flight
+// KMAJ (unit K stride): one wave per row and STAT_KR-element K range (four
+// 1024-element parts, all of whose loads go out together), lanes along K;
+// otherwise one thread per row and 256-element K range, lanes along the rows
+// (coalesced for a transposed view), 16 loads in flight
 template <int DT, bool KMAJ>
 __device__ __forceinline__ void stats_body(const SliceStatArgs& a, int64_t blk) {
   int top = SL_TOP_NONE, low = SL_LOW_NONE;
@@ -1347,35 +1350,44 @@ __device__ __forceinline__ void stats_body(const SliceStatArgs& a, int64_t blk) 
   int64_t row;
   bool lead;
   if (KMAJ) {
-    const int64_t nkr = (a.K + 1023) / 1024;
+    const int64_t nkr = (a.K + STAT_KR - 1) / STAT_KR;
     const int64_t wid = (blk * 256 + threadIdx.x) >> 6;
     const int lane = threadIdx.x & 63;
     if (wid >= a.R * nkr) return;               // uniform per wave
     row = wid / nkr;
-    const int64_t k0 = (wid % nkr) * 1024;
+    const int64_t kr = (wid % nkr) * STAT_KR;
     constexpr int EPV = DT == DET_F32 ? 4 : 8;              // elements per 16-byte load
-    if (a.vec && k0 + 1024 <= a.K) {                         // lane: 16 consecutive elements
-      const uint4* const q = reinterpret_cast<const uint4*>(
-          static_cast<const char*>(a.p) + (row * a.s_r + k0 + lane * 16) * (DT == DET_F32 ? 4 : 2));
+    if (a.vec && kr + STAT_KR <= a.K) {                      // lane: 16 consecutive elements per part
+      uint4 v[STAT_KR / 1024][16 / EPV];
 #pragma unroll
-      for (int i = 0; i < 16 / EPV; ++i) {
-        const uint4 v = q[i];
-        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+      for (int part = 0; part < STAT_KR / 1024; ++part) {
+        const uint4* const q = reinterpret_cast<const uint4*>(
+            static_cast<const char*>(a.p) + (row * a.s_r + kr + part * 1024 + lane * 16) * (DT == DET_F32 ? 4 : 2));
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (DT == DET_F32) {
-            stat_elem<DT>(w4[u], top, low, bad);
-          } else {
-            stat_elem<DT>(w4[u] & 0xFFFFu, top, low, bad);
-            stat_elem<DT>(w4[u] >> 16, top, low, bad);
+        for (int i = 0; i < 16 / EPV; ++i) v[part][i] = q[i];
+      }
+#pragma unroll
+      for (int part = 0; part < STAT_KR / 1024; ++part)
+#pragma unroll
+        for (int i = 0; i < 16 / EPV; ++i) {
+          const uint32_t w4[4] = {v[part][i].x, v[part][i].y, v[part][i].z, v[part][i].w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (DT == DET_F32) {
+              stat_elem<DT>(w4[u], top, low, bad);
+            } else {
+              stat_elem<DT>(w4[u] & 0xFFFFu, top, low, bad);
+              stat_elem<DT>(w4[u] >> 16, top, low, bad);
+            }
           }
         }
-      }
     } else {
+      for (int64_t k0 = kr; k0 < min(kr + STAT_KR, a.K); k0 += 1024) {
 #pragma unroll 4
-      for (int i = 0; i < 16; ++i) {
-        const int64_t k = k0 + i * 64 + lane;
-        if (k < a.K) stat_elem<DT>(load_elem<DT>(a.p, row * a.s_r + k), top, low, bad);
+        for (int i = 0; i < 16; ++i) {
+          const int64_t k = k0 + i * 64 + lane;
+          if (k < a.K) stat_elem<DT>(load_elem<DT>(a.p, row * a.s_r + k), top, low, bad);
+        }
       }
     }
 #pragma unroll
@@ -1777,10 +1789,48 @@ __device__ __forceinline__ void slice_digits_in(const uint32_t (&e)[16], int bas
   }
 }
 
+// The same digits for S <= 4 (|V| < 2^30), four elements at a time: the
+// balanced digits of V are the bytes of V + B, B = 0x80 in each of the S
+// bytes, each less 128 (that is, with its top bit flipped), so the digit
+// planes are a 4 x 4 byte transpose of the four words V + B (eight
+// v_perm_b32) and one xor per word, in place of a shift-and-subtract per
+// digit and element.
+template <int DT>
+__device__ __forceinline__ void slice_digits_perm(const uint32_t (&e)[16], int base, int S, uint32_t (&d)[SL_MAX][4]) {
+  const uint32_t bias = S >= 4 ? 0x80808080u : 0x80808080u & ((1u << (8 * S)) - 1u);
+  uint32_t u[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    bool neg;
+    uint32_t m;
+    int ex;
+    split_elem<DT>(e[j], neg, m, ex);
+    const int sh = ex - base;
+    int32_t v = 0;
+    if (m != 0u && sh + __ffs(static_cast<int>(m)) - 1 >= 0) {    // not zero, not below the window
+      v = static_cast<int32_t>(sh >= 0 ? m << sh : m >> (-sh));
+      if (neg) v = -v;
+    }
+    u[j] = static_cast<uint32_t>(v) + bias;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t* const w = u + 4 * q;
+    const uint32_t t0 = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);   // w0.b0 w1.b0 w0.b1 w1.b1
+    const uint32_t t1 = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);   // w0.b2 w1.b2 w0.b3 w1.b3
+    const uint32_t t2 = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
+    const uint32_t t3 = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
+    d[0][q] = __builtin_amdgcn_perm(t2, t0, 0x05040100u) ^ 0x80808080u;     // byte s of w0..w3
+    d[1][q] = __builtin_amdgcn_perm(t2, t0, 0x07060302u) ^ 0x80808080u;
+    if (S > 2) d[2][q] = __builtin_amdgcn_perm(t3, t1, 0x05040100u) ^ 0x80808080u;
+    if (S > 3) d[3][q] = __builtin_amdgcn_perm(t3, t1, 0x07060302u) ^ 0x80808080u;
+  }
+}
+
 // |V| < 2^(8S - 2): 32-bit arithmetic up to S = 4, 64-bit above
 template <int DT>
 __device__ __forceinline__ void slice_digits(const uint32_t (&e)[16], int base, int S, uint32_t (&d)[SL_MAX][4]) {
-  if (S <= 4) slice_digits_in<DT, int32_t, 4>(e, base, S, d);
+  if (S <= 4) slice_digits_perm<DT>(e, base, S, d);
   else slice_digits_in<DT, int64_t, SL_MAX>(e, base, S, d);
 }
 
@@ -2856,8 +2906,8 @@ SliceStatArgs stat_args(const void* p, int64_t R, int64_t K, int64_t s_r, int64_
   SliceStatArgs a{p, R, K, s_r, s_k, top, low, false, false};
   const int64_t esz = DT == DET_F32 ? 4 : 2;
   a.vec = s_k == 1 && (reinterpret_cast<uintptr_t>(p) % 16) == 0 && (s_r * esz) % 16 == 0;
-  a.direct = K <= (s_k == 1 ? 1024 : 256);
-  blocks = s_k == 1 ? (R * ((K + 1023) / 1024) + 3) / 4 : (R * ((K + 255) / 256) + 255) / 256;
+  a.direct = K <= (s_k == 1 ? STAT_KR : 256);
+  blocks = s_k == 1 ? (R * ((K + STAT_KR - 1) / STAT_KR) + 3) / 4 : (R * ((K + 255) / 256) + 255) / 256;
   return a;
 }
 
