@@ -51,6 +51,7 @@ def load() -> ctypes.CDLL:
         "det_combine": ([ctypes.POINTER(vp), c_int, vp, i64, vp], c_int),
         "det_finalize": ([vp, vp, i64, vp], c_int),
         "det_round_f32_to_bf16": ([vp, vp, i64, vp], c_int),
+        "det_mse_grad": ([c_int, vp, vp, i64, ctypes.c_float, vp, vp, vp, vp], c_int),
         "det_check_finite": ([c_int, vp, i64, i64, i64, i64, vp, vp], c_int),
         "det_dot_partial": ([c_int, vp, i64, vp, i64, i64, vp, c_int, vp], c_int),
         "det_sqdiff_partial": ([c_int, vp, i64, vp, i64, i64, vp, c_int, vp], c_int),

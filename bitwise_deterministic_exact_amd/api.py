@@ -354,6 +354,30 @@ def device_status(device=None, clear: bool = True) -> set:
     return {name for bit, name in ((1, "nonfinite"), (2, "range")) if flags.value & bit}
 
 
+def mse_grad(y: torch.Tensor, t: Optional[torch.Tensor], g: torch.Tensor, need_dy: bool = True,
+             need_dt: bool = False):
+    """(dy, dt) of the exact mean squared error sum((y - t)^2) / n with
+    incoming gradient g (a one-element tensor): dy = RNE_dtype(RNE32(RNE32(y -
+    t) * c) * g), c = 2/n rounded to fp32, dt = -dy before the dtype rounding
+    (det_mse_grad).  Either is None when not needed."""
+    import numpy as np
+    if y.dtype not in _DT or y.device.type != "cuda":
+        raise ValueError("mse_grad takes float32 or bfloat16 GPU tensors")
+    if t is not None and (t.shape != y.shape or t.dtype != y.dtype or t.device != y.device):
+        raise ValueError("y and t must share shape, dtype and device")
+    n = y.numel()
+    c = float(np.float32(2.0) / np.float32(max(n, 1)))         # one IEEE fp32 division
+    yc = y.contiguous()
+    tc = t.contiguous() if t is not None else None
+    gv = g.reshape(-1)[:1].to(device=y.device, dtype=torch.float32).contiguous()
+    dy = torch.empty_like(yc) if need_dy else None
+    dt = torch.empty_like(yc) if need_dt else None
+    ptr = lambda v: ctypes.c_void_p(v.data_ptr()) if v is not None else None      # noqa: E731
+    _call(y.device, _lib.load().det_mse_grad, _DT[y.dtype], ptr(yc), ptr(tc), n, c, ptr(gv), ptr(dy), ptr(dt),
+          _stream(y.device))
+    return (dy.reshape(y.shape) if dy is not None else None, dt.reshape(y.shape) if dt is not None else None)
+
+
 def round_f32_to_bf16(t: torch.Tensor) -> torch.Tensor:
     """Round float32 to bfloat16, nearest with ties to even (HIP kernel)."""
     if t.dtype != torch.float32 or t.device.type != "cuda":

@@ -1251,6 +1251,36 @@ __global__ __launch_bounds__(256) void k_round_bf16(const uint32_t* __restrict__
   }
 }
 
+// The gradient of the mean squared error, elementwise: d = RNE32(y - t),
+// gy = RNE32(RNE32(d * c) * g), dy = gy and dt = -gy in the operands' dtype
+// (nearest-even for bf16).  Every fp32 operation is one IEEE operation, in
+// this order, so the bits are those of the same expression evaluated one
+// correctly rounded operation at a time.
+template <int DT>
+__device__ __forceinline__ float mse_load(const void* p, int64_t i) {
+  if (DT == DET_F32) return static_cast<const float*>(p)[i];
+  return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
+}
+template <int DT>
+__device__ __forceinline__ void mse_store(void* p, int64_t i, float v) {
+  if (DT == DET_F32) static_cast<float*>(p)[i] = v;
+  else static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(round_bits_bf16(__float_as_uint(v)));
+}
+template <int DT>
+__global__ __launch_bounds__(256) void k_mse_grad(const void* __restrict__ y, const void* __restrict__ t, int64_t n,
+                                                   float c, const float* __restrict__ g, void* __restrict__ dy,
+                                                   void* __restrict__ dt) {
+  const float gv = *g;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+    float d = mse_load<DT>(y, i);
+    if (t != nullptr) d = __fsub_rn(d, mse_load<DT>(t, i));
+    const float gy = __fmul_rn(__fmul_rn(d, c), gv);
+    if (dy != nullptr) mse_store<DT>(dy, i, gy);
+    if (dt != nullptr) mse_store<DT>(dt, i, -gy);
+  }
+}
+
 template <int DT>
 __global__ __launch_bounds__(256) void k_check_finite(const void* __restrict__ p, int64_t rows, int64_t cols,
                                                        int64_t s_row, int64_t s_col, int32_t* flag) {
@@ -3472,6 +3502,24 @@ det_status det_dot_partial(det_dtype dt, const void* a, int64_t inc_a, const voi
 det_status det_sqdiff_partial(det_dtype dt, const void* a, int64_t inc_a, const void* b, int64_t inc_b,
                               int64_t n, int64_t* acc, int accumulate, void* stream) {
   return dot_common(b == nullptr ? DOT_SQUARE : DOT_SQDIFF, dt, a, inc_a, b, inc_b, n, acc, accumulate, stream);
+}
+
+det_status det_mse_grad(det_dtype dt, const void* y, const void* t, int64_t n, float c, const float* g, void* dy,
+                        void* dt_out, void* stream) {
+  if (dt != DET_F32 && dt != DET_BF16) return fail(DET_EDTYPE, "unknown dtype %d", static_cast<int>(dt));
+  if (n < 0) return fail(DET_EINVAL, "negative count");
+  if (n == 0 || (dy == nullptr && dt_out == nullptr)) return DET_OK;
+  if (y == nullptr || g == nullptr) return fail(DET_EINVAL, "null pointer");
+  const uintptr_t align = dt == DET_F32 ? 3u : 1u;
+  if ((reinterpret_cast<uintptr_t>(y) | reinterpret_cast<uintptr_t>(t) | reinterpret_cast<uintptr_t>(dy) |
+       reinterpret_cast<uintptr_t>(dt_out)) & align)
+    return fail(DET_EINVAL, "operands must be aligned to their element size");
+  if (reinterpret_cast<uintptr_t>(g) & 3u) return fail(DET_EINVAL, "g must be 4-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(grid_for(n, 256, 8192));
+  if (dt == DET_F32) hipLaunchKernelGGL(k_mse_grad<DET_F32>, grid, dim3(256), 0, s, y, t, n, c, g, dy, dt_out);
+  else hipLaunchKernelGGL(k_mse_grad<DET_BF16>, grid, dim3(256), 0, s, y, t, n, c, g, dy, dt_out);
+  return hip_check(hipGetLastError(), "mse gradient launch");
 }
 
 det_status det_round_f32_to_bf16(const float* in, uint16_t* out, int64_t n, void* stream) {

@@ -14,10 +14,12 @@ correctly rounded, by n as an fp32 value (n itself rounded to fp32 above
 Without a target the loss is sum y^2 / n.
 
 The gradient 2 (y - t) / n is elementwise (no reduction, so no order to fix)
-and is formed with torch's elementwise fp32 ops, each correctly rounded:
+and is formed by the library's det_mse_grad kernel, one correctly rounded fp32
+operation at a time:
   dy = RNE_dtype( RNE32( RNE32(y - t) * c ) * g ),  c = RNE32(2 / fp32(n)),
 with g the incoming gradient (1 when the loss is the output) and the last
-rounding only for bfloat16 y.  When n is a power of two (and nothing
+rounding only for bfloat16 y; the target's gradient is the negation.  c is one
+IEEE fp32 division on the host.  When n is a power of two (and nothing
 underflows) c is exact and the scaling adds no rounding.
 """
 from __future__ import annotations
@@ -26,7 +28,7 @@ from typing import Optional
 
 import torch
 
-from .api import det_finalize, exact_sqdiff_digits
+from .api import det_finalize, exact_sqdiff_digits, mse_grad
 
 
 class _ExactMSE(torch.autograd.Function):
@@ -43,16 +45,8 @@ class _ExactMSE(torch.autograd.Function):
     @staticmethod
     def backward(ctx, g: torch.Tensor):
         y, t = ctx.saved_tensors
-        # c = 2 / n as one IEEE fp32 division on the device (a Python scalar
-        # would reach the kernel as a double rounded to fp32: two roundings)
-        two = torch.full((), 2.0, dtype=torch.float32, device=y.device)
-        c = two / torch.full((), float(max(y.numel(), 1)), dtype=torch.float32, device=y.device)
-        d = y.to(torch.float32)
-        if ctx.has_target:
-            d = d - t.to(torch.float32)
-        gy = (d * c) * g
-        dy = gy.to(y.dtype) if ctx.needs_input_grad[0] else None
-        dt = (-gy).to(t.dtype) if ctx.has_target and ctx.needs_input_grad[1] else None
+        need_dt = ctx.has_target and ctx.needs_input_grad[1]
+        dy, dt = mse_grad(y, t if ctx.has_target else None, g, ctx.needs_input_grad[0], need_dt)
         return dy, dt
 
 

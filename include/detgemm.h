@@ -332,6 +332,24 @@ det_status det_sqdiff_partial(det_dtype dt, const void* a, int64_t inc_a, const 
                               int64_t n, int64_t* acc, int accumulate, void* stream);
 
 /*
+ * det_mse_grad -- the gradient of the exact mean squared error (the loss of
+ * det_sqdiff_partial divided by n) with respect to its operands, for the
+ * training step of the "Usage" section.  Elementwise, with no reduction:
+ *     d  = RNE32(y_i - t_i)            (d = y_i without a target)
+ *     gy = RNE32(RNE32(d * c) * g)     c = RNE32(2 / n), g = *g
+ *     dy_i = gy,  dt_i = -gy           rounded to dt (nearest-even for bf16)
+ * each fp32 step one IEEE operation, so the bits are fixed by the inputs.
+ *   dt           DET_F32 or DET_BF16: the element type of y, t, dy and dt_out
+ *   y, t         device operands of n elements, contiguous; t may be NULL
+ *   c            2/n rounded to fp32 (by the caller, one IEEE division)
+ *   g            device pointer to one fp32 value (the incoming gradient)
+ *   dy, dt_out   device outputs of n elements; either may be NULL (not written)
+ * Returns DET_OK, DET_EINVAL, DET_EDTYPE or DET_EHIP.
+ */
+det_status det_mse_grad(det_dtype dt, const void* y, const void* t, int64_t n, float c, const float* g, void* dy,
+                        void* dt_out, void* stream);
+
+/*
  * det_round_f32_to_bf16 -- round fp32 values to bf16 (nearest, ties to even),
  * used by the DetLinear backward of the "Usage" section to hand dY to a bf16
  * exact GEMM.  in: n fp32, out: n bf16 bit patterns; contiguous.  NaN stays NaN.

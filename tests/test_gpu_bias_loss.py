@@ -219,12 +219,13 @@ def _loss_oracle(yb, tb, dt):
     return np.float32(np.array([s], dtype=np.uint32).view(np.float32)[0] / np.float32(yb.size))
 
 
-def _mse_grad_reference(yb, tb, n, dt):
+def _mse_grad_reference(yb, tb, n, dt, gscale=1.0, negate=False):
     """The exact-MSE gradient's bits as the loss defines them:
-    RNE_dt(RNE32(RNE32(y - t) * RNE32(2 / fp32(n)))), from exact rationals: the
-    difference and the scale rounded to fp32 by pins.rne_fraction, their product
-    formed exactly in fp64 (two 24-bit significands), one IEEE cast to fp32,
-    and for bf16 rne_fraction to 8 bits."""
+    RNE_dt(RNE32(RNE32(RNE32(y - t) * RNE32(2 / fp32(n))) * g)), negated for the
+    target's gradient, from exact rationals: the difference and the scale
+    rounded to fp32 by pins.rne_fraction, each product formed exactly in fp64
+    (two 24-bit significands, or one and a small integer g), one IEEE cast to
+    fp32, and for bf16 rne_fraction to 8 bits."""
     as_f32 = lambda b: float(np.array([b], dtype=np.uint32).view(np.float32)[0])
     val = (lambda b: Fraction(as_f32(int(b)))) if dt == "f32" else (lambda b: Fraction(as_f32(int(b) << 16)))
     c = pins.rne_fraction(Fraction(2) / Fraction(float(np.float32(n))), 24)
@@ -235,6 +236,10 @@ def _mse_grad_reference(yb, tb, n, dt):
             d = (as_f32(int(yv)) if dt == "f32" else as_f32(int(yv) << 16)) - \
                 (as_f32(int(tv)) if dt == "f32" else as_f32(int(tv) << 16))
         g = np.float32(np.float64(float(d)) * np.float64(float(c)))      # exact product, one rounding
+        if gscale != 1.0:
+            g = np.float32(np.float64(g) * np.float64(gscale))
+        if negate:
+            g = -g
         if dt == "bf16":
             gb = g if np.isinf(g) else np.float32(float(pins.rne_fraction(Fraction(float(g)), 8)))
             bits = int(np.array([gb], dtype=np.float32).view(np.uint32)[0]) >> 16
@@ -269,6 +274,21 @@ def test_exact_mse_loss(dt):
         want_g = _mse_grad_reference(yb, tb, n, dt)
         got_g = tensor_bits(y.grad)
         assert np.array_equal(got_g, want_g), mismatch_report(got_g, want_g)
+    # a target that needs its gradient too, and an incoming gradient of 3
+    yb, tb = random_operands(rng, 1, 1, 777, dt, "wide")
+    yb, tb = yb.reshape(777), tb.reshape(777)
+    y = to_device(yb, dt).requires_grad_(True)
+    t = to_device(tb, dt).requires_grad_(True)
+    (det.exact_mse_loss(y, t) * 3.0).backward()
+    for got, neg in ((y.grad, False), (t.grad, True)):
+        want_g = _mse_grad_reference(yb, tb, 777, dt, gscale=3.0, negate=neg)
+        assert np.array_equal(tensor_bits(got), want_g), mismatch_report(tensor_bits(got), want_g)
+    # without a target: the gradient of sum y^2 / n
+    y = to_device(yb, dt).requires_grad_(True)
+    det.exact_mse_loss(y).backward()
+    zero = np.zeros_like(yb)
+    want_g = _mse_grad_reference(yb, zero, 777, dt)
+    assert np.array_equal(tensor_bits(y.grad), want_g), mismatch_report(tensor_bits(y.grad), want_g)
     # the fp32 division of the rounded sum by n is correctly rounded
     s32 = rng.standard_normal(4096).astype(np.float32) * np.float32(1e3)
     for n in (3, 7, 1000, 12293, 8191, 1 << 20):
