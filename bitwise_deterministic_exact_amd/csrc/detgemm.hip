@@ -92,16 +92,10 @@ constexpr uint32_t SIGN_BIT = 15;
 // ties to even, gradual underflow, overflow to inf; exact zero -> +0).
 // Precondition |dg[j]| <= 2^62.  Fully unrolled: every index is static, so the
 // 18 words stay in registers.
-__device__ uint32_t round_digits_to_f32(const int64_t (&dg)[ND]) {
-  uint32_t w[ND];
-  int64_t carry = 0;
-#pragma unroll
-  for (int j = 0; j < ND; ++j) {
-    const int64_t t = dg[j] + carry;
-    w[j] = static_cast<uint32_t>(t);
-    carry = t >> 32;                  // arithmetic: floor(t / 2^32)
-  }
-  // value = W + carry * 2^576 with W = sum w[j] 2^(32j)
+//
+// round_words_to_f32: the same value after the carries have been propagated,
+// (W + carry * 2^576) * 2^-298 with W = sum w[j] 2^(32j), 0 <= w[j] < 2^32.
+__device__ uint32_t round_words_to_f32(uint32_t (&w)[ND], int64_t carry) {
   if (carry != 0 && carry != -1) return carry < 0 ? 0xFF800000u : 0x7F800000u;
   const bool neg = carry < 0;
   if (neg) {                          // |value| = 2^576 - W
@@ -145,6 +139,19 @@ __device__ uint32_t round_digits_to_f32(const int64_t (&dg)[ND]) {
     mag = E >= 255 ? 0x7F800000u : (static_cast<uint32_t>(E) << 23) | (r - (1u << 23));
   }
   return (neg ? 0x80000000u : 0u) | mag;
+}
+
+// round_digits_to_f32: the carries of the digits, then the rounding
+__device__ uint32_t round_digits_to_f32(const int64_t (&dg)[ND]) {
+  uint32_t w[ND];
+  int64_t carry = 0;
+#pragma unroll
+  for (int j = 0; j < ND; ++j) {
+    const int64_t t = dg[j] + carry;
+    w[j] = static_cast<uint32_t>(t);
+    carry = t >> 32;                  // arithmetic: floor(t / 2^32)
+  }
+  return round_words_to_f32(w, carry);
 }
 
 // ---------------------------------------------------------------- GEMM kernels: shared parts
@@ -918,17 +925,20 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, const void* __rest
     int cur = wave;
     if (cur >= lim) return;
     if constexpr (!G::CLAIM) {
-      // fixed shares: wave v takes chunks e0 + v + i*W
+      // fixed shares: wave v takes chunks e0 + v + i*W; the two ring slots
+      // written out (constant slot indices keep the ring in registers)
+      auto slot = [&](auto slc) {
+        constexpr int sl = decltype(slc)::value;
+        const int nxt = cur + W;
+        if (nxt < lim) load(e0 + nxt, wq[sl ^ 1], weq[sl ^ 1], xq[sl ^ 1], xwq[sl ^ 1]);
+        compute(e0 + cur, sl);
+        cur = nxt;
+        return nxt >= lim;
+      };
 #pragma unroll 1
       for (;;) {
-#pragma unroll
-        for (int sl = 0; sl < 2; ++sl) {
-          const int nxt = cur + W;
-          if (nxt < lim) load(e0 + nxt, wq[sl ^ 1], weq[sl ^ 1], xq[sl ^ 1], xwq[sl ^ 1]);
-          compute(e0 + cur, sl);
-          if (nxt >= lim) return;
-          cur = nxt;
-        }
+        if (slot(std::integral_constant<int, 0>{})) return;
+        if (slot(std::integral_constant<int, 1>{})) return;
       }
     }
     int got = 0;
@@ -1011,6 +1021,215 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, const void* __rest
   }
 }
 
+// The pre-decoded f32 form of k_gemm8 (one workgroup per CU, waves
+// claiming chunks) over a workgroup's consecutive tiles t0 .. t1-1, with
+// two barriers per tile: after the epoch's adds, and after the digit sums.
+// Between them every wave issues the loads of the next tile's first chunk
+// (so they are in flight while it folds), folds its cells into its windows
+// (leaving the cells zero) and adds the windows into the digit array D, which
+// has its own LDS beside the cells.  After the second barrier waves 0 .. R-1
+// read their rows of D, clear them and round, while the other waves already
+// add the next tile's products; the claims let the late waves take fewer
+// chunks.  Nothing waits for the rounding and its y store, and no tile but
+// the first clears LDS.
+template <class G, int DT, int R, int W>
+__device__ __forceinline__ void gemm8_claim_tiles(const GemmArgs& a, int t0, int t1, char* cells, int64_t* D,
+                                                  int& claim) {
+  static_assert(G::CLAIM && G::SX && !G::XPACK, "the claiming form with x significands in SGPRs");
+  constexpr int CW = G::NCELL / W;                          // cells each wave folds
+  constexpr int OFF = (G::BITS * G::FIRST) & 31;            // bit of a wave's first cell within its digit
+  constexpr int VB = sizeof(typename G::cell_t) == 8 ? 63 : 31;
+  constexpr int LOG2CW = CW <= 1 ? 0 : CW <= 2 ? 1 : CW <= 4 ? 2 : CW <= 8 ? 3 : CW <= 16 ? 4 : 5;
+  constexpr int WD = (OFF + G::BITS * (CW - 1) + VB + LOG2CW + 1 + 31) / 32;
+  constexpr int64_t EPOCH = G::KFLUSH / V_KC;               // chunks per epoch, all waves together
+  static_assert(CW * W == G::NCELL && EPOCH >= W && (G::BITS * CW) % 32 == 0, "epoch layout");
+
+  // 32-bit tile, row, column and chunk indices (fewer SGPRs; tiles < 2^31,
+  // K < 2^19 in one launch)
+  const int nchunks = static_cast<int>((a.K + V_KC - 1) / V_KC);
+  const int tm = static_cast<int>(a.tiles_m);
+  // the thread's indices, re-derived at each tile (the lane from the exec
+  // mask, the wave index from an SGPR opaque to the compiler): nothing
+  // derived from them is hoisted out of the tile loop to hold registers, and
+  // the thread index itself is not kept
+  int wave0 = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  int tid, lane, wave;
+  uint32_t xj4, lane_off;
+  char* my_cells;
+  auto derive = [&]() {
+    asm volatile("" : "+s"(wave0));
+    wave = wave0;
+    uint32_t ones = ~0u;
+    asm volatile("" : "+s"(ones));
+    lane = static_cast<int>(__builtin_amdgcn_mbcnt_hi(ones, __builtin_amdgcn_mbcnt_lo(ones, 0u)));
+    tid = wave * 64 + lane;
+    xj4 = static_cast<uint32_t>(lane & 15) * 4u;
+    lane_off = static_cast<uint32_t>(lane * G::ES);
+    my_cells = cells + (G::ALLOC - G::NCELL + wave * CW) * G::CS + lane * G::ES;
+  };
+
+  uint32_t wq[2][V_KC], weq[2][V_KC], xwq[2][R];
+  const int xm0[R] = {};                          // unused: the significands come as SGPR operands
+
+  // chunk c of the tile at (m0, n0): the lane's w chunk and x's words
+  auto load = [&](int m0, int n0, int c, uint32_t (&w)[V_KC], uint32_t (&we)[V_KC], uint32_t (&xw)[R]) {
+    const int64_t k0 = static_cast<int64_t>(c) * V_KC;
+    load_w_pre8(a, a.wsig + static_cast<int64_t>(n0) * V_KC + lane * 4,
+                a.wexp32 + static_cast<int64_t>(n0) * V_KC + lane * 4, k0, w, we);
+    const char* const wb = reinterpret_cast<const char*>(a.xword + m0 * a.xld + k0);
+#pragma unroll
+    for (int r = 0; r < R; ++r) xw[r] = *reinterpret_cast<const uint32_t*>(wb + r * a.xld * 4 + xj4);
+  };
+  // chunk c from ring slot sl; the x significands by scalar loads (the chunk
+  // index is the same in every lane), just before its products
+  auto compute = [&](int m0, int c, int sl) {
+    int xe[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) xe[r] = static_cast<int>(xwq[sl][r]);
+    uint32_t xs[R][V_KC];
+    const int64_t cu = __builtin_amdgcn_readfirstlane(c);
+    typedef const __attribute__((address_space(4))) uint32_t* cword;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const cword q = (cword)(a.xsig + (m0 + r) * a.xld + cu * V_KC);
+#pragma unroll
+      for (int i = 0; i < V_KC; ++i) xs[r][i] = q[i];
+    }
+    steps8<G, DT, true, R, 0>(cells, static_cast<uint32_t>(lane), lane_off, wq[sl], weq[sl], xm0, xe, xs);
+  };
+  // an epoch's chunks e0 .. e0 + lim - 1: wave v starts with chunk e0 + v
+  // (in ring slot 0), then takes the next unclaimed one, claimed a chunk ahead
+  auto run_epoch = [&](int m0, int n0, int e0) {
+    const int lim = min(nchunks - e0, static_cast<int>(EPOCH));
+    int cur = wave;
+    if (cur >= lim) return;
+    int got = 0;
+    if (lane == 0) got = atomicAdd(&claim, 1);
+    int nxt = __shfl(got, 0);
+    // (the last chunk's products are written out apart, so that the other
+    // slot is read only on the path that loaded it: the compiler then keeps
+    // no ring slot but slot 0 live across tiles)
+    auto slot = [&](auto slc) {
+      constexpr int sl = decltype(slc)::value;
+      if (nxt >= lim) {
+        compute(m0, e0 + cur, sl);
+        return true;
+      }
+      int pend = 0;
+      if (lane == 0) pend = atomicAdd(&claim, 1);
+      load(m0, n0, e0 + nxt, wq[sl ^ 1], weq[sl ^ 1], xwq[sl ^ 1]);
+      compute(m0, e0 + cur, sl);
+      cur = nxt;
+      nxt = __shfl(pend, 0);
+      return false;
+    };
+#pragma unroll 1
+    for (;;) {
+      if (slot(std::integral_constant<int, 0>{})) return;
+      if (slot(std::integral_constant<int, 1>{})) return;
+    }
+  };
+
+  // the tile's first row and column, stepped down the rows (column-major
+  // tile order)
+  int m0 = (t0 % tm) * R, n0 = (t0 / tm) * V_BN;
+  for (int t = t0; t < t1; ++t) {
+    derive();
+    if (t == t0) {
+      // the first tile: every cell and D clear, its first chunks in flight
+      load(m0, n0, min(wave, nchunks - 1), wq[0], weq[0], xwq[0]);
+      for (int q = tid; q < G::ALLOC * static_cast<int>(G::CS) / 16; q += 64 * W)
+        reinterpret_cast<uint4*>(cells)[q] = make_uint4(0u, 0u, 0u, 0u);
+      for (int q = tid; q < R * ND * 64 * 8 / 16; q += 64 * W)
+        reinterpret_cast<uint4*>(D)[q] = make_uint4(0u, 0u, 0u, 0u);
+      if (tid == 0) claim = W;
+      __syncthreads();
+    }
+    const int jb = (G::BITS * (G::FIRST + wave * CW)) >> 5;    // window digit 0 in the accumulator
+    // the next tile (after the last one: this one again, a wasted load)
+    int m1 = m0, n1 = n0;
+    if (t + 1 < t1) {
+      m1 += R;
+      if (m1 >= tm * R) { m1 = 0; n1 += V_BN; }
+    }
+    // Ring slot 0 is loaded on every path (chunk indices clamped into the
+    // operands; a wave past the chunks never computes it), so no earlier
+    // value of it stays live across the rounding.
+    const int cw = min(wave, nchunks - 1);
+    // after an epoch's adds: the claims restart, and the first chunks of the
+    // next epoch, else (waves R..W-1) of the next tile, go out
+    auto after_epoch = [&](int e1) {
+      __syncthreads();                            // the epoch's adds are in
+      if (tid == 0) claim = W;
+      if (e1 < nchunks) load(m0, n0, min(e1 + wave, nchunks - 1), wq[0], weq[0], xwq[0]);
+      else if (wave >= R) load(m1, n1, cw, wq[0], weq[0], xwq[0]);
+    };
+    // the first epoch is peeled off: its fold defines the windows, which
+    // then hold no registers during its adds
+    run_epoch(m0, n0, 0);
+    after_epoch(EPOCH);
+    int64_t dg[R][WD];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+      for (int j = 0; j < WD; ++j) dg[r][j] = 0;
+      fold8<G, CW, OFF, WD>(my_cells + r * G::RB, dg[r], G::NORM_EVERY == 1 || EPOCH >= nchunks);
+    }
+    int epoch = 1;
+    for (int e0 = static_cast<int>(EPOCH); e0 < nchunks; e0 += static_cast<int>(EPOCH), ++epoch) {
+      __syncthreads();                            // cells clear before the epoch
+      run_epoch(m0, n0, e0);
+      after_epoch(e0 + EPOCH);
+      const bool norm = (epoch % G::NORM_EVERY) == G::NORM_EVERY - 1 || e0 + EPOCH >= nchunks;
+#pragma unroll
+      for (int r = 0; r < R; ++r) fold8<G, CW, OFF, WD>(my_cells + r * G::RB, dg[r], norm);
+    }
+    // windows -> the rows' digit arrays D[(r * ND + j) * 64 + lane] (clear:
+    // their readers cleared them before this tile's first barrier)
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+      for (int d = WD - 1; d > 0; --d)            // anything beyond digit ND-1 joins digit ND-1
+        if (jb + d >= ND) { dg[r][d - 1] += dg[r][d] * (int64_t(1) << 32); dg[r][d] = 0; }
+#pragma unroll
+      for (int d = 0; d < WD; ++d)
+        if (jb + d < ND) atomicAdd(reinterpret_cast<unsigned long long*>(D + (r * ND + jb + d) * 64 + lane),
+                                   static_cast<unsigned long long>(dg[r][d]));
+    }
+    __syncthreads();                              // the digit sums are in, every cell is zero
+    // wave r finishes row r and clears its part of D.  The digits stream
+    // through the carry pass one at a time (32-bit words kept, not 64-bit
+    // digits), with the workspace's digits added or stored on the way.
+    if (wave < R) {
+      const int r = wave;
+      const int64_t m = m0 + r, n = n0 + lane;
+      const bool ok = m < a.M && n < a.N;
+      const bool add = ok && (a.epi == EPI_ADD || a.epi == EPI_ADD_ROUND);
+      const bool store = ok && (a.epi == EPI_STORE || a.epi == EPI_ADD);
+      int64_t* const dd = a.acc + (m * a.N + n) * ND;
+      uint32_t wv[ND];
+      int64_t carry = 0;
+#pragma unroll
+      for (int j = 0; j < ND; ++j) {
+        int64_t v = D[(r * ND + j) * 64 + lane];
+        D[(r * ND + j) * 64 + lane] = 0;
+        if (add) v += dd[j];
+        if (store) dd[j] = v;
+        const int64_t u = v + carry;
+        wv[j] = static_cast<uint32_t>(u);
+        carry = u >> 32;                          // arithmetic: floor(u / 2^32)
+      }
+      if (ok && !(a.epi == EPI_STORE || a.epi == EPI_ADD)) {
+        const int64_t ym = a.xmap != nullptr ? a.xmap[m] : m, yn = a.wmap != nullptr ? a.wmap[n] : n;
+        a.y[ym * a.y_sm + yn * a.y_sn] = __uint_as_float(round_words_to_f32(wv, carry));
+      }
+      load(m1, n1, cw, wq[0], weq[0], xwq[0]);  // then the next tile's first chunk
+    }
+    m0 = m1;
+    n0 = n1;
+  }
+}
+
 // det_gemm: one workgroup per tile in the XCD-aware order.  LOOP: each
 // workgroup takes tpw consecutive tiles of that order, with M and N from the
 // device counts if given: the launches whose work the device decides (a
@@ -1023,8 +1242,21 @@ __global__ __launch_bounds__(64 * W, WPE) void k_gemm8(GemmArgs a, const void* _
                                                        const void* __restrict__ wg) {
   __shared__ __align__(16) char cells[G::ALLOC * G::CS];
   __shared__ int claim;                           // the epoch's next unclaimed chunk (from e0)
+  // the claiming form's digit array (beside the cells; one int64 elsewhere)
+  __shared__ __align__(16) int64_t dsum[G::CLAIM && PRE ? R * ND * 64 : 1];
   if (a.gate != nullptr && *a.gate == 0) return;
-  if constexpr (!LOOP) {
+  if constexpr (G::CLAIM && PRE) {
+    int64_t t0 = xcd_tile(), t1 = t0 + 1;
+    if constexpr (LOOP) {
+      if (a.mcount != nullptr) a.M = *a.mcount;
+      if (a.ncount != nullptr) a.N = *a.ncount;
+      a.tiles_m = (a.M + R - 1) / R;
+      a.tiles_n = (a.N + V_BN - 1) / V_BN;
+      t0 *= a.tpw;
+      t1 = min(t0 + a.tpw, a.tiles_m * a.tiles_n);
+    }
+    if (t0 < t1) gemm8_claim_tiles<G, DT, R, W>(a, static_cast<int>(t0), static_cast<int>(t1), cells, dsum, claim);
+  } else if constexpr (!LOOP) {
     gemm8_tile<G, DT, PRE, R, W>(a, xg, wg, xcd_tile(), threadIdx.x, true, cells, claim);
   } else {
     if (a.mcount != nullptr) a.M = *a.mcount;
@@ -2113,7 +2345,7 @@ __device__ __forceinline__ void slice_steps(const v4i (&fa)[S][2], const v4i (&f
 }
 
 template <int S, int CB, int WR, int NBUF>
-__global__ __launch_bounds__(128 * WR, 2) void k_slice_mma(SliceMmaArgs a) {
+__global__ __launch_bounds__(128 * WR, S >= 7 ? 1 : 2) void k_slice_mma(SliceMmaArgs a) {
   using T = SliceTile<S, CB, WR, NBUF>;
   constexpr int NG = T::NG, NW = T::NW, FA = T::FA, FT = T::FT, PW = T::PER_WAVE;
   __shared__ __align__(16) int8_t lds[T::LDS_BYTES];
@@ -2308,7 +2540,8 @@ __device__ __forceinline__ void dot_add(unsigned long long* set, uint32_t m1, ui
 // or a*a); `pos` is the lane's positive set, the negative set follows it
 template <int DT, int MODE>
 __device__ __forceinline__ void dot_elem(unsigned long long* pos, uint32_t ab, uint32_t bb, bool& bad) {
-  bad |= nonfinite_bits<DT>(ab) | (MODE != DOT_SQUARE && nonfinite_bits<DT>(bb));
+  bad |= nonfinite_bits<DT>(ab);
+  if (MODE != DOT_SQUARE) bad |= nonfinite_bits<DT>(bb);
   // o = (Ez_a - bias) + (Ez_b - bias) + 298: 298 - 300 for f32, 298 - 268 for bf16
   constexpr uint32_t OFF = DT == DET_F32 ? uint32_t(-2) : 30u;
   uint32_t ma, ea;
@@ -2610,7 +2843,8 @@ det_status launch_partial(GemmArgs a, void* ws, hipStream_t s) {
 // VALU, binds).  bf16 keeps two 64 KB workgroups of 8 waves (four rows on 128
 // KB: 4570 against 5369).
 constexpr int64_t GEMM8_LIST_GRID = 1024;    // workgroups of a device-counted recompute
-constexpr int64_t GEMM8_GATED_TPW = 8;       // tiles per workgroup of a gated launch
+constexpr int64_t GEMM8_LOOP_TPW = 32;       // most tiles per workgroup of a looping launch
+constexpr int64_t GEMM8_LOOP_GRID = 2048;    // fewest workgroups a looping launch keeps
 
 template <int DT> struct Gemm8Config;
 template <> struct Gemm8Config<DET_F32> {
@@ -2653,12 +2887,18 @@ det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s, int marks = MARK_BO
     det_status st = hip_check(hipGetLastError(), "predecode launch");
     if (st != DET_OK) return st;
   }
-  // work the device decides: consecutive tiles per workgroup (a capped grid
-  // for device-counted rows or columns, GEMM8_GATED_TPW for a gated launch)
+  // The looping form (consecutive tiles per workgroup) for the work the
+  // device decides (a gate, device-counted rows or columns) and for every
+  // pre-decoded launch of the claiming (f32) kernel, whose tiles after a
+  // workgroup's first neither clear LDS nor wait for a rounding.  Tiles per
+  // workgroup: a capped grid for device-counted rows or columns, else up to
+  // GEMM8_LOOP_TPW, keeping eight workgroups per CU where the tiles allow.
   const bool listed = a.mcount != nullptr || a.ncount != nullptr;
-  const bool loop = listed || a.gate != nullptr;
-  if (loop && !pre) return fail(DET_EINVAL, "a launch decided on the device needs the workspace");
-  a.tpw = listed ? (blocks + GEMM8_LIST_GRID - 1) / GEMM8_LIST_GRID : loop ? GEMM8_GATED_TPW : 1;
+  if ((listed || a.gate != nullptr) && !pre) return fail(DET_EINVAL, "a launch decided on the device needs the workspace");
+  const bool loop = listed || a.gate != nullptr || (G::CLAIM && pre);
+  a.tpw = listed ? (blocks + GEMM8_LIST_GRID - 1) / GEMM8_LIST_GRID
+         : loop   ? std::max<int64_t>(1, std::min(GEMM8_LOOP_TPW, blocks / GEMM8_LOOP_GRID))
+                  : 1;
   const dim3 grid(static_cast<unsigned>((blocks + a.tpw - 1) / a.tpw)), block(64 * W);
   // K blocks; beyond one block the exact digits are carried in the
   // workspace, behind the decoded w
@@ -2681,9 +2921,13 @@ det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s, int marks = MARK_BO
     }
     det_status st = mark_event(g_ev_start, (marks & MARK_START) && first, s);
     if (st != DET_OK) return st;
-    if (loop) hipLaunchKernelGGL((k_gemm8<G, DT, true, R, W, WPE, true>), grid, block, 0, s, b, xb, a.w);
-    else if (pre) hipLaunchKernelGGL((k_gemm8<G, DT, true, R, W, WPE, false>), grid, block, 0, s, b, xb, a.w);
-    else hipLaunchKernelGGL((k_gemm8<G, DT, false, R, W, WPE, false>), grid, block, 0, s, b, xb, a.w);
+    if (loop) {
+      hipLaunchKernelGGL((k_gemm8<G, DT, true, R, W, WPE, true>), grid, block, 0, s, b, xb, a.w);
+    } else if (!pre) {
+      hipLaunchKernelGGL((k_gemm8<G, DT, false, R, W, WPE, false>), grid, block, 0, s, b, xb, a.w);
+    } else if constexpr (!G::CLAIM) {
+      hipLaunchKernelGGL((k_gemm8<G, DT, true, R, W, WPE, false>), grid, block, 0, s, b, xb, a.w);
+    }
     st = hip_check(hipGetLastError(), "gemm launch");
     if (st == DET_OK) st = mark_event(g_ev_stop, (marks & MARK_STOP) && last, s);
     if (st != DET_OK) return st;
@@ -3046,7 +3290,7 @@ det_status launch_sliced(GemmArgs a, char* ws, bool only_slices, int forced, boo
   auto take = [&](int64_t n) { int32_t* r = q; q += n; return r; };
   int32_t* const topx = take(M); int32_t* const topw = take(N);      // top, then low: contiguous for init
   int32_t* const lowx = take(M); int32_t* const loww = take(N);
-  int32_t* const needx = take(M); int32_t* const needw = take(N);
+  int32_t* const needx = take(M); take(N);                           // need of x, then of w
   int32_t* const listx = take(M); int32_t* const listw = take(N);
   int32_t* const posx = take(M); int32_t* const posw = take(N);
   int32_t* const cntx = take(M); int32_t* const cntw = take(N);
