@@ -1498,13 +1498,72 @@ __device__ __forceinline__ void mse_store(void* p, int64_t i, float v) {
   if (DT == DET_F32) static_cast<float*>(p)[i] = v;
   else static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(round_bits_bf16(__float_as_uint(v)));
 }
+// eight consecutive elements (group q) with 16-byte accesses
 template <int DT>
+__device__ __forceinline__ void mse_load8(const void* p, int64_t q, float (&v)[8]) {
+  if (DT == DET_F32) {
+    const uint4 a = static_cast<const uint4*>(p)[2 * q], b = static_cast<const uint4*>(p)[2 * q + 1];
+    const uint32_t u[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(u[i]);
+  } else {
+    const uint4 a = static_cast<const uint4*>(p)[q];
+    const uint32_t u[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(u[i] << 16);
+      v[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+    }
+  }
+}
+template <int DT>
+__device__ __forceinline__ void mse_store8(void* p, int64_t q, const float (&v)[8]) {
+  if (DT == DET_F32) {
+    static_cast<uint4*>(p)[2 * q] = make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                               __float_as_uint(v[3]));
+    static_cast<uint4*>(p)[2 * q + 1] = make_uint4(__float_as_uint(v[4]), __float_as_uint(v[5]),
+                                                   __float_as_uint(v[6]), __float_as_uint(v[7]));
+  } else {
+    uint32_t u[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      u[i] = round_bits_bf16(__float_as_uint(v[2 * i])) | (round_bits_bf16(__float_as_uint(v[2 * i + 1])) << 16);
+    static_cast<uint4*>(p)[q] = make_uint4(u[0], u[1], u[2], u[3]);
+  }
+}
+
+// VEC: every operand 16-byte aligned; groups of eight elements with 16-byte
+// accesses, then the last n mod 8 one at a time
+template <int DT, bool VEC>
 __global__ __launch_bounds__(256) void k_mse_grad(const void* __restrict__ y, const void* __restrict__ t, int64_t n,
                                                    float c, const float* __restrict__ g, void* __restrict__ dy,
                                                    void* __restrict__ dt) {
   const float gv = *g;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+  const int64_t first = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  int64_t done = 0;
+  if constexpr (VEC) {
+    const int64_t groups = n / 8;
+    for (int64_t q = first; q < groups; q += stride) {
+      float d[8], gy[8], ng[8];
+      mse_load8<DT>(y, q, d);
+      if (t != nullptr) {
+        float e[8];
+        mse_load8<DT>(t, q, e);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d[i] = __fsub_rn(d[i], e[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        gy[i] = __fmul_rn(__fmul_rn(d[i], c), gv);
+        ng[i] = -gy[i];
+      }
+      if (dy != nullptr) mse_store8<DT>(dy, q, gy);
+      if (dt != nullptr) mse_store8<DT>(dt, q, ng);
+    }
+    done = groups * 8;
+  }
+  for (int64_t i = done + first; i < n; i += stride) {
     float d = mse_load<DT>(y, i);
     if (t != nullptr) d = __fsub_rn(d, mse_load<DT>(t, i));
     const float gy = __fmul_rn(__fmul_rn(d, c), gv);
@@ -1584,7 +1643,8 @@ constexpr int64_t STAT_KR = 4096;         // K elements per wave of the K-major 
 struct SliceStatArgs {
   const void* p; int64_t R, K, s_r, s_k;
   int32_t* top; int32_t* low;
-  bool vec;                               // unit K stride, rows 16-byte aligned
+  bool vec;                               // 16-byte loads: unit K stride and rows 16-byte aligned (K-major),
+                                          // or unit row stride and 16-byte aligned columns (transposed)
   bool direct;                            // one wave (one thread) takes a whole row: store, no atomics
 };
 
@@ -1603,8 +1663,9 @@ __device__ __forceinline__ void stat_elem(uint32_t b, int& top, int& low, bool& 
 
 // KMAJ (unit K stride): one wave per row and STAT_KR-element K range (four
 // 1024-element parts, all of whose loads go out together), lanes along K;
-// otherwise one thread per row and 256-element K range, lanes along the rows
-// (coalesced for a transposed view), 16 loads in flight
+// otherwise one thread per 256-element K range of one row (lanes along the
+// rows, coalesced for a transposed view, 16 loads in flight), or with `vec`
+// one block per 64 rows and 256-element K range, 16-byte loads along the rows
 template <int DT, bool KMAJ>
 __device__ __forceinline__ void stats_body(const SliceStatArgs& a, int64_t blk) {
   int top = SL_TOP_NONE, low = SL_LOW_NONE;
@@ -1658,6 +1719,79 @@ __device__ __forceinline__ void stats_body(const SliceStatArgs& a, int64_t blk) 
       low = min(low, __shfl_xor(low, o));
     }
     lead = lane == 0;
+  } else if (a.vec) {
+    // rows contiguous and 16-byte aligned: a block takes 64 rows x 256 k;
+    // thread t takes EPL consecutive rows (group t mod RG) and RG
+    // consecutive k (one 16-byte load each); the threads of a row group
+    // combine through shuffles, the waves through LDS, and one thread per
+    // row stores it or adds it atomically
+    constexpr int EPL = DT == DET_F32 ? 4 : 8, RG = 64 / EPL;
+    constexpr int64_t ESZ = DT == DET_F32 ? 4 : 2;
+    __shared__ int red[2][4][64];
+    const int64_t nkr = (a.K + 255) / 256;
+    const int64_t rb = blk / nkr, k0 = (blk % nkr) * 256;
+    const int t = static_cast<int>(threadIdx.x), g = t % RG;
+    const int64_t row0 = rb * 64 + g * EPL;
+    const int64_t kq = k0 + (t / RG) * RG, k1 = min(kq + RG, a.K);
+    int tops[EPL], lows[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) { tops[j] = SL_TOP_NONE; lows[j] = SL_LOW_NONE; }
+    if (row0 + EPL <= a.R) {
+      if (kq < k1) {
+        uint4 q[RG];
+#pragma unroll
+        for (int u = 0; u < RG; ++u)          // clamped: a repeated element leaves max and min as they are
+          q[u] = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.p) +
+                                                 (row0 + min(kq + u, k1 - 1) * a.s_k) * ESZ);
+#pragma unroll
+        for (int u = 0; u < RG; ++u) {
+          const uint32_t w4[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (DT == DET_F32) {
+              stat_elem<DT>(w4[i], tops[i], lows[i], bad);
+            } else {
+              stat_elem<DT>(w4[i] & 0xFFFFu, tops[2 * i], lows[2 * i], bad);
+              stat_elem<DT>(w4[i] >> 16, tops[2 * i + 1], lows[2 * i + 1], bad);
+            }
+          }
+        }
+      }
+    } else {
+      for (int64_t k = kq; k < k1; ++k)
+#pragma unroll
+        for (int j = 0; j < EPL; ++j)
+          if (row0 + j < a.R) stat_elem<DT>(load_elem<DT>(a.p, row0 + j + k * a.s_k), tops[j], lows[j], bad);
+    }
+    note_nonfinite(bad);
+#pragma unroll
+    for (int o = RG; o < 64; o <<= 1)
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        tops[j] = max(tops[j], __shfl_xor(tops[j], o));
+        lows[j] = min(lows[j], __shfl_xor(lows[j], o));
+      }
+    const int wave = t >> 6;
+    if ((t & 63) < RG) {
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        red[0][wave][g * EPL + j] = tops[j];
+        red[1][wave][g * EPL + j] = lows[j];
+      }
+    }
+    __syncthreads();
+    if (t < 64 && rb * 64 + t < a.R) {
+      const int top = max(max(red[0][0][t], red[0][1][t]), max(red[0][2][t], red[0][3][t]));
+      const int low = min(min(red[1][0][t], red[1][1][t]), min(red[1][2][t], red[1][3][t]));
+      if (a.direct) {
+        a.top[rb * 64 + t] = top;
+        a.low[rb * 64 + t] = low;
+      } else if (top != SL_TOP_NONE) {
+        atomicMax(a.top + rb * 64 + t, top);
+        atomicMin(a.low + rb * 64 + t, low);
+      }
+    }
+    return;
   } else {
     const int64_t t = blk * 256 + threadIdx.x;
     const int64_t nkr = (a.K + 255) / 256;
@@ -2159,7 +2293,39 @@ __device__ __forceinline__ void make_t_body(const SliceMakeArgs& a, int64_t blk)
   __shared__ uint32_t tile[64][65];
   const int64_t rb4 = blk / a.Kb, kb = blk % a.Kb;
   const int t = threadIdx.x;
-  {
+  if (a.vec) {
+    // 16-byte loads along the contiguous rows: EPL elements per load, LPK
+    // lanes per k of the tile; rows past R (a partial load) element by element
+    constexpr int EPL = DT == DET_F32 ? 4 : 8, LPK = 64 / EPL, KPP = 256 / LPK;
+    constexpr int64_t ESZ = DT == DET_F32 ? 4 : 2;
+    const int rg = (t % LPK) * EPL;
+    const int64_t row0 = rb4 * 64 + rg;
+#pragma unroll
+    for (int pass = 0; pass < 64 / KPP; ++pass) {
+      const int kl = pass * KPP + t / LPK;
+      const int64_t k = kb * 64 + kl;
+      uint32_t v[EPL];
+      if (k < a.K && row0 + EPL <= a.R) {
+        const uint4 q = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.p) + (row0 + k * a.s_k) * ESZ);
+        const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (DT == DET_F32) {
+            v[j] = u[j];
+          } else {
+            v[2 * j] = u[j] & 0xFFFFu;
+            v[2 * j + 1] = u[j] >> 16;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < EPL; ++j)
+          v[j] = row0 + j < a.R && k < a.K ? load_elem<DT>(a.p, row0 + j + k * a.s_k) : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) tile[kl][rg + j] = v[j];
+    }
+  } else {
     const int rl = t & 63, kq = t >> 6;                   // row of the tile (lane), quarter of its k
     const int64_t row = rb4 * 64 + rl;
 #pragma unroll
@@ -3179,9 +3345,12 @@ SliceStatArgs stat_args(const void* p, int64_t R, int64_t K, int64_t s_r, int64_
                         int64_t& blocks) {
   SliceStatArgs a{p, R, K, s_r, s_k, top, low, false, false};
   const int64_t esz = DT == DET_F32 ? 4 : 2;
-  a.vec = s_k == 1 && (reinterpret_cast<uintptr_t>(p) % 16) == 0 && (s_r * esz) % 16 == 0;
+  const bool aligned = (reinterpret_cast<uintptr_t>(p) % 16) == 0;
+  a.vec = s_k == 1 ? aligned && (s_r * esz) % 16 == 0 : s_r == 1 && aligned && (s_k * esz) % 16 == 0;
   a.direct = K <= (s_k == 1 ? STAT_KR : 256);
-  blocks = s_k == 1 ? (R * ((K + STAT_KR - 1) / STAT_KR) + 3) / 4 : (R * ((K + 255) / 256) + 255) / 256;
+  blocks = s_k == 1 ? (R * ((K + STAT_KR - 1) / STAT_KR) + 3) / 4
+         : a.vec    ? (R + 63) / 64 * ((K + 255) / 256)
+                    : (R * ((K + 255) / 256) + 255) / 256;
   return a;
 }
 
@@ -3226,8 +3395,10 @@ SliceMakeArgs make_args(const void* p, int64_t R, int64_t K, int64_t s_r, int64_
   a.p = p; a.R = R; a.K = K; a.s_r = s_r; a.s_k = s_k; a.top = top; a.out = out;
   a.Rb = rows_padded / 16; a.Kb = round_up(K, 2 * SL_KB) / SL_KB;
   a.S = S;
-  a.vec = s_k == 1 && (reinterpret_cast<uintptr_t>(p) % 16) == 0 && (s_r * esz) % 16 == 0;
   trans = s_r == 1 && s_k > 1;            // a transposed view: through LDS (Rb is a multiple of 8)
+  // 16-byte loads along k (K-major) or along the rows (transposed)
+  a.vec = (reinterpret_cast<uintptr_t>(p) % 16) == 0 &&
+          (trans ? (s_k * esz) % 16 == 0 : s_k == 1 && (s_r * esz) % 16 == 0);
   blocks = trans ? a.Rb / 4 * a.Kb : grid_for(a.Rb * a.Kb * 64, 256, 8192);
   return a;
 }
@@ -3760,9 +3931,16 @@ det_status det_mse_grad(det_dtype dt, const void* y, const void* t, int64_t n, f
     return fail(DET_EINVAL, "operands must be aligned to their element size");
   if (reinterpret_cast<uintptr_t>(g) & 3u) return fail(DET_EINVAL, "g must be 4-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid(grid_for(n, 256, 8192));
-  if (dt == DET_F32) hipLaunchKernelGGL(k_mse_grad<DET_F32>, grid, dim3(256), 0, s, y, t, n, c, g, dy, dt_out);
-  else hipLaunchKernelGGL(k_mse_grad<DET_BF16>, grid, dim3(256), 0, s, y, t, n, c, g, dy, dt_out);
+  const bool vec = ((reinterpret_cast<uintptr_t>(y) | reinterpret_cast<uintptr_t>(t) | reinterpret_cast<uintptr_t>(dy) |
+                     reinterpret_cast<uintptr_t>(dt_out)) & 15u) == 0;
+  const dim3 grid(grid_for(vec ? (n + 7) / 8 : n, 256, 8192));
+  if (dt == DET_F32) {
+    if (vec) hipLaunchKernelGGL((k_mse_grad<DET_F32, true>), grid, dim3(256), 0, s, y, t, n, c, g, dy, dt_out);
+    else hipLaunchKernelGGL((k_mse_grad<DET_F32, false>), grid, dim3(256), 0, s, y, t, n, c, g, dy, dt_out);
+  } else {
+    if (vec) hipLaunchKernelGGL((k_mse_grad<DET_BF16, true>), grid, dim3(256), 0, s, y, t, n, c, g, dy, dt_out);
+    else hipLaunchKernelGGL((k_mse_grad<DET_BF16, false>), grid, dim3(256), 0, s, y, t, n, c, g, dy, dt_out);
+  }
   return hip_check(hipGetLastError(), "mse gradient launch");
 }
 

@@ -283,6 +283,13 @@ def test_exact_mse_loss(dt):
     for got, neg in ((y.grad, False), (t.grad, True)):
         want_g = _mse_grad_reference(yb, tb, 777, dt, gscale=3.0, negate=neg)
         assert np.array_equal(tensor_bits(got), want_g), mismatch_report(tensor_bits(got), want_g)
+    # operands one element past a 16-byte boundary: the one-at-a-time form
+    yv = to_device(np.concatenate([yb[:1], yb]), dt)[1:].detach().requires_grad_(True)
+    tv = to_device(np.concatenate([tb[:1], tb]), dt)[1:]
+    assert yv.data_ptr() % 16 != 0
+    det.exact_mse_loss(yv, tv).backward()
+    want_g = _mse_grad_reference(yb, tb, 777, dt)
+    assert np.array_equal(tensor_bits(yv.grad), want_g), mismatch_report(tensor_bits(yv.grad), want_g)
     # without a target: the gradient of sum y^2 / n
     y = to_device(yb, dt).requires_grad_(True)
     det.exact_mse_loss(y).backward()

@@ -200,13 +200,18 @@ def test_golden_rounding_fixtures_on_the_matrix_cores():
 
 def test_strided_and_transposed_views():
     rng = np.random.default_rng(580)
-    for dt in ("f32", "bf16"):
-        xb, wb = random_operands(rng, 67, 90, 140, dt, "normal")
+    for dt, K in (("f32", 140), ("bf16", 140), ("f32", 300), ("bf16", 300)):
+        xb, wb = random_operands(rng, 67, 90, K, dt, "normal")
         x, w = to_device(xb, dt), to_device(wb, dt)
         xt = x.t().contiguous().t()                      # unit M stride
         wt = w.t().contiguous().t()
         xs = to_device(np.ascontiguousarray(np.pad(xb, ((0, 0), (5, 3)))), dt)[:, 5:-3]
-        for xx, ww in ((xt, w), (x, wt), (xt, wt), (xs, w)):
+        # transposed views with 16-byte aligned columns and a ragged row count:
+        # the span check and digits take 16-byte loads, the last rows one at a time
+        xp = to_device(np.ascontiguousarray(np.pad(xb.T, ((0, 0), (0, 5)))), dt)[:, :67].t()
+        wp = to_device(np.ascontiguousarray(np.pad(wb.T, ((0, 0), (0, 6)))), dt)[:, :90].t()
+        assert xp.stride() == (1, 72) and wp.stride() == (1, 96)
+        for xx, ww in ((xt, w), (x, wt), (xt, wt), (xs, w), (xp, w), (x, wp), (xp, wp)):
             _check(xb, wb, dt, 4, "views", x=xx, w=ww)
 
 
