@@ -1332,17 +1332,18 @@ __global__ __launch_bounds__(256) void k_predecode_w(PredecodeArgs a) {
   note_nonfinite(bad);
 }
 
-// the same for k_gemm8: the grid's w-side words (32-bit), lane = n mod 64
+// the same for k_gemm8: the grid's w-side words (32-bit), lane = n mod 64;
+// block `blk` of `nblk` in a grid-stride loop
 template <class G, int DT>
-__global__ __launch_bounds__(256) void k_predecode_w8(PredecodeArgs a) {
+__device__ __forceinline__ void predecode_w8_body(PredecodeArgs a, int64_t blk, int64_t nblk) {
   if (a.gate != nullptr && *a.gate == 0) return;
   if (a.ncount != nullptr) a.N = *a.ncount;
   // with a device count only the chunks' first npd columns are decoded
   const int64_t npd = a.ncount != nullptr ? (a.N + V_BN - 1) / V_BN * V_BN : a.Np;
   const int64_t total = npd * a.Kp;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  const int64_t stride = nblk * blockDim.x;
   bool bad = false;
-  for (int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; j < total; j += stride) {
+  for (int64_t j = blk * blockDim.x + threadIdx.x; j < total; j += stride) {
     const int64_t i = npd == a.Np ? j : j / (npd * V_KC) * (a.Np * V_KC) + j % (npd * V_KC);
     int64_t n, k;
     subblock_nk(i, a.Np, n, k);
@@ -1356,6 +1357,11 @@ __global__ __launch_bounds__(256) void k_predecode_w8(PredecodeArgs a) {
     static_cast<uint32_t*>(a.wexp)[i] = e;
   }
   note_nonfinite(bad);
+}
+
+template <class G, int DT>
+__global__ __launch_bounds__(256) void k_predecode_w8(PredecodeArgs a) {
+  predecode_w8_body<G, DT>(a, blockIdx.x, gridDim.x);
 }
 
 // x of one K block [M][K] (any strides) -> the x side's significands and
@@ -1375,16 +1381,16 @@ struct PredecodeXArgs {
 };
 
 template <class D, int DT>
-__global__ __launch_bounds__(256) void k_predecode_x(PredecodeXArgs a) {
+__device__ __forceinline__ void predecode_x_body(PredecodeXArgs a, int64_t blk, int64_t nblk) {
   if (a.gate != nullptr && *a.gate == 0) return;
   if (a.mcount != nullptr) {
     a.M = *a.mcount;
     a.Mp = (a.M + a.mround - 1) / a.mround * a.mround;
   }
   const int64_t total = a.Mp * a.Kp;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  const int64_t stride = nblk * blockDim.x;
   bool bad = false;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
+  for (int64_t i = blk * blockDim.x + threadIdx.x; i < total; i += stride) {
     const int64_t m = i / a.Kp, k = i % a.Kp;
     const int64_t src = m < a.M && a.rmap != nullptr ? a.rmap[m] : m;
     int32_t v;
@@ -1400,6 +1406,19 @@ __global__ __launch_bounds__(256) void k_predecode_x(PredecodeXArgs a) {
     }
   }
   note_nonfinite(bad);
+}
+
+template <class D, int DT>
+__global__ __launch_bounds__(256) void k_predecode_x(PredecodeXArgs a) {
+  predecode_x_body<D, DT>(a, blockIdx.x, gridDim.x);
+}
+
+// both operands of a one-block k_gemm8 launch in one launch: blocks [0, nbw)
+// decode w, the rest x
+template <class G, int DT>
+__global__ __launch_bounds__(256) void k_predecode_wx8(PredecodeArgs w, PredecodeXArgs x, int64_t nbw) {
+  if (blockIdx.x < nbw) predecode_w8_body<G, DT>(w, blockIdx.x, nbw);
+  else predecode_x_body<G, DT>(x, blockIdx.x - nbw, gridDim.x - nbw);
 }
 
 // the raw-digit kernel's x decode, in the form k_predecode_x takes
@@ -1613,7 +1632,21 @@ constexpr int SL_KB = 64;                 // K per MFMA step
 constexpr int64_t SL_FOLD = 256;          // MFMA steps (2^14 k) per int32 sum
 constexpr int SL_TOP_NONE = -1000;        // top of an all-zero row
 constexpr int SL_LOW_NONE = 1000;
-constexpr int SL_HIST = 16;               // histogram bins per operand: need 0..8
+constexpr int SL_HIST = 12;               // histogram bins per operand: need 0..8
+
+// The plan of one call, made on the device from the span histogram (by the
+// last workgroup of k_slice_need, or by k_slice_plan), and read by every
+// later kernel of the call: int32 words in the workspace, behind the
+// histograms.
+constexpr int PL_S = 0;                   // digits per operand of the matrix-core pass; 0: the accumulator path
+constexpr int PL_ACC = 1;                 // 1 when the accumulator path runs instead (its gate)
+constexpr int PL_PREF = 2;                // the S the cost model prefers (0: the accumulator path)
+constexpr int PL_TAILS = 3;               // 1: listed outputs keep their sums and get their tails added
+constexpr int PL_FX = 4, PL_FW = 5;       // listed rows of x, of w
+constexpr int PL_OX = 6, PL_OW = 7;       // rows of x, of w recomputed on the accumulator path
+constexpr int PL_DONE = 8;                // workgroups of k_slice_need done (its last one makes the plan)
+constexpr int PL_WORDS = 16;
+constexpr int HP_WORDS = 2 * SL_HIST + PL_WORDS;   // the histograms and the plan, cleared by the span check
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
@@ -1820,7 +1853,7 @@ __device__ __forceinline__ void stats_body(const SliceStatArgs& a, int64_t blk) 
 
 // x's and w's span check in one launch: blocks [0, nb0) take op[0], the
 // rest op[1] (both operands need the same layout, KMAJ).  Block 0 also
-// clears the histograms (k_slice_need fills them next).
+// clears the histograms and the plan's words (k_slice_need fills them next).
 struct SliceStatPair {
   SliceStatArgs op[2];
   int64_t nb0;
@@ -1830,7 +1863,7 @@ struct SliceStatPair {
 template <int DT, bool KMAJ>
 __global__ __launch_bounds__(256) void k_slice_stats(SliceStatPair p) {
   const int64_t b = blockIdx.x;
-  if (b == 0 && threadIdx.x < 2 * SL_HIST && p.hist != nullptr) p.hist[threadIdx.x] = 0;
+  if (b == 0 && threadIdx.x < HP_WORDS && p.hist != nullptr) p.hist[threadIdx.x] = 0;   // the plan follows
   if (b < p.nb0) stats_body<DT, KMAJ>(p.op[0], b);
   else stats_body<DT, KMAJ>(p.op[1], b - p.nb0);
 }
@@ -1844,12 +1877,68 @@ __global__ __launch_bounds__(256) void k_slice_init(int32_t* top, int32_t* low, 
   }
 }
 
+// The choice between the paths: estimated seconds from the accumulator
+// kernels' MAC rate and the int8 MAC rate of the slice pass (both measured
+// on MI355X), S^2 int8 MACs per MAC plus the fallback rows and columns.
+constexpr double RATE_ACC_F32 = 3.4e12, RATE_ACC_BF16 = 5.0e12, RATE_MMA = 1.2e15;
+constexpr double SLICE_MIN_MACS = 134217728.0;    // 2^27: below, the accumulator path alone
+
+// The plan of one call on the device, from the span histograms: the S the
+// cost model prefers (the estimate above; `only`: no accumulator, `forced`:
+// that S alone), the S the call runs (`mode` > 0: that one, fixed by the
+// host; 0: the preferred one), the listed rows and whether their outputs
+// keep their sums (at most `zfix` of them).  One thread.
+struct PlanArgs {
+  const int32_t* hist;                    // x's bins, then w's
+  int32_t* plan;
+  int64_t M, N, K, zfix;
+  double rate_acc;
+  int mode, only, forced;
+};
+
+__device__ void plan_body(const PlanArgs& a) {
+  const int32_t* const hx = a.hist;
+  const int32_t* const hw = a.hist + SL_HIST;
+  const double macs = static_cast<double>(a.M) * a.N * a.K;
+  double best = a.only ? 1e300 : macs / a.rate_acc;
+  int pref = 0;
+  for (int S = SL_MIN; S <= SL_MAX; ++S) {
+    if (a.forced != 0 && S != a.forced) continue;
+    int64_t cx = 0, cw = 0;
+    for (int n = S + 1; n <= SL_MAX + 1; ++n) { cx += hx[n]; cw += hw[n]; }
+    const double t = static_cast<double>(S) * S * macs / RATE_MMA +
+                     (static_cast<double>(cx) * a.N * a.K + static_cast<double>(cw) * a.M * a.K) / a.rate_acc;
+    if (t < best) { best = t; pref = S; }
+  }
+  const int run = a.mode > 0 ? a.mode : pref;
+  int64_t fx = 0, fw = 0;
+  if (run > 0)
+    for (int n = run + 1; n <= SL_MAX + 1; ++n) { fx += hx[n]; fw += hw[n]; }
+  const bool tails = run > 0 && fx + fw > 0 && fx * a.N + fw * a.M <= a.zfix;
+  a.plan[PL_S] = run;
+  a.plan[PL_ACC] = run == 0;
+  a.plan[PL_PREF] = pref;
+  a.plan[PL_TAILS] = tails;
+  a.plan[PL_FX] = static_cast<int32_t>(fx);
+  a.plan[PL_FW] = static_cast<int32_t>(fw);
+  a.plan[PL_OX] = 0;
+  a.plan[PL_OW] = 0;
+}
+
+__global__ __launch_bounds__(64) void k_slice_plan(PlanArgs a) {
+  if (threadIdx.x == 0) plan_body(a);
+}
+
 // digits each row needs: the smallest S with top - low + 1 <= 8S - 2
 // (0 for an all-zero row, 8 for more than SL_MAX), and their histograms
 // (x's rows [0, split) count into hist[0..SL_HIST), w's rows after them into
 // hist[SL_HIST..2 SL_HIST)); also clears the rows' tail counts
+// With `fuse`, the last workgroup to finish makes the plan from the
+// completed histograms (`pa`; the span check cleared the count of finished
+// workgroups): one launch fewer per call.
 __global__ __launch_bounds__(256) void k_slice_need(const int32_t* top, const int32_t* low, int64_t n,
-                                                    int64_t split, int32_t* need, int32_t* hist, int32_t* cnt) {
+                                                    int64_t split, int32_t* need, int32_t* hist, int32_t* cnt,
+                                                    PlanArgs pa, int fuse) {
   __shared__ int32_t h[2 * SL_HIST];
   if (threadIdx.x < 2 * SL_HIST) h[threadIdx.x] = 0;
   __syncthreads();
@@ -1862,18 +1951,14 @@ __global__ __launch_bounds__(256) void k_slice_need(const int32_t* top, const in
   }
   __syncthreads();
   if (threadIdx.x < 2 * SL_HIST && h[threadIdx.x] != 0) atomicAdd(hist + threadIdx.x, h[threadIdx.x]);
+  if (!fuse) return;
+  __threadfence();                        // this workgroup's histogram adds, before it counts itself done
+  __syncthreads();
+  if (threadIdx.x == 0 && atomicAdd(pa.plan + PL_DONE, 1) == static_cast<int>(gridDim.x) - 1) {
+    __threadfence();                      // every other workgroup's adds are visible
+    plan_body(pa);
+  }
 }
-
-// The plan of one call, made on the device (k_slice_plan) from the span
-// histogram, and read by every later kernel of the call: int32 words in the
-// workspace, behind the histograms.
-constexpr int PL_S = 0;                   // digits per operand of the matrix-core pass; 0: the accumulator path
-constexpr int PL_ACC = 1;                 // 1 when the accumulator path runs instead (its gate)
-constexpr int PL_PREF = 2;                // the S the cost model prefers (0: the accumulator path)
-constexpr int PL_TAILS = 3;               // 1: listed outputs keep their sums and get their tails added
-constexpr int PL_FX = 4, PL_FW = 5;       // listed rows of x, of w
-constexpr int PL_OX = 6, PL_OW = 7;       // rows of x, of w recomputed on the accumulator path
-constexpr int PL_WORDS = 8;
 
 // list[] = the rows with need > S, in increasing order, and pos[r] = the
 // place of row r in list[] or -1: workgroup 0 for x's M rows, workgroup 1 for
@@ -2905,9 +2990,9 @@ int64_t workspace_bytes(int out_mode, int64_t M, int64_t N, int64_t K) {
   return b;
 }
 
-// decode x's K block [k0, k0 + kb) into the workspace region at `xr`
-template <class D, int DT>
-det_status predecode_x_block(GemmArgs& b, const void* xblock, char* xr, hipStream_t s) {
+// the decode of x's K block [k0, k0 + kb) into the workspace region at
+// `xr` (b.K = kb), and b's pointers to it
+PredecodeXArgs x_decode_args(GemmArgs& b, const void* xblock, char* xr) {
   PredecodeXArgs p{};
   p.x = xblock; p.x_sm = b.x_sm; p.x_sk = b.x_sk;
   p.M = b.M; p.K = b.K; p.Mp = round_up(b.M, TILE_ROWS); p.Kp = round_up(b.K, V_KC);
@@ -2916,6 +3001,12 @@ det_status predecode_x_block(GemmArgs& b, const void* xblock, char* xr, hipStrea
   p.rmap = b.xmap;
   p.gate = b.gate; p.mcount = b.mcount; p.mround = TILE_ROWS;
   b.xsig = p.xsig; b.xword = p.xword; b.xld = p.Kp;
+  return p;
+}
+
+template <class D, int DT>
+det_status predecode_x_block(GemmArgs& b, const void* xblock, char* xr, hipStream_t s) {
+  const PredecodeXArgs p = x_decode_args(b, xblock, xr);
   hipLaunchKernelGGL((k_predecode_x<D, DT>), dim3(grid_for(p.Mp * p.Kp, 256, 8192)), dim3(256), 0, s, p);
   return hip_check(hipGetLastError(), "x predecode launch");
 }
@@ -3039,6 +3130,10 @@ det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s, int marks = MARK_BO
     det_status st = note_raw_operands<DT>(a, s);
     if (st != DET_OK) return st;
   }
+  // K blocks; beyond one block the exact digits are carried in the
+  // workspace, behind the decoded w
+  const int64_t kblk = pre ? K_BLOCK : a.K;
+  const int64_t nblk = a.K > 0 ? (a.K + kblk - 1) / kblk : 1;
   if (pre) {
     PredecodeArgs p{};
     p.w = a.w; p.w_sn = a.w_sn; p.w_sk = a.w_sk;
@@ -3048,8 +3143,15 @@ det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s, int marks = MARK_BO
     a.wsig = p.wsig; a.wexp32 = static_cast<const uint32_t*>(p.wexp); a.wld = p.Np * V_KC;
     p.rmap = a.wmap;
     p.gate = a.gate; p.ncount = a.ncount;
-    const dim3 pg(grid_for(p.Np * p.Kp, 256, 8192));
-    hipLaunchKernelGGL((k_predecode_w8<G, DT>), pg, dim3(256), 0, s, p);
+    const int64_t nbw = grid_for(p.Np * p.Kp, 256, 8192);
+    if (nblk == 1) {                              // x's only K block with w, in one launch
+      const PredecodeXArgs px = x_decode_args(a, a.x, static_cast<char*>(ws) + predecode_bytes(1, a.N, a.K));
+      const int64_t nbx = grid_for(px.Mp * px.Kp, 256, 8192);
+      hipLaunchKernelGGL((k_predecode_wx8<G, DT>), dim3(static_cast<unsigned>(nbw + nbx)), dim3(256), 0, s, p, px,
+                         nbw);
+    } else {
+      hipLaunchKernelGGL((k_predecode_w8<G, DT>), dim3(static_cast<unsigned>(nbw)), dim3(256), 0, s, p);
+    }
     det_status st = hip_check(hipGetLastError(), "predecode launch");
     if (st != DET_OK) return st;
   }
@@ -3066,10 +3168,6 @@ det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s, int marks = MARK_BO
          : loop   ? std::max<int64_t>(1, std::min(GEMM8_LOOP_TPW, blocks / GEMM8_LOOP_GRID))
                   : 1;
   const dim3 grid(static_cast<unsigned>((blocks + a.tpw - 1) / a.tpw)), block(64 * W);
-  // K blocks; beyond one block the exact digits are carried in the
-  // workspace, behind the decoded w
-  const int64_t kblk = pre ? K_BLOCK : a.K;
-  const int64_t nblk = a.K > 0 ? (a.K + kblk - 1) / kblk : 1;
   if (nblk > 1)
     a.acc = reinterpret_cast<int64_t*>(static_cast<char*>(ws) + predecode_bytes(1, a.N, a.K) +
                                        xdecode_bytes(a.M, a.K));
@@ -3081,7 +3179,7 @@ det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s, int marks = MARK_BO
     if (pre) { b.wsig = a.wsig + k0 / V_KC * a.wld; b.wexp32 = a.wexp32 + k0 / V_KC * a.wld; }
     const bool first = ib == 0, last = ib + 1 == nblk;
     b.epi = nblk == 1 ? EPI_ROUND : first ? EPI_STORE : last ? EPI_ADD_ROUND : EPI_ADD;
-    if (pre) {
+    if (pre && nblk > 1) {
       det_status st = predecode_x_block<G, DT>(b, xb, static_cast<char*>(ws) + predecode_bytes(1, a.N, a.K), s);
       if (st != DET_OK) return st;
     }
@@ -3119,54 +3217,6 @@ int64_t slice_bytes(int64_t M, int64_t N, int64_t K) {
          (Kp / SL_KB > SL_FOLD ? 16 * M * N : 0) + 4 * SL_TAIL_CAP * (M + N) + 16 * slice_zfix_outputs(M, N);
 }
 
-// Host choice between the paths: estimated seconds from the accumulator
-// kernels' MAC rate and the int8 MAC rate of the slice pass (both measured
-// on MI355X), S^2 int8 MACs per MAC plus the fallback rows and columns.
-constexpr double RATE_ACC_F32 = 3.4e12, RATE_ACC_BF16 = 5.0e12, RATE_MMA = 1.2e15;
-constexpr double SLICE_MIN_MACS = 134217728.0;    // 2^27: below, the accumulator path alone
-
-// The plan of one call on the device, from the span histograms: the S the
-// cost model prefers (the estimate above; `only`: no accumulator, `forced`:
-// that S alone), the S the call runs (`mode` > 0: that one, fixed by the
-// host; 0: the preferred one), the listed rows and whether their outputs
-// keep their sums (at most `zfix` of them).  One thread.
-struct PlanArgs {
-  const int32_t* hist;                    // x's bins, then w's
-  int32_t* plan;
-  int64_t M, N, K, zfix;
-  double rate_acc;
-  int mode, only, forced;
-};
-
-__global__ __launch_bounds__(64) void k_slice_plan(PlanArgs a) {
-  if (threadIdx.x != 0) return;
-  const int32_t* const hx = a.hist;
-  const int32_t* const hw = a.hist + SL_HIST;
-  const double macs = static_cast<double>(a.M) * a.N * a.K;
-  double best = a.only ? 1e300 : macs / a.rate_acc;
-  int pref = 0;
-  for (int S = SL_MIN; S <= SL_MAX; ++S) {
-    if (a.forced != 0 && S != a.forced) continue;
-    int64_t cx = 0, cw = 0;
-    for (int n = S + 1; n <= SL_MAX + 1; ++n) { cx += hx[n]; cw += hw[n]; }
-    const double t = static_cast<double>(S) * S * macs / RATE_MMA +
-                     (static_cast<double>(cx) * a.N * a.K + static_cast<double>(cw) * a.M * a.K) / a.rate_acc;
-    if (t < best) { best = t; pref = S; }
-  }
-  const int run = a.mode > 0 ? a.mode : pref;
-  int64_t fx = 0, fw = 0;
-  if (run > 0)
-    for (int n = run + 1; n <= SL_MAX + 1; ++n) { fx += hx[n]; fw += hw[n]; }
-  const bool tails = run > 0 && fx + fw > 0 && fx * a.N + fw * a.M <= a.zfix;
-  a.plan[PL_S] = run;
-  a.plan[PL_ACC] = run == 0;
-  a.plan[PL_PREF] = pref;
-  a.plan[PL_TAILS] = tails;
-  a.plan[PL_FX] = static_cast<int32_t>(fx);
-  a.plan[PL_FW] = static_cast<int32_t>(fw);
-  a.plan[PL_OX] = 0;
-  a.plan[PL_OW] = 0;
-}
 
 std::atomic<int> g_path{DET_PATH_AUTO};
 std::atomic<int> g_forced_slices{0};
@@ -3444,7 +3494,8 @@ det_status recompute(GemmArgs a, char* ws, const int32_t* rows, const int32_t* c
 }
 
 // det_gemm with the room for both paths in `ws`: span statistics, then the
-// plan, made on the device (k_slice_plan) so that the host never waits: the
+// plan, made on the device (by k_slice_need's last workgroup) so that the
+// host never waits: the
 // kernels of every path the plan may pick are enqueued, each reading the
 // plan and doing nothing unless it is the one picked.  With `host_choice`
 // (DET_PATH_AUTO_HOST) the host instead waits for the histogram, picks, and
@@ -3483,13 +3534,19 @@ det_status launch_sliced(GemmArgs a, char* ws, bool only_slices, int forced, boo
 
   det_status st = slice_stats<DT>(a, topx, lowx, topw, loww, hist, s);
   if (st != DET_OK) return st;
-  // x's and w's tops, lows and needs are adjacent: one pass over M + N rows
+  int mode = only_slices ? forced : 0;              // > 0: S fixed here
+  PlanArgs pa{};
+  pa.hist = hist; pa.plan = plan;
+  pa.M = M; pa.N = N; pa.K = K; pa.zfix = slice_zfix_outputs(M, N);
+  pa.rate_acc = DT == DET_F32 ? RATE_ACC_F32 : RATE_ACC_BF16;
+  pa.mode = mode; pa.only = only_slices; pa.forced = forced;
+  // x's and w's tops, lows and needs are adjacent: one pass over M + N rows,
+  // whose last workgroup makes the plan (unless the host picks the path)
   hipLaunchKernelGGL(k_slice_need, dim3(grid_for(M + N, 256, 256)), dim3(256), 0, s, topx, lowx, M + N, M, needx,
-                     hist, cntx);
+                     hist, cntx, pa, host_choice ? 0 : 1);
   st = hip_check(hipGetLastError(), "slice need launch");
   if (st != DET_OK) return st;
 
-  int mode = only_slices ? forced : 0;              // > 0: S fixed here
   if (host_choice) {
     int32_t* const h = pinned(g_pin_hist, 2 * SL_HIST);
     if (h == nullptr) return fail(DET_EHIP, "pinned host buffer for the span histogram");
@@ -3508,13 +3565,11 @@ det_status launch_sliced(GemmArgs a, char* ws, bool only_slices, int forced, boo
       return launch_gemm8<DT>(a, ws, s);
     }
   }
-  PlanArgs pa{};
-  pa.hist = hist; pa.plan = plan;
-  pa.M = M; pa.N = N; pa.K = K; pa.zfix = slice_zfix_outputs(M, N);
-  pa.rate_acc = DT == DET_F32 ? RATE_ACC_F32 : RATE_ACC_BF16;
-  pa.mode = mode; pa.only = only_slices; pa.forced = forced;
-  hipLaunchKernelGGL(k_slice_plan, dim3(1), dim3(64), 0, s, pa);
-  st = hip_check(hipGetLastError(), "plan launch");
+  if (host_choice) {
+    pa.mode = mode;
+    hipLaunchKernelGGL(k_slice_plan, dim3(1), dim3(64), 0, s, pa);
+    st = hip_check(hipGetLastError(), "plan launch");
+  }
   if (st == DET_OK) st = log_device_plan(plan, s);
   if (st != DET_OK) return st;
 
