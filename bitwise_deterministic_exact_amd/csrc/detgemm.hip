@@ -1880,7 +1880,7 @@ __global__ __launch_bounds__(256) void k_slice_init(int32_t* top, int32_t* low, 
 // The choice between the paths: estimated seconds from the accumulator
 // kernels' MAC rate and the int8 MAC rate of the slice pass (both measured
 // on MI355X), S^2 int8 MACs per MAC plus the fallback rows and columns.
-constexpr double RATE_ACC_F32 = 3.4e12, RATE_ACC_BF16 = 5.0e12, RATE_MMA = 1.2e15;
+constexpr double RATE_ACC_F32 = 4.5e12, RATE_ACC_BF16 = 5.4e12, RATE_MMA = 1.2e15;
 constexpr double SLICE_MIN_MACS = 134217728.0;    // 2^27: below, the accumulator path alone
 
 // The plan of one call on the device, from the span histograms: the S the
