@@ -36,7 +36,7 @@
  *     passes in); what it keeps on each GPU it runs on are two static device
  *     arrays, det_gemm_noalloc's workspace and the 16-byte status word of
  *     det_device_status, held until the process ends.  Host-side state, per
- *     calling thread and kept until the process ends: a 128-byte pinned
+ *     calling thread and kept until the process ends: a 96-byte pinned
  *     buffer for the span histogram that DET_PATH_AUTO_HOST reads back, and
  *     four 32-byte pinned records with their events for det_last_gemm_plan.
  *   - Strides are in elements, must be >= 0, and may describe transposed or
@@ -178,9 +178,9 @@ det_status det_gemm_ws(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk,
  * the workspace that every later kernel of the call reads), so the host
  * never waits: the call enqueues the kernels of every path the plan may
  * pick, and those not picked exit at once (a gated launch of the
- * accumulator takes 8 tiles per workgroup, so skipping it costs an eighth
- * of a full grid's dispatch).  The rows the accumulator recomputes are
- * counted on the device too.
+ * accumulator takes up to 32 tiles per workgroup, so skipping it costs a
+ * small grid's dispatch).  The rows the accumulator recomputes are counted
+ * on the device too.
  *
  * det_set_gemm_path sets, for the whole process, which path det_gemm_ws
  * takes:
@@ -190,7 +190,7 @@ det_status det_gemm_ws(det_dtype dt, const void* x, int64_t x_sm, int64_t x_sk,
  *                         and the device picks S, or the accumulator path,
  *                         by estimated time
  *   DET_PATH_AUTO_HOST    the same choice made by the host: the call waits
- *                         for the stream to read the 128-byte span histogram
+ *                         for the stream to read the 96-byte span histogram
  *                         (polling an event, so the thread keeps a CPU core
  *                         busy) and enqueues only the path it picks; not for
  *                         graph capture
