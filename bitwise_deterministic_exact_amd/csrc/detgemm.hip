@@ -817,13 +817,17 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, const void* __rest
 
   const int64_t n = n0 + lane;
   const bool n_ok = n < a.N;
-  const int64_t wrow = (n_ok ? n : a.N - 1) * a.w_sn;
+  // raw operands: rows and columns through the maps (pre-decoded ones were
+  // gathered by the decode)
+  const int64_t wn = n_ok ? n : a.N - 1;
+  const int64_t wrow = (!PRE && a.wmap != nullptr ? a.wmap[wn] : wn) * a.w_sn;
   bool row_ok[R];
   int64_t xrow[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     row_ok[r] = m0 + r < a.M;
-    xrow[r] = min(m0 + r, a.M - 1) * a.x_sm;
+    const int64_t mr = min(m0 + r, a.M - 1);
+    xrow[r] = (!PRE && a.xmap != nullptr ? a.xmap[mr] : mr) * a.x_sm;
   }
   const int xj = lane & 15;
   const uint32_t xj4 = static_cast<uint32_t>(xj) * 4u;
@@ -841,7 +845,7 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, const void* __rest
   constexpr int64_t ESZ = DT == DET_F32 ? 4 : 2;
   const char* const xp = static_cast<const char*>(xg) + (xrow[0] + xj * a.x_sk) * ESZ;
   const int64_t xstep = V_KC * a.x_sk * ESZ, xrstep = a.x_sm * ESZ;
-  const bool rows_in = m0 + R <= a.M;             // all R rows exist: rows are x_sm apart
+  const bool rows_in = m0 + R <= a.M && (PRE || a.xmap == nullptr);   // all R rows exist, x_sm apart
   const int32_t* const wsl = a.wsig + n0 * V_KC + lane * 4;       // the lane's sub-block 0 of chunk 0
   const uint32_t* const wel = a.wexp32 + n0 * V_KC + lane * 4;
   auto load = [&](int64_t c, uint32_t (&w)[V_KC], uint32_t (&we)[V_KC], uint32_t (&x)[R], uint32_t (&xw)[R]) {
@@ -3126,7 +3130,8 @@ det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s, int marks = MARK_BO
   const int64_t esz = DT == DET_F32 ? 4 : 2;
   a.w_vec = a.w_sk == 1 && (reinterpret_cast<uintptr_t>(a.w) % 16) == 0 && (a.w_sn * esz) % 16 == 0;
   const bool pre = ws != nullptr && a.K > 0;
-  if (!pre && a.K > 0) {
+  const bool listed = a.mcount != nullptr || a.ncount != nullptr;
+  if (!pre && a.K > 0 && !listed) {               // (listed rows' operands were checked by the span check)
     det_status st = note_raw_operands<DT>(a, s);
     if (st != DET_OK) return st;
   }
@@ -3161,8 +3166,7 @@ det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s, int marks = MARK_BO
   // workgroup's first neither clear LDS nor wait for a rounding.  Tiles per
   // workgroup: a capped grid for device-counted rows or columns, else up to
   // GEMM8_LOOP_TPW, keeping eight workgroups per CU where the tiles allow.
-  const bool listed = a.mcount != nullptr || a.ncount != nullptr;
-  if ((listed || a.gate != nullptr) && !pre) return fail(DET_EINVAL, "a launch decided on the device needs the workspace");
+  if (a.gate != nullptr && !listed && !pre) return fail(DET_EINVAL, "a gated launch needs the workspace");
   const bool loop = listed || a.gate != nullptr || (G::CLAIM && pre);
   a.tpw = listed ? (blocks + GEMM8_LIST_GRID - 1) / GEMM8_LIST_GRID
          : loop   ? std::max<int64_t>(1, std::min(GEMM8_LOOP_TPW, blocks / GEMM8_LOOP_GRID))
@@ -3185,7 +3189,9 @@ det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s, int marks = MARK_BO
     }
     det_status st = mark_event(g_ev_start, (marks & MARK_START) && first, s);
     if (st != DET_OK) return st;
-    if (loop) {
+    if (loop && !pre) {
+      hipLaunchKernelGGL((k_gemm8<G, DT, false, R, W, WPE, true>), grid, block, 0, s, b, xb, a.w);
+    } else if (loop) {
       hipLaunchKernelGGL((k_gemm8<G, DT, true, R, W, WPE, true>), grid, block, 0, s, b, xb, a.w);
     } else if (!pre) {
       hipLaunchKernelGGL((k_gemm8<G, DT, false, R, W, WPE, false>), grid, block, 0, s, b, xb, a.w);
@@ -3482,15 +3488,17 @@ det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s, int marks);
 // The accumulator path on a subset whose size the device decided: the
 // *count rows `rows` of x (and all of w), or the *count rows `cols` of w
 // (and all of x), overwriting those outputs of y; nothing when *count is 0.
+// One launch: the kernel reads the raw operands through the maps (no
+// pre-decode launch, no workspace), which costs a skipped recompute one
+// dispatch instead of three.
 template <int DT>
-det_status recompute(GemmArgs a, char* ws, const int32_t* rows, const int32_t* cols, const int32_t* count,
-                     hipStream_t s) {
+det_status recompute(GemmArgs a, const int32_t* rows, const int32_t* cols, const int32_t* count, hipStream_t s) {
   GemmArgs b = a;
   b.xmap = rows; b.wmap = cols;
   b.gate = count;
   if (rows != nullptr) b.mcount = count;
   else b.ncount = count;
-  return launch_gemm8<DT>(b, ws, s, 0);
+  return launch_gemm8<DT>(b, nullptr, s, 0);
 }
 
 // det_gemm with the room for both paths in `ws`: span statistics, then the
@@ -3644,8 +3652,8 @@ det_status launch_sliced(GemmArgs a, char* ws, bool only_slices, int forced, boo
   hipLaunchKernelGGL((k_slice_fix<DT>), dim3(grid_for(slice_zfix_outputs(M, N), 256, 4096)), dim3(256), 0, s, f);
   st = hip_check(hipGetLastError(), "tail launch");
   // rows and columns the accumulator path recomputes
-  if (st == DET_OK) st = recompute<DT>(a, ws, ovlx, nullptr, plan + PL_OX, s);
-  if (st == DET_OK) st = recompute<DT>(a, ws, nullptr, ovlw, plan + PL_OW, s);
+  if (st == DET_OK) st = recompute<DT>(a, ovlx, nullptr, plan + PL_OX, s);
+  if (st == DET_OK) st = recompute<DT>(a, nullptr, ovlw, plan + PL_OW, s);
   return st;
 }
 
