@@ -151,6 +151,23 @@ def test_many_tails_and_many_listed_outputs(dt):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_recompute_on_views_and_past_one_k_block(dt):
+    # the recompute reads the raw operands through its row and column maps:
+    # transposed and padded views, and K past one 2^15 block in one launch
+    rng = np.random.default_rng(547 + (dt == "bf16"))
+    xb, wb = random_operands(rng, 40, 70, 700, dt, "wide")
+    x, w = to_device(xb, dt), to_device(wb, dt)
+    xt = x.t().contiguous().t()                              # unit M stride
+    wp = to_device(np.ascontiguousarray(np.pad(wb, ((0, 0), (3, 5)))), dt)[:, 3:-5]
+    for xx, ww in ((xt, w), (x, wp), (xt, wp)):
+        plan = _check(xb, wb, dt, 2, "recompute views", x=xx, w=ww)
+        assert plan["fallback_rows"] > 0 and plan["fallback_cols"] > 0
+    xb, wb = random_operands(rng, 5, 6, 40000, dt, "wide")
+    plan = _check(xb, wb, dt, 2, "recompute long K")
+    assert plan["fallback_rows"] > 0
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_k_beyond_one_block(dt):
     # K > 2^14: the 128-bit sums are carried between launches in the workspace
     rng = np.random.default_rng(550 + (dt == "bf16"))
