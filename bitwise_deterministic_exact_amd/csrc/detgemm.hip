@@ -1299,7 +1299,28 @@ struct PredecodeArgs {
   // *gate != 0; N rows from *ncount (Np stays the layout's pitch)
   const int32_t* gate;
   const int32_t* ncount;
+  int vec;                            // unit K stride, rows aligned for 4-element loads (k_predecode_w8)
 };
+
+// four consecutive elements of a row, k .. k+3 (k a multiple of 4): one
+// 16-byte (f32) or 8-byte (bf16) load when all four lie within K, else one
+// at a time with the elements past K zero
+template <int DT>
+__device__ __forceinline__ void load_elem4(const void* base, int64_t row_at, int64_t k, int64_t K, int64_t s_k,
+                                           bool vec, uint32_t (&b)[4]) {
+  if (vec && k + 4 <= K) {
+    if (DT == DET_F32) {
+      const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(base) + row_at + k);
+      b[0] = v.x; b[1] = v.y; b[2] = v.z; b[3] = v.w;
+    } else {
+      const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + row_at + k);
+      b[0] = v.x & 0xFFFFu; b[1] = v.x >> 16; b[2] = v.y & 0xFFFFu; b[3] = v.y >> 16;
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) b[u] = k + u < K ? load_elem<DT>(base, row_at + (k + u) * s_k) : 0u;
+  }
+}
 
 // Element i of a 32-bit array (layout [Kp/16][Np/64][4][64][4]) is (n, k);
 // the 16-bit exponent array of k_gemm is [Kp/16][Np/64][2][64][8].
@@ -1347,6 +1368,28 @@ __device__ __forceinline__ void predecode_w8_body(PredecodeArgs a, int64_t blk, 
   const int64_t total = npd * a.Kp;
   const int64_t stride = nblk * blockDim.x;
   bool bad = false;
+  if (a.vec) {
+    // four consecutive words (one column, four consecutive k) per thread
+    for (int64_t g = blk * blockDim.x + threadIdx.x; g < total / 4; g += stride) {
+      const int64_t j = 4 * g;
+      const int64_t i = npd == a.Np ? j : j / (npd * V_KC) * (a.Np * V_KC) + j % (npd * V_KC);
+      int64_t n, k;
+      subblock_nk(i, a.Np, n, k);
+      uint32_t b[4] = {0u, 0u, 0u, 0u};
+      if (n < a.N) load_elem4<DT>(a.w, (a.rmap != nullptr ? a.rmap[n] : n) * a.w_sn, k, a.K, a.w_sk, true, b);
+      int32_t m[4];
+      uint32_t e[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        bad |= nonfinite_bits<DT>(b[u]);
+        G::decode_w(b[u], static_cast<uint32_t>(n & (V_BN - 1)), m[u], e[u]);
+      }
+      *reinterpret_cast<int4*>(a.wsig + i) = make_int4(m[0], m[1], m[2], m[3]);
+      *reinterpret_cast<uint4*>(static_cast<uint32_t*>(a.wexp) + i) = make_uint4(e[0], e[1], e[2], e[3]);
+    }
+    note_nonfinite(bad);
+    return;
+  }
   for (int64_t j = blk * blockDim.x + threadIdx.x; j < total; j += stride) {
     const int64_t i = npd == a.Np ? j : j / (npd * V_KC) * (a.Np * V_KC) + j % (npd * V_KC);
     int64_t n, k;
@@ -1382,7 +1425,9 @@ struct PredecodeXArgs {
   const int32_t* gate;
   const int32_t* mcount;
   int64_t mround;
+  int vec;                            // unit K stride, rows aligned for 4-element loads
 };
+
 
 template <class D, int DT>
 __device__ __forceinline__ void predecode_x_body(PredecodeXArgs a, int64_t blk, int64_t nblk) {
@@ -1394,6 +1439,30 @@ __device__ __forceinline__ void predecode_x_body(PredecodeXArgs a, int64_t blk, 
   const int64_t total = a.Mp * a.Kp;
   const int64_t stride = nblk * blockDim.x;
   bool bad = false;
+  if (a.vec) {
+    // four consecutive k of one row per thread
+    for (int64_t g = blk * blockDim.x + threadIdx.x; g < total / 4; g += stride) {
+      const int64_t i = 4 * g, m = i / a.Kp, k = i % a.Kp;
+      uint32_t b[4] = {0u, 0u, 0u, 0u};
+      if (m < a.M) load_elem4<DT>(a.x, (a.rmap != nullptr ? a.rmap[m] : m) * a.x_sm, k, a.K, a.x_sk, true, b);
+      int32_t v[4];
+      uint32_t e[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        bad |= nonfinite_bits<DT>(b[u]);
+        D::decode_x(b[u], static_cast<int>(m % D::ROWS), v[u], e[u]);
+      }
+      if constexpr (D::XPACK) {
+        *reinterpret_cast<uint4*>(a.xsig + i) =
+            make_uint4(D::pack_x(v[0], e[0]), D::pack_x(v[1], e[1]), D::pack_x(v[2], e[2]), D::pack_x(v[3], e[3]));
+      } else {
+        *reinterpret_cast<int4*>(a.xsig + i) = make_int4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<uint4*>(a.xword + i) = make_uint4(e[0], e[1], e[2], e[3]);
+      }
+    }
+    note_nonfinite(bad);
+    return;
+  }
   for (int64_t i = blk * blockDim.x + threadIdx.x; i < total; i += stride) {
     const int64_t m = i / a.Kp, k = i % a.Kp;
     const int64_t src = m < a.M && a.rmap != nullptr ? a.rmap[m] : m;
@@ -2996,7 +3065,7 @@ int64_t workspace_bytes(int out_mode, int64_t M, int64_t N, int64_t K) {
 
 // the decode of x's K block [k0, k0 + kb) into the workspace region at
 // `xr` (b.K = kb), and b's pointers to it
-PredecodeXArgs x_decode_args(GemmArgs& b, const void* xblock, char* xr) {
+PredecodeXArgs x_decode_args(GemmArgs& b, const void* xblock, char* xr, int64_t esz) {
   PredecodeXArgs p{};
   p.x = xblock; p.x_sm = b.x_sm; p.x_sk = b.x_sk;
   p.M = b.M; p.K = b.K; p.Mp = round_up(b.M, TILE_ROWS); p.Kp = round_up(b.K, V_KC);
@@ -3004,14 +3073,16 @@ PredecodeXArgs x_decode_args(GemmArgs& b, const void* xblock, char* xr) {
   p.xword = reinterpret_cast<uint32_t*>(xr + p.Mp * p.Kp * 4);
   p.rmap = b.xmap;
   p.gate = b.gate; p.mcount = b.mcount; p.mround = TILE_ROWS;
+  p.vec = b.x_sk == 1 && reinterpret_cast<uintptr_t>(xblock) % (4 * esz) == 0 && (b.x_sm * esz) % (4 * esz) == 0;
   b.xsig = p.xsig; b.xword = p.xword; b.xld = p.Kp;
   return p;
 }
 
 template <class D, int DT>
 det_status predecode_x_block(GemmArgs& b, const void* xblock, char* xr, hipStream_t s) {
-  const PredecodeXArgs p = x_decode_args(b, xblock, xr);
-  hipLaunchKernelGGL((k_predecode_x<D, DT>), dim3(grid_for(p.Mp * p.Kp, 256, 8192)), dim3(256), 0, s, p);
+  const PredecodeXArgs p = x_decode_args(b, xblock, xr, DT == DET_F32 ? 4 : 2);
+  hipLaunchKernelGGL((k_predecode_x<D, DT>), dim3(grid_for(p.Mp * p.Kp / (p.vec ? 4 : 1), 256, 8192)), dim3(256), 0,
+                     s, p);
   return hip_check(hipGetLastError(), "x predecode launch");
 }
 
@@ -3148,10 +3219,11 @@ det_status launch_gemm8(GemmArgs a, void* ws, hipStream_t s, int marks = MARK_BO
     a.wsig = p.wsig; a.wexp32 = static_cast<const uint32_t*>(p.wexp); a.wld = p.Np * V_KC;
     p.rmap = a.wmap;
     p.gate = a.gate; p.ncount = a.ncount;
-    const int64_t nbw = grid_for(p.Np * p.Kp, 256, 8192);
+    p.vec = a.w_sk == 1 && reinterpret_cast<uintptr_t>(a.w) % (4 * esz) == 0 && (a.w_sn * esz) % (4 * esz) == 0;
+    const int64_t nbw = grid_for(p.Np * p.Kp / (p.vec ? 4 : 1), 256, 8192);
     if (nblk == 1) {                              // x's only K block with w, in one launch
-      const PredecodeXArgs px = x_decode_args(a, a.x, static_cast<char*>(ws) + predecode_bytes(1, a.N, a.K));
-      const int64_t nbx = grid_for(px.Mp * px.Kp, 256, 8192);
+      const PredecodeXArgs px = x_decode_args(a, a.x, static_cast<char*>(ws) + predecode_bytes(1, a.N, a.K), esz);
+      const int64_t nbx = grid_for(px.Mp * px.Kp / (px.vec ? 4 : 1), 256, 8192);
       hipLaunchKernelGGL((k_predecode_wx8<G, DT>), dim3(static_cast<unsigned>(nbw + nbx)), dim3(256), 0, s, p, px,
                          nbw);
     } else {
