@@ -51,6 +51,13 @@ def test_one_captured_graph_follows_the_data():
     for kind in ("normal", "wide", "normal", "special"):
         xb, wb = random_operands(rng, M, N, K, "f32", kind)
         cases.append((kind, xb, wb))
+    # N(0,1) with every 7th row of x and 9th of w wide-range: the matrix
+    # cores for the rest, and the device-counted recompute of those rows
+    # (far more than 256 tails each) inside the same graph
+    xn, wn = random_operands(rng, M, N, K, "f32", "normal")
+    xw, ww = random_operands(rng, M, N, K, "f32", "wide")
+    xn[::7], wn[::9] = xw[::7], ww[::9]
+    cases.append(("mixed", xn, wn))
     x = torch.empty(M, K, device="cuda")
     w = torch.empty(N, K, device="cuda")
     y = torch.empty(M, N, device="cuda")
@@ -78,6 +85,11 @@ def test_one_captured_graph_follows_the_data():
             assert np.array_equal(got, eager), mismatch_report(got, eager)
             rr, cc, want = _sampled_oracle(xb, wb)
             assert np.array_equal(got[rr, cc], want)
+    # eager, the mixed operands take the matrix cores with listed rows
+    with det.gemm_path("auto"):
+        det.det_gemm(x, w, check_finite=False)
+        plan = det.last_gemm_plan()
+    assert plan["path"] == "slices" and plan["fallback_rows"] > 0 and plan["fallback_cols"] > 0, plan
 
 
 @pytest.mark.parametrize("dt,kind", [("bf16", "normal"), ("f32", "normal"), ("f32", "wide")])
