@@ -298,12 +298,14 @@ __device__ __forceinline__ int bcast(int v) {     // lane J of each 16-lane row,
 // Workgroups are dispatched to the 8 XCDs round-robin, each XCD with its own
 // L2.  Give every XCD a contiguous range of tiles in column-major tile order,
 // so the workgroups resident on one XCD share one 64-column slice of w (kept
-// in that L2) while they walk down the rows.
-__device__ __forceinline__ int64_t xcd_tile() {
-  const int64_t nb = gridDim.x, b = blockIdx.x;
+// in that L2) while they walk down the rows.  xcd_tile_of(n): the same over
+// the first n workgroups of a larger grid (blockIdx.x < n).
+__device__ __forceinline__ int64_t xcd_tile_of(int64_t nb) {
+  const int64_t b = blockIdx.x;
   const int64_t xcd = b % 8, per = nb / 8, extra = nb % 8;
   return xcd * per + min(xcd, extra) + b / 8;
 }
+__device__ __forceinline__ int64_t xcd_tile() { return xcd_tile_of(gridDim.x); }
 
 // ---------------------------------------------------------------- raw-digit kernel (det_gemm_partial)
 //
@@ -2668,12 +2670,12 @@ __device__ __forceinline__ void slice_steps(const v4i (&fa)[S][2], const v4i (&f
         }
 }
 
+// one workgroup's tile of the pass (`tile` in the XCD-aware order), with
+// SliceTile<S, CB, WR, NBUF>::LDS_BYTES of LDS at `lds`
 template <int S, int CB, int WR, int NBUF>
-__global__ __launch_bounds__(128 * WR, S >= 7 ? 1 : 2) void k_slice_mma(SliceMmaArgs a) {
+__device__ __forceinline__ void slice_mma_tile(SliceMmaArgs a, int8_t* lds, int64_t tile) {
   using T = SliceTile<S, CB, WR, NBUF>;
   constexpr int NG = T::NG, NW = T::NW, FA = T::FA, FT = T::FT, PW = T::PER_WAVE;
-  __shared__ __align__(16) int8_t lds[T::LDS_BYTES];
-  if (a.plan[PL_S] != S) return;
   const bool tails = a.plan[PL_TAILS] != 0;
   a.zc = a.zr + 2 * static_cast<int64_t>(a.plan[PL_FX]) * a.N;      // column sums follow the row sums
   const int lane = threadIdx.x & 63;
@@ -2683,7 +2685,6 @@ __global__ __launch_bounds__(128 * WR, S >= 7 ? 1 : 2) void k_slice_mma(SliceMma
   // workgroups resident on one XCD (consecutive in its range) cover about
   // 8 x 8 tiles, so each x and w fragment is fetched into that XCD's L2 once
   // for 8 workgroups
-  const int64_t tile = xcd_tile();
   const int64_t gsz = 8 * a.tiles_n, grp = tile / gsz, rows_g = min<int64_t>(8, a.tiles_m - 8 * grp);
   const int64_t tm = 8 * grp + (tile % gsz) % rows_g, tn = (tile % gsz) / rows_g;
   const int64_t rbw = 2 * WR * tm;                              // the workgroup's first 16-row block
@@ -2781,6 +2782,54 @@ __global__ __launch_bounds__(128 * WR, S >= 7 ? 1 : 2) void k_slice_mma(SliceMma
         }
         asm volatile("" ::: "memory");          // one output at a time
       }
+  }
+}
+
+template <int S, int CB, int WR, int NBUF>
+__global__ __launch_bounds__(128 * WR, S >= 7 ? 1 : 2) void k_slice_mma(SliceMmaArgs a) {
+  __shared__ __align__(16) int8_t lds[SliceTile<S, CB, WR, NBUF>::LDS_BYTES];
+  if (a.plan[PL_S] != S) return;
+  slice_mma_tile<S, CB, WR, NBUF>(a, lds, xcd_tile());
+}
+
+// Products of at most 512 tiles of 64 x 64 when the device's plan picks S:
+// the shapes of S = 2 .. 6 in one launch (S = 7, which needs one workgroup
+// per CU, keeps its own), so that the digit counts the plan did not pick
+// cost one launch, not five.  Each shape is the narrow-tile one of
+// launch_mma (16-column blocks halved), with the tile count of its own shape;
+// the grid is the largest of them and the workgroups past a shape's count
+// exit.
+constexpr int SMALL_CB[8] = {0, 0, 2, 1, 1, 1, 1, 0};
+constexpr int small_lds_bytes() {
+  int m = 0;
+  for (int S = 2; S <= 6; ++S) {
+    const int b = 2 * (4 * S + 2 * SMALL_CB[S] * S) * 1024;
+    m = b > m ? b : m;
+  }
+  return m;
+}
+constexpr int SMALL_LDS_BYTES = small_lds_bytes();
+
+template <int S>
+__device__ __forceinline__ void slice_mma_small(SliceMmaArgs a, int8_t* lds) {
+  constexpr int CB = SMALL_CB[S];
+  static_assert(SliceTile<S, CB, 2, 2>::LDS_BYTES <= SMALL_LDS_BYTES, "LDS");
+  a.tiles_m = (a.M + 127) / 128 * 2;
+  a.tiles_n = (a.N + 32 * CB - 1) / (32 * CB);
+  const int64_t n = a.tiles_m * a.tiles_n;
+  if (static_cast<int64_t>(blockIdx.x) >= n) return;
+  slice_mma_tile<S, CB, 2, 2>(a, lds, xcd_tile_of(n));
+}
+
+__global__ __launch_bounds__(256, 2) void k_slice_mma_small(SliceMmaArgs a) {
+  __shared__ __align__(16) int8_t lds[SMALL_LDS_BYTES];
+  switch (a.plan[PL_S]) {
+    case 2: slice_mma_small<2>(a, lds); break;
+    case 3: slice_mma_small<3>(a, lds); break;
+    case 4: slice_mma_small<4>(a, lds); break;
+    case 5: slice_mma_small<5>(a, lds); break;
+    case 6: slice_mma_small<6>(a, lds); break;
+    default: break;
   }
 }
 
@@ -3425,6 +3474,26 @@ template <> struct SliceShape<5> { static constexpr int CB = 1, WR = 2, NBUF = 2
 template <> struct SliceShape<6> { static constexpr int CB = 1, WR = 2, NBUF = 2; };
 template <> struct SliceShape<7> { static constexpr int CB = 1, WR = 2, NBUF = 2; };
 
+// the launches of one pass over K, in blocks of 2^14 k (SL_FOLD steps) so
+// that each int32 sum stays below 2^31: `go(b)` launches block b
+template <class Go>
+det_status launch_mma_kblocks(const SliceMmaArgs& m, hipStream_t s, int marks, Go go) {
+  const int64_t nblk = (m.Kb + SL_FOLD - 1) / SL_FOLD;
+  for (int64_t ib = 0; ib < nblk; ++ib) {
+    SliceMmaArgs b = m;
+    b.kb0 = ib * SL_FOLD;
+    b.kb1 = min(m.Kb, b.kb0 + SL_FOLD);
+    b.epi = nblk == 1 ? EPI_ROUND : ib == 0 ? EPI_STORE : ib + 1 == nblk ? EPI_ADD_ROUND : EPI_ADD;
+    det_status st = mark_event(g_ev_start, (marks & MARK_START) && ib == 0, s);
+    if (st != DET_OK) return st;
+    go(b);
+    st = hip_check(hipGetLastError(), "slice mma launch");
+    if (st == DET_OK) st = mark_event(g_ev_stop, (marks & MARK_STOP) && ib + 1 == nblk, s);
+    if (st != DET_OK) return st;
+  }
+  return DET_OK;
+}
+
 template <int S, int CB>
 det_status launch_mma_cb(SliceMmaArgs m, hipStream_t s, int marks) {
   using Sh = SliceShape<S>;
@@ -3435,21 +3504,9 @@ det_status launch_mma_cb(SliceMmaArgs m, hipStream_t s, int marks) {
   const int64_t blocks = m.tiles_m * m.tiles_n;
   if (blocks > 0x7FFFFFFF) return fail(DET_EINVAL, "too many output tiles");
   const dim3 grid(static_cast<unsigned>(blocks)), block(128 * WR);
-  // K blocks of 2^14 (SL_FOLD steps): each int32 sum stays below 2^31
-  const int64_t nblk = (m.Kb + SL_FOLD - 1) / SL_FOLD;
-  for (int64_t ib = 0; ib < nblk; ++ib) {
-    SliceMmaArgs b = m;
-    b.kb0 = ib * SL_FOLD;
-    b.kb1 = min(m.Kb, b.kb0 + SL_FOLD);
-    b.epi = nblk == 1 ? EPI_ROUND : ib == 0 ? EPI_STORE : ib + 1 == nblk ? EPI_ADD_ROUND : EPI_ADD;
-    det_status st = mark_event(g_ev_start, (marks & MARK_START) && ib == 0, s);
-    if (st != DET_OK) return st;
+  return launch_mma_kblocks(m, s, marks, [&](const SliceMmaArgs& b) {
     hipLaunchKernelGGL((k_slice_mma<S, CB, WR, NBUF>), grid, block, 0, s, b);
-    st = hip_check(hipGetLastError(), "slice mma launch");
-    if (st == DET_OK) st = mark_event(g_ev_stop, (marks & MARK_STOP) && ib + 1 == nblk, s);
-    if (st != DET_OK) return st;
-  }
-  return DET_OK;
+  });
 }
 
 // A product with at most 1024 tiles of the regular shape leaves slots of the
@@ -3465,6 +3522,27 @@ det_status launch_mma(SliceMmaArgs m, hipStream_t s, int marks) {
     if (tiles <= 1024) return launch_mma_cb<S, CB / 2>(m, s, marks);
   }
   return launch_mma_cb<S, CB>(m, s, marks);
+}
+
+// Whether S = 2 .. 6 go in one launch of k_slice_mma_small: every S takes
+// the narrow tiles of launch_mma (at most 1024 tiles of 64 x 64), and the
+// product is small enough that the launches saved outweigh the merged
+// kernel's lower occupancy (its registers are those of S = 6: two
+// workgroups per CU where S = 4 alone fits three).  Measured on bf16 N(0,1):
+// 1024^3 84 -> 72 us per call, 512^3 61 -> 52 us; 2048^3 (1024 tiles)
+// 192 -> 196 us, so it keeps a launch per S.
+bool mma_small(int64_t M, int64_t N) { return slice_rows_x(M) / 64 * ((N + 63) / 64) <= 512; }
+
+det_status launch_mma_small(SliceMmaArgs m, hipStream_t s, int marks) {
+  static_assert(SL_MIN == 2 && SL_MAX == 7, "k_slice_mma_small holds S = 2 .. 6");
+  static_assert(SliceShape<2>::CB == 2 * SMALL_CB[2] && SliceShape<3>::CB == 2 * SMALL_CB[3] &&
+                SliceShape<4>::CB == 2 * SMALL_CB[4] && SliceShape<5>::CB == SMALL_CB[5] &&
+                SliceShape<6>::CB == SMALL_CB[6], "the narrow shapes of launch_mma");
+  const int64_t blocks = slice_rows_x(m.M) / 64 * ((m.N + 31) / 32);     // the largest count: 32 columns
+  const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+  return launch_mma_kblocks(m, s, marks, [&](const SliceMmaArgs& b) {
+    hipLaunchKernelGGL(k_slice_mma_small, grid, block, 0, s, b);
+  });
 }
 
 // one operand's span-check arguments and its block count
@@ -3698,7 +3776,12 @@ det_status launch_sliced(GemmArgs a, char* ws, bool only_slices, int forced, boo
   // timing interval runs from the first to the last
   const int s_lo = mode > 0 ? mode : (forced != 0 ? forced : SL_MIN);
   const int s_hi = mode > 0 ? mode : (forced != 0 ? forced : SL_MAX);
-  for (int S = s_lo; S <= s_hi && st == DET_OK; ++S) {
+  int s_next = s_lo;
+  if (s_lo == SL_MIN && s_hi == SL_MAX && mma_small(M, N)) {     // S = 2 .. 6 in one launch
+    st = launch_mma_small(m, s, acc_alt ? 0 : MARK_START);
+    s_next = SL_MAX;
+  }
+  for (int S = s_next; S <= s_hi && st == DET_OK; ++S) {
     const int marks = acc_alt ? 0 : (S == s_lo ? MARK_START : 0) | (S == s_hi ? MARK_STOP : 0);
     switch (S) {
       case 2: st = launch_mma<2>(m, s, marks); break;

@@ -185,6 +185,47 @@ def test_chosen_digits_on_normal_data():
         assert 2 <= plan["slices"] <= 7
 
 
+def _rows_needing(rng, R, K, S, dt):
+    """R rows of K values in which every row needs exactly S digits: its top
+    set bit lies 8S - 4 bits above its lowest (one element 2^(8S-4), one 1,
+    the others 8-bit integers scaled inside that window, random signs, some
+    zeros), all scaled by 2^-20."""
+    span = 8 * S - 4
+    m = rng.integers(1, 256, size=(R, K)).astype(np.float64)
+    e = rng.integers(0, span - 7 + 1, size=(R, K))
+    v = np.ldexp(m, e) * rng.choice([-1.0, 1.0], size=(R, K))
+    v[rng.random((R, K)) < 0.1] = 0.0
+    cols = rng.permuted(np.tile(np.arange(K), (R, 1)), axis=1)
+    v[np.arange(R), cols[:, 0]] = 2.0 ** span
+    v[np.arange(R), cols[:, 1]] = -1.0
+    a = np.ldexp(v, -20).astype(np.float32)
+    bits = np_f32_bits(a) if dt == "f32" else to_bf16_bits(a)
+    assert np.array_equal(_needs(bits, dt), np.full(R, S))
+    return bits
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("path", ["auto", "slices"])
+def test_device_plan_picks_each_digit_count(path, dt):
+    # every row of x and w needs exactly S digits, so the plan made on the
+    # device picks that S, at sizes where one launch holds S = 2 .. 6 and at
+    # one past them (a launch per S), and with K past one 2^14 block; auto
+    # considers the matrix cores from 2^27 MACs on
+    rng = np.random.default_rng(565 + 2 * (path == "auto") + (dt == "bf16"))
+    M, N, K = (600, 500, 600) if path == "auto" else (70, 130, 100)
+    cases = [(S, M, N, K) for S in range(2, 8)] + [(5, 2100, 2100, 64), (3, 130, 70, 17000)]
+    for S, M, N, K in cases:
+        xb, wb = _rows_needing(rng, M, K, S, dt), _rows_needing(rng, N, K, S, dt)
+        announce(f"device plan {path} {dt} S={S} M={M} N={N} K={K}")
+        x, w = to_device(xb, dt), to_device(wb, dt)
+        det.set_gemm_path(path, 0)
+        got = f32_bits(det.det_gemm(x, w))
+        plan = det.last_gemm_plan()
+        assert plan == {"path": "slices", "slices": S, "fallback_rows": 0, "fallback_cols": 0}, plan
+        want = c_oracle.gemm(xb, wb)
+        assert np.array_equal(got, want), mismatch_report(got, want)
+
+
 def _row_scaled(rng, M, K, emin, emax, spread, dt):
     """Rows of N(0,1)-like values with few significant bits, each row scaled
     by its own power of two: narrow spans at extreme magnitudes."""
