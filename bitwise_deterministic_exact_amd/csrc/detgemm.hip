@@ -1238,11 +1238,12 @@ __device__ __forceinline__ void gemm8_claim_tiles(const GemmArgs& a, int t0, int
 
 // det_gemm: one workgroup per tile in the XCD-aware order.  LOOP: each
 // workgroup takes tpw consecutive tiles of that order, with M and N from the
-// device counts if given: the launches whose work the device decides (a
-// gated one, whose skipped workgroups then cost a tpw-th of a full grid's
-// dispatch, and the recompute of device-counted rows or columns).  Between
-// tiles a barrier: waves 0 and 1 read the digit array over the cells while
-// the others would clear them.
+// device counts if given: every pre-decoded launch of the claiming (f32)
+// kernel (gemm8_claim_tiles), and the launches whose work the device decides
+// (a gated one, whose skipped workgroups then cost a tpw-th of a full grid's
+// dispatch, and the recompute of device-counted rows or columns).  In
+// gemm8_tile's loop a barrier sits between tiles: waves 0 and 1 read the
+// digit array over the cells while the others would clear them.
 template <class G, int DT, bool PRE, int R, int W, int WPE, bool LOOP>
 __global__ __launch_bounds__(64 * W, WPE) void k_gemm8(GemmArgs a, const void* __restrict__ xg,
                                                        const void* __restrict__ wg) {
