@@ -949,7 +949,9 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, const void* __rest
     }
     int got = 0;
     if (lane == 0) got = atomicAdd(&claim, 1);
-    int nxt = __shfl(got, 0);
+    // lane 0's claim, as a scalar: the chunk's addresses are then scalar
+    // arithmetic, where a shuffle would leave them to per-lane 64-bit VALU work
+    int nxt = __builtin_amdgcn_readfirstlane(got);
 #pragma unroll 1
     for (;;) {
 #pragma unroll
@@ -960,7 +962,7 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, const void* __rest
         compute(e0 + cur, sl);
         if (nxt >= lim) return;
         cur = nxt;
-        nxt = __shfl(pend, 0);
+        nxt = __builtin_amdgcn_readfirstlane(pend);
       }
     }
   };
@@ -1111,7 +1113,9 @@ __device__ __forceinline__ void gemm8_claim_tiles(const GemmArgs& a, int t0, int
     if (cur >= lim) return;
     int got = 0;
     if (lane == 0) got = atomicAdd(&claim, 1);
-    int nxt = __shfl(got, 0);
+    // lane 0's claim, as a scalar: the chunk's addresses are then scalar
+    // arithmetic, where a shuffle would leave them to per-lane 64-bit VALU work
+    int nxt = __builtin_amdgcn_readfirstlane(got);
     // (the last chunk's products are written out apart, so that the other
     // slot is read only on the path that loaded it: the compiler then keeps
     // no ring slot but slot 0 live across tiles)
@@ -1126,7 +1130,7 @@ __device__ __forceinline__ void gemm8_claim_tiles(const GemmArgs& a, int t0, int
       load(m0, n0, e0 + nxt, wq[sl ^ 1], weq[sl ^ 1], xwq[sl ^ 1]);
       compute(m0, e0 + cur, sl);
       cur = nxt;
-      nxt = __shfl(pend, 0);
+      nxt = __builtin_amdgcn_readfirstlane(pend);
       return false;
     };
 #pragma unroll 1
