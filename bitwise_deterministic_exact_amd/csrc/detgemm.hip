@@ -723,6 +723,23 @@ __device__ __forceinline__ void load_w_pre8(const GemmArgs& a, const int32_t* ws
   }
 }
 
+// The workgroup's chunk counter, through a register that the compiler cannot
+// see is the same in every lane.  lane 0's add on it then stays a single
+// ds_add_rtn_u32; on a visibly uniform address the compiler wraps the add in
+// a wave-wide count of the active lanes (about six vector instructions).
+__device__ __forceinline__ int* claim_counter(int& claim) {
+  uint32_t z = 0;
+  asm volatile("" : "+v"(z));
+  return &claim + z;
+}
+
+// lane 0 takes the next chunk from the counter; the other lanes get 0
+__device__ __forceinline__ int claim_chunk(int* counter, uint32_t lane) {
+  int got = 0;
+  if (lane == 0) got = atomicAdd(counter, 1);
+  return got;
+}
+
 // One chunk: step J takes x element J of each row (DPP broadcast from lane J
 // of every 16-lane row) and the lane's w element J.
 template <class G, int DT, bool PRE, int R, int J>
@@ -947,17 +964,15 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, const void* __rest
         if (slot(std::integral_constant<int, 1>{})) return;
       }
     }
-    int got = 0;
-    if (lane == 0) got = atomicAdd(&claim, 1);
+    int* const counter = claim_counter(claim);
     // lane 0's claim, as a scalar: the chunk's addresses are then scalar
     // arithmetic, where a shuffle would leave them to per-lane 64-bit VALU work
-    int nxt = __builtin_amdgcn_readfirstlane(got);
+    int nxt = __builtin_amdgcn_readfirstlane(claim_chunk(counter, static_cast<uint32_t>(lane)));
 #pragma unroll 1
     for (;;) {
 #pragma unroll
       for (int sl = 0; sl < 2; ++sl) {
-        int pend = 0;
-        if (lane == 0 && nxt < lim) pend = atomicAdd(&claim, 1);
+        const int pend = nxt < lim ? claim_chunk(counter, static_cast<uint32_t>(lane)) : 0;
         if (nxt < lim) load(e0 + nxt, wq[sl ^ 1], weq[sl ^ 1], xq[sl ^ 1], xwq[sl ^ 1]);
         compute(e0 + cur, sl);
         if (nxt >= lim) return;
@@ -1064,6 +1079,7 @@ __device__ __forceinline__ void gemm8_claim_tiles(const GemmArgs& a, int t0, int
   int tid, lane, wave;
   uint32_t xj4, lane_off;
   char* my_cells;
+  int* counter;
   auto derive = [&]() {
     asm volatile("" : "+s"(wave0));
     wave = wave0;
@@ -1074,6 +1090,7 @@ __device__ __forceinline__ void gemm8_claim_tiles(const GemmArgs& a, int t0, int
     xj4 = static_cast<uint32_t>(lane & 15) * 4u;
     lane_off = static_cast<uint32_t>(lane * G::ES);
     my_cells = cells + (G::ALLOC - G::NCELL + wave * CW) * G::CS + lane * G::ES;
+    counter = claim_counter(claim);
   };
 
   uint32_t wq[2][V_KC], weq[2][V_KC], xwq[2][R];
@@ -1111,11 +1128,9 @@ __device__ __forceinline__ void gemm8_claim_tiles(const GemmArgs& a, int t0, int
     const int lim = min(nchunks - e0, static_cast<int>(EPOCH));
     int cur = wave;
     if (cur >= lim) return;
-    int got = 0;
-    if (lane == 0) got = atomicAdd(&claim, 1);
     // lane 0's claim, as a scalar: the chunk's addresses are then scalar
     // arithmetic, where a shuffle would leave them to per-lane 64-bit VALU work
-    int nxt = __builtin_amdgcn_readfirstlane(got);
+    int nxt = __builtin_amdgcn_readfirstlane(claim_chunk(counter, static_cast<uint32_t>(lane)));
     // (the last chunk's products are written out apart, so that the other
     // slot is read only on the path that loaded it: the compiler then keeps
     // no ring slot but slot 0 live across tiles)
@@ -1125,8 +1140,7 @@ __device__ __forceinline__ void gemm8_claim_tiles(const GemmArgs& a, int t0, int
         compute(m0, e0 + cur, sl);
         return true;
       }
-      int pend = 0;
-      if (lane == 0) pend = atomicAdd(&claim, 1);
+      const int pend = claim_chunk(counter, static_cast<uint32_t>(lane));
       load(m0, n0, e0 + nxt, wq[sl ^ 1], weq[sl ^ 1], xwq[sl ^ 1]);
       compute(m0, e0 + cur, sl);
       cur = nxt;
